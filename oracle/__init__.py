@@ -1,0 +1,233 @@
+"""Float64 CPU oracle for the fused causal GQA + RoPE attention forward.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package. The HIP library never calls it and
+shares no code with it; the product path fails when its extension is missing.
+
+What it computes is the plain definition, written out with numpy in float64,
+one (batch, head) at a time, with the full T x T score matrix materialised:
+
+1. RoPE tables ("Embeddings & the Residual Stream", section "Positional
+   information: RoPE"): inv_freq[i] = base^(-2i/d) for i < d/2, and the angle
+   at position p is p * inv_freq[i].
+2. Rotation of Q and K only, never V (same section; "Attention from Scratch",
+   section "Attention, the math", step "Rotate"). Two pairings: "interleaved"
+   rotates the adjacent pairs (2i, 2i+1), as the RoPE prose describes;
+   "half" rotates (i, i + d/2), the x*cos + rotate_half(x)*sin form of the
+   printed helper. See ``apply_rope``.
+3. GQA sharing ("Attention, the math", step "Share"): query head h reads K/V
+   head h // (n_head / n_kv_head), the repeat_interleave order.
+4. Scores q.k * scale with scale = 1/sqrt(d) unless given (step "Score").
+5. Causal mask: key j > query i gets -inf (the lower-triangular mask buffer and
+   step "Mask + softmax"); or no mask.
+6. Softmax over keys with the max shifted out, and the weighted sum of V
+   (steps "Mask + softmax" and "Gather"). The forward also returns the natural
+   log-sum-exp of each row's scaled, masked scores (not on the pages; it is
+   what the row's softmax denominator is, in log form).
+
+Packed variable-length batches (the kohakutt page, Highlights: "packed
+variable-length batches") are the concatenation of independent sequences:
+positions restart at 0 in every sequence and the mask never crosses a
+sequence boundary.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` to results the
+pages and the mathematics fix (closed forms, invariants, a library routine on
+a special case, brute force on tiny inputs).
+"""
+
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "rope_inv_freq",
+    "rope_tables",
+    "apply_rope",
+    "attention_dense",
+    "attention_varlen",
+    "attention_rows",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Upcast a numpy array or a CPU torch tensor (any float dtype) to float64 numpy."""
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        # bf16 has no numpy dtype: go through float32, which holds every bf16 value exactly.
+        x = x.float().numpy() if str(x.dtype) in ("torch.bfloat16", "torch.float16") else x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
+    """inv_freq[i] = base^(-2i/head_dim), i < head_dim/2.
+
+    "Embeddings & the Residual Stream", section "Positional information: RoPE":
+    the angle shrinks with the feature index through this power of the fixed
+    base (theta).
+    """
+    if head_dim % 2:
+        raise ValueError("RoPE needs an even head_dim")
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * i / head_dim)
+
+
+def rope_tables(max_pos: int, head_dim: int, base: float):
+    """cos and sin of angle(p, i) = p * inv_freq[i], each [max_pos, head_dim/2] float64.
+
+    Same section as ``rope_inv_freq``. The page duplicates the half table to
+    full width for its rotate_half form; both pairings here index the half
+    table by pair number instead, which carries the same numbers.
+    """
+    pos = np.arange(max_pos, dtype=np.float64)
+    ang = np.outer(pos, rope_inv_freq(head_dim, base))
+    return np.cos(ang), np.sin(ang)
+
+
+def apply_rope(x, positions, base: float, style: str = "interleaved") -> np.ndarray:
+    """Rotate the last dim of x ([T, ..., d]) at the given positions ([T]).
+
+    Pair i (partners a_i, b_i) turns by angle(p, i):
+        y[a_i] = x[a_i] cos - x[b_i] sin,  y[b_i] = x[a_i] sin + x[b_i] cos.
+    "interleaved": (a_i, b_i) = (2i, 2i+1), "each adjacent pair of features"
+    in the RoPE prose. "half": (a_i, b_i) = (i, i + d/2), which is exactly
+    x*cos + rotate_half(x)*sin with rotate_half(x) = (-x2, x1) and the
+    duplicated half table ("Embeddings & the Residual Stream", printed
+    rotate_half / apply_rope).
+    """
+    x = _f64(x)
+    d = x.shape[-1]
+    pos = np.asarray(positions, dtype=np.float64)
+    ang = np.outer(pos, rope_inv_freq(d, base))  # [T, d/2]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (d // 2,)
+    c = np.cos(ang).reshape(shape)
+    s = np.sin(ang).reshape(shape)
+    y = np.empty_like(x)
+    if style == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+        y[..., 0::2] = a * c - b * s
+        y[..., 1::2] = a * s + b * c
+    elif style == "half":
+        a, b = x[..., : d // 2], x[..., d // 2:]
+        y[..., : d // 2] = a * c - b * s
+        y[..., d // 2:] = a * s + b * c
+    else:
+        raise ValueError(f"unknown rope style {style!r}")
+    return y
+
+
+def _one_sequence(q, k, v, causal: bool, scale: float, base: float, style: str):
+    """Attention for one sequence. q [L, H, d], k/v [L, KV, d] float64.
+
+    Returns O [L, H, d] and lse [H, L]. The score matrix of every head is
+    materialised in full ("Attention, the math": scores, masked_fill, softmax,
+    weights @ v).
+    """
+    L, H, d = q.shape
+    KV = k.shape[1]
+    G = H // KV
+    pos = np.arange(L)
+    qr = apply_rope(q, pos, base, style)
+    kr = apply_rope(k, pos, base, style)
+    O = np.empty((L, H, d), dtype=np.float64)
+    lse = np.empty((H, L), dtype=np.float64)
+    if L == 0:
+        return O, lse
+    future = np.triu(np.ones((L, L), dtype=bool), k=1) if causal else None
+    for h in range(H):
+        kv = h // G  # repeat_interleave: heads of one group are adjacent
+        S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
+        if causal:
+            S[future] = -np.inf
+        m = S.max(axis=1)
+        e = np.exp(S - m[:, None])
+        den = e.sum(axis=1)
+        lse[h] = m + np.log(den)
+        P = e / den[:, None]
+        O[:, h, :] = P @ v[:, kv, :]
+    return O, lse
+
+
+def _check_heads(n_head: int, n_kv_head: int):
+    if n_kv_head < 1 or n_head % n_kv_head:
+        raise ValueError("n_head must be divisible by n_kv_head")
+
+
+def attention_dense(q, k, v, *, causal: bool = True, base: float = 10000.0,
+                    style: str = "interleaved", scale: Optional[float] = None):
+    """Dense batch: q [B,T,H,d], k/v [B,T,KV,d]. Returns O [B,T,H,d], lse [B,H,T] (float64)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, d = q.shape
+    _check_heads(H, k.shape[2])
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    O = np.empty_like(q)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    for b in range(B):
+        O[b], lse[b] = _one_sequence(q[b], k[b], v[b], causal, scale, base, style)
+    return O, lse
+
+
+def attention_varlen(q, k, v, cu_seqlens, *, causal: bool = True, base: float = 10000.0,
+                     style: str = "interleaved", scale: Optional[float] = None):
+    """Packed batch: q [total,H,d], k/v [total,KV,d], cu_seqlens [n+1].
+
+    Each sequence s occupies tokens cu[s]..cu[s+1]-1 and is attended to on its
+    own, positions restarting at 0. Returns O [total,H,d], lse [H,total].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    total, H, d = q.shape
+    _check_heads(H, k.shape[1])
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    O = np.empty_like(q)
+    lse = np.empty((H, total), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style)
+    return O, lse
+
+
+def attention_rows(q, k, v, rows: Sequence, *, causal: bool = True, base: float = 10000.0,
+                   style: str = "interleaved", scale: Optional[float] = None,
+                   cu_seqlens=None):
+    """O and lse of selected output rows only, one row at a time.
+
+    ``rows`` lists (b, t, h) for a dense batch (q [B,T,H,d]) or (s, t, h) for a
+    packed one (t local to sequence s, q [total,H,d] with ``cu_seqlens``).
+    Row (t, h) needs the rotated query at position t and every rotated key of
+    its sequence that the mask allows; nothing else is computed, so sampled
+    checks at full size stay cheap. Returns (O [n, d], lse [n]) float64.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if cu_seqlens is None:
+        H, KV = q.shape[2], k.shape[2]
+    else:
+        H, KV = q.shape[1], k.shape[1]
+        cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    _check_heads(H, KV)
+    G = H // KV
+    outs, lses = [], []
+    for (b, t, h) in rows:
+        if cu_seqlens is None:
+            L = q.shape[1]
+            qrow = q[b, t, h]
+            keys, vals = k[b, :, h // G], v[b, :, h // G]
+        else:
+            a = cu[b]
+            L = cu[b + 1] - a
+            qrow = q[a + t, h]
+            keys, vals = k[a:a + L, h // G], v[a:a + L, h // G]
+        n = t + 1 if causal else L
+        qr = apply_rope(qrow[None, :], [t], base, style)[0]
+        kr = apply_rope(keys[:n], np.arange(n), base, style)
+        s = (kr @ qr) * scale
+        m = s.max()
+        e = np.exp(s - m)
+        den = e.sum()
+        outs.append((e / den) @ vals[:n])
+        lses.append(m + math.log(den))
+    return np.array(outs).reshape(len(rows), d), np.array(lses)

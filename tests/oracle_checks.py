@@ -1,0 +1,388 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each ``check_*`` raises AssertionError when the oracle disagrees with an
+independent statement of the same fact: a closed form, an invariant, a
+special case that reduces to a library routine, or brute force on tiny inputs.
+``test_oracle_pins.py`` runs every check on the oracle as it is, and runs them
+again on copies of the oracle with a planted mistake to show that each
+plausible mistake fails at least one check.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+RNG = np.random.default_rng
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def check_inv_freq_closed_forms():
+    # i = 0 never rotates slower than one radian per position, whatever the base.
+    for base in (10000.0, 500000.0, 1e6):
+        for d in (2, 8, 64, 128):
+            assert oracle.rope_inv_freq(d, base)[0] == 1.0
+    # i = d/4 sits halfway through the exponent range: base^(-1/2).
+    assert abs(oracle.rope_inv_freq(64, 10000.0)[16] - 0.01) < 1e-15
+    assert abs(oracle.rope_inv_freq(128, 1e6)[32] - 0.001) < 1e-16
+    # The last pair's frequency is base^(-(d-2)/d): for d = 4, base^(-1/2).
+    assert abs(oracle.rope_inv_freq(4, 10000.0)[1] - 0.01) < 1e-15
+    f = oracle.rope_inv_freq(128, 500000.0)
+    assert f.shape == (64,) and np.all(np.diff(f) < 0), "angle must shrink with feature index"
+
+
+def check_tables_closed_forms():
+    cos, sin = oracle.rope_tables(301, 64, 10000.0)
+    assert cos.shape == (301, 32) and sin.shape == (301, 32)
+    # Position 0: no rotation at all.
+    assert np.all(cos[0] == 1.0) and np.all(sin[0] == 0.0)
+    # i = 0 turns one radian per position; i = d/4 turns 0.01 rad per position.
+    assert abs(cos[300, 0] - math.cos(300.0)) < 1e-12 and abs(sin[300, 0] - math.sin(300.0)) < 1e-12
+    assert abs(cos[100, 16] - math.cos(1.0)) < 1e-13 and abs(sin[100, 16] - math.sin(1.0)) < 1e-13
+    assert abs(cos[157, 16] - math.cos(1.57)) < 1e-13
+
+
+def check_rope_d2_is_plane_rotation():
+    # With d = 2 both pairings are the single pair (0, 1) and inv_freq = 1, so the
+    # rotation at position p is the textbook 2x2 rotation matrix by p radians.
+    x = RNG(1).standard_normal((7, 3, 2))
+    pos = np.arange(7) * 3 + 1
+    for style in ("interleaved", "half"):
+        y = oracle.apply_rope(x, pos, 10000.0, style)
+        for t, p in enumerate(pos):
+            R = np.array([[math.cos(p), -math.sin(p)], [math.sin(p), math.cos(p)]])
+            assert np.allclose(y[t], x[t] @ R.T, atol=1e-13, rtol=0)
+
+
+def check_rope_interleaved_complex_form():
+    # Interleaved RoPE is multiplication of z_i = x[2i] + 1j*x[2i+1] by exp(1j*p*f_i).
+    d, T = 16, 9
+    x = RNG(2).standard_normal((T, 2, d))
+    pos = np.arange(T) * 37
+    f = 10000.0 ** (-np.arange(0, d, 2) / d)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    w = z * np.exp(1j * np.outer(pos, f))[:, None, :]
+    y = oracle.apply_rope(x, pos, 10000.0, "interleaved")
+    assert np.allclose(y[..., 0::2], w.real, atol=1e-12, rtol=0)
+    assert np.allclose(y[..., 1::2], w.imag, atol=1e-12, rtol=0)
+
+
+def check_rope_half_matches_rotate_half_form():
+    # The printed helper: duplicate the half-width angle table to full width and
+    # compute x*cos + rotate_half(x)*sin with rotate_half(x) = (-x2, x1).
+    d, T = 12, 11
+    x = RNG(3).standard_normal((T, 3, d))
+    pos = np.arange(T)
+    f = 500000.0 ** (-np.arange(0, d, 2) / d)
+    ang = np.outer(pos, f)
+    full = np.concatenate([ang, ang], axis=-1)[:, None, :]
+    rot_half = np.concatenate([-x[..., d // 2:], x[..., : d // 2]], axis=-1)
+    want = x * np.cos(full) + rot_half * np.sin(full)
+    got = oracle.apply_rope(x, pos, 500000.0, "half")
+    assert np.allclose(got, want, atol=1e-12, rtol=0)
+
+
+def check_rope_norm_and_identity():
+    d = 64
+    x = RNG(4).standard_normal((300, 2, d))
+    pos = np.arange(300)
+    for style, (ia, ib) in (("interleaved", (np.arange(0, d, 2), np.arange(1, d, 2))),
+                            ("half", (np.arange(d // 2), np.arange(d // 2, d)))):
+        y = oracle.apply_rope(x, pos, 10000.0, style)
+        n0 = x[..., ia] ** 2 + x[..., ib] ** 2
+        n1 = y[..., ia] ** 2 + y[..., ib] ** 2
+        assert np.allclose(n0, n1, atol=1e-12, rtol=1e-12), "each pair keeps its length"
+        assert np.array_equal(y[0], x[0]), "position 0 is the identity"
+        assert not np.allclose(y[5], x[5]), "later positions rotate"
+
+
+def check_rope_relative():
+    # (R(m) q) . (R(n) k) depends only on n - m.
+    d = 32
+    rng = RNG(5)
+    q, k = rng.standard_normal(d), rng.standard_normal(d)
+    for style in ("interleaved", "half"):
+        def dot(m, n):
+            qr = oracle.apply_rope(q[None, :], [m], 10000.0, style)[0]
+            kr = oracle.apply_rope(k[None, :], [n], 10000.0, style)[0]
+            return float(qr @ kr)
+        for (m, n, c) in ((3, 10, 100), (0, 0, 4000), (77, 5, 8191), (1000, 999, 17)):
+            assert abs(dot(m, n) - dot(m + c, n + c)) < 1e-9
+            # and equals q . R(n - m) k
+            kr = oracle.apply_rope(k[None, :], [n - m], 10000.0, style)[0]
+            assert abs(dot(m, n) - float(q @ kr)) < 1e-9
+
+
+def deinterleave(x):
+    """Permute the last dim so interleaved pair i (2i, 2i+1) lands on (i, i + d/2)."""
+    return np.concatenate([x[..., 0::2], x[..., 1::2]], axis=-1)
+
+
+def check_rope_styles_related_by_permutation():
+    rng = RNG(6)
+    q = rng.standard_normal((2, 20, 4, 16))
+    k = rng.standard_normal((2, 20, 2, 16))
+    v = rng.standard_normal((2, 20, 2, 16))
+    o_int, l_int = oracle.attention_dense(q, k, v, base=10000.0, style="interleaved")
+    o_half, l_half = oracle.attention_dense(deinterleave(q), deinterleave(k), v, base=10000.0,
+                                            style="half")
+    assert np.allclose(o_int, o_half, atol=1e-12) and np.allclose(l_int, l_half, atol=1e-12)
+    o_bad, _ = oracle.attention_dense(q, k, v, base=10000.0, style="half")
+    assert not np.allclose(o_int, o_bad, atol=1e-3), "the pairing must matter"
+
+
+# ------------------------------------------------------------------------ attention
+
+def brute_force(q, k, v, causal, base, style, scale=None):
+    """Scalar loops over Python floats: rotate, share, score, mask, softmax, gather.
+
+    Follows the six steps of "Attention from Scratch", section "Attention, the
+    math", for one batch entry at a time, with no vectorisation and no
+    max-shift (the inputs are small enough that exp cannot overflow).
+    q [B][T][H][d], k/v [B][T][KV][d] nested lists.
+    """
+    B, T, H, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    KV = len(k[0][0])
+    G = H // KV
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+
+    def rot(x, p):
+        y = list(x)
+        for i in range(d // 2):
+            ang = p * base ** (-(2.0 * i) / d)
+            a, b = (2 * i, 2 * i + 1) if style == "interleaved" else (i, i + d // 2)
+            y[a] = x[a] * math.cos(ang) - x[b] * math.sin(ang)
+            y[b] = x[a] * math.sin(ang) + x[b] * math.cos(ang)
+        return y
+
+    O = [[[[0.0] * d for _ in range(H)] for _ in range(T)] for _ in range(B)]
+    L = [[[0.0] * T for _ in range(H)] for _ in range(B)]
+    for b in range(B):
+        for h in range(H):
+            g = h // G
+            for i in range(T):
+                qi = rot(q[b][i][h], i)
+                w = []
+                for j in range(T):
+                    if causal and j > i:
+                        w.append(0.0)
+                        continue
+                    kj = rot(k[b][j][g], j)
+                    w.append(math.exp(sc * sum(qi[c] * kj[c] for c in range(d))))
+                z = sum(w)
+                L[b][h][i] = math.log(z)
+                for c in range(d):
+                    O[b][i][h][c] = sum(w[j] * v[b][j][g][c] for j in range(T)) / z
+    return np.array(O), np.array(L)
+
+
+def check_brute_force():
+    rng = RNG(7)
+    for (B, T, H, KV, d, causal, style, base) in (
+            (2, 9, 4, 2, 8, True, "interleaved", 10000.0),
+            (1, 12, 4, 2, 8, False, "interleaved", 500000.0),
+            (1, 10, 3, 1, 6, True, "half", 1e6),
+            (2, 7, 2, 2, 4, False, "half", 10000.0)):
+        q = rng.standard_normal((B, T, H, d))
+        k = rng.standard_normal((B, T, KV, d))
+        v = rng.standard_normal((B, T, KV, d))
+        o_ref, l_ref = brute_force(q.tolist(), k.tolist(), v.tolist(), causal, base, style)
+        o, lse = oracle.attention_dense(q, k, v, causal=causal, base=base, style=style)
+        assert np.allclose(o, o_ref, atol=1e-12, rtol=0), (B, T, H, KV, d, causal, style)
+        assert np.allclose(lse, l_ref, atol=1e-12, rtol=0)
+
+
+def check_library_sdpa():
+    # After rotation, the rest is scaled-dot-product attention: cross-check the
+    # score/mask/softmax/gather part against torch's float64 CPU routine (GQA
+    # sharing through enable_gqa), and the log-sum-exp against scipy's.
+    from scipy.special import logsumexp
+    rng = RNG(8)
+    B, T, H, KV, d = 2, 33, 6, 2, 16
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, T, KV, d))
+    v = rng.standard_normal((B, T, KV, d))
+    for causal in (True, False):
+        o, lse = oracle.attention_dense(q, k, v, causal=causal, base=10000.0)
+        pos = np.arange(T)
+        qr = np.stack([oracle.apply_rope(q[b], pos, 10000.0) for b in range(B)])
+        kr = np.stack([oracle.apply_rope(k[b], pos, 10000.0) for b in range(B)])
+        tq = torch.from_numpy(qr).permute(0, 2, 1, 3)
+        tk = torch.from_numpy(kr).permute(0, 2, 1, 3)
+        tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, enable_gqa=True).permute(0, 2, 1, 3).numpy()
+        assert np.allclose(o, ref, atol=1e-12, rtol=0)
+        for b in range(B):
+            for h in range(H):
+                S = qr[b, :, h] @ kr[b, :, h // (H // KV)].T / math.sqrt(d)
+                if causal:
+                    S = np.where(np.tril(np.ones((T, T), bool)), S, -np.inf)
+                assert np.allclose(lse[b, h], logsumexp(S, axis=1), atol=1e-12, rtol=0)
+
+
+def check_softmax_rows():
+    # With V[j] = e_j (d >= T) the output rows are the softmax weights themselves:
+    # rows sum to one, nothing above the diagonal, and P = exp(S - lse).
+    T, d = 16, 16
+    rng = RNG(9)
+    q = rng.standard_normal((1, T, 2, d))
+    k = rng.standard_normal((1, T, 1, d))
+    v = np.eye(T, d)[None, :, None, :]
+    for causal in (True, False):
+        o, lse = oracle.attention_dense(q, k, v, causal=causal, base=10000.0)
+        P = o[0]  # [T, H, d]
+        assert np.allclose(P.sum(axis=-1), 1.0, atol=1e-14)
+        if causal:
+            assert np.all(P[np.triu_indices(T, 1)[0], :, np.triu_indices(T, 1)[1]] == 0.0)
+        pos = np.arange(T)
+        qr = oracle.apply_rope(q[0], pos, 10000.0)
+        kr = oracle.apply_rope(k[0], pos, 10000.0)
+        for h in range(2):
+            S = qr[:, h] @ kr[:, 0].T / math.sqrt(d)
+            want = np.exp(S - lse[0, h][:, None])
+            if causal:
+                want = np.tril(want)
+            assert np.allclose(P[:, h, :], want, atol=1e-14)
+
+
+def check_causal_row0():
+    rng = RNG(10)
+    q = rng.standard_normal((3, 25, 8, 32))
+    k = rng.standard_normal((3, 25, 2, 32))
+    v = rng.standard_normal((3, 25, 2, 32))
+    o, lse = oracle.attention_dense(q, k, v, causal=True, base=500000.0)
+    for h in range(8):
+        assert np.array_equal(o[:, 0, h], v[:, 0, h // 4]), "row 0 sees only key 0 of its KV head"
+        want = np.einsum("bd,bd->b", q[:, 0, h], k[:, 0, h // 4]) / math.sqrt(32)
+        assert np.allclose(lse[:, h, 0], want, atol=1e-13, rtol=0)
+
+
+def check_gqa_is_mha_with_repeat_interleave():
+    rng = RNG(11)
+    G = 3
+    q = rng.standard_normal((2, 19, 6, 8))
+    k = rng.standard_normal((2, 19, 2, 8))
+    v = rng.standard_normal((2, 19, 2, 8))
+    o, lse = oracle.attention_dense(q, k, v, base=10000.0)
+    o2, l2 = oracle.attention_dense(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2),
+                                    base=10000.0)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+def check_zero_query_closed_form():
+    # q = 0: every allowed score is 0, so row i averages the values it may see
+    # and its log-sum-exp is ln(#allowed keys), whatever the rotation.
+    rng = RNG(12)
+    T = 40
+    k = rng.standard_normal((1, T, 2, 16))
+    v = rng.standard_normal((1, T, 2, 16))
+    q = np.zeros((1, T, 4, 16))
+    o, lse = oracle.attention_dense(q, k, v, causal=True, base=10000.0)
+    for h in range(4):
+        cm = np.cumsum(v[0, :, h // 2], axis=0) / np.arange(1, T + 1)[:, None]
+        assert np.allclose(o[0, :, h], cm, atol=1e-14)
+        assert np.allclose(lse[0, h], np.log(np.arange(1, T + 1)), atol=1e-14)
+    o, lse = oracle.attention_dense(q, k, v, causal=False, base=10000.0)
+    assert np.allclose(o[0, :, 3], np.broadcast_to(v[0, :, 1].mean(axis=0), (T, 16)), atol=1e-14)
+    assert np.allclose(lse, math.log(T), atol=1e-14)
+
+
+def check_single_token():
+    rng = RNG(13)
+    q = rng.standard_normal((4, 1, 2, 8))
+    k = rng.standard_normal((4, 1, 1, 8))
+    v = rng.standard_normal((4, 1, 1, 8))
+    for causal in (True, False):
+        o, lse = oracle.attention_dense(q, k, v, causal=causal, base=10000.0, scale=0.25)
+        assert np.array_equal(o[:, 0, 0], v[:, 0, 0]) and np.array_equal(o[:, 0, 1], v[:, 0, 0])
+        assert np.allclose(lse[:, 1, 0], 0.25 * np.einsum("bd,bd->b", q[:, 0, 1], k[:, 0, 0]),
+                           atol=1e-14)
+
+
+def check_scale_argument():
+    rng = RNG(14)
+    q = rng.standard_normal((1, 12, 2, 16))
+    k = rng.standard_normal((1, 12, 2, 16))
+    v = rng.standard_normal((1, 12, 2, 16))
+    a = oracle.attention_dense(q, k, v, base=10000.0)
+    b = oracle.attention_dense(q, k, v, base=10000.0, scale=0.25)
+    assert np.allclose(a[0], b[0], atol=1e-14) and np.allclose(a[1], b[1], atol=1e-14)
+    c = oracle.attention_dense(q, k, v, base=10000.0, scale=0.7)
+    d = oracle.attention_dense(q * 0.7 * 4.0, k, v, base=10000.0)
+    assert np.allclose(c[0], d[0], atol=1e-12) and np.allclose(c[1], d[1], atol=1e-12)
+
+
+def check_varlen_is_concat_of_dense():
+    rng = RNG(15)
+    lengths = [5, 1, 0, 17, 9]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    q = rng.standard_normal((total, 4, 8))
+    k = rng.standard_normal((total, 1, 8))
+    v = rng.standard_normal((total, 1, 8))
+    for causal in (True, False):
+        o, lse = oracle.attention_varlen(q, k, v, cu, causal=causal, base=10000.0, style="half")
+        for s, L in enumerate(lengths):
+            a = int(cu[s])
+            if L == 0:
+                continue
+            od, ld = oracle.attention_dense(q[None, a:a + L], k[None, a:a + L], v[None, a:a + L],
+                                            causal=causal, base=10000.0, style="half")
+            assert np.array_equal(o[a:a + L], od[0]) and np.array_equal(lse[:, a:a + L], ld[0])
+        # One brute-force sequence pins the packed indexing directly.
+        a, L = int(cu[3]), lengths[3]
+        ob, lb = brute_force(q[None, a:a + L].tolist(), k[None, a:a + L].tolist(),
+                             v[None, a:a + L].tolist(), causal, 10000.0, "half")
+        assert np.allclose(o[a:a + L], ob[0], atol=1e-12) and np.allclose(lse[:, a:a + L], lb[0],
+                                                                          atol=1e-12)
+
+
+def check_rows_match_full():
+    rng = RNG(16)
+    q = rng.standard_normal((2, 30, 4, 16))
+    k = rng.standard_normal((2, 30, 2, 16))
+    v = rng.standard_normal((2, 30, 2, 16))
+    rows = [(0, 0, 0), (1, 29, 3), (0, 17, 2), (1, 5, 1)]
+    for causal in (True, False):
+        o, lse = oracle.attention_dense(q, k, v, causal=causal, base=10000.0)
+        ro, rl = oracle.attention_rows(q, k, v, rows, causal=causal, base=10000.0)
+        for n, (b, t, h) in enumerate(rows):
+            assert np.allclose(ro[n], o[b, t, h], atol=1e-13) and abs(rl[n] - lse[b, h, t]) < 1e-13
+    lengths = [3, 11, 6]
+    cu = np.array([0, 3, 14, 20], dtype=np.int32)
+    q2, k2, v2 = q[0, :20], k[0, :20], v[0, :20]
+    o, lse = oracle.attention_varlen(q2, k2, v2, cu, base=10000.0)
+    rows = [(0, 2, 1), (1, 10, 0), (2, 0, 3), (1, 4, 2)]
+    ro, rl = oracle.attention_rows(q2, k2, v2, rows, base=10000.0, cu_seqlens=cu)
+    for n, (s, t, h) in enumerate(rows):
+        tok = int(cu[s]) + t
+        assert np.allclose(ro[n], o[tok, h], atol=1e-13) and abs(rl[n] - lse[h, tok]) < 1e-13
+    assert lengths == [3, 11, 6]
+
+
+ALL_CHECKS = [
+    check_inv_freq_closed_forms,
+    check_tables_closed_forms,
+    check_rope_d2_is_plane_rotation,
+    check_rope_interleaved_complex_form,
+    check_rope_half_matches_rotate_half_form,
+    check_rope_norm_and_identity,
+    check_rope_relative,
+    check_rope_styles_related_by_permutation,
+    check_brute_force,
+    check_library_sdpa,
+    check_softmax_rows,
+    check_causal_row0,
+    check_gqa_is_mha_with_repeat_interleave,
+    check_zero_query_closed_form,
+    check_single_token,
+    check_scale_argument,
+    check_varlen_is_concat_of_dense,
+    check_rows_match_full,
+]

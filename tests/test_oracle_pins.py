@@ -1,0 +1,68 @@
+"""The oracle against its pins, and planted mistakes against the pins (CPU only)."""
+
+import importlib.util
+import os
+import types
+
+import pytest
+
+import oracle
+from tests import oracle_checks
+
+ORACLE_SRC = os.path.join(os.path.dirname(oracle.__file__), "__init__.py")
+
+
+@pytest.mark.parametrize("check", oracle_checks.ALL_CHECKS, ids=lambda c: c.__name__)
+def test_oracle_pin(check):
+    check()
+
+
+# Each mutant is one plausible mistake, planted by editing the oracle's source
+# text in memory: (what it breaks, text to find, replacement).
+MUTANTS = [
+    ("exponent -i/d", "-2.0 * i / head_dim", "-1.0 * i / head_dim"),
+    ("base^(+2i/d)", "-2.0 * i / head_dim", "2.0 * i / head_dim"),
+    ("rotation sign", "y[..., 0::2] = a * c - b * s", "y[..., 0::2] = a * c + b * s"),
+    ("dropped sin term", "y[..., 1::2] = a * s + b * c", "y[..., 1::2] = b * c"),
+    ("half pairing swapped", "y[..., d // 2:] = a * s + b * c", "y[..., d // 2:] = a * c + b * s"),
+    ("GQA repeat instead of repeat_interleave", "kv = h // G  #", "kv = h % KV  #"),
+    ("mask includes diagonal", "np.triu(np.ones((L, L), dtype=bool), k=1)",
+     "np.triu(np.ones((L, L), dtype=bool), k=2)"),
+    ("no softmax scale", "S = (qr[:, h, :] @ kr[:, kv, :].T) * scale",
+     "S = (qr[:, h, :] @ kr[:, kv, :].T)"),
+    ("transposed P", "O[:, h, :] = P @ v[:, kv, :]", "O[:, h, :] = P.T @ v[:, kv, :]"),
+    ("lse without max", "lse[h] = m + np.log(den)", "lse[h] = np.log(den)"),
+    ("K not rotated", "kr = apply_rope(k, pos, base, style)", "kr = k"),
+    ("positions do not restart per sequence",
+     "O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style)",
+     "O[a:b], lse[:, a:b] = _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style)[0][a:b],"
+     " _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style)[1][:, a:b]"),
+    ("sampled row sees one key too few", "n = t + 1 if causal else L", "n = t if causal else L"),
+    ("sampled row uses wrong KV head", "keys, vals = k[b, :, h // G], v[b, :, h // G]",
+     "keys, vals = k[b, :, h % KV], v[b, :, h % KV]"),
+]
+
+
+def _load_mutant(find, repl):
+    src = open(ORACLE_SRC).read()
+    assert src.count(find) >= 1, f"mutation target vanished from the oracle: {find!r}"
+    src = src.replace(find, repl)
+    spec = importlib.util.spec_from_loader("oracle_mutant", loader=None)
+    mod = types.ModuleType(spec.name)
+    exec(compile(src, "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,find,repl", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(name, find, repl, monkeypatch):
+    mutant = _load_mutant(find, repl)
+    monkeypatch.setattr(oracle_checks, "oracle", mutant)
+    failed = []
+    for check in oracle_checks.ALL_CHECKS:
+        try:
+            with __import__("warnings").catch_warnings():
+                __import__("warnings").simplefilter("ignore")
+                check()
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(check.__name__)
+    assert failed, f"planted mistake '{name}' passed every pin"

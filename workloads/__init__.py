@@ -1,0 +1,186 @@
+"""Seeded synthetic inputs for causal GQA + RoPE attention.
+
+This module only draws random tensors and names shapes. It holds none of the
+attention or RoPE arithmetic, so both the float64 oracle (``oracle/``) and the
+HIP path (``causal_gqa_rope_amd``) can take their inputs from here without
+sharing any of the method's code.
+
+Shapes follow the workloads the pages describe:
+
+* "Attention from Scratch", section "Attention, the math": n_head query heads
+  share n_kv_groups K/V heads; tensors are laid out [B, T, heads, head_dim]
+  after the projection view.
+* "The Transformer Block & the Model", section "Scaling nano to ~80M": the
+  nanollama3 config (6 heads, 3 KV groups, theta 500000, block_size 256,
+  n_embd 384, so head_dim 64).
+* "kohakutt" (PyPI page), Highlights and the tt-xla comparison table: flash
+  attention over MHA/GQA/MQA, causal masks and packed variable-length batches;
+  a Qwen2.5-0.5B 77-token prefill.
+
+Draw recipe (every workload): ``torch.Generator('cpu').manual_seed(seed)``;
+for packed batches the sequence lengths are drawn first with
+``torch.randint(lo, hi + 1, (num_seqs,))``; then ``torch.randn`` in float32 in
+the order Q, K, V; optional K outliers (``torch.rand(K.shape) < frac`` scaled by
+``factor``); finally one cast to the I/O dtype. Consumers upcast the cast values,
+so every side sees bit-identical inputs.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "Workload",
+    "WORKLOADS",
+    "PARITY_EXTRAS",
+    "get",
+    "make_inputs",
+    "varlen_lengths",
+    "algorithmic_flops",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One synthetic attention workload.
+
+    ``lengths is None`` means a dense [B, T, H, d] batch; otherwise a packed
+    batch of ``num_seqs`` sequences whose lengths are drawn uniformly from
+    ``[len_lo, len_hi]`` (inclusive) by the workload's seed.
+    """
+
+    name: str
+    B: int
+    T: int
+    n_head: int
+    n_kv_head: int
+    head_dim: int
+    base: float
+    dtype: str  # "f32" or "bf16": the I/O dtype
+    seed: int
+    causal: bool = True
+    rope_style: str = "interleaved"  # "interleaved" pairs (2i, 2i+1); "half" pairs (i, i + d/2)
+    outlier_frac: float = 0.0
+    outlier_factor: float = 1.0
+    num_seqs: int = 0  # > 0 marks a packed variable-length batch
+    len_lo: int = 0
+    len_hi: int = 0
+
+    @property
+    def varlen(self) -> bool:
+        return self.num_seqs > 0
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the measurements are quoted on (sizes as named).
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny_fp32_T64_H4_KV2_d32", B=1, T=64, n_head=4, n_kv_head=2, head_dim=32,
+                 base=10000.0, dtype="f32", seed=0),
+        Workload("nanollama3_train_B8_T256_H6_KV2_d64", B=8, T=256, n_head=6, n_kv_head=2,
+                 head_dim=64, base=10000.0, dtype="bf16", seed=1),
+        Workload("qwen05b_prefill_T77_H14_KV2_d64_koutliers", B=1, T=77, n_head=14, n_kv_head=2,
+                 head_dim=64, base=1e6, dtype="bf16", seed=2, outlier_frac=0.005,
+                 outlier_factor=20.0),
+        Workload("long_context_T8192_H32_KV8_d128", B=1, T=8192, n_head=32, n_kv_head=8,
+                 head_dim=128, base=500000.0, dtype="bf16", seed=3),
+        Workload("varlen_mqa_32seqs_16to2048_H16_KV1_d128", B=1, T=0, n_head=16, n_kv_head=1,
+                 head_dim=128, base=10000.0, dtype="bf16", seed=4, num_seqs=32, len_lo=16,
+                 len_hi=2048),
+    ]
+}
+
+# Extra parity cases (never bench lines).
+PARITY_EXTRAS = {
+    w.name: w
+    for w in [
+        # The pages' own nanollama3 attention: 6 heads, 3 KV groups, theta 500000, T 256.
+        Workload("nanollama3_pages_B8_T256_H6_KV3_d64", B=8, T=256, n_head=6, n_kv_head=3,
+                 head_dim=64, base=500000.0, dtype="bf16", seed=11),
+        # rotate_half pairing on the three small workloads.
+        WORKLOADS["tiny_fp32_T64_H4_KV2_d32"].replace(
+            name="tiny_fp32_T64_H4_KV2_d32_half", rope_style="half"),
+        WORKLOADS["nanollama3_train_B8_T256_H6_KV2_d64"].replace(
+            name="nanollama3_train_B8_T256_H6_KV2_d64_half", rope_style="half"),
+        WORKLOADS["qwen05b_prefill_T77_H14_KV2_d64_koutliers"].replace(
+            name="qwen05b_prefill_T77_H14_KV2_d64_koutliers_half", rope_style="half"),
+        # No mask.
+        WORKLOADS["nanollama3_train_B8_T256_H6_KV2_d64"].replace(
+            name="nanollama3_train_B8_T256_H6_KV2_d64_nomask", causal=False),
+    ]
+}
+
+
+def get(name: str) -> Workload:
+    if name in WORKLOADS:
+        return WORKLOADS[name]
+    return PARITY_EXTRAS[name]
+
+
+def varlen_lengths(w: Workload, gen: Optional[torch.Generator] = None) -> torch.Tensor:
+    """Sequence lengths of a packed workload (int64, CPU), drawn first from the seed."""
+    if gen is None:
+        gen = torch.Generator("cpu").manual_seed(w.seed)
+    return torch.randint(w.len_lo, w.len_hi + 1, (w.num_seqs,), generator=gen)
+
+
+def _io_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make_inputs(w: Workload) -> dict:
+    """Draw the seeded CPU tensors of a workload.
+
+    Returns a dict with ``q``, ``k``, ``v`` in the I/O dtype and, for packed
+    batches, ``cu_seqlens`` (int32, [num_seqs + 1]), ``lengths`` and
+    ``max_seqlen``. Dense tensors are [B, T, H, d] / [B, T, KV, d]; packed ones
+    are [total, H, d] / [total, KV, d].
+    """
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    out = {}
+    if w.varlen:
+        lengths = varlen_lengths(w, gen)
+        total = int(lengths.sum())
+        cu = torch.zeros(w.num_seqs + 1, dtype=torch.int32)
+        cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
+        qshape = (total, w.n_head, w.head_dim)
+        kshape = (total, w.n_kv_head, w.head_dim)
+        out.update(cu_seqlens=cu, lengths=lengths, max_seqlen=int(lengths.max()),
+                   total_tokens=total)
+    else:
+        qshape = (w.B, w.T, w.n_head, w.head_dim)
+        kshape = (w.B, w.T, w.n_kv_head, w.head_dim)
+    q = torch.randn(qshape, generator=gen, dtype=torch.float32)
+    k = torch.randn(kshape, generator=gen, dtype=torch.float32)
+    v = torch.randn(kshape, generator=gen, dtype=torch.float32)
+    if w.outlier_frac > 0.0:
+        sel = torch.rand(kshape, generator=gen) < w.outlier_frac
+        k = torch.where(sel, k * w.outlier_factor, k)
+    dt = _io_dtype(w.dtype)
+    out.update(q=q.to(dt), k=k.to(dt), v=v.to(dt))
+    return out
+
+
+def custom(name: str = "custom", **kw) -> Workload:
+    """A workload with explicit fields (used by edge-case parity tests)."""
+    defaults = dict(B=1, T=1, n_head=1, n_kv_head=1, head_dim=64, base=10000.0, dtype="bf16",
+                    seed=0)
+    defaults.update(kw)
+    return Workload(name, **defaults)
+
+
+def algorithmic_flops(n_head: int, head_dim: int, lengths, causal: bool) -> int:
+    """FLOPs credited to one forward: 4*d per allowed (query, key) pair per query head.
+
+    2*d for the score dot product and 2*d for the weighted sum of V. A causal
+    sequence of length L has L(L+1)/2 allowed pairs, an unmasked one L^2.
+    Exponentials, RoPE and rescaling are not counted.
+    """
+    pairs = sum((int(L) * (int(L) + 1)) // 2 if causal else int(L) * int(L) for L in lengths)
+    return 4 * head_dim * n_head * pairs
