@@ -1,0 +1,263 @@
+"""Python binding of libcgr: fused causal GQA + RoPE attention forward on gfx950.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of ``libcgr.so``; torch supplies device memory and the current
+stream. The functions carry the names of the C entry points declared in
+``include/cgr.h`` (``cgr_rope_tables``, ``cgr_gqa_rope_attn_fwd``,
+``cgr_gqa_rope_attn_fwd_varlen``, ...); the short names (``rope_tables``,
+``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``) are the same functions.
+
+The library leaves the HIP runtime's symbols unresolved; before loading it,
+the binding makes the runtime torch already loaded globally visible, so the
+kernels run on torch's runtime instance. There is no fallback: without the
+built library (``python -m causal_gqa_rope_amd.build``) every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "CgrError",
+    "library",
+    "library_path",
+    "cgr_rope_tables",
+    "cgr_gqa_rope_attn_fwd",
+    "cgr_gqa_rope_attn_fwd_varlen",
+    "cgr_attn_fwd_varlen_workspace_size",
+    "cgr_varlen_device_status",
+    "cgr_version",
+    "rope_tables",
+    "gqa_rope_attn_fwd",
+    "gqa_rope_attn_fwd_varlen",
+    "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libcgr.so")
+
+# Status codes (cgr_status).
+CGR_OK, CGR_ERR_INVALID_ARG, CGR_ERR_UNSUPPORTED, CGR_ERR_ALIGNMENT, CGR_ERR_WORKSPACE, CGR_ERR_HIP = range(6)
+_STATUS_NAMES = {1: "INVALID_ARG", 2: "UNSUPPORTED", 3: "ALIGNMENT", 4: "WORKSPACE", 5: "HIP"}
+CGR_F32, CGR_BF16 = 0, 1
+CGR_ROPE_INTERLEAVED, CGR_ROPE_HALF = 0, 1
+CGR_MASK_NONE, CGR_MASK_CAUSAL = 0, 1
+CGR_QK_F16, CGR_QK_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "cgr_rope_tables",
+    "cgr_gqa_rope_attn_fwd",
+    "cgr_attn_fwd_varlen_workspace_size",
+    "cgr_gqa_rope_attn_fwd_varlen",
+    "cgr_varlen_device_status",
+    "cgr_last_error",
+    "cgr_version",
+)
+
+
+class CgrError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"cgr status {status} ({_STATUS_NAMES.get(status, '?')}): {message}")
+        self.status = status
+
+
+_LIB = None
+
+
+def _make_hip_runtime_global() -> None:
+    """Promote the HIP runtime torch loaded to RTLD_GLOBAL (no second runtime is loaded)."""
+    import torch.cuda  # noqa: F401  (loads torch's HIP libraries)
+    with open("/proc/self/maps") as f:
+        paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln})
+    if not paths:
+        raise CgrError(CGR_ERR_HIP, "no HIP runtime (libamdhip64) is loaded in this process")
+    mode = ctypes.RTLD_GLOBAL | getattr(os, "RTLD_NOLOAD", 4)
+    for p in paths:
+        ctypes.CDLL(p, mode=mode)
+
+
+def library() -> ctypes.CDLL:
+    """Load libcgr.so (once) and declare its C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(library_path):
+        raise CgrError(CGR_ERR_HIP, f"{library_path} is not built: run python -m causal_gqa_rope_amd.build")
+    _make_hip_runtime_global()
+    lib = ctypes.CDLL(library_path)
+    vp, i32, f32, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    lib.cgr_rope_tables.argtypes = [i32, i32, f64, vp, vp, vp]
+    lib.cgr_rope_tables.restype = i32
+    lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
+                                          i32, i32, i32, f32, i32, vp]
+    lib.cgr_gqa_rope_attn_fwd.restype = i32
+    lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
+    lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_gqa_rope_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                                 i32, i32, vp, vp, i32, i32, i32, f32, i32, vp,
+                                                 ctypes.c_size_t, vp]
+    lib.cgr_gqa_rope_attn_fwd_varlen.restype = i32
+    lib.cgr_varlen_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.cgr_varlen_device_status.restype = i32
+    lib.cgr_last_error.argtypes = []
+    lib.cgr_last_error.restype = ctypes.c_char_p
+    lib.cgr_version.argtypes = []
+    lib.cgr_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != CGR_OK:
+        msg = library().cgr_last_error()
+        raise CgrError(status, msg.decode() if msg else "")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+_DTYPES = {torch.float32: CGR_F32, torch.bfloat16: CGR_BF16}
+_STYLES = {"interleaved": CGR_ROPE_INTERLEAVED, "half": CGR_ROPE_HALF}
+_QK = {"f16": CGR_QK_F16, "bf16": CGR_QK_BF16}
+
+
+def _dev_tensor(name: str, t: torch.Tensor, dtype=None) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise CgrError(CGR_ERR_INVALID_ARG, f"{name} must be a CUDA/HIP tensor")
+    if not t.is_contiguous():
+        raise CgrError(CGR_ERR_INVALID_ARG, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+
+
+def cgr_version() -> int:
+    return int(library().cgr_version())
+
+
+def cgr_rope_tables(max_pos: int, head_dim: int, base: float,
+                    device=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """cos, sin float32 [max_pos, head_dim/2] of p * base^(-2i/head_dim) (see include/cgr.h)."""
+    lib = library()
+    device = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    half = max(head_dim // 2, 1)
+    cos = torch.empty((max(max_pos, 1), half), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    with torch.cuda.device(device):
+        _check(lib.cgr_rope_tables(int(max_pos), int(head_dim), float(base), _ptr(cos), _ptr(sin),
+                                   _stream(device)))
+    return cos, sin
+
+
+def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope_cos: torch.Tensor,
+                          rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
+                          softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True):
+    """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 4-D [B, T, heads, head_dim]")
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise CgrError(CGR_ERR_UNSUPPORTED, "q, k, v must all be float32 or all bfloat16")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, q.dtype)
+    if out.shape != q.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev_tensor("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H, T):
+            raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
+            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
+            CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _stream(q.device)))
+    return out, lse
+
+
+def cgr_attn_fwd_varlen_workspace_size(num_seqs: int, total_tokens: int) -> int:
+    return int(library().cgr_attn_fwd_varlen_workspace_size(int(num_seqs), int(total_tokens)))
+
+
+def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                 cu_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
+                                 rope_sin: torch.Tensor, *, causal: bool = True,
+                                 rope_style: str = "interleaved", softmax_scale: Optional[float] = None,
+                                 qk_operand: str = "f16", out: Optional[torch.Tensor] = None,
+                                 lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                                 workspace: Optional[torch.Tensor] = None):
+    """Packed forward: q [total,H,d], k/v [total,KV,d], cu_seqlens int32 [n+1] (device).
+
+    Returns (o [total,H,d], lse [H,total] float32 or None).
+    """
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 3-D [total, heads, head_dim]")
+    total, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != total or k.shape[2] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise CgrError(CGR_ERR_UNSUPPORTED, "q, k, v must all be float32 or all bfloat16")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    nseq = cu_seqlens.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    _dev_tensor("out", out, q.dtype)
+    if lse is None and return_lse:
+        lse = torch.empty((H, total), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev_tensor("lse", lse, torch.float32)
+    need = lib.cgr_attn_fwd_varlen_workspace_size(max(nseq, 1), total)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_fwd_varlen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), nseq, total,
+            int(max_seqlen), H, k.shape[1], D, _DTYPES[q.dtype], _ptr(rope_cos), _ptr(rope_sin),
+            rope_cos.shape[0], _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out, lse
+
+
+def cgr_varlen_device_status(workspace: torch.Tensor) -> int:
+    """Device error word of the last varlen call on `workspace` (0 = well formed). Synchronises."""
+    lib = library()
+    st = ctypes.c_int32(-1)
+    with torch.cuda.device(workspace.device):
+        _check(lib.cgr_varlen_device_status(_ptr(workspace), _stream(workspace.device), ctypes.byref(st)))
+    return int(st.value)
+
+
+rope_tables = cgr_rope_tables
+gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
+gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen

@@ -1,0 +1,251 @@
+// C-ABI entry points of libcgr: argument checks, launch configuration and
+// error reporting. Every check that can be made on the host is made before
+// anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "attn_fwd_kernel.h"
+#include "cgr.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cgr_status fail(cgr_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+cgr_status hip_fail(const char* what, hipError_t e) {
+  return fail(CGR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Compute units of the current device, cached per device ordinal.
+int cu_count(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *out = c;
+      return 0;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return 0;
+}
+
+// Checks shared by the dense and the packed forward. `need_pos` is the
+// largest RoPE position + 1 the call can reach.
+cgr_status check_common(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, int n_head, int n_kv_head, int head_dim,
+                        cgr_dtype dtype, const float* cs, const float* sn, int rope_max_pos,
+                        int need_pos, cgr_rope_style style, cgr_mask mask, float softmax_scale,
+                        cgr_qk_operand qk) {
+  if (!q || !k || !v || !o) return fail(CGR_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  if (!cs || !sn) return fail(CGR_ERR_INVALID_ARG, "rope_cos and rope_sin must be non-null");
+  if (n_head < 1 || n_kv_head < 1)
+    return fail(CGR_ERR_INVALID_ARG, "n_head (%d) and n_kv_head (%d) must be >= 1", n_head,
+                n_kv_head);
+  if (n_head % n_kv_head != 0)
+    return fail(CGR_ERR_INVALID_ARG, "n_head (%d) must be divisible by n_kv_head (%d)", n_head,
+                n_kv_head);
+  if (head_dim < 2 || head_dim % 2 != 0)
+    return fail(CGR_ERR_INVALID_ARG, "head_dim (%d) must be even: RoPE rotates pairs", head_dim);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(CGR_ERR_UNSUPPORTED, "head_dim %d is not one of 32, 64, 128", head_dim);
+  if (dtype != CGR_F32 && dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "dtype %d is not CGR_F32 or CGR_BF16", (int)dtype);
+  if (style != CGR_ROPE_INTERLEAVED && style != CGR_ROPE_HALF)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown rope style %d", (int)style);
+  if (mask != CGR_MASK_NONE && mask != CGR_MASK_CAUSAL)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown mask %d", (int)mask);
+  if (qk != CGR_QK_F16 && qk != CGR_QK_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown qk operand %d", (int)qk);
+  if (!std::isfinite(softmax_scale))
+    return fail(CGR_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(cs, 16) || !aligned(sn, 16))
+    return fail(CGR_ERR_ALIGNMENT, "q, k, v, o, rope_cos and rope_sin must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(CGR_ERR_ALIGNMENT, "lse must be 4-byte aligned");
+  if (rope_max_pos < need_pos)
+    return fail(CGR_ERR_INVALID_ARG, "rope tables cover %d positions, the call needs %d",
+                rope_max_pos, need_pos);
+  return CGR_OK;
+}
+
+cgr::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* cs, const float* sn, int n_head, int n_kv_head, int head_dim,
+                        float softmax_scale) {
+  cgr::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.rope_cos = cs;
+  a.rope_sin = sn;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  a.qscale = (float)(scale * 1.4426950408889634074);  // log2(e): exp2 does the exponentials
+  return a;
+}
+
+hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, cgr_qk_operand qk,
+                         cgr_rope_style style, cgr_mask mask, bool varlen, int grid,
+                         hipStream_t s) {
+  const int f32 = dtype == CGR_F32, qkb = qk == CGR_QK_BF16, sty = (int)style,
+            cau = mask == CGR_MASK_CAUSAL;
+  switch (head_dim) {
+    case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s);
+    case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s);
+    default: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s);
+  }
+}
+
+long varlen_max_items(int num_seqs, int total_tokens) {
+  return ((long)total_tokens + cgr::kBM - 1) / cgr::kBM + (long)num_seqs;
+}
+
+}  // namespace
+
+extern "C" {
+
+cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float* cos_out, float* sin_out,
+                           void* stream) {
+  if (!cos_out || !sin_out) return fail(CGR_ERR_INVALID_ARG, "cos_out and sin_out must be non-null");
+  if (max_pos < 1) return fail(CGR_ERR_INVALID_ARG, "max_pos (%d) must be >= 1", max_pos);
+  if (head_dim < 2 || head_dim % 2 != 0)
+    return fail(CGR_ERR_INVALID_ARG, "head_dim (%d) must be even and >= 2", head_dim);
+  if (!(base > 0.0) || !std::isfinite(base))
+    return fail(CGR_ERR_INVALID_ARG, "base must be positive and finite");
+  if (!aligned(cos_out, 4) || !aligned(sin_out, 4))
+    return fail(CGR_ERR_ALIGNMENT, "tables must be 4-byte aligned");
+  if ((long)max_pos * (head_dim / 2) > (long)INT_MAX * 256)
+    return fail(CGR_ERR_INVALID_ARG, "table too large");
+  const hipError_t e = cgr::launch_rope_tables(max_pos, head_dim, base, cos_out, sin_out,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("rope_tables launch", e);
+  return CGR_OK;
+}
+
+cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int T, int n_head, int n_kv_head, int head_dim,
+                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* stream) {
+  if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
+  cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
+                               rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
+  if (st != CGR_OK) return st;
+  if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
+  const long grid = (long)((T + cgr::kBM - 1) / cgr::kBM) * B * n_head;
+  if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
+                              softmax_scale);
+  a.B = B;
+  a.T = T;
+  a.total_tokens = B * T;
+  const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("attention launch", e);
+  return CGR_OK;
+}
+
+size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens) {
+  if (num_seqs < 1 || total_tokens < 0) return 0;
+  return (size_t)cgr::kSchedHeaderInts * 4 + (size_t)varlen_max_items(num_seqs, total_tokens) * 8;
+}
+
+cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, const int32_t* cu_seqlens, int num_seqs,
+                                        int total_tokens, int max_seqlen, int n_head,
+                                        int n_kv_head, int head_dim, cgr_dtype dtype,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                        float softmax_scale, cgr_qk_operand qk_operand,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cu_seqlens) return fail(CGR_ERR_INVALID_ARG, "cu_seqlens must be non-null");
+  if (!aligned(cu_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cu_seqlens must be 4-byte aligned");
+  if (num_seqs < 1) return fail(CGR_ERR_INVALID_ARG, "num_seqs (%d) must be >= 1", num_seqs);
+  if (total_tokens < 0 || max_seqlen < 0)
+    return fail(CGR_ERR_INVALID_ARG, "total_tokens and max_seqlen must be >= 0");
+  if (max_seqlen > total_tokens)
+    return fail(CGR_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen,
+                total_tokens);
+  cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
+                               rope_sin, rope_max_pos, max_seqlen, style, mask, softmax_scale,
+                               qk_operand);
+  if (st != CGR_OK) return st;
+  const size_t need = cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
+                need);
+  const long max_items = varlen_max_items(num_seqs, total_tokens);
+  if (max_items * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  int cus = 0;
+  const int ce = cu_count(&cus);
+  if (ce != 0) return hip_fail("device query", (hipError_t)ce);
+
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* sched = (int32_t*)workspace;
+  hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                             cgr::kBM, cgr::kBN, mask == CGR_MASK_CAUSAL, sched,
+                                             (int)max_items, s);
+  if (e != hipSuccess) return hip_fail("schedule launch", e);
+  cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
+                              softmax_scale);
+  a.cu_seqlens = cu_seqlens;
+  a.sched = sched;
+  a.B = num_seqs;
+  a.T = max_seqlen;
+  a.total_tokens = total_tokens;
+  // Persistent grid: two workgroups per compute unit, never more than the units.
+  long grid = 2L * cus;
+  if (grid > max_items * n_head) grid = max_items * n_head;
+  if (grid < 1) grid = 1;
+  e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
+  if (e != hipSuccess) return hip_fail("attention launch", e);
+  return CGR_OK;
+}
+
+cgr_status cgr_varlen_device_status(const void* workspace, void* stream, int32_t* host_status) {
+  if (!workspace || !host_status)
+    return fail(CGR_ERR_INVALID_ARG, "workspace and host_status must be non-null");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(host_status, (const int32_t*)workspace + 2, sizeof(int32_t),
+                                hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail("status copy", e);
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail("stream synchronize", e);
+  return CGR_OK;
+}
+
+const char* cgr_last_error(void) { return g_last_error.c_str(); }
+
+int cgr_version(void) { return 10000; }
+
+}  // extern "C"

@@ -1,0 +1,26 @@
+// Host-side launchers shared by the C-ABI entry points (internal to libcgr).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cgr {
+
+struct AttnArgs;
+
+hipError_t launch_attn_d32(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
+                           bool varlen, int grid, hipStream_t stream);
+hipError_t launch_attn_d64(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
+                           bool varlen, int grid, hipStream_t stream);
+hipError_t launch_attn_d128(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
+                            bool varlen, int grid, hipStream_t stream);
+
+hipError_t launch_rope_tables(int max_pos, int head_dim, double base, float* cos_out,
+                              float* sin_out, hipStream_t stream);
+
+// Builds the work list of a packed batch into `sched` (see varlen_sched.hip).
+hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                                  int max_seqlen, int bm, int bn, int causal, int32_t* sched,
+                                  int max_items, hipStream_t stream);
+
+}  // namespace cgr

@@ -1,0 +1,173 @@
+/*
+ * cgr.h -- fused causal grouped-query attention with rotary position
+ * embedding (RoPE), forward pass, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation, as the pages define it:
+ *   - RoPE tables: "Embeddings & the Residual Stream", section "Positional
+ *     information: RoPE" -- inv_freq[i] = base^(-2i/d) for i < d/2, angle at
+ *     position p = p * inv_freq[i], rotation applied to Q and K only.
+ *   - Attention: "Attention from Scratch", section "Attention, the math" --
+ *     n_head query heads share n_kv_head K/V heads (query head h reads K/V
+ *     head h / (n_head / n_kv_head)), scores q.k / sqrt(d), causal mask
+ *     (no token attends to a later one) or none, softmax over keys, weighted
+ *     sum of V, output laid out [B, T, n_head, d].
+ *   - Computed tile by tile with an online softmax so the T x T score matrix
+ *     never reaches memory: same page, section "Coming from CUDA:
+ *     FlashAttention".
+ *   - Packed variable-length batches with MHA/GQA/MQA: "kohakutt" (PyPI
+ *     page), Highlights.
+ * Both forward entry points also return, per query row, the natural
+ * log-sum-exp of that row's scaled, masked scores (the softmax denominator in
+ * log form), so that partial results over disjoint key sets can be merged.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are device memory of the current HIP device;
+ *     the caller allocates and owns all of them. The library allocates no
+ *     device memory and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Work is
+ *     enqueued on it and the call returns without synchronising.
+ *   - Errors: a host-checkable problem returns a non-zero cgr_status and
+ *     enqueues nothing; cgr_last_error() then describes it (thread-local).
+ *     A failed kernel launch returns CGR_ERR_HIP. No C++ exception crosses
+ *     this interface.
+ *   - Tensors are contiguous, row-major, and every pointer is 16-byte aligned.
+ *   - Linking: the library leaves the HIP runtime's symbols to the process
+ *     (link the program with -lamdhip64, or load the runtime first), so that
+ *     it always runs on the same runtime instance as its caller.
+ */
+#ifndef CGR_H
+#define CGR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CGR_API __attribute__((visibility("default")))
+#else
+#define CGR_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CGR_OK = 0,
+  CGR_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, n_head % n_kv_head != 0, ... */
+  CGR_ERR_UNSUPPORTED = 2, /* head_dim not in {32, 64, 128}, unknown dtype/style/mask */
+  CGR_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned */
+  CGR_ERR_WORKSPACE = 4,   /* varlen workspace missing or too small */
+  CGR_ERR_HIP = 5          /* a HIP call failed; cgr_last_error() holds its message */
+} cgr_status;
+
+/* I/O element type of q, k, v and o. */
+typedef enum { CGR_F32 = 0, CGR_BF16 = 1 } cgr_dtype;
+
+/* Which features rotate together.
+ *   CGR_ROPE_INTERLEAVED: pair i is (2i, 2i+1) -- "rotate each adjacent pair of
+ *     features" in the RoPE prose of "Embeddings & the Residual Stream".
+ *   CGR_ROPE_HALF: pair i is (i, i + d/2) -- the x*cos + rotate_half(x)*sin
+ *     form of the helper printed on the same page. */
+typedef enum { CGR_ROPE_INTERLEAVED = 0, CGR_ROPE_HALF = 1 } cgr_rope_style;
+
+/* CGR_MASK_CAUSAL: key j is visible to query i iff j <= i (positions within
+ * the sequence). CGR_MASK_NONE: every key of the sequence is visible. */
+typedef enum { CGR_MASK_NONE = 0, CGR_MASK_CAUSAL = 1 } cgr_mask;
+
+/* Operand type of the Q.K^T matrix product (bf16 I/O only; f32 I/O always
+ * multiplies in f32). RoPE is applied in f32 and rounded once to this type.
+ *   CGR_QK_F16 (default): 3 more mantissa bits than bf16. Every |rotated q *
+ *     softmax_scale * log2(e)| and |rotated k| must stay below 65504, or the
+ *     output holds inf/NaN: inputs with |x| < 46000 always qualify.
+ *   CGR_QK_BF16: bf16's full range, coarser rounding.
+ * The P.V product always multiplies bf16 P by bf16 V, accumulating in f32. */
+typedef enum { CGR_QK_F16 = 0, CGR_QK_BF16 = 1 } cgr_qk_operand;
+
+/*
+ * RoPE tables ("Embeddings & the Residual Stream", "Positional information:
+ * RoPE"). For p < max_pos and i < head_dim/2:
+ *   cos_out[p * (head_dim/2) + i] = cos(p * base^(-2i/head_dim))
+ *   sin_out[p * (head_dim/2) + i] = sin(p * base^(-2i/head_dim))
+ * The angle and its cosine and sine are evaluated in float64 and stored as
+ * float32.
+ *   max_pos >= 1; head_dim even and >= 2; base > 0 (and finite).
+ *   cos_out, sin_out: device float32 [max_pos, head_dim/2], caller-owned.
+ */
+CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float* cos_out,
+                           float* sin_out, void* stream);
+
+/*
+ * Dense batch forward.
+ *   q: device [B, T, n_head, head_dim]      (dtype)
+ *   k, v: device [B, T, n_kv_head, head_dim] (dtype)
+ *   o: device [B, T, n_head, head_dim]      (dtype), written in full
+ *   lse: device float32 [B, n_head, T], or NULL to skip it
+ *   B, T, n_head, n_kv_head >= 1; n_head % n_kv_head == 0;
+ *   head_dim in {32, 64, 128}.
+ *   rope_cos, rope_sin: device float32 [rope_max_pos, head_dim/2] as written by
+ *     cgr_rope_tables; rope_max_pos >= T (token t of every batch entry is at
+ *     position t).
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   qk_operand: see cgr_qk_operand (ignored for CGR_F32).
+ * o and lse must not overlap the inputs.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int T, int n_head, int n_kv_head, int head_dim,
+                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* stream);
+
+/*
+ * Bytes of device workspace cgr_gqa_rope_attn_fwd_varlen needs for a packed
+ * batch of num_seqs sequences holding total_tokens tokens. Returns 0 for
+ * invalid sizes (num_seqs < 1 or total_tokens < 0).
+ */
+CGR_API size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens);
+
+/*
+ * Packed variable-length batch forward. Sequence s holds tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1; RoPE positions restart at 0 in every
+ * sequence and the mask never crosses a sequence boundary.
+ *   q: device [total_tokens, n_head, head_dim]; k, v: device [total_tokens,
+ *     n_kv_head, head_dim]; o: device [total_tokens, n_head, head_dim].
+ *   lse: device float32 [n_head, total_tokens], or NULL.
+ *   cu_seqlens: device int32 [num_seqs + 1] with cu_seqlens[0] = 0,
+ *     non-decreasing, cu_seqlens[num_seqs] = total_tokens, and no sequence
+ *     longer than max_seqlen. Zero-length sequences are allowed.
+ *   rope_max_pos >= max_seqlen. Other arguments as for the dense call.
+ *   workspace: device memory of at least
+ *     cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens) bytes,
+ *     16-byte aligned, used as scratch by this call only (it holds the
+ *     work schedule); calls that overlap in time need separate workspaces.
+ * cu_seqlens lives on the device, so its contents are checked there: a
+ * malformed array schedules no work (o and lse are left unwritten) and sets
+ * an error word that cgr_varlen_device_status() reports.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                                        float* lse, const int32_t* cu_seqlens, int num_seqs,
+                                        int total_tokens, int max_seqlen, int n_head,
+                                        int n_kv_head, int head_dim, cgr_dtype dtype,
+                                        const float* rope_cos, const float* rope_sin,
+                                        int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                        float softmax_scale, cgr_qk_operand qk_operand,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Reads the device error word the last varlen call on `workspace` left:
+ * waits for `stream`, then stores 0 (cu_seqlens was well formed) or a
+ * positive code (1: cu_seqlens[0] != 0, 2: decreasing, 3: a sequence longer
+ * than max_seqlen, 4: cu_seqlens[num_seqs] != total_tokens) in *host_status.
+ */
+CGR_API cgr_status cgr_varlen_device_status(const void* workspace, void* stream, int32_t* host_status);
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+CGR_API const char* cgr_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+CGR_API int cgr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CGR_H */

@@ -1,0 +1,156 @@
+"""The C-ABI library: it loads, exports what include/cgr.h declares, and its
+host-side argument checks reject bad calls before anything is enqueued.
+
+No compute call is made here: every call below fails validation first, with
+pointers that are never dereferenced. These tests skip when a GPU is visible
+(the GPU tests cover the same checks with real tensors).
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_gqa_rope_amd as cgr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cgr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"CGR_API\s+[\w\s\*]+?\b(cgr_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(cgr.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cgr.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", cgr.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+    # Only the C entry points are exported: the kernels and helpers stay hidden.
+    assert {s for s in exported if s.startswith("cgr")} == set(declared_functions())
+
+
+def test_library_leaves_the_hip_runtime_to_the_process():
+    out = subprocess.run(["readelf", "-d", cgr.library_path], capture_output=True, text=True,
+                         check=True).stdout
+    assert "amdhip64" not in out, "libcgr must not pull in its own HIP runtime"
+
+
+def test_version_and_workspace_size():
+    assert cgr.cgr_version() == 10000
+    lib = cgr.library()
+    assert lib.cgr_attn_fwd_varlen_workspace_size(0, 10) == 0
+    assert lib.cgr_attn_fwd_varlen_workspace_size(1, -1) == 0
+    small = lib.cgr_attn_fwd_varlen_workspace_size(1, 1)
+    big = lib.cgr_attn_fwd_varlen_workspace_size(32, 32226)
+    assert 16 < small < big
+    assert big >= 16 + 8 * (32226 // 128 + 32)
+
+
+no_gpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(), reason="host-only checks with placeholder pointers")
+
+P = ctypes.c_void_p(0x10000)      # 16-byte aligned placeholder, never dereferenced
+PMIS = ctypes.c_void_p(0x10002)   # misaligned placeholder
+
+
+def dense(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
+             P=16, style=0, mask=1, scale=0.0, qk=0)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"],
+                                   a["KV"], a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
+                                   a["style"], a["mask"], a["scale"], a["qk"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(cos=None), 1, "non-null"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(T=-3), 1, ">= 1"),
+    (dict(H=0), 1, ">= 1"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(D=63), 1, "even"),
+    (dict(D=96), 2, "not one of"),
+    (dict(D=256), 2, "not one of"),
+    (dict(dtype=7), 2, "dtype"),
+    (dict(style=3), 2, "style"),
+    (dict(mask=2), 2, "mask"),
+    (dict(qk=9), 2, "qk operand"),
+    (dict(scale=float("nan")), 1, "finite"),
+    (dict(q=PMIS), 3, "aligned"),
+    (dict(sin=PMIS), 3, "aligned"),
+    (dict(P=15), 1, "positions"),
+])
+def test_dense_rejects_bad_arguments(kw, status, needle):
+    st, msg = dense(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+def varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cu=P, nseq=2, total=100, maxlen=60, H=4, KV=1, D=128,
+             dtype=1, cos=P, sin=P, P=60, style=0, mask=1, scale=0.0, qk=0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
+                                          a["nseq"], a["total"], a["maxlen"], a["H"], a["KV"],
+                                          a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
+                                          a["style"], a["mask"], a["scale"], a["qk"], a["ws"],
+                                          a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cu=None), 1, "cu_seqlens"),
+    (dict(nseq=0), 1, "num_seqs"),
+    (dict(total=-1), 1, ">= 0"),
+    (dict(maxlen=101), 1, "exceeds"),
+    (dict(P=59), 1, "positions"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(wsb=16), 4, "needs"),
+    (dict(ws=PMIS), 3, "aligned"),
+    (dict(H=3, KV=2), 1, "divisible"),
+    (dict(D=48), 2, "not one of"),
+])
+def test_varlen_rejects_bad_arguments(kw, status, needle):
+    st, msg = varlen(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+@no_gpu
+@pytest.mark.parametrize("args,needle", [
+    ((0, 64, 1e4), ">= 1"),
+    ((16, 63, 1e4), "even"),
+    ((16, 0, 1e4), "even"),
+    ((16, 64, 0.0), "positive"),
+    ((16, 64, float("inf")), "positive"),
+])
+def test_rope_tables_rejects_bad_arguments(args, needle):
+    lib = cgr.library()
+    st = lib.cgr_rope_tables(args[0], args[1], args[2], P, P, None)
+    assert st == 1
+    assert needle in lib.cgr_last_error().decode()
+
+
+@no_gpu
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(cgr.CgrError):
+        cgr.gqa_rope_attn_fwd(x, x, x, torch.zeros(4, 32), torch.zeros(4, 32))

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP path through the C-ABI against the float64 oracle on the
+same seeded inputs, element by element, at sizes that span several tiles and a
+ragged tail, and on sampled rows at the full long-context and packed sizes."""
+
+import numpy as np
+import pytest
+import torch
+
+import causal_gqa_rope_amd as cgr
+import oracle
+import workloads as W
+from tests.gpu_cases import TOL, announce, assert_close, f64, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_fp32_T64_H4_KV2_d32", "nanollama3_train_B8_T256_H6_KV2_d64",
+         "qwen05b_prefill_T77_H14_KV2_d64_koutliers"] + list(W.PARITY_EXTRAS)
+
+
+@pytest.mark.parametrize("P,d,base", [(8192, 128, 5e5), (2048, 128, 1e4), (77, 64, 1e6),
+                                      (64, 32, 1e4), (17, 2, 1e4), (300, 6, 3.5)])
+def test_rope_tables(gpu, P, d, base):
+    announce(f"rope_tables P={P} d={d} base={base}")
+    cos, sin = cgr.rope_tables(P, d, base, device=gpu)
+    rc, rs = oracle.rope_tables(P, d, base)
+    # float64 evaluation, one rounding to float32: within half an ulp of 1.0.
+    assert np.abs(f64(cos) - rc).max() <= 2.0 ** -24
+    assert np.abs(f64(sin) - rs).max() <= 2.0 ** -24
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_workload_full(gpu, name):
+    w = W.get(name)
+    announce(f"{name}: full comparison")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    ro, rl = run_oracle(w, x)
+    assert_close(name, f64(o), ro, f64(lse), rl, w.dtype)
+
+
+def sampled_rows_dense(w, n, seed):
+    rng = np.random.default_rng(seed)
+    T = w.T
+    ts = [0, 1, 63, 64, 127, 128, T // 2, T - 129, T - 128, T - 65, T - 64, T - 1]
+    ts += list(rng.integers(0, T, n - len(ts)))
+    return [(int(rng.integers(0, w.B)), int(t), int(rng.integers(0, w.n_head))) for t in ts]
+
+
+def test_long_context_full_size_sampled(gpu):
+    """The full long-context workload in the launch configuration the benchmark times."""
+    w = W.get("long_context_T8192_H32_KV8_d128")
+    announce(f"{w.name}: full-size run, sampled rows")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    o, lse = f64(o), f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = sampled_rows_dense(w, 96, 0) + [(0, 8191, h) for h in range(32)] + [(0, 0, h) for h in range(0, 32, 5)]
+    ro, rl = oracle.attention_rows(x["q"], x["k"], x["v"], rows, causal=True, base=w.base)
+    go = np.stack([o[b, t, h] for (b, t, h) in rows])
+    gl = np.array([lse[b, h, t] for (b, t, h) in rows])
+    assert_close(w.name + " (sampled)", go, ro, gl, rl, w.dtype)
+    # Every row: the softmax weights are a convex combination, so each output
+    # lies within the range of the values its row may see; the LSE of a causal
+    # row i is at least its largest single score and at most that + ln(i+1).
+    vmax = np.maximum.accumulate(f64(x["v"].to(torch.float32)).max(axis=-1), axis=1)  # [B,T,KV]
+    G = w.n_head // w.n_kv_head
+    bound = vmax[:, :, np.arange(w.n_head) // G]  # [B,T,H]
+    assert (o.max(axis=-1) <= bound + TOL["bf16"]["max_abs"]).all()
+
+
+def test_varlen_workload_full_size_sampled(gpu):
+    w = W.get("varlen_mqa_32seqs_16to2048_H16_KV1_d128")
+    announce(f"{w.name}: full-size run, sampled rows")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    o, lse = f64(o), f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(1)
+    lengths = x["lengths"].tolist()
+    cu = x["cu_seqlens"].numpy()
+    rows = []
+    for s, L in enumerate(lengths):
+        for t in {0, L - 1, min(127, L - 1), min(128, L - 1), int(rng.integers(0, L))}:
+            rows.append((s, t, int(rng.integers(0, w.n_head))))
+    ro, rl = oracle.attention_rows(x["q"], x["k"], x["v"], rows, causal=True, base=w.base,
+                                   cu_seqlens=cu)
+    go = np.stack([o[cu[s] + t, h] for (s, t, h) in rows])
+    gl = np.array([lse[h, cu[s] + t] for (s, t, h) in rows])
+    assert_close(w.name + " (sampled)", go, ro, gl, rl, w.dtype)
+
+
+EDGE = [
+    # B, T, H, KV, d, dtype, causal, style
+    (1, 1, 1, 1, 128, "bf16", True, "interleaved"),
+    (3, 1, 4, 2, 64, "bf16", False, "half"),
+    (2, 2, 2, 1, 32, "f32", True, "half"),
+    (1, 31, 4, 4, 64, "bf16", True, "interleaved"),
+    (2, 63, 6, 3, 128, "bf16", False, "interleaved"),
+    (1, 64, 8, 1, 128, "bf16", True, "half"),
+    (1, 65, 2, 2, 32, "bf16", True, "interleaved"),
+    (2, 127, 4, 2, 64, "f32", True, "interleaved"),
+    (1, 129, 4, 1, 128, "bf16", True, "interleaved"),
+    (1, 300, 8, 2, 128, "bf16", False, "half"),
+    (1, 521, 4, 2, 128, "bf16", True, "interleaved"),
+    (2, 200, 3, 1, 64, "f32", False, "half"),
+    (1, 1000, 8, 2, 128, "bf16", True, "interleaved"),
+]
+
+
+@pytest.mark.parametrize("B,T,H,KV,d,dtype,causal,style", EDGE,
+                         ids=["-".join(map(str, e)) for e in EDGE])
+def test_edge_shapes(gpu, B, T, H, KV, d, dtype, causal, style):
+    w = W.custom("edge", B=B, T=T, n_head=H, n_kv_head=KV, head_dim=d, dtype=dtype, causal=causal,
+                 rope_style=style, base=10000.0, seed=B * 1000 + T)
+    announce(f"edge {w}")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    ro, rl = run_oracle(w, x)
+    assert_close("edge", f64(o), ro, f64(lse), rl, dtype)
+
+
+VARLEN = [
+    # lengths, H, KV, d, dtype, causal, style
+    ([5, 1, 0, 130, 64, 257, 1], 4, 1, 128, "bf16", True, "interleaved"),
+    ([0, 300, 17], 6, 2, 64, "bf16", False, "half"),
+    ([129, 128, 127, 2], 4, 4, 32, "f32", True, "interleaved"),
+    ([1], 2, 1, 64, "bf16", True, "half"),
+    ([700, 0, 0, 33], 8, 2, 128, "bf16", True, "interleaved"),
+]
+
+
+def packed_inputs(lengths, H, KV, d, dtype, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    total = sum(lengths)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths), 0).to(torch.int32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn((total, H, d), generator=g).to(dt)
+    k = torch.randn((total, KV, d), generator=g).to(dt)
+    v = torch.randn((total, KV, d), generator=g).to(dt)
+    return dict(q=q, k=k, v=v, cu_seqlens=cu, max_seqlen=max(lengths), lengths=torch.tensor(lengths))
+
+
+@pytest.mark.parametrize("lengths,H,KV,d,dtype,causal,style", VARLEN,
+                         ids=[f"v{i}" for i in range(len(VARLEN))])
+def test_varlen_small_full(gpu, lengths, H, KV, d, dtype, causal, style):
+    announce(f"varlen lengths={lengths} H={H} KV={KV} d={d} {dtype} causal={causal} {style}")
+    x = packed_inputs(lengths, H, KV, d, dtype, seed=len(lengths) * 7 + d)
+    w = W.custom("varlen", n_head=H, n_kv_head=KV, head_dim=d, dtype=dtype, causal=causal,
+                 rope_style=style, base=5e5, num_seqs=len(lengths), len_lo=0, len_hi=1)
+    xd = to_dev(x, gpu)
+    o, lse = run_gpu(w, xd, gpu)
+    ro, rl = run_oracle(w, x)
+    assert_close("varlen", f64(o), ro, f64(lse), rl, dtype)
+
+
+def test_varlen_equals_dense_per_sequence(gpu):
+    """A packed batch is, bit for bit, the dense forward of each of its sequences."""
+    lengths = [200, 77, 1, 129]
+    announce(f"varlen vs dense, lengths {lengths}")
+    x = packed_inputs(lengths, 8, 2, 128, "bf16", seed=5)
+    xd = to_dev(x, gpu)
+    cos, sin = cgr.rope_tables(256, 128, 1e4, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["cu_seqlens"], 200, cos, sin)
+    cu = x["cu_seqlens"].tolist()
+    for s, L in enumerate(lengths):
+        a = cu[s]
+        od, ld = cgr.gqa_rope_attn_fwd(xd["q"][None, a:a + L].contiguous(), xd["k"][None, a:a + L].contiguous(),
+                                       xd["v"][None, a:a + L].contiguous(), cos, sin)
+        assert torch.equal(o[a:a + L], od[0])
+        assert torch.equal(lse[:, a:a + L], ld[0])
+
+
+def test_deterministic_and_fully_written(gpu):
+    w = W.get("nanollama3_train_B8_T256_H6_KV2_d64")
+    announce("determinism + poison fill")
+    x = to_dev(W.make_inputs(w), gpu)
+    cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=gpu)
+    outs = []
+    for _ in range(2):
+        o = torch.full_like(x["q"], float("nan"))
+        lse = torch.full((w.B, w.n_head, w.T), float("nan"), device=gpu)
+        cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, out=o, lse=lse)
+        assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    # Packed: poison both, run twice.
+    xv = to_dev(packed_inputs([100, 0, 333, 5], 4, 1, 128, "bf16", 9), gpu)
+    cos, sin = cgr.rope_tables(333, 128, 1e4, device=gpu)
+    res = []
+    for _ in range(2):
+        o = torch.full_like(xv["q"], float("nan"))
+        lse = torch.full((4, xv["q"].shape[0]), float("nan"), device=gpu)
+        cgr.gqa_rope_attn_fwd_varlen(xv["q"], xv["k"], xv["v"], xv["cu_seqlens"], 333, cos, sin,
+                                     out=o, lse=lse)
+        assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+        res.append((o, lse))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_causal_row0_is_value_row0(gpu):
+    """Query 0 may only see key 0: its output is V[0] of its K/V head, exactly."""
+    w = W.get("long_context_T8192_H32_KV8_d128").replace(T=300)
+    announce("causal row 0")
+    x = to_dev(W.make_inputs(w), gpu)
+    o, _ = run_gpu(w, x, gpu)
+    G = w.n_head // w.n_kv_head
+    for h in range(w.n_head):
+        assert torch.equal(o[:, 0, h], x["v"][:, 0, h // G])
+
+
+def test_softmax_scale_and_no_lse(gpu):
+    w = W.custom("scale", B=2, T=150, n_head=4, n_kv_head=2, head_dim=64, base=1e4, seed=3)
+    announce("explicit softmax scale, lse omitted")
+    x = W.make_inputs(w)
+    xd = to_dev(x, gpu)
+    cos, sin = cgr.rope_tables(150, 64, 1e4, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd(xd["q"], xd["k"], xd["v"], cos, sin, softmax_scale=0.05,
+                                   return_lse=False)
+    assert lse is None
+    ro, _ = oracle.attention_dense(x["q"], x["k"], x["v"], base=1e4, scale=0.05)
+    from tests.gpu_cases import errors
+    mx, med = errors(f64(o), ro)
+    assert mx <= TOL["bf16"]["max_abs"] and med <= TOL["bf16"]["med_rel"], (mx, med)
+
+
+def test_qk_bf16_operand_option(gpu):
+    """bf16 Q.K^T operands: same kernels, coarser rounding; within tolerance on
+    N(0,1) inputs (the outlier workload needs the default f16 operands)."""
+    w = W.get("nanollama3_train_B8_T256_H6_KV2_d64")
+    announce("qk operand bf16")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu, qk_operand="bf16")
+    ro, rl = run_oracle(w, x)
+    assert_close("qk-bf16", f64(o), ro, f64(lse), rl, "bf16")
+
+
+@pytest.mark.parametrize("cu,code", [([1, 5, 9], 1), ([0, 6, 4, 9], 2), ([0, 2, 9], 3),
+                                     ([0, 4, 8], 4)])
+def test_malformed_cu_seqlens_schedules_nothing(gpu, cu, code):
+    announce(f"malformed cu_seqlens {cu}")
+    total = 9
+    q = torch.randn(total, 2, 64, device=gpu).to(torch.bfloat16)
+    kv = torch.randn(total, 1, 64, device=gpu).to(torch.bfloat16)
+    cos, sin = cgr.rope_tables(8, 64, 1e4, device=gpu)
+    o = torch.full_like(q, float("nan"))
+    ws = torch.zeros(cgr.cgr_attn_fwd_varlen_workspace_size(len(cu) - 1, total), dtype=torch.uint8,
+                     device=gpu)
+    cgr.gqa_rope_attn_fwd_varlen(q, kv, kv, torch.tensor(cu, dtype=torch.int32, device=gpu), 6,
+                                 cos, sin, out=o, workspace=ws)
+    assert cgr.cgr_varlen_device_status(ws) == code
+    assert torch.isnan(o).all(), "a malformed batch must leave the output untouched"
+
+
+def test_host_checks_with_real_tensors(gpu):
+    announce("host-side argument checks")
+    q = torch.zeros(1, 8, 4, 64, device=gpu, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 8, 3, 64, device=gpu, dtype=torch.bfloat16)
+    cos, sin = cgr.rope_tables(8, 64, 1e4, device=gpu)
+    with pytest.raises(cgr.CgrError) as e:
+        cgr.gqa_rope_attn_fwd(q, kv, kv, cos, sin)
+    assert e.value.status == cgr.CGR_ERR_INVALID_ARG
+    short_cos, short_sin = cgr.rope_tables(7, 64, 1e4, device=gpu)
+    kv = torch.zeros(1, 8, 2, 64, device=gpu, dtype=torch.bfloat16)
+    with pytest.raises(cgr.CgrError):
+        cgr.gqa_rope_attn_fwd(q, kv, kv, short_cos, short_sin)
+    q96 = torch.zeros(1, 8, 4, 96, device=gpu, dtype=torch.bfloat16)
+    c96, s96 = cgr.rope_tables(8, 96, 1e4, device=gpu)
+    with pytest.raises(cgr.CgrError) as e:
+        cgr.gqa_rope_attn_fwd(q96, q96[:, :, :2].contiguous(), q96[:, :, :2].contiguous(), c96, s96)
+    assert e.value.status == cgr.CGR_ERR_UNSUPPORTED
+
+
+def test_runs_on_the_callers_stream(gpu):
+    w = W.custom("stream", B=1, T=500, n_head=4, n_kv_head=1, head_dim=128, base=1e4, seed=8)
+    announce("side stream")
+    x = W.make_inputs(w)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        xd = to_dev(x, gpu)
+        cos, sin = cgr.rope_tables(500, 128, 1e4, device=gpu)
+        o, lse = cgr.gqa_rope_attn_fwd(xd["q"], xd["k"], xd["v"], cos, sin)
+    s.synchronize()
+    ro, rl = run_oracle(w, x)
+    assert_close("stream", f64(o), ro, f64(lse), rl, "bf16")
