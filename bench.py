@@ -1,0 +1,216 @@
+"""Throughput of the fused causal GQA + RoPE attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+build the RoPE cos/sin tables, then run the fused forward (RoPE on Q/K tiles,
+online softmax, O and LSE) on the long-context workload B=1, T=8192,
+n_head=32, n_kv_head=8, head_dim=128, bf16 I/O, RoPE base 500000, causal.
+Inputs are already resident in HBM when the timed region starts.
+
+Prints one JSON line. `value` is algorithmic TFLOP/s of the step (causal
+FLOPs counted exactly: 4*d per visible (query, key) pair per query head).
+`roofline` reports the attention kernel itself: its average launch duration
+measured with HIP events on the stream it is launched on, against the MI355X
+dense f16/bf16 MFMA peak; `traffic` is HBM bytes per launch from rocprofv3
+counters (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
+read from profiles/ and reported only while the kernel sources still hash to
+the value recorded with them. `cpu_baseline` times the float64 oracle on a
+bounded sample of the same workload on this host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --copy-calibration   (plain copies, for counter scaling)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal GQA+RoPE attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+WORKLOAD = "long_context_T8192_H32_KV8_d128"
+PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+KERNEL_SOURCES = ["attn_fwd_kernel.h", "device_common.h", "attn_fwd_d128.hip"]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", f"attn_fwd_{WORKLOAD}.counters.txt")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_gqa_rope_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch from the committed counter summary, if still current."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    kv = {}
+    for ln in open(COUNTERS_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(inputs, w) -> dict:
+    """The float64 oracle, as it stands, on 2 of the 8 K/V groups (8 of 32 query
+    heads) at the full T = 8192: a quarter of the workload."""
+    import numpy as np  # noqa: F401
+    import oracle
+    import workloads as W
+
+    heads, groups = 8, 2
+    q = inputs["q"][:, :, :heads].contiguous()
+    k = inputs["k"][:, :, :groups].contiguous()
+    v = inputs["v"][:, :, :groups].contiguous()
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    oracle.attention_dense(q, k, v, causal=True, base=w.base, style=w.rope_style)
+    dt = time.perf_counter() - t0
+    flops = W.algorithmic_flops(heads, w.head_dim, [w.T], True)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle, B=1 T={w.T}, query heads 0-{heads - 1} (K/V heads "
+                  f"0-{groups - 1}), causal: 1/4 of the workload, {dt:.1f} s",
+    }
+
+
+def copy_calibration(torch, dev) -> None:
+    """Plain device copies of COPY_BYTES each: the reference for FETCH_SIZE/WRITE_SIZE scaling."""
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    x.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 3}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention of one GPU's head share is the unit that would shard).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import causal_gqa_rope_amd as cgr
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
+        return 0
+
+    w = W.get(WORKLOAD)
+    inputs = W.make_inputs(w)
+    q = inputs["q"].to(dev)
+    k = inputs["k"].to(dev)
+    v = inputs["v"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.n_head, w.T), dtype=torch.float32, device=dev)
+    cos = torch.empty((w.T, w.head_dim // 2), dtype=torch.float32, device=dev)
+    sin = torch.empty_like(cos)
+    lib = cgr.library()
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def tables():
+        cgr._check(lib.cgr_rope_tables(w.T, w.head_dim, w.base, cgr._ptr(cos), cgr._ptr(sin), sptr))
+
+    def attention():
+        cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        tables()
+        attention()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        tables()
+        ev[i][0].record(stream)
+        attention()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True)
+    ms_step = wall * 1e3 / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+            "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
+            "io": "bf16", "qk_operand": "f16", "pv_operand": "bf16", "accumulate": "f32",
+            "step": "rope_tables + gqa_rope_attn_fwd", "flops_per_step": flops,
+            "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "attn_fwd_dense_kernel (head_dim 128, bf16 I/O, f16 QK, causal, interleaved)",
+            "kernel_ms": round(kernel_ms, 5),
+        },
+        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(inputs, w),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -40,6 +40,11 @@ namespace cgr {
 
 enum { STYLE_INTERLEAVED = 0, STYLE_HALF = 1 };
 
+// Waves each SIMD keeps resident (register budget 512 / this per lane).
+#ifndef CGR_WAVES_PER_SIMD
+#define CGR_WAVES_PER_SIMD 2
+#endif
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -79,18 +84,26 @@ struct Cfg {
   static constexpr int NW = 4;
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 32 * NW;  // query rows per unit
-  static constexpr int BN = 64;       // keys per tile
+#ifndef CGR_BN
+#define CGR_BN 64
+#endif
+  static constexpr int BN = CGR_BN;   // keys per tile
   static constexpr int ESZ = F32 ? 4 : 2;
   static constexpr int KSTEPS = D / 16;  // 32x32x16 k-steps over the head dim
   static constexpr int DB = D / 32;      // 32-wide blocks of the head dim
   static constexpr int NKB = BN / 32;    // 32-key blocks per tile
 
   static constexpr int K_STRIDE = D * ESZ + 16;  // bytes per K row in LDS
-  static constexpr int V_STRIDE = F32 ? D * 4 + 16 : 4 * v_stride_dwords(D / 2);
+  // f32 I/O: padded row-major V. bf16 I/O: unpadded row-major V, 16-byte
+  // chunks XOR-swizzled per row (see UnitFast), written by direct
+  // global->LDS loads.
+  static constexpr int V_STRIDE = F32 ? D * 4 + 16 : 2 * D;
   static constexpr int K_BYTES = BN * K_STRIDE;
   static constexpr int V_BYTES = BN * V_STRIDE;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int SMEM = 2 * STAGE;
+  // Direct V loads: 1 KiB (64 lanes x 16 B) per wave instruction.
+  static constexpr int V_WAVE_LOADS = (V_BYTES / 1024 + NW - 1) / NW;
 
   // Loader work items. K: (row, 8-element group g < D/16), which carries the
   // group pair (g, g + D/16) so that both RoPE pairings find their partners.
@@ -444,12 +457,359 @@ struct Unit {
   }
 };
 
+// ---------------------------------------------------------------------------
+// bf16 I/O body. Same unit and same arithmetic as Unit, with the work per key
+// tile cut down to what the matrix cores cannot do:
+//   * All global reads are buffer loads: the per-lane offsets are fixed for
+//     the unit and the tile advance is one scalar offset; rows past the end of
+//     the sequence fall outside the buffer's range and read as zeros, so
+//     ragged tails need no predicates.
+//   * V goes from global memory straight into LDS (no registers): each wave
+//     load writes 1 KiB, 16 bytes per lane, in lane order. The row-major V
+//     tile is stored with its 16-byte chunks XOR-swizzled per row so the
+//     transposing reads of one half-wave (4 rows x 64 bytes) hit distinct
+//     banks.
+//   * The loop body is straight-line code: tiles that need the causal or
+//     sequence-end mask run in a second loop, so the accumulators never pass
+//     a data-dependent join (which would make the compiler copy them).
+//   * Row sums add the bf16-rounded p (the values the P.V product uses) with
+//     packed dot products against (1, 1).
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // Raw buffer (stride 0): reads at byte offsets >= bytes return zeros.
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ f32x4 buf_load16f(rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+// 16 bytes per lane into LDS at lds_base + 16 * lane (lds_base wave-uniform).
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+// Wait until this wave's outstanding global/buffer loads (including those
+// that write LDS directly) have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <class C>
+struct UnitFast {
+  static constexpr int D = C::D, BN = C::BN, NW = C::NW, THREADS = C::THREADS;
+  static constexpr int KI = C::KU;
+  using QK = typename C::QK;
+
+  // XOR swizzle of the 16-byte chunks of V row r (an involution).
+  static __device__ __forceinline__ int vswz_mask(int r) {
+    if constexpr (D == 128) return (r & 3) << 2;
+    else if constexpr (D == 64) return ((r >> 1) & 1) << 2;
+    else return 0;
+  }
+
+  static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head,
+                                             long lse_base, char* smem) {
+    // `wave` is the same in every lane: keeping it scalar makes every wave-level
+    // decision below (active tiles, masking, V blocks) a scalar branch.
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int G = a.H / a.KV, kvh = head / G;
+    const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
+    const uint16_t* qbase = (const uint16_t*)a.q + (long)tok0 * qs + (long)head * D;
+    const uint16_t* kbase = (const uint16_t*)a.k + (long)tok0 * ks + (long)kvh * D;
+    const uint16_t* vbase = (const uint16_t*)a.v + (long)tok0 * ks + (long)kvh * D;
+    const rsrc_t rq = make_rsrc(qbase, (uint32_t)(((L - 1) * qs + D) * 2));
+    const rsrc_t rk = make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
+    const rsrc_t rv = make_rsrc(vbase, (uint32_t)(((L - 1) * ks + D) * 2));
+    const rsrc_t rc = make_rsrc(a.rope_cos, (uint32_t)(L * (D / 2) * 4));
+    const rsrc_t rs = make_rsrc(a.rope_sin, (uint32_t)(L * (D / 2) * 4));
+
+    const int q0 = qb * C::BM;
+    const int qw0 = q0 + wave * 32;
+    const int my_q = qw0 + l32;
+    const bool wave_has_rows = qw0 < L;
+    const int wave_last = min(qw0 + 31, L - 1);
+    const int q_hi = min(q0 + C::BM, L);
+    const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
+
+    // ---- Q: rotate at position my_q, fold in scale*log2(e), round once.
+    Frag<QK> qf[C::KSTEPS];
+    {
+      const int qo = my_q * qs * 2, to = my_q * (D / 2) * 4;
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) {
+        const int g = 2 * s2 + hh;
+        u32x4 w0[1], w1[1];
+        w0[0] = buf_load16(rq, qo + g * 16, 0);
+        w1[0] = buf_load16(rq, qo + g * 16 + D, 0);
+        const int o0 = C::STYLE == STYLE_INTERLEAVED ? 4 * g : 8 * g;
+        const int o1 = C::STYLE == STYLE_INTERLEAVED ? 4 * g + D / 4 : 8 * g + 4;
+        f32x4 c[2], sn[2];
+        c[0] = buf_load16f(rc, to + o0 * 4, 0);
+        c[1] = buf_load16f(rc, to + o1 * 4, 0);
+        sn[0] = buf_load16f(rs, to + o0 * 4, 0);
+        sn[1] = buf_load16f(rs, to + o1 * 4, 0);
+        float x0[8], x1[8];
+        raw_to_f32<uint16_t>(w0, x0);
+        raw_to_f32<uint16_t>(w1, x1);
+        rope_pair<C::STYLE>(x0, x1, c, sn);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x0[j] *= a.qscale;
+          x1[j] *= a.qscale;
+        }
+        qf[s2] = to_frag<QK>(x0);
+        qf[s2 + D / 32] = to_frag<QK>(x1);
+      }
+    }
+
+    // ---- Per-lane load offsets. K item u of this thread is (row0 + u*RPU,
+    // group g0): the lane part is fixed, the item and tile parts are uniform
+    // (scalar offsets) or compile-time (instruction immediates).
+    constexpr int RPU = THREADS / (D / 16);  // K rows between a thread's items
+    const int row0 = tid / (D / 16), g0 = tid % (D / 16);
+    const int k_vo = (row0 * ks + 8 * g0) * 2;
+    constexpr int TAB_O1 = C::STYLE == STYLE_INTERLEAVED ? D : 16;  // bytes from o0 to o1
+    const int t_vo = (row0 * (D / 2) + (C::STYLE == STYLE_INTERLEAVED ? 4 * g0 : 8 * g0)) * 4;
+    const int k_lds = row0 * C::K_STRIDE + g0 * 16;
+    // V: 1 KiB per wave load = VROWS rows; the lane's row within the block and
+    // its swizzled chunk do not depend on the block.
+    constexpr int VWL = C::V_WAVE_LOADS;
+    constexpr int VROWS = 1024 / (2 * D);
+    const int v_r = lane / (2 * D / 16), v_pch = lane % (2 * D / 16);
+    const int v_vo = v_r * ks * 2 + 16 * (v_pch ^ vswz_mask(v_r));
+
+    // K (to registers) and V (straight to LDS) of the tile at kt0; the K
+    // registers are consumed by store_k once this tile's products are issued.
+#ifndef CGR_TABLE_PREFETCH
+#define CGR_TABLE_PREFETCH 1
+#endif
+#ifndef CGR_V_DIRECT
+#define CGR_V_DIRECT 1
+#endif
+    constexpr int VU_REG = CGR_V_DIRECT ? 1 : C::VU;
+    auto issue_loads = [&](int kt0, char* stage, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+                           f32x4 (&ksn)[KI][2], u32x4 (&vw)[VU_REG]) {
+      if constexpr (CGR_V_DIRECT) {
+#pragma unroll
+        for (int u = 0; u < VWL; ++u) {
+          const int blk = wave * VWL + u;
+          if (blk * 1024 < C::V_BYTES)
+            buf_load16_lds(rv, stage + C::K_BYTES + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+          const int blk = (tid + u * THREADS) / 64;  // 64 lanes x 16 B per block, as the direct path
+          vw[u] = buf_load16(rv, v_vo, (kt0 + blk * VROWS) * ks * 2);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KI; ++u) {
+        if (row0 + u * RPU < BN) {
+          const int so = (kt0 + u * RPU) * ks * 2;
+          kw[u][0] = buf_load16(rk, k_vo, so);
+          kw[u][1] = buf_load16(rk, k_vo + D, so);
+          if constexpr (CGR_TABLE_PREFETCH) {
+            const int st = (kt0 + u * RPU) * (D / 2) * 4;
+            kc[u][0] = buf_load16f(rc, t_vo, st);
+            kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
+            ksn[u][0] = buf_load16f(rs, t_vo, st);
+            ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
+          }
+        }
+      }
+    };
+    // Rotate K at the key positions and write it (and V, when it came through
+    // registers) to LDS.
+    auto store_k = [&](int kt0, char* stage, const u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+                       f32x4 (&ksn)[KI][2], const u32x4 (&vw)[VU_REG]) {
+      if constexpr (!CGR_V_DIRECT) {
+#pragma unroll
+        for (int u = 0; u < C::VU; ++u) {
+          const int blk = (tid + u * THREADS) / 64;
+          *(u32x4*)(stage + C::K_BYTES + blk * 1024 + lane * 16) = vw[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < KI; ++u) {
+        if (row0 + u * RPU < BN) {
+          if constexpr (!CGR_TABLE_PREFETCH) {
+            const int st = (kt0 + u * RPU) * (D / 2) * 4;
+            kc[u][0] = buf_load16f(rc, t_vo, st);
+            kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
+            ksn[u][0] = buf_load16f(rs, t_vo, st);
+            ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
+          }
+          float x0[8], x1[8];
+          const u32x4 w0[1] = {kw[u][0]}, w1[1] = {kw[u][1]};
+          raw_to_f32<uint16_t>(w0, x0);
+          raw_to_f32<uint16_t>(w1, x1);
+          rope_pair<C::STYLE>(x0, x1, kc[u], ksn[u]);
+          char* dst = stage + k_lds + u * RPU * C::K_STRIDE;
+          *(u32x4*)dst = to_frag<QK>(x0).v;
+          *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+        }
+      }
+    };
+
+    // Lane offsets of the K fragment reads and of the transposing V reads.
+    const int k_rd = l32 * C::K_STRIDE + hh * 16;
+    const int gi = lane >> 4, li = lane & 15;
+    const int vx = D == 128 ? (li >> 2) : (D == 64 ? (((4 * hh + (li >> 2)) >> 1) & 1) : 0);
+    const int v_lane = (4 * hh + (li >> 2)) * (2 * D) + 16 * (2 * (gi & 1) + ((li & 3) >> 1)) +
+                       8 * (li & 1);
+    int v_rd[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) v_rd[db] = v_lane + 64 * (db ^ vx);
+
+    float m_run = -INFINITY;  // running row max (log2 units, scale folded in)
+    float l_run = 0.f;        // this lane's share of the row sum against m_run
+    f32x16 oacc[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+    const uint32_t ones_bf16 = 0x3f803f80u;
+
+    u32x4 kw[KI][2];
+    f32x4 kc[KI][2], ksn[KI][2];
+    u32x4 vw[VU_REG];
+    __syncthreads();  // the previous unit of this workgroup is done with LDS
+    issue_loads(0, smem, kw, kc, ksn, vw);
+    store_k(0, smem, kw, kc, ksn, vw);
+    wait_vmem();
+    __syncthreads();
+
+    // One key tile. MASK: the tile may hold keys past this wave's rows
+    // (causal) or past the sequence end, so scores are masked first. Tiles
+    // are split into an unmasked run and a masked tail (two loops) so the loop
+    // body is straight-line code and the accumulators never pass a join.
+    auto tile = [&](int j, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      const int kt0 = j * BN;
+      const char* Ks = smem + (j & 1) * C::STAGE;
+      const char* Vs = Ks + C::K_BYTES;
+      char* next = smem + ((j + 1) & 1) * C::STAGE;
+      const bool more = j + 1 < n_tiles;
+      if (more) issue_loads(kt0 + BN, next, kw, kc, ksn, vw);
+      const bool active = wave_has_rows && (!C::CAUSAL || kt0 <= wave_last);
+      if (active) {
+        // S^T = K Q^T (log2 units, scale folded into Q).
+        f32x16 sacc[C::NKB];
+#pragma unroll
+        for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) {
+            Frag<QK> kf;
+            kf.v = *(const u32x4*)(Ks + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
+            sacc[kb] = mma32(kf, qf[s], s == 0 ? (f32x16){} : sacc[kb]);
+          }
+        if constexpr (MASK) {
+          // Key kt0 + kb*32 + 8*(i/4) + 4*hh + i%4 against this lane's row.
+          const int lim = (C::CAUSAL ? min(my_q, L - 1) : L - 1) - kt0 - 4 * hh;
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+        }
+        // Online softmax: m' = max(m, tile max); O, l scaled by 2^(m - m').
+        // Tile 0 holds key 0, which every row may see, so m' is finite from
+        // the first tile on (and 2^(-inf) = 0 clears nothing but zeros).
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+        const float m_new = fmaxf(m_run, pair_max(mx));
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        // P = 2^(s - m'), rounded to bf16 for the P.V product; the row sum adds
+        // the rounded values (packed dot products against (1, 1)).
+        u32x4 pf[C::NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t pk = pack2(OpBF16{}, fast_exp2(sacc[kb][8 * t + 2 * q] - m_new),
+                                        fast_exp2(sacc[kb][8 * t + 2 * q + 1] - m_new));
+              pf[kb][t][q] = pk;
+              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                      __builtin_bit_cast(bf16x2, ones_bf16), l_run,
+                                                      false);
+            }
+        // O^T = alpha O^T + V^T P^T
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            Frag<OpBF16> pfr;
+            pfr.v = pf[kb][t];
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const char* p = Vs + v_rd[db] + (kb * 32 + 16 * t) * (2 * D);
+              const s16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+              const s16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 2 * D));
+              const u32x2 ua = __builtin_bit_cast(u32x2, ra), ub = __builtin_bit_cast(u32x2, rb);
+              Frag<OpBF16> vf;
+              vf.v = (u32x4){ua[0], ua[1], ub[0], ub[1]};
+              oacc[db] = mma32(vf, pfr, (kb == 0 && t == 0) ? oacc[db] * alpha : oacc[db]);
+            }
+          }
+      }
+      if (more) store_k(kt0 + BN, next, kw, kc, ksn, vw);
+      wait_vmem();
+      __syncthreads();
+    };
+
+    // Tiles below n_plain need no mask for any wave of the unit: every key of
+    // the tile precedes the unit's first row (causal) and lies inside the
+    // sequence.
+    const int n_plain = C::CAUSAL ? min(n_tiles, (q0 + 1) / BN) : L / BN;
+    int j = 0;
+    for (; j < n_plain; ++j) tile(j, std::false_type{});
+    for (; j < n_tiles; ++j) tile(j, std::true_type{});
+
+    // ---- Epilogue.
+    const float l_tot = pair_sum(l_run);
+    if (my_q < L) {
+      const float inv = 1.f / l_tot;
+      uint16_t* dst = (uint16_t*)a.o + (long)(tok0 + my_q) * qs + (long)head * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const int d = db * 32 + 8 * a4 + 4 * hh;
+          const float o0 = oacc[db][4 * a4] * inv, o1 = oacc[db][4 * a4 + 1] * inv;
+          const float o2 = oacc[db][4 * a4 + 2] * inv, o3 = oacc[db][4 * a4 + 3] * inv;
+          *(u32x2*)(dst + d) = (u32x2){pack2(OpBF16{}, o0, o1), pack2(OpBF16{}, o2, o3)};
+        }
+      if (a.lse != nullptr && hh == 0)
+        a.lse[lse_base + my_q] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    }
+  }
+};
+
+template <class C>
+__device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head,
+                                         long lse_base, char* smem) {
+  if constexpr (C::F32)
+    Unit<C>::run(a, tok0, L, qb, head, lse_base, smem);
+  else
+    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, smem);
+}
+
 // Dense batch: one workgroup per unit. Heavy units (late query blocks, which
 // see the most keys under the causal mask) are issued first, and when the
 // (batch, kv-head) groups divide evenly over the 8 XCDs, each XCD takes whole
 // groups so the query heads that share a K/V head share that XCD's L2.
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 2) void attn_fwd_dense_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   const int nQ = (a.T + C::BM - 1) / C::BM;
   const int G = a.H / a.KV, groups = a.B * a.KV;
@@ -471,13 +831,13 @@ __global__ __launch_bounds__(C::THREADS, 2) void attn_fwd_dense_kernel(AttnArgs 
   const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
   const int head = kvh * G + hq;
-  Unit<C>::run(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, smem);
+  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, smem);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
 // schedule in order (most expensive first); each item expands to all heads.
 template <class C>
-__global__ __launch_bounds__(C::THREADS, 2) void attn_fwd_varlen_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varlen_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
   __shared__ int s_unit;
   const int n_units = a.sched[0] * a.H;
@@ -493,7 +853,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void attn_fwd_varlen_kernel(AttnArgs
     const int2 sq = items[it];
     const int tok0 = a.cu_seqlens[sq.x];
     const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    Unit<C>::run(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, smem);
+    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, smem);
   }
 }
 
@@ -508,7 +868,7 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
 }
 
 constexpr int kBM = 128;  // query rows per unit (all instances)
-constexpr int kBN = 64;   // keys per tile (all instances)
+constexpr int kBN = CGR_BN;  // keys per tile (all instances)
 
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,

@@ -91,6 +91,10 @@ cgr_status check_common(const void* q, const void* k, const void* v, const void*
   if (rope_max_pos < need_pos)
     return fail(CGR_ERR_INVALID_ARG, "rope tables cover %d positions, the call needs %d",
                 rope_max_pos, need_pos);
+  // The kernels address one sequence of one tensor with 32-bit byte offsets.
+  if ((long)(need_pos + 256) * n_head * head_dim * 4 > (long)INT_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "a sequence of %d tokens x %d heads x %d exceeds 2 GiB",
+                need_pos, n_head, head_dim);
   return CGR_OK;
 }
 
