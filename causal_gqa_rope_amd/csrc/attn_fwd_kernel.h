@@ -10,22 +10,25 @@
 // softmax, so it never leaves the chip ("Attention from Scratch", "Coming
 // from CUDA: FlashAttention").
 //
-// Work unit: one (sequence, query head, block of BM = 128 query rows). A
-// workgroup of four waves runs it; wave w owns query rows 32w..32w+31.
+// Work unit: one (sequence, query head, block of BM = 32 * NW query rows),
+// run by a workgroup of NW waves; wave w owns query rows 32w..32w+31. Two
+// bodies share the unit decomposition:
+//   * UnitFast (bf16 I/O): buffer loads, V straight into LDS, a fixed per-row
+//     softmax reference with a rescaling fallback, a one-tile software
+//     pipeline (see its own comments).
+//   * Unit (f32 I/O): the plain tile loop on f32 matrix cores, described next.
 //
-// Per unit:
+// Per unit (Unit):
 //   * Q rows are loaded once, rotated in f32 at their positions, multiplied by
 //     scale*log2(e) and rounded once to the Q.K^T operand type; they stay in
 //     registers as the B operand of S^T = K Q^T.
-//   * Key/value tiles of BN = 64 rows stream through LDS, double-buffered:
-//     while tile j is multiplied, tile j+1 is already loading into registers
-//     (16-byte global loads); K is rotated at the key positions and rounded to
-//     the operand type on its way into LDS; V goes in unchanged, row-major.
-//   * S^T (keys x queries) comes out of 32x32x16 MFMAs with each lane holding
+//   * Key/value tiles of BN rows stream through LDS, double-buffered: while
+//     tile j is multiplied, tile j+1 is already loading into registers; K is
+//     rotated at the key positions on its way into LDS.
+//   * S^T (keys x queries) comes out of 32x32 MFMAs with each lane holding
 //     one query column, so the row max / row sum need only one exchange with
 //     the partner lane (lane ^ 32) and the probabilities P feed the next
-//     product straight from registers: O^T += V^T P^T, where V^T fragments are
-//     read from the row-major V tile with transposing LDS reads.
+//     product straight from registers: O^T += V^T P^T.
 //   * Causal: tiles entirely above the diagonal are never visited; only tiles
 //     that straddle the diagonal (or the ragged end of a sequence) evaluate
 //     the mask.
@@ -81,7 +84,10 @@ struct Cfg {
   static constexpr bool CAUSAL = CAUSAL_;
   static constexpr int STYLE = STYLE_;
 
-  static constexpr int NW = 4;
+#ifndef CGR_NW
+#define CGR_NW 8
+#endif
+  static constexpr int NW = CGR_NW;
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 32 * NW;  // query rows per unit
 #ifndef CGR_BN
@@ -585,28 +591,18 @@ struct UnitFast {
     // K (to registers) and V (straight to LDS) of the tile at kt0; the K
     // registers are consumed by store_k once this tile's products are issued.
 #ifndef CGR_TABLE_PREFETCH
-#define CGR_TABLE_PREFETCH 1
+#define CGR_TABLE_PREFETCH 0
 #endif
-#ifndef CGR_V_DIRECT
-#define CGR_V_DIRECT 1
-#endif
-    constexpr int VU_REG = CGR_V_DIRECT ? 1 : C::VU;
-    auto issue_loads = [&](int kt0, char* stage, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
-                           f32x4 (&ksn)[KI][2], u32x4 (&vw)[VU_REG]) {
-      if constexpr (CGR_V_DIRECT) {
+    constexpr int VU_REG = 1;  // (V never passes through registers)
+    auto load_v = [&](int kt0, char* stage, u32x4 (&vw)[VU_REG]) {
 #pragma unroll
-        for (int u = 0; u < VWL; ++u) {
-          const int blk = wave * VWL + u;
-          if (blk * 1024 < C::V_BYTES)
-            buf_load16_lds(rv, stage + C::K_BYTES + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < C::VU; ++u) {
-          const int blk = (tid + u * THREADS) / 64;  // 64 lanes x 16 B per block, as the direct path
-          vw[u] = buf_load16(rv, v_vo, (kt0 + blk * VROWS) * ks * 2);
-        }
+      for (int u = 0; u < VWL; ++u) {
+        const int blk = wave * VWL + u;
+        if (blk * 1024 < C::V_BYTES)
+          buf_load16_lds(rv, stage + C::K_BYTES + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
       }
+    };
+    auto load_k = [&](int kt0, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
         if (row0 + u * RPU < BN) {
@@ -623,17 +619,14 @@ struct UnitFast {
         }
       }
     };
-    // Rotate K at the key positions and write it (and V, when it came through
-    // registers) to LDS.
+    auto issue_loads = [&](int kt0, char* stage, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+                           f32x4 (&ksn)[KI][2], u32x4 (&vw)[VU_REG]) {
+      load_v(kt0, stage, vw);
+      load_k(kt0, kw, kc, ksn);
+    };
+    // Rotate K at the key positions and write it to LDS.
     auto store_k = [&](int kt0, char* stage, const u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
                        f32x4 (&ksn)[KI][2], const u32x4 (&vw)[VU_REG]) {
-      if constexpr (!CGR_V_DIRECT) {
-#pragma unroll
-        for (int u = 0; u < C::VU; ++u) {
-          const int blk = (tid + u * THREADS) / 64;
-          *(u32x4*)(stage + C::K_BYTES + blk * 1024 + lane * 16) = vw[u];
-        }
-      }
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
         if (row0 + u * RPU < BN) {
@@ -666,114 +659,203 @@ struct UnitFast {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) v_rd[db] = v_lane + 64 * (db ^ vx);
 
-    float m_run = -INFINITY;  // running row max (log2 units, scale folded in)
-    float l_run = 0.f;        // this lane's share of the row sum against m_run
-    f32x16 oacc[C::DB];
-#pragma unroll
-    for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
     const uint32_t ones_bf16 = 0x3f803f80u;
-
+    f32x16 oacc[C::DB];
+    float l_run = 0.f;  // this lane's share of the row sum
     u32x4 kw[KI][2];
     f32x4 kc[KI][2], ksn[KI][2];
     u32x4 vw[VU_REG];
-    __syncthreads();  // the previous unit of this workgroup is done with LDS
-    issue_loads(0, smem, kw, kc, ksn, vw);
-    store_k(0, smem, kw, kc, ksn, vw);
-    wait_vmem();
-    __syncthreads();
 
-    // One key tile. MASK: the tile may hold keys past this wave's rows
-    // (causal) or past the sequence end, so scores are masked first. Tiles
-    // are split into an unmasked run and a masked tail (two loops) so the loop
-    // body is straight-line code and the accumulators never pass a join.
-    auto tile = [&](int j, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
-      const int kt0 = j * BN;
-      const char* Ks = smem + (j & 1) * C::STAGE;
-      const char* Vs = Ks + C::K_BYTES;
-      char* next = smem + ((j + 1) & 1) * C::STAGE;
-      const bool more = j + 1 < n_tiles;
-      if (more) issue_loads(kt0 + BN, next, kw, kc, ksn, vw);
-      const bool active = wave_has_rows && (!C::CAUSAL || kt0 <= wave_last);
-      if (active) {
-        // S^T = K Q^T (log2 units, scale folded into Q).
-        f32x16 sacc[C::NKB];
+    // Stage tile 0 (K rotated, V) in LDS.
+    auto start = [&]() {
 #pragma unroll
-        for (int s = 0; s < C::KSTEPS; ++s)
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb) {
-            Frag<QK> kf;
-            kf.v = *(const u32x4*)(Ks + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
-            sacc[kb] = mma32(kf, qf[s], s == 0 ? (f32x16){} : sacc[kb]);
-          }
-        if constexpr (MASK) {
-          // Key kt0 + kb*32 + 8*(i/4) + 4*hh + i%4 against this lane's row.
-          const int lim = (C::CAUSAL ? min(my_q, L - 1) : L - 1) - kt0 - 4 * hh;
-#pragma unroll
-          for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-              if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kb][i] = -INFINITY;
-        }
-        // Online softmax: m' = max(m, tile max); O, l scaled by 2^(m - m').
-        // Tile 0 holds key 0, which every row may see, so m' is finite from
-        // the first tile on (and 2^(-inf) = 0 clears nothing but zeros).
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-        const float m_new = fmaxf(m_run, pair_max(mx));
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        // P = 2^(s - m'), rounded to bf16 for the P.V product; the row sum adds
-        // the rounded values (packed dot products against (1, 1)).
-        u32x4 pf[C::NKB][2];
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t pk = pack2(OpBF16{}, fast_exp2(sacc[kb][8 * t + 2 * q] - m_new),
-                                        fast_exp2(sacc[kb][8 * t + 2 * q + 1] - m_new));
-              pf[kb][t][q] = pk;
-              l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
-                                                      __builtin_bit_cast(bf16x2, ones_bf16), l_run,
-                                                      false);
-            }
-        // O^T = alpha O^T + V^T P^T
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            Frag<OpBF16> pfr;
-            pfr.v = pf[kb][t];
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-              const char* p = Vs + v_rd[db] + (kb * 32 + 16 * t) * (2 * D);
-              const s16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-              const s16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 2 * D));
-              const u32x2 ua = __builtin_bit_cast(u32x2, ra), ub = __builtin_bit_cast(u32x2, rb);
-              Frag<OpBF16> vf;
-              vf.v = (u32x4){ua[0], ua[1], ub[0], ub[1]};
-              oacc[db] = mma32(vf, pfr, (kb == 0 && t == 0) ? oacc[db] * alpha : oacc[db]);
-            }
-          }
-      }
-      if (more) store_k(kt0 + BN, next, kw, kc, ksn, vw);
+      for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+      l_run = 0.f;
+      __syncthreads();  // earlier users of this workgroup's LDS are done
+      issue_loads(0, smem, kw, kc, ksn, vw);
+      store_k(0, smem, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
     };
-
+    // Start loading tile j+1 (every wave, every tile).
+    auto prefetch = [&](int j) {
+      if (j + 1 < n_tiles)
+        issue_loads((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, kw, kc, ksn, vw);
+    };
+    // S^T = K Q^T + cinit (log2 units, scale folded in).
+    auto scores = [&](int j, f32x16 (&sacc)[C::NKB], const f32x16& cinit) {
+      const char* Ks = smem + (j & 1) * C::STAGE;
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) {
+          Frag<QK> kf;
+          kf.v = *(const u32x4*)(Ks + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
+          sacc[kb] = mma32(kf, qf[s], s == 0 ? cinit : sacc[kb]);
+        }
+    };
+    // Keys past this lane's row (causal) or past the sequence end get -inf.
+    // Key of accumulator (kb, i): kt0 + kb*32 + 8*(i/4) + 4*hh + i%4.
+    auto mask = [&](int j, f32x16 (&sacc)[C::NKB]) {
+      const int lim = (C::CAUSAL ? min(my_q, L - 1) : L - 1) - j * BN - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+    };
+    auto rowmax = [&](const f32x16 (&sacc)[C::NKB]) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+      return pair_max(mx);
+    };
+    // P = 2^(s - shift), rounded to bf16 for the P.V product (the row sum adds
+    // the rounded values, by packed dot products with (1, 1)); then
+    // O^T = alpha O^T + V^T P^T. SHIFT/SCALE select the optional terms.
+    auto softmax_pv = [&](int j, const f32x16 (&sacc)[C::NKB], auto shift_tag, float shift,
+                          auto scale_tag, float alpha) {
+      constexpr bool SHIFT = decltype(shift_tag)::value;
+      constexpr bool SCALE = decltype(scale_tag)::value;
+      const char* Vs = smem + (j & 1) * C::STAGE + C::K_BYTES;
+      u32x4 pf[C::NKB][2];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float s0 = sacc[kb][8 * t + 2 * q], s1 = sacc[kb][8 * t + 2 * q + 1];
+            if constexpr (SHIFT) {
+              s0 -= shift;
+              s1 -= shift;
+            }
+            const uint32_t pk = pack2(OpBF16{}, fast_exp2(s0), fast_exp2(s1));
+            pf[kb][t][q] = pk;
+            l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk),
+                                                    __builtin_bit_cast(bf16x2, ones_bf16), l_run,
+                                                    false);
+          }
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          Frag<OpBF16> pfr;
+          pfr.v = pf[kb][t];
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db) {
+            const char* p = Vs + v_rd[db] + (kb * 32 + 16 * t) * (2 * D);
+            const s16x4 ra = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+            const s16x4 rb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 8 * 2 * D));
+            const u32x2 ua = __builtin_bit_cast(u32x2, ra), ub = __builtin_bit_cast(u32x2, rb);
+            Frag<OpBF16> vf;
+            vf.v = (u32x4){ua[0], ua[1], ub[0], ub[1]};
+            if constexpr (SCALE)
+              oacc[db] = mma32(vf, pfr, (kb == 0 && t == 0) ? oacc[db] * alpha : oacc[db]);
+            else
+              oacc[db] = mma32(vf, pfr, oacc[db]);
+          }
+        }
+    };
+    // Rotate and store K of tile j+1, wait for its V, then barrier.
+    auto finish = [&](int j) {
+      if (j + 1 < n_tiles) store_k((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, kw, kc, ksn, vw);
+      wait_vmem();
+      __syncthreads();
+    };
     // Tiles below n_plain need no mask for any wave of the unit: every key of
     // the tile precedes the unit's first row (causal) and lies inside the
-    // sequence.
+    // sequence. Tile 0 holds key 0, which every row may see.
     const int n_plain = C::CAUSAL ? min(n_tiles, (q0 + 1) / BN) : L / BN;
-    int j = 0;
-    for (; j < n_plain; ++j) tile(j, std::false_type{});
-    for (; j < n_tiles; ++j) tile(j, std::true_type{});
+
+    // ---- Fast path. Each row's reference m is its exact max over tile 0;
+    // the S^T accumulator of later tiles starts from -m, so the matrix cores
+    // return s - m and p = 2^(s - m) needs no further arithmetic. p may exceed
+    // 1 when later keys score higher; that is exact as long as no p
+    // overflows, which the row sum checks below (any row sum above 2^40, or
+    // not finite, sends the unit to the rescaling path).
+    //
+    // Software-pipelined by one tile: iteration j computes S of tile j+1 on
+    // the matrix cores while the vector units turn S of tile j into P, then
+    // O += V_j P_j while tile j+2's K is rotated. LDS holds K one tile ahead
+    // of V: at the top of iteration j, stage (j+1)&1 has K_{j+1} and stage
+    // j&1 has V_j; the loads of iteration j fill V_{j+1} and, through
+    // registers, K_{j+2}.
+    float m_ref = 0.f;
+    {
+      auto active = [&](int t) { return wave_has_rows && (!C::CAUSAL || t * BN <= wave_last); };
+      // Stage K_0, V_0.
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+      l_run = 0.f;
+      __syncthreads();
+      issue_loads(0, smem, kw, kc, ksn, vw);
+      store_k(0, smem, kw, kc, ksn, vw);
+      wait_vmem();
+      __syncthreads();
+      // S_0, the reference, and stage K_1, V_1.
+      f32x16 s_cur[C::NKB];
+      if (n_tiles > 1) load_k(BN, kw, kc, ksn);
+      if (wave_has_rows) {
+        scores(0, s_cur, (f32x16){});
+        mask(0, s_cur);
+        m_ref = rowmax(s_cur);
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
+      }
+      if (n_tiles > 1) store_k(BN, smem + C::STAGE, kw, kc, ksn, vw);
+      wait_vmem();
+      __syncthreads();
+      const f32x16 negm = (f32x16){} - m_ref;
+
+      auto iter = [&](int j, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        // Loads for V_{j+1} (LDS, stage (j+1)&1) and K_{j+2} (registers).
+        if (j + 1 < n_tiles) load_v((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, vw);
+        if (j + 2 < n_tiles) load_k((j + 2) * BN, kw, kc, ksn);
+        f32x16 s_next[C::NKB];
+        if (j + 1 < n_tiles && active(j + 1)) scores(j + 1, s_next, negm);
+        if (active(j)) {
+          if constexpr (MASK) mask(j, s_cur);
+          softmax_pv(j, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
+        }
+        if (j + 2 < n_tiles) store_k((j + 2) * BN, smem + (j & 1) * C::STAGE, kw, kc, ksn, vw);
+        wait_vmem();
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
+      };
+      int j = 0;
+      for (; j < n_plain; ++j) iter(j, std::false_type{});
+      for (; j < n_tiles; ++j) iter(j, std::true_type{});
+    }
+    float m_fin = m_ref;
+    const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
+
+    // ---- Rescaling path (classic online softmax: m' = max(m, tile max), O
+    // and l scaled by 2^(m - m') every tile), for units whose scores grow too
+    // far beyond the first tile. The whole workgroup redoes the unit.
+    if (__syncthreads_or(overflow)) {
+      float m_run = -INFINITY;
+      start();
+      for (int j = 0; j < n_tiles; ++j) {
+        prefetch(j);
+        if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last)) {
+          f32x16 sacc[C::NKB];
+          scores(j, sacc, (f32x16){});
+          mask(j, sacc);
+          const float m_new = fmaxf(m_run, rowmax(sacc));
+          const float alpha = fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+          softmax_pv(j, sacc, std::true_type{}, m_new, std::true_type{}, alpha);
+        }
+        finish(j);
+      }
+      m_fin = m_run;
+    }
 
     // ---- Epilogue.
     const float l_tot = pair_sum(l_run);
@@ -790,7 +872,7 @@ struct UnitFast {
           *(u32x2*)(dst + d) = (u32x2){pack2(OpBF16{}, o0, o1), pack2(OpBF16{}, o2, o3)};
         }
       if (a.lse != nullptr && hh == 0)
-        a.lse[lse_base + my_q] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+        a.lse[lse_base + my_q] = (m_fin + log2f(l_tot)) * 0.69314718055994531f;
     }
   }
 };
@@ -867,7 +949,7 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
   return hipGetLastError();
 }
 
-constexpr int kBM = 128;  // query rows per unit (all instances)
+constexpr int kBM = 32 * CGR_NW;  // query rows per unit (all instances)
 constexpr int kBN = CGR_BN;  // keys per tile (all instances)
 
 template <int D>

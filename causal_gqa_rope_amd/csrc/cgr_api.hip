@@ -128,8 +128,12 @@ hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, 
   }
 }
 
+// Upper bound on the (sequence, query block) items of a packed batch:
+// sum_s ceil(L_s / BM) <= total / BM + num_seqs. The workspace is sized for
+// blocks of 64 rows, which covers every block height the kernels use.
 long varlen_max_items(int num_seqs, int total_tokens) {
-  return ((long)total_tokens + cgr::kBM - 1) / cgr::kBM + (long)num_seqs;
+  static_assert(cgr::kBM >= 64, "workspace bound assumes query blocks of >= 64 rows");
+  return ((long)total_tokens + 63) / 64 + (long)num_seqs;
 }
 
 }  // namespace

@@ -283,3 +283,52 @@ def test_runs_on_the_callers_stream(gpu):
     s.synchronize()
     ro, rl = run_oracle(w, x)
     assert_close("stream", f64(o), ro, f64(lse), rl, "bf16")
+
+
+@pytest.mark.parametrize("magnitude", [140.0, 600.0])
+def test_scores_growing_far_beyond_the_first_tile(gpu, magnitude):
+    """Keys in later tiles score far above every key of the first tile (by up
+    to ~76 log2 units at magnitude 140; past the float range of 2^(s - m) at
+    600), so the fast path's row sums exceed their bound: the unit must take
+    the rescaling path and still match the oracle."""
+    w = W.custom("growth", B=1, T=300, n_head=4, n_kv_head=2, head_dim=128, base=1e4, seed=21)
+    announce(f"scores growing beyond the first tile's reference, magnitude {magnitude}")
+    x = W.make_inputs(w)
+    q = x["q"].float()
+    k = x["k"].float().clone()
+    # Keys 150.. align with each head group's mean query direction, scaled up.
+    for kvh in range(2):
+        dirn = q[0, :, 2 * kvh:2 * kvh + 2].mean(dim=(0, 1))
+        k[0, 150:, kvh] = k[0, 150:, kvh] + magnitude * dirn / dirn.norm()
+    x["k"] = k.to(torch.bfloat16)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    ro, rl = run_oracle(w, x)
+    o, lse = f64(o), f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "overflow must route to the rescaling path"
+    if magnitude <= 140.0:
+        assert_close("growth", o, ro, lse, rl, "bf16")
+    else:
+        # Scores here reach ~300 log2 units: one f16 rounding of the rotated
+        # operands (relative 2^-11) moves them by ~0.15, which perturbs the
+        # near one-hot weights; the bound scales with the score magnitude.
+        from tests.gpu_cases import errors
+        mx, _ = errors(o, ro)
+        lmx, _ = errors(lse, rl)
+        assert mx <= 0.1 and lmx <= 0.1, (mx, lmx)
+
+
+def test_first_tile_dominates(gpu):
+    """Keys of the first tile score far above all later keys: later
+    probabilities underflow against the first tile's reference, as they do
+    against the exact row max."""
+    w = W.custom("sink", B=1, T=400, n_head=4, n_kv_head=1, head_dim=64, base=1e4, seed=22)
+    announce("first tile dominates")
+    x = W.make_inputs(w)
+    q = x["q"].float()
+    k = x["k"].float().clone()
+    dirn = q[0].mean(dim=(0, 1))
+    k[0, :8, 0] = k[0, :8, 0] + 30.0 * dirn / dirn.norm()
+    x["k"] = k.to(torch.bfloat16)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    ro, rl = run_oracle(w, x)
+    assert_close("sink", f64(o), ro, f64(lse), rl, "bf16")
