@@ -577,6 +577,11 @@ struct UnitFast {
     // (scalar offsets) or compile-time (instruction immediates).
     constexpr int RPU = THREADS / (D / 16);  // K rows between a thread's items
     const int row0 = tid / (D / 16), g0 = tid % (D / 16);
+    // Does this thread own K item u? Compile-time yes when the items divide evenly.
+    auto has_k = [&](int u) {
+      if constexpr (C::K_ITEMS % THREADS == 0) return true;
+      else return row0 + u * RPU < BN;
+    };
     const int k_vo = (row0 * ks + 8 * g0) * 2;
     constexpr int TAB_O1 = C::STYLE == STYLE_INTERLEAVED ? D : 16;  // bytes from o0 to o1
     const int t_vo = (row0 * (D / 2) + (C::STYLE == STYLE_INTERLEAVED ? 4 * g0 : 8 * g0)) * 4;
@@ -598,14 +603,14 @@ struct UnitFast {
 #pragma unroll
       for (int u = 0; u < VWL; ++u) {
         const int blk = wave * VWL + u;
-        if (blk * 1024 < C::V_BYTES)
+        if (C::V_BYTES == NW * VWL * 1024 || blk * 1024 < C::V_BYTES)
           buf_load16_lds(rv, stage + C::K_BYTES + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
       }
     };
     auto load_k = [&](int kt0, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
-        if (row0 + u * RPU < BN) {
+        if (has_k(u)) {
           const int so = (kt0 + u * RPU) * ks * 2;
           kw[u][0] = buf_load16(rk, k_vo, so);
           kw[u][1] = buf_load16(rk, k_vo + D, so);
@@ -629,7 +634,7 @@ struct UnitFast {
                        f32x4 (&ksn)[KI][2], const u32x4 (&vw)[VU_REG]) {
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
-        if (row0 + u * RPU < BN) {
+        if (has_k(u)) {
           if constexpr (!CGR_TABLE_PREFETCH) {
             const int st = (kt0 + u * RPU) * (D / 2) * 4;
             kc[u][0] = buf_load16f(rc, t_vo, st);
@@ -827,7 +832,26 @@ struct UnitFast {
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
       };
+      // Steady state: tiles j+1 and j+2 exist, tile j needs no mask and the
+      // wave has rows, so the iteration is one straight-line block in which
+      // the matrix-core and vector work of independent tiles can interleave.
+      auto iter_steady = [&](int j) {
+        load_v((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, vw);
+        load_k((j + 2) * BN, kw, kc, ksn);
+        f32x16 s_next[C::NKB];
+        scores(j + 1, s_next, negm);
+        softmax_pv(j, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
+        store_k((j + 2) * BN, smem + (j & 1) * C::STAGE, kw, kc, ksn, vw);
+        wait_vmem();
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
+      };
       int j = 0;
+      if (wave_has_rows) {
+        const int n_steady = min(n_plain, n_tiles - 2);
+        for (; j < n_steady; ++j) iter_steady(j);
+      }
       for (; j < n_plain; ++j) iter(j, std::false_type{});
       for (; j < n_tiles; ++j) iter(j, std::true_type{});
     }
