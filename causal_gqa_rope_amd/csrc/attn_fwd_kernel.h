@@ -65,6 +65,16 @@ struct AttnArgs {
 
 constexpr int kSchedHeaderInts = 4;
 
+// The workgroup's LDS: two stages of K and two of V, each its own array, so
+// the compiler can tell a direct-to-LDS load into one of them from reads of
+// the others and does not wait for the load before those reads. The four
+// base pointers are plain values that no lambda captures (a captured copy
+// lives in memory, and a run-time choice read back from memory sends the
+// accesses through flat pointers): helpers take the stage they touch as an
+// argument.
+#define CGR_LDS_PARAMS char *ks0, char *ks1, char *vs0, char *vs1
+__device__ __forceinline__ char* stage_of(int j, char* s0, char* s1) { return (j & 1) ? s1 : s0; }
+
 // Row stride (dwords) of the V tile in LDS: the transposing reads of one
 // half-wave touch 4 rows x 64 bytes, which land on disjoint banks when the
 // stride is 16 or 48 (mod 64) dwords.
@@ -307,7 +317,7 @@ struct Unit {
   // One work unit: query rows qb*BM .. of a sequence of L tokens starting at
   // token tok0, query head `head`. lse_base indexes lse[] for local row 0.
   static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                             long lse_base, char* smem) {
+                                             long lse_base, CGR_LDS_PARAMS) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     const int G = a.H / a.KV, kvh = head / G;
@@ -365,14 +375,14 @@ struct Unit {
     TileRegs<C> regs;
     __syncthreads();  // the previous unit of this workgroup is done with LDS
     load_tile(regs, kp, vp, ks, 0, L, a.rope_cos, a.rope_sin);
-    store_tile(regs, smem, smem + C::K_BYTES);
+    store_tile(regs, ks0, vs0);
     __syncthreads();
 
     for (int j = 0; j < n_tiles; ++j) {
       const int kt0 = j * BN;
       if (j + 1 < n_tiles) load_tile(regs, kp, vp, ks, kt0 + BN, L, a.rope_cos, a.rope_sin);
-      const char* Ks = smem + (j & 1) * C::STAGE;
-      const char* Vs = Ks + C::K_BYTES;
+      const char* Ks = stage_of(j, ks0, ks1);
+      const char* Vs = stage_of(j, vs0, vs1);
       const bool active = wave_has_rows && (!C::CAUSAL || kt0 <= wave_last);
       if (active) {
         // S^T = K Q^T for the BN keys of this tile (log2 units, scale folded in).
@@ -433,10 +443,7 @@ struct Unit {
               oacc[db] = mma32(v_frag(Vs, vbase, kb, t, db), pf, oacc[db]);
           }
       }
-      if (j + 1 < n_tiles) {
-        char* nK = smem + ((j + 1) & 1) * C::STAGE;
-        store_tile(regs, nK, nK + C::K_BYTES);
-      }
+      if (j + 1 < n_tiles) store_tile(regs, stage_of(j + 1, ks0, ks1), stage_of(j + 1, vs0, vs1));
       __syncthreads();
     }
 
@@ -516,7 +523,7 @@ struct UnitFast {
   }
 
   static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                             long lse_base, char* smem) {
+                                             long lse_base, CGR_LDS_PARAMS) {
     // `wave` is the same in every lane: keeping it scalar makes every wave-level
     // decision below (active tiles, masking, V blocks) a scalar branch.
     const int tid = threadIdx.x, lane = tid & 63;
@@ -595,16 +602,13 @@ struct UnitFast {
 
     // K (to registers) and V (straight to LDS) of the tile at kt0; the K
     // registers are consumed by store_k once this tile's products are issued.
-#ifndef CGR_TABLE_PREFETCH
-#define CGR_TABLE_PREFETCH 0
-#endif
     constexpr int VU_REG = 1;  // (V never passes through registers)
-    auto load_v = [&](int kt0, char* stage, u32x4 (&vw)[VU_REG]) {
+    auto load_v = [&](int kt0, char* vs, u32x4 (&vw)[VU_REG]) {
 #pragma unroll
       for (int u = 0; u < VWL; ++u) {
         const int blk = wave * VWL + u;
         if (C::V_BYTES == NW * VWL * 1024 || blk * 1024 < C::V_BYTES)
-          buf_load16_lds(rv, stage + C::K_BYTES + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
+          buf_load16_lds(rv, vs + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
       }
     };
     auto load_k = [&](int kt0, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
@@ -614,40 +618,31 @@ struct UnitFast {
           const int so = (kt0 + u * RPU) * ks * 2;
           kw[u][0] = buf_load16(rk, k_vo, so);
           kw[u][1] = buf_load16(rk, k_vo + D, so);
-          if constexpr (CGR_TABLE_PREFETCH) {
-            const int st = (kt0 + u * RPU) * (D / 2) * 4;
-            kc[u][0] = buf_load16f(rc, t_vo, st);
-            kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
-            ksn[u][0] = buf_load16f(rs, t_vo, st);
-            ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
-          }
+          const int st = (kt0 + u * RPU) * (D / 2) * 4;
+          kc[u][0] = buf_load16f(rc, t_vo, st);
+          kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
+          ksn[u][0] = buf_load16f(rs, t_vo, st);
+          ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
         }
       }
     };
-    auto issue_loads = [&](int kt0, char* stage, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+    auto issue_loads = [&](int kt0, char* vs, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
                            f32x4 (&ksn)[KI][2], u32x4 (&vw)[VU_REG]) {
-      load_v(kt0, stage, vw);
+      load_v(kt0, vs, vw);
       load_k(kt0, kw, kc, ksn);
     };
     // Rotate K at the key positions and write it to LDS.
-    auto store_k = [&](int kt0, char* stage, const u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+    auto store_k = [&](int kt0, char* kst, const u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
                        f32x4 (&ksn)[KI][2], const u32x4 (&vw)[VU_REG]) {
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
         if (has_k(u)) {
-          if constexpr (!CGR_TABLE_PREFETCH) {
-            const int st = (kt0 + u * RPU) * (D / 2) * 4;
-            kc[u][0] = buf_load16f(rc, t_vo, st);
-            kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
-            ksn[u][0] = buf_load16f(rs, t_vo, st);
-            ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
-          }
           float x0[8], x1[8];
           const u32x4 w0[1] = {kw[u][0]}, w1[1] = {kw[u][1]};
           raw_to_f32<uint16_t>(w0, x0);
           raw_to_f32<uint16_t>(w1, x1);
           rope_pair<C::STYLE>(x0, x1, kc[u], ksn[u]);
-          char* dst = stage + k_lds + u * RPU * C::K_STRIDE;
+          char* dst = kst + k_lds + u * RPU * C::K_STRIDE;
           *(u32x4*)dst = to_frag<QK>(x0).v;
           *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
         }
@@ -672,24 +667,22 @@ struct UnitFast {
     u32x4 vw[VU_REG];
 
     // Stage tile 0 (K rotated, V) in LDS.
-    auto start = [&]() {
+    auto start = [&](char* kst, char* vst) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
       l_run = 0.f;
       __syncthreads();  // earlier users of this workgroup's LDS are done
-      issue_loads(0, smem, kw, kc, ksn, vw);
-      store_k(0, smem, kw, kc, ksn, vw);
+      issue_loads(0, vst, kw, kc, ksn, vw);
+      store_k(0, kst, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
     };
     // Start loading tile j+1 (every wave, every tile).
-    auto prefetch = [&](int j) {
-      if (j + 1 < n_tiles)
-        issue_loads((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, kw, kc, ksn, vw);
+    auto prefetch = [&](int j, char* vnext) {
+      if (j + 1 < n_tiles) issue_loads((j + 1) * BN, vnext, kw, kc, ksn, vw);
     };
     // S^T = K Q^T + cinit (log2 units, scale folded in).
-    auto scores = [&](int j, f32x16 (&sacc)[C::NKB], const f32x16& cinit) {
-      const char* Ks = smem + (j & 1) * C::STAGE;
+    auto scores = [&](const char* Ks, f32x16 (&sacc)[C::NKB], const f32x16& cinit) {
 #pragma unroll
       for (int s = 0; s < C::KSTEPS; ++s)
 #pragma unroll
@@ -720,12 +713,9 @@ struct UnitFast {
     // P = 2^(s - shift), rounded to bf16 for the P.V product (the row sum adds
     // the rounded values, by packed dot products with (1, 1)); then
     // O^T = alpha O^T + V^T P^T. SHIFT/SCALE select the optional terms.
-    auto softmax_pv = [&](int j, const f32x16 (&sacc)[C::NKB], auto shift_tag, float shift,
-                          auto scale_tag, float alpha) {
+    auto probs = [&](const f32x16 (&sacc)[C::NKB], auto shift_tag, float shift,
+                     u32x4 (&pf)[C::NKB][2]) {
       constexpr bool SHIFT = decltype(shift_tag)::value;
-      constexpr bool SCALE = decltype(scale_tag)::value;
-      const char* Vs = smem + (j & 1) * C::STAGE + C::K_BYTES;
-      u32x4 pf[C::NKB][2];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -743,6 +733,9 @@ struct UnitFast {
                                                     __builtin_bit_cast(bf16x2, ones_bf16), l_run,
                                                     false);
           }
+    };
+    auto pv = [&](const char* Vs, const u32x4 (&pf)[C::NKB][2], auto scale_tag, float alpha) {
+      constexpr bool SCALE = decltype(scale_tag)::value;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -764,9 +757,15 @@ struct UnitFast {
           }
         }
     };
+    auto softmax_pv = [&](const char* Vs, const f32x16 (&sacc)[C::NKB], auto shift_tag,
+                          float shift, auto scale_tag, float alpha) {
+      u32x4 pf[C::NKB][2];
+      probs(sacc, shift_tag, shift, pf);
+      pv(Vs, pf, scale_tag, alpha);
+    };
     // Rotate and store K of tile j+1, wait for its V, then barrier.
-    auto finish = [&](int j) {
-      if (j + 1 < n_tiles) store_k((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, kw, kc, ksn, vw);
+    auto finish = [&](int j, char* knext) {
+      if (j + 1 < n_tiles) store_k((j + 1) * BN, knext, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
     };
@@ -796,64 +795,77 @@ struct UnitFast {
       for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
       l_run = 0.f;
       __syncthreads();
-      issue_loads(0, smem, kw, kc, ksn, vw);
-      store_k(0, smem, kw, kc, ksn, vw);
+      issue_loads(0, vs0, kw, kc, ksn, vw);
+      store_k(0, ks0, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
       // S_0, the reference, and stage K_1, V_1.
       f32x16 s_cur[C::NKB];
       if (n_tiles > 1) load_k(BN, kw, kc, ksn);
       if (wave_has_rows) {
-        scores(0, s_cur, (f32x16){});
+        scores(ks0, s_cur, (f32x16){});
         mask(0, s_cur);
         m_ref = rowmax(s_cur);
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
       }
-      if (n_tiles > 1) store_k(BN, smem + C::STAGE, kw, kc, ksn, vw);
+      if (n_tiles > 1) store_k(BN, ks1, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
       const f32x16 negm = (f32x16){} - m_ref;
 
-      auto iter = [&](int j, auto mask_tag) {
+      // kj/vj: the stages of tile j; kj1/vj1: those of tile j+1.
+      auto iter = [&](int j, auto mask_tag, char* kj, char* kj1, char* vj, char* vj1) {
         constexpr bool MASK = decltype(mask_tag)::value;
         // Loads for V_{j+1} (LDS, stage (j+1)&1) and K_{j+2} (registers).
-        if (j + 1 < n_tiles) load_v((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, vw);
+        if (j + 1 < n_tiles) load_v((j + 1) * BN, vj1, vw);
         if (j + 2 < n_tiles) load_k((j + 2) * BN, kw, kc, ksn);
         f32x16 s_next[C::NKB];
-        if (j + 1 < n_tiles && active(j + 1)) scores(j + 1, s_next, negm);
+        if (j + 1 < n_tiles && active(j + 1)) scores(kj1, s_next, negm);
         if (active(j)) {
           if constexpr (MASK) mask(j, s_cur);
-          softmax_pv(j, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
+          softmax_pv(vj, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
         }
-        if (j + 2 < n_tiles) store_k((j + 2) * BN, smem + (j & 1) * C::STAGE, kw, kc, ksn, vw);
+        if (j + 2 < n_tiles) store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
         wait_vmem();
         __syncthreads();
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
       };
       // Steady state: tiles j+1 and j+2 exist, tile j needs no mask and the
-      // wave has rows, so the iteration is one straight-line block in which
-      // the matrix-core and vector work of independent tiles can interleave.
-      auto iter_steady = [&](int j) {
-        load_v((j + 1) * BN, smem + ((j + 1) & 1) * C::STAGE, vw);
+      // wave has rows. Unrolled by two so every LDS stage is fixed at compile
+      // time (the direct V load into one stage then needs no wait before the
+      // reads of the others) and S alternates between two register sets; the
+      // iteration is one straight-line block in which the matrix-core and
+      // vector work of the two tiles can interleave.
+      f32x16 s_alt[C::NKB];
+      auto iter_steady = [&](int j, f32x16 (&s_in)[C::NKB], f32x16 (&s_out)[C::NKB], char* kj,
+                             char* kj1, char* vj, char* vj1) {
+        load_v((j + 1) * BN, vj1, vw);
         load_k((j + 2) * BN, kw, kc, ksn);
-        f32x16 s_next[C::NKB];
-        scores(j + 1, s_next, negm);
-        softmax_pv(j, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
-        store_k((j + 2) * BN, smem + (j & 1) * C::STAGE, kw, kc, ksn, vw);
+        // Keep the global loads at the top of the block, a whole block ahead
+        // of their use (left alone, the scheduler sinks them next to it).
+        __builtin_amdgcn_sched_barrier(0);
+        scores(kj1, s_out, negm);
+        softmax_pv(vj, s_in, std::false_type{}, 0.f, std::false_type{}, 1.f);
+        store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
         wait_vmem();
         __syncthreads();
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
       };
       int j = 0;
       if (wave_has_rows) {
         const int n_steady = min(n_plain, n_tiles - 2);
-        for (; j < n_steady; ++j) iter_steady(j);
+        for (; j + 1 < n_steady; j += 2) {
+          iter_steady(j, s_cur, s_alt, ks0, ks1, vs0, vs1);
+          iter_steady(j + 1, s_alt, s_cur, ks1, ks0, vs1, vs0);
+        }
       }
-      for (; j < n_plain; ++j) iter(j, std::false_type{});
-      for (; j < n_tiles; ++j) iter(j, std::true_type{});
+      for (; j < n_plain; ++j)
+        iter(j, std::false_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
+             stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
+      for (; j < n_tiles; ++j)
+        iter(j, std::true_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
+             stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
     }
     float m_fin = m_ref;
     const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
@@ -863,20 +875,20 @@ struct UnitFast {
     // far beyond the first tile. The whole workgroup redoes the unit.
     if (__syncthreads_or(overflow)) {
       float m_run = -INFINITY;
-      start();
+      start(ks0, vs0);
       for (int j = 0; j < n_tiles; ++j) {
-        prefetch(j);
+        prefetch(j, stage_of(j + 1, vs0, vs1));
         if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last)) {
           f32x16 sacc[C::NKB];
-          scores(j, sacc, (f32x16){});
+          scores(stage_of(j, ks0, ks1), sacc, (f32x16){});
           mask(j, sacc);
           const float m_new = fmaxf(m_run, rowmax(sacc));
           const float alpha = fast_exp2(m_run - m_new);
           m_run = m_new;
           l_run *= alpha;
-          softmax_pv(j, sacc, std::true_type{}, m_new, std::true_type{}, alpha);
+          softmax_pv(stage_of(j, vs0, vs1), sacc, std::true_type{}, m_new, std::true_type{}, alpha);
         }
-        finish(j);
+        finish(j, stage_of(j + 1, ks0, ks1));
       }
       m_fin = m_run;
     }
@@ -903,11 +915,11 @@ struct UnitFast {
 
 template <class C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                         long lse_base, char* smem) {
+                                         long lse_base, CGR_LDS_PARAMS) {
   if constexpr (C::F32)
-    Unit<C>::run(a, tok0, L, qb, head, lse_base, smem);
+    Unit<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1);
   else
-    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, smem);
+    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1);
 }
 
 // Dense batch: one workgroup per unit. Heavy units (late query blocks, which
@@ -916,7 +928,8 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int
 // groups so the query heads that share a K/V head share that XCD's L2.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   const int nQ = (a.T + C::BM - 1) / C::BM;
   const int G = a.H / a.KV, groups = a.B * a.KV;
   const int u = blockIdx.x;
@@ -937,14 +950,15 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense
   const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
   const int head = kvh * G + hq;
-  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, smem);
+  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
 // schedule in order (most expensive first); each item expands to all heads.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varlen_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   __shared__ int s_unit;
   const int n_units = a.sched[0] * a.H;
   int* counter = a.sched + 1;
@@ -959,7 +973,7 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varle
     const int2 sq = items[it];
     const int tok0 = a.cu_seqlens[sq.x];
     const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, smem);
+    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, k0, k1, v0, v1);
   }
 }
 
