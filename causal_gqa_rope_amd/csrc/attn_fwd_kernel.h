@@ -548,27 +548,35 @@ struct UnitFast {
     const int q_hi = min(q0 + C::BM, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
 
-    // ---- Q: rotate at position my_q, fold in scale*log2(e), round once.
-    Frag<QK> qf[C::KSTEPS];
+    // ---- Q: the loads are issued here, the rotation (at position my_q, with
+    // scale*log2(e) folded in and one rounding) once the first K tiles' loads
+    // are in flight too.
+    u32x4 q_raw[D / 32][2];
+    f32x4 q_cos[D / 32][2], q_sin[D / 32][2];
     {
       const int qo = my_q * qs * 2, to = my_q * (D / 2) * 4;
 #pragma unroll
       for (int s2 = 0; s2 < D / 32; ++s2) {
         const int g = 2 * s2 + hh;
-        u32x4 w0[1], w1[1];
-        w0[0] = buf_load16(rq, qo + g * 16, 0);
-        w1[0] = buf_load16(rq, qo + g * 16 + D, 0);
+        q_raw[s2][0] = buf_load16(rq, qo + g * 16, 0);
+        q_raw[s2][1] = buf_load16(rq, qo + g * 16 + D, 0);
         const int o0 = C::STYLE == STYLE_INTERLEAVED ? 4 * g : 8 * g;
         const int o1 = C::STYLE == STYLE_INTERLEAVED ? 4 * g + D / 4 : 8 * g + 4;
-        f32x4 c[2], sn[2];
-        c[0] = buf_load16f(rc, to + o0 * 4, 0);
-        c[1] = buf_load16f(rc, to + o1 * 4, 0);
-        sn[0] = buf_load16f(rs, to + o0 * 4, 0);
-        sn[1] = buf_load16f(rs, to + o1 * 4, 0);
+        q_cos[s2][0] = buf_load16f(rc, to + o0 * 4, 0);
+        q_cos[s2][1] = buf_load16f(rc, to + o1 * 4, 0);
+        q_sin[s2][0] = buf_load16f(rs, to + o0 * 4, 0);
+        q_sin[s2][1] = buf_load16f(rs, to + o1 * 4, 0);
+      }
+    }
+    Frag<QK> qf[C::KSTEPS];
+    auto rotate_q = [&]() {
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) {
         float x0[8], x1[8];
+        const u32x4 w0[1] = {q_raw[s2][0]}, w1[1] = {q_raw[s2][1]};
         raw_to_f32<uint16_t>(w0, x0);
         raw_to_f32<uint16_t>(w1, x1);
-        rope_pair<C::STYLE>(x0, x1, c, sn);
+        rope_pair<C::STYLE>(x0, x1, q_cos[s2], q_sin[s2]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           x0[j] *= a.qscale;
@@ -577,7 +585,7 @@ struct UnitFast {
         qf[s2] = to_frag<QK>(x0);
         qf[s2 + D / 32] = to_frag<QK>(x1);
       }
-    }
+    };
 
     // ---- Per-lane load offsets. K item u of this thread is (row0 + u*RPU,
     // group g0): the lane part is fixed, the item and tile parts are uniform
@@ -790,18 +798,23 @@ struct UnitFast {
     float m_ref = 0.f;
     {
       auto active = [&](int t) { return wave_has_rows && (!C::CAUSAL || t * BN <= wave_last); };
-      // Stage K_0, V_0.
+      // Stage K_0, V_0 and K_1, with the loads of Q, K_0 and K_1 all in
+      // flight before the first wait.
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
       l_run = 0.f;
-      __syncthreads();
-      issue_loads(0, vs0, kw, kc, ksn, vw);
+      load_k(0, kw, kc, ksn);
+      u32x4 kw1[KI][2];
+      f32x4 kc1[KI][2], ksn1[KI][2];
+      if (n_tiles > 1) load_k(BN, kw1, kc1, ksn1);
+      __syncthreads();  // earlier users of this workgroup's LDS are done
+      load_v(0, vs0, vw);
+      rotate_q();
       store_k(0, ks0, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
-      // S_0, the reference, and stage K_1, V_1.
+      // S_0 and the reference; K_1 into LDS.
       f32x16 s_cur[C::NKB];
-      if (n_tiles > 1) load_k(BN, kw, kc, ksn);
       if (wave_has_rows) {
         scores(ks0, s_cur, (f32x16){});
         mask(0, s_cur);
@@ -809,7 +822,7 @@ struct UnitFast {
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
       }
-      if (n_tiles > 1) store_k(BN, ks1, kw, kc, ksn, vw);
+      if (n_tiles > 1) store_k(BN, ks1, kw1, kc1, ksn1, vw);
       wait_vmem();
       __syncthreads();
       const f32x16 negm = (f32x16){} - m_ref;
@@ -843,6 +856,11 @@ struct UnitFast {
                              char* kj1, char* vj, char* vj1) {
         load_v((j + 1) * BN, vj1, vw);
         load_k((j + 2) * BN, kw, kc, ksn);
+        // Waves w and w+4 share a SIMD. At equal priority the older one wins
+        // every issue tie, finishes the tile first and then idles at the
+        // barrier while the younger one runs alone; raising the younger
+        // wave's priority for the tile evens the two out.
+        if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
         // Keep the global loads at the top of the block, a whole block ahead
         // of their use (left alone, the scheduler sinks them next to it).
         __builtin_amdgcn_sched_barrier(0);
@@ -851,6 +869,7 @@ struct UnitFast {
         store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
         wait_vmem();
         __syncthreads();
+        __builtin_amdgcn_s_setprio(0);
       };
       int j = 0;
       if (wave_has_rows) {
