@@ -18,6 +18,8 @@ bounded sample of the same workload on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration   (plain copies, for counter scaling)
+  python bench.py --all-configs        (one JSON line per workload configuration,
+                                        attention call only; not the headline line)
 """
 
 from __future__ import annotations
@@ -109,6 +111,51 @@ def copy_calibration(torch, dev) -> None:
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
+def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
+    """Time the attention call alone on every workload configuration (HIP events on
+    the launch stream, mean over `steps` launches after `warmup`)."""
+    stream = torch.cuda.current_stream(dev)
+    for w in W.WORKLOADS.values():
+        inputs = W.make_inputs(w)
+        q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+        max_pos = inputs["max_seqlen"] if w.varlen else w.T
+        cos, sin = cgr.rope_tables(max_pos, w.head_dim, w.base, device=dev)
+        o = torch.empty_like(q)
+        if w.varlen:
+            cu = inputs["cu_seqlens"].to(dev)
+            lengths = (inputs["cu_seqlens"][1:] - inputs["cu_seqlens"][:-1]).tolist()
+            lse = torch.empty((w.n_head, q.shape[0]), dtype=torch.float32, device=dev)
+            ws = torch.empty(max(16, cgr.cgr_attn_fwd_varlen_workspace_size(len(lengths), q.shape[0])),
+                             dtype=torch.uint8, device=dev)
+
+            def call():
+                cgr.gqa_rope_attn_fwd_varlen(q, k, v, cu, int(inputs["max_seqlen"]), cos, sin,
+                                             causal=w.causal, rope_style=w.rope_style, out=o, lse=lse,
+                                             workspace=ws)
+        else:
+            lengths = [w.T] * w.B
+            lse = torch.empty((w.B, w.n_head, w.T), dtype=torch.float32, device=dev)
+
+            def call():
+                cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=w.causal, rope_style=w.rope_style,
+                                      out=o, lse=lse)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        flops = W.algorithmic_flops(w.n_head, w.head_dim, lengths, w.causal)
+        tf = flops / (us * 1e-6) / 1e12
+        print(json.dumps({"workload": w.name, "io": "f32" if w.dtype == "f32" else "bf16",
+                          "us_per_call": round(us, 2), "flops": flops, "tflops": round(tf, 3),
+                          "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2)}), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -116,6 +163,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--all-configs", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -132,6 +180,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(torch, dev)
+        return 0
+    if args.all_configs:
+        all_configs(torch, cgr, W, dev, args.steps, args.warmup)
         return 0
 
     w = W.get(WORKLOAD)

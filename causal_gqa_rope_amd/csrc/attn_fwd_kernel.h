@@ -72,7 +72,7 @@ constexpr int kSchedHeaderInts = 4;
 // lives in memory, and a run-time choice read back from memory sends the
 // accesses through flat pointers): helpers take the stage they touch as an
 // argument.
-#define CGR_LDS_PARAMS char *ks0, char *ks1, char *vs0, char *vs1
+#define CGR_LDS_PARAMS char *ks0, char *ks1, char *vs0, char *vs1, char *qst
 __device__ __forceinline__ char* stage_of(int j, char* s0, char* s1) { return (j & 1) ? s1 : s0; }
 
 // Row stride (dwords) of the V tile in LDS: the transposing reads of one
@@ -120,6 +120,12 @@ struct Cfg {
   static constexpr int SMEM = 2 * STAGE;
   // Direct V loads: 1 KiB (64 lanes x 16 B) per wave instruction.
   static constexpr int V_WAVE_LOADS = (V_BYTES / 1024 + NW - 1) / NW;
+  // Per-wave staging of its 32 query rows (bf16 I/O): Q on the way into the
+  // matrix-core operand layout, O on the way out; rows padded like K. It is
+  // dynamic LDS, which sits after the static K/V stages: those stay within
+  // reach of the 16-bit offsets of the LDS instructions.
+  static constexpr int Q_STRIDE = 2 * D + 16;
+  static constexpr int Q_STAGE_BYTES = F32 ? 0 : NW * 32 * Q_STRIDE;
 
   // Loader work items. K: (row, 8-element group g < D/16), which carries the
   // group pair (g, g + D/16) so that both RoPE pairings find their partners.
@@ -548,43 +554,76 @@ struct UnitFast {
     const int q_hi = min(q0 + C::BM, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
 
-    // ---- Q: the loads are issued here, the rotation (at position my_q, with
-    // scale*log2(e) folded in and one rounding) once the first K tiles' loads
-    // are in flight too.
-    u32x4 q_raw[D / 32][2];
-    f32x4 q_cos[D / 32][2], q_sin[D / 32][2];
-    {
-      const int qo = my_q * qs * 2, to = my_q * (D / 2) * 4;
+    // ---- Q. A lane of the matrix-core operand holds one query row, so loading
+    // Q (and its cos/sin rows) straight into that layout would touch 32 rows
+    // per wave instruction. Instead each wave loads its 32 rows with whole
+    // rows per instruction, rotates them at their positions in that layout
+    // (scale*log2(e) folded in, one rounding to the operand type), writes them
+    // to its own LDS staging area and reads them back as operand fragments.
+    // The loads are issued here; the rest (stage_q) runs once the first K
+    // tiles' loads are in flight too.
+    constexpr int QCH = D / 8;  // 16-byte chunks (8 elements) per row
+    constexpr bool Q_HALF = C::STYLE == STYLE_HALF;
+    // An item is one chunk (interleaved pairs sit inside it) or, for the half
+    // pairing, a chunk and its partner chunk D/2 further on.
+    constexpr int QI_PER_ROW = Q_HALF ? QCH / 2 : QCH;
+    constexpr int QI = 32 * QI_PER_ROW / 64;  // items per lane
+    static_assert(32 * QI_PER_ROW % 64 == 0, "whole items per lane");
+    char* const q_stage = qst + wave * 32 * C::Q_STRIDE;
+    u32x4 q_raw[QI][Q_HALF ? 2 : 1];
+    f32x4 q_cos[QI][Q_HALF ? 2 : 1], q_sin[QI][Q_HALF ? 2 : 1];
 #pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2) {
-        const int g = 2 * s2 + hh;
-        q_raw[s2][0] = buf_load16(rq, qo + g * 16, 0);
-        q_raw[s2][1] = buf_load16(rq, qo + g * 16 + D, 0);
-        const int o0 = C::STYLE == STYLE_INTERLEAVED ? 4 * g : 8 * g;
-        const int o1 = C::STYLE == STYLE_INTERLEAVED ? 4 * g + D / 4 : 8 * g + 4;
-        q_cos[s2][0] = buf_load16f(rc, to + o0 * 4, 0);
-        q_cos[s2][1] = buf_load16f(rc, to + o1 * 4, 0);
-        q_sin[s2][0] = buf_load16f(rs, to + o0 * 4, 0);
-        q_sin[s2][1] = buf_load16f(rs, to + o1 * 4, 0);
+    for (int i = 0; i < QI; ++i) {
+      const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+      const int row = qw0 + r;  // rows past the sequence read as zeros (buffer range)
+      const int qo = row * qs * 2 + c * 16, to = row * (D / 2) * 4;
+      q_raw[i][0] = buf_load16(rq, qo, 0);
+      if constexpr (Q_HALF) {
+        q_raw[i][1] = buf_load16(rq, qo + D, 0);
+        q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
+        q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
+        q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
+        q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
+      } else {
+        q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
+        q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
       }
     }
     Frag<QK> qf[C::KSTEPS];
-    auto rotate_q = [&]() {
+    auto stage_q = [&]() {
 #pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2) {
+      for (int i = 0; i < QI; ++i) {
+        const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+        char* dst = q_stage + r * C::Q_STRIDE + c * 16;
         float x0[8], x1[8];
-        const u32x4 w0[1] = {q_raw[s2][0]}, w1[1] = {q_raw[s2][1]};
+        const u32x4 w0[1] = {q_raw[i][0]};
         raw_to_f32<uint16_t>(w0, x0);
-        raw_to_f32<uint16_t>(w1, x1);
-        rope_pair<C::STYLE>(x0, x1, q_cos[s2], q_sin[s2]);
+        if constexpr (Q_HALF) {
+          const u32x4 w1[1] = {q_raw[i][1]};
+          raw_to_f32<uint16_t>(w1, x1);
+          rope_pair<STYLE_HALF>(x0, x1, q_cos[i], q_sin[i]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x0[j] *= a.qscale;
-          x1[j] *= a.qscale;
+          for (int m = 0; m < 4; ++m) {
+            const float x = x0[2 * m], y = x0[2 * m + 1];
+            x0[2 * m] = x * q_cos[i][0][m] - y * q_sin[i][0][m];
+            x0[2 * m + 1] = x * q_sin[i][0][m] + y * q_cos[i][0][m];
+          }
         }
-        qf[s2] = to_frag<QK>(x0);
-        qf[s2 + D / 32] = to_frag<QK>(x1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x0[j] *= a.qscale;
+        *(u32x4*)dst = to_frag<QK>(x0).v;
+        if constexpr (Q_HALF) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x1[j] *= a.qscale;
+          *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+        }
       }
+      // Operand fragments: k-step s of lane (l32, hh) holds elements 16s+8hh..+7
+      // of row l32, the same split as the K fragments.
+#pragma unroll
+      for (int s2 = 0; s2 < C::KSTEPS; ++s2)
+        qf[s2].v = *(const u32x4*)(q_stage + l32 * C::Q_STRIDE + 32 * s2 + 16 * hh);
     };
 
     // ---- Per-lane load offsets. K item u of this thread is (row0 + u*RPU,
@@ -809,7 +848,7 @@ struct UnitFast {
       if (n_tiles > 1) load_k(BN, kw1, kc1, ksn1);
       __syncthreads();  // earlier users of this workgroup's LDS are done
       load_v(0, vs0, vw);
-      rotate_q();
+      stage_q();
       store_k(0, ks0, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
@@ -912,23 +951,33 @@ struct UnitFast {
       m_fin = m_run;
     }
 
-    // ---- Epilogue.
+    // ---- Epilogue: O = O^T / l, rounded to bf16, goes through the wave's
+    // staging area and leaves with whole rows per wave instruction; rows past
+    // the sequence end fall outside the buffer range and are dropped.
     const float l_tot = pair_sum(l_run);
-    if (my_q < L) {
-      const float inv = 1.f / l_tot;
-      uint16_t* dst = (uint16_t*)a.o + (long)(tok0 + my_q) * qs + (long)head * D;
+    const float inv = 1.f / l_tot;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const int d = db * 32 + 8 * a4 + 4 * hh;
-          const float o0 = oacc[db][4 * a4] * inv, o1 = oacc[db][4 * a4 + 1] * inv;
-          const float o2 = oacc[db][4 * a4 + 2] * inv, o3 = oacc[db][4 * a4 + 3] * inv;
-          *(u32x2*)(dst + d) = (u32x2){pack2(OpBF16{}, o0, o1), pack2(OpBF16{}, o2, o3)};
-        }
-      if (a.lse != nullptr && hh == 0)
-        a.lse[lse_base + my_q] = (m_fin + log2f(l_tot)) * 0.69314718055994531f;
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = db * 32 + 8 * a4 + 4 * hh;
+        const float o0 = oacc[db][4 * a4] * inv, o1 = oacc[db][4 * a4 + 1] * inv;
+        const float o2 = oacc[db][4 * a4 + 2] * inv, o3 = oacc[db][4 * a4 + 3] * inv;
+        *(u32x2*)(q_stage + l32 * C::Q_STRIDE + d * 2) =
+            (u32x2){pack2(OpBF16{}, o0, o1), pack2(OpBF16{}, o2, o3)};
+      }
+    {
+      uint16_t* obase = (uint16_t*)a.o + (long)tok0 * qs + (long)head * D;
+      const rsrc_t ro = make_rsrc(obase, (uint32_t)(((L - 1) * qs + D) * 2));
+#pragma unroll
+      for (int i = 0; i < 32 * QCH / 64; ++i) {
+        const int flat = i * 64 + lane, r = flat / QCH, c = flat % QCH;
+        const u32x4 row = *(const u32x4*)(q_stage + r * C::Q_STRIDE + c * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(row, ro, (qw0 + r) * qs * 2 + c * 16, 0, 0);
+      }
     }
+    if (a.lse != nullptr && hh == 0 && my_q < L)
+      a.lse[lse_base + my_q] = (m_fin + log2f(l_tot)) * 0.69314718055994531f;
   }
 };
 
@@ -936,9 +985,9 @@ template <class C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head,
                                          long lse_base, CGR_LDS_PARAMS) {
   if constexpr (C::F32)
-    Unit<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1);
+    Unit<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1, qst);
   else
-    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1);
+    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1, qst);
 }
 
 // Dense batch: one workgroup per unit. Heavy units (late query blocks, which
@@ -949,6 +998,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
+  extern __shared__ __attribute__((aligned(16))) char qst[];
   const int nQ = (a.T + C::BM - 1) / C::BM;
   const int G = a.H / a.KV, groups = a.B * a.KV;
   const int u = blockIdx.x;
@@ -969,7 +1019,7 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense
   const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
   const int head = kvh * G + hq;
-  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1);
+  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1, qst);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
@@ -978,6 +1028,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varlen_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
+  extern __shared__ __attribute__((aligned(16))) char qst[];
   __shared__ int s_unit;
   const int n_units = a.sched[0] * a.H;
   int* counter = a.sched + 1;
@@ -992,7 +1043,7 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varle
     const int2 sq = items[it];
     const int tok0 = a.cu_seqlens[sq.x];
     const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, k0, k1, v0, v1);
+    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, k0, k1, v0, v1, qst);
   }
 }
 
@@ -1000,9 +1051,11 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varle
 template <class C>
 hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t stream) {
   if (varlen)
-    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
+                       stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), 0, stream, a);
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
+                       stream, a);
   return hipGetLastError();
 }
 
