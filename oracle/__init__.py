@@ -25,6 +25,12 @@ one (batch, head) at a time, with the full T x T score matrix materialised:
    log-sum-exp of each row's scaled, masked scores (not on the pages; it is
    what the row's softmax denominator is, in log form).
 
+The backward (``attention_dense_bwd``, ``attention_varlen_bwd``) is the chain
+rule applied to that definition, op by op in reverse ("Train It & Run for
+Real", section "Coming from CUDA: where's .backward()?": backprop is the
+chain rule through every op, RoPE and attention included): from dL/dO it
+returns dL/dq, dL/dk, dL/dv of the un-rotated inputs.
+
 Packed variable-length batches (the kohakutt page, Highlights: "packed
 variable-length batches") are the concatenation of independent sequences:
 positions restart at 0 in every sequence and the mask never crosses a
@@ -49,6 +55,9 @@ __all__ = [
     "attention_dense",
     "attention_varlen",
     "attention_rows",
+    "apply_rope_transpose",
+    "attention_dense_bwd",
+    "attention_varlen_bwd",
 ]
 
 
@@ -231,3 +240,105 @@ def attention_rows(q, k, v, rows: Sequence, *, causal: bool = True, base: float 
         outs.append((e / den) @ vals[:n])
         lses.append(m + math.log(den))
     return np.array(outs).reshape(len(rows), d), np.array(lses)
+
+
+# ----------------------------------------------------------------------------- backward
+
+def apply_rope_transpose(g, positions, base: float, style: str = "interleaved") -> np.ndarray:
+    """The transpose of the rotation of ``apply_rope``, applied to g ([T, ..., d]).
+
+    The chain rule through y = R(p) x gives dL/dx = R(p)^T dL/dy. Pair i
+    (partners a_i, b_i) turns back by angle(p, i):
+        x[a_i] = g[a_i] cos + g[b_i] sin,  x[b_i] = -g[a_i] sin + g[b_i] cos.
+    """
+    g = _f64(g)
+    d = g.shape[-1]
+    pos = np.asarray(positions, dtype=np.float64)
+    ang = np.outer(pos, rope_inv_freq(d, base))
+    shape = (g.shape[0],) + (1,) * (g.ndim - 2) + (d // 2,)
+    c = np.cos(ang).reshape(shape)
+    s = np.sin(ang).reshape(shape)
+    x = np.empty_like(g)
+    if style == "interleaved":
+        a, b = g[..., 0::2], g[..., 1::2]
+        x[..., 0::2] = a * c + b * s
+        x[..., 1::2] = -a * s + b * c
+    elif style == "half":
+        a, b = g[..., : d // 2], g[..., d // 2:]
+        x[..., : d // 2] = a * c + b * s
+        x[..., d // 2:] = -a * s + b * c
+    else:
+        raise ValueError(f"unknown rope style {style!r}")
+    return x
+
+
+def _one_sequence_bwd(q, k, v, dout, causal: bool, scale: float, base: float, style: str):
+    """Gradients for one sequence: q, dout [L, H, d], k/v [L, KV, d] float64.
+
+    Reverse of ``_one_sequence``, op by op, for every head:
+        O = P V                  ->  dV += P^T dO,  dP = dO V^T
+        P = softmax_j(S)         ->  dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+        S = scale * Qr Kr^T      ->  dQr = scale dS Kr,  dKr += scale dS^T Qr
+        Qr = R Q, Kr = R K       ->  dQ = R^T dQr,  dK = R^T dKr
+    The heads of one K/V group add their contributions to that group's dK and
+    dV. Masked entries have P = 0 and so dS = 0.
+    """
+    L, H, d = q.shape
+    KV = k.shape[1]
+    G = H // KV
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    if L == 0:
+        return dq, dk, dv
+    pos = np.arange(L)
+    qr = apply_rope(q, pos, base, style)
+    kr = apply_rope(k, pos, base, style)
+    dqr = np.zeros_like(q)
+    dkr = np.zeros_like(k)
+    future = np.triu(np.ones((L, L), dtype=bool), k=1) if causal else None
+    for h in range(H):
+        kv = h // G
+        S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
+        if causal:
+            S[future] = -np.inf
+        e = np.exp(S - S.max(axis=1)[:, None])
+        P = e / e.sum(axis=1)[:, None]
+        dv[:, kv, :] += P.T @ dout[:, h, :]
+        dP = dout[:, h, :] @ v[:, kv, :].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dqr[:, h, :] = (dS @ kr[:, kv, :]) * scale
+        dkr[:, kv, :] += (dS.T @ qr[:, h, :]) * scale
+    dq = apply_rope_transpose(dqr, pos, base, style)
+    dk = apply_rope_transpose(dkr, pos, base, style)
+    return dq, dk, dv
+
+
+def attention_dense_bwd(q, k, v, dout, *, causal: bool = True, base: float = 10000.0,
+                        style: str = "interleaved", scale: Optional[float] = None):
+    """Dense batch backward: q/dout [B,T,H,d], k/v [B,T,KV,d] -> dq, dk, dv (float64, same shapes)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, T, H, d = q.shape
+    _check_heads(H, k.shape[2])
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        dq[b], dk[b], dv[b] = _one_sequence_bwd(q[b], k[b], v[b], dout[b], causal, scale, base, style)
+    return dq, dk, dv
+
+
+def attention_varlen_bwd(q, k, v, dout, cu_seqlens, *, causal: bool = True, base: float = 10000.0,
+                         style: str = "interleaved", scale: Optional[float] = None):
+    """Packed batch backward: q/dout [total,H,d], k/v [total,KV,d], cu_seqlens [n+1]; each sequence
+    on its own, positions restarting at 0. Returns dq, dk, dv (float64, same shapes)."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    total, H, d = q.shape
+    _check_heads(H, k.shape[1])
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        dq[a:b], dk[a:b], dv[a:b] = _one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,
+                                                      base, style)
+    return dq, dk, dv

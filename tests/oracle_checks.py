@@ -366,6 +366,179 @@ def check_rows_match_full():
     assert lengths == [3, 11, 6]
 
 
+# ------------------------------------------------------------------------ backward
+#
+# The gradients are pinned to finite differences of the (already pinned) forward,
+# to torch's float64 autograd through its own scaled-dot-product attention, and to
+# identities that any correct gradient of this function satisfies.
+
+def check_rope_transpose_inverts_rotation():
+    # R(p) is orthogonal: its transpose undoes it, and <R x, y> = <x, R^T y>.
+    rng = RNG(30)
+    pos = np.array([0, 1, 7, 300, 4095])
+    for style in ("interleaved", "half"):
+        for d in (2, 8, 64):
+            x = rng.standard_normal((5, 3, d))
+            y = rng.standard_normal((5, 3, d))
+            rx = oracle.apply_rope(x, pos, 10000.0, style)
+            assert np.allclose(oracle.apply_rope_transpose(rx, pos, 10000.0, style), x, atol=1e-12)
+            lhs = np.sum(rx * y)
+            rhs = np.sum(x * oracle.apply_rope_transpose(y, pos, 10000.0, style))
+            assert abs(lhs - rhs) < 1e-11
+
+
+def check_bwd_finite_differences():
+    # Central differences of L = sum(O * W) with respect to every entry of q, k, v.
+    rng = RNG(31)
+    B, T, H, KV, d = 1, 6, 4, 2, 4
+    eps = 1e-5
+    for causal, style, base in ((True, "interleaved", 10000.0), (False, "interleaved", 500000.0),
+                                (True, "half", 10000.0), (False, "half", 1e6)):
+        q = rng.standard_normal((B, T, H, d))
+        k = rng.standard_normal((B, T, KV, d))
+        v = rng.standard_normal((B, T, KV, d))
+        W = rng.standard_normal((B, T, H, d))
+
+        def loss(q_, k_, v_):
+            o, _ = oracle.attention_dense(q_, k_, v_, causal=causal, base=base, style=style)
+            return float(np.sum(o * W))
+
+        dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=causal, base=base, style=style)
+        for which, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[which]
+                args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[which]
+                fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+                assert abs(fd - g[idx]) < 1e-7, (which, idx, causal, style, fd, g[idx])
+
+
+def check_bwd_torch_autograd():
+    # torch's float64 autograd through a rotation written as a complex product
+    # (pair (a, b) is the complex number a + ib, turned by e^{i angle}) and
+    # torch's scaled_dot_product_attention with GQA sharing.
+    rng = RNG(32)
+    B, T, H, KV, d = 2, 23, 6, 2, 16
+    for causal, style, base in ((True, "interleaved", 10000.0), (False, "half", 500000.0)):
+        q = rng.standard_normal((B, T, H, d))
+        k = rng.standard_normal((B, T, KV, d))
+        v = rng.standard_normal((B, T, KV, d))
+        W = rng.standard_normal((B, T, H, d))
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        ang = torch.outer(torch.arange(T, dtype=torch.float64),
+                          base ** (-torch.arange(0, d, 2, dtype=torch.float64) / d))
+        turn = torch.polar(torch.ones_like(ang), ang)[None, :, None, :]
+
+        def rot(x):
+            if style == "interleaved":
+                z = torch.view_as_complex(x.reshape(*x.shape[:-1], d // 2, 2).contiguous())
+                return torch.view_as_real(z * turn).reshape(x.shape)
+            z = torch.complex(x[..., : d // 2], x[..., d // 2:]) * turn
+            return torch.cat([z.real, z.imag], dim=-1)
+
+        o = torch.nn.functional.scaled_dot_product_attention(
+            rot(tq).transpose(1, 2), rot(tk).transpose(1, 2), tv.transpose(1, 2),
+            is_causal=causal, enable_gqa=True).transpose(1, 2)
+        (o * torch.from_numpy(W)).sum().backward()
+        dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=causal, base=base, style=style)
+        assert np.allclose(dq, tq.grad.numpy(), atol=1e-11, rtol=0)
+        assert np.allclose(dk, tk.grad.numpy(), atol=1e-11, rtol=0)
+        assert np.allclose(dv, tv.grad.numpy(), atol=1e-11, rtol=0)
+
+
+def check_bwd_gqa_is_mha_summed():
+    # A K/V head shared by G query heads gets the sum of the gradients that G
+    # private copies of it would get; dq does not change.
+    rng = RNG(33)
+    G = 3
+    q = rng.standard_normal((2, 15, 6, 8))
+    k = rng.standard_normal((2, 15, 2, 8))
+    v = rng.standard_normal((2, 15, 2, 8))
+    W = rng.standard_normal((2, 15, 6, 8))
+    dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W)
+    dq2, dk2, dv2 = oracle.attention_dense_bwd(q, np.repeat(k, G, axis=2), np.repeat(v, G, axis=2), W)
+    assert np.allclose(dq, dq2, atol=1e-13)
+    assert np.allclose(dk, dk2.reshape(2, 15, 2, G, 8).sum(axis=3), atol=1e-13)
+    assert np.allclose(dv, dv2.reshape(2, 15, 2, G, 8).sum(axis=3), atol=1e-13)
+
+
+def check_bwd_invariants():
+    rng = RNG(34)
+    B, T, H, KV, d = 2, 21, 4, 2, 8
+    G = H // KV
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, T, KV, d))
+    v = rng.standard_normal((B, T, KV, d))
+    W = rng.standard_normal((B, T, H, d))
+    for causal in (True, False):
+        dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=causal)
+        for g in range(KV):
+            hs = slice(g * G, (g + 1) * G)
+            # O(q * c, k / c) = O(q, k): the derivative in c at c = 1 is
+            # <dq, q> - <dk, k> = 0, per K/V group and per sequence.
+            for b in range(B):
+                assert abs(np.sum(dq[b, :, hs] * q[b, :, hs]) - np.sum(dk[b, :, g] * k[b, :, g])) < 1e-11
+            # Every output row is a convex combination of value rows, so adding a
+            # constant vector to every value row adds it to every output row:
+            # sum over tokens of dv = sum over tokens and the group's heads of dO.
+            assert np.allclose(dv[:, :, g].sum(axis=1), W[:, :, hs].sum(axis=(1, 2)), atol=1e-12)
+
+
+def check_bwd_closed_forms():
+    rng = RNG(35)
+    T = 30
+    k = rng.standard_normal((1, T, 2, 16))
+    v = rng.standard_normal((1, T, 2, 16))
+    W = rng.standard_normal((1, T, 4, 16))
+    # q = 0: all allowed scores are 0, so P is uniform over the allowed keys.
+    # Then dk = 0 (every dS_ij multiplies a zero query), and key j of group g
+    # receives sum over i >= j and the group's heads of dO_i / (i + 1).
+    q = np.zeros((1, T, 4, 16))
+    dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=True)
+    assert np.array_equal(dk, np.zeros_like(dk))
+    for g in range(2):
+        w = W[0, :, 2 * g:2 * g + 2].sum(axis=1) / np.arange(1, T + 1)[:, None]
+        expect = np.cumsum(w[::-1], axis=0)[::-1]
+        assert np.allclose(dv[0, :, g], expect, atol=1e-13)
+    # Without the mask and q = 0, every key gets the mean of the group's dO.
+    dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=False)
+    assert np.allclose(dv[0, :, 1], np.broadcast_to(W[0, :, 2:].sum(axis=1).mean(axis=0), (T, 16)),
+                       atol=1e-13)
+    # Row 0 under the mask sees only key 0: P = 1, so dS = 0 and query 0 gets no gradient.
+    q = rng.standard_normal((1, T, 4, 16))
+    dq, _, _ = oracle.attention_dense_bwd(q, k, v, W, causal=True)
+    assert np.all(dq[0, 0] == 0.0)
+    # One token: O = v, so dq = dk = 0 and dv is the sum of the group's dO.
+    q1, k1, v1, W1 = q[:, :1], k[:, :1], v[:, :1], W[:, :1]
+    for causal in (True, False):
+        dq, dk, dv = oracle.attention_dense_bwd(q1, k1, v1, W1, causal=causal)
+        assert np.all(dq == 0.0) and np.all(dk == 0.0)
+        assert np.allclose(dv[0, 0], W1[0, 0].reshape(2, 2, 16).sum(axis=1), atol=1e-15)
+
+
+def check_bwd_varlen_is_concat_of_dense():
+    rng = RNG(36)
+    lengths = [5, 1, 0, 13, 8]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total = int(cu[-1])
+    q = rng.standard_normal((total, 4, 8))
+    k = rng.standard_normal((total, 2, 8))
+    v = rng.standard_normal((total, 2, 8))
+    W = rng.standard_normal((total, 4, 8))
+    for causal, style in ((True, "interleaved"), (False, "half")):
+        dq, dk, dv = oracle.attention_varlen_bwd(q, k, v, W, cu, causal=causal, style=style)
+        for s, L in enumerate(lengths):
+            a = int(cu[s])
+            if L == 0:
+                continue
+            r = oracle.attention_dense_bwd(q[None, a:a + L], k[None, a:a + L], v[None, a:a + L],
+                                           W[None, a:a + L], causal=causal, style=style)
+            assert np.array_equal(dq[a:a + L], r[0][0]) and np.array_equal(dk[a:a + L], r[1][0])
+            assert np.array_equal(dv[a:a + L], r[2][0])
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -385,4 +558,11 @@ ALL_CHECKS = [
     check_scale_argument,
     check_varlen_is_concat_of_dense,
     check_rows_match_full,
+    check_rope_transpose_inverts_rotation,
+    check_bwd_finite_differences,
+    check_bwd_torch_autograd,
+    check_bwd_gqa_is_mha_summed,
+    check_bwd_invariants,
+    check_bwd_closed_forms,
+    check_bwd_varlen_is_concat_of_dense,
 ]

@@ -40,6 +40,33 @@ MUTANTS = [
     ("sampled row sees one key too few", "n = t + 1 if causal else L", "n = t if causal else L"),
     ("sampled row uses wrong KV head", "keys, vals = k[b, :, h // G], v[b, :, h // G]",
      "keys, vals = k[b, :, h % KV], v[b, :, h % KV]"),
+    # Backward.
+    ("softmax backward without the row-sum term",
+     "dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))", "dS = P * dP"),
+    ("rotation transposed with the wrong sign", "x[..., 0::2] = a * c + b * s",
+     "x[..., 0::2] = a * c - b * s"),
+    ("half-pairing transpose with the wrong sign", "x[..., d // 2:] = -a * s + b * c",
+     "x[..., d // 2:] = a * s + b * c"),
+    ("dq without the softmax scale", "dqr[:, h, :] = (dS @ kr[:, kv, :]) * scale",
+     "dqr[:, h, :] = dS @ kr[:, kv, :]"),
+    ("dk from un-rotated queries", "dkr[:, kv, :] += (dS.T @ qr[:, h, :]) * scale",
+     "dkr[:, kv, :] += (dS.T @ q[:, h, :]) * scale"),
+    ("dk not accumulated over the group", "dkr[:, kv, :] += (dS.T @ qr[:, h, :]) * scale",
+     "dkr[:, kv, :] = (dS.T @ qr[:, h, :]) * scale"),
+    ("dv not accumulated over the group", "dv[:, kv, :] += P.T @ dout[:, h, :]",
+     "dv[:, kv, :] = P.T @ dout[:, h, :]"),
+    ("dv from P instead of its transpose", "dv[:, kv, :] += P.T @ dout[:, h, :]",
+     "dv[:, kv, :] += P @ dout[:, h, :]"),
+    ("dP against the wrong K/V head", "dP = dout[:, h, :] @ v[:, kv, :].T",
+     "dP = dout[:, h, :] @ v[:, h % KV, :].T"),
+    ("dq left rotated", "dq = apply_rope_transpose(dqr, pos, base, style)", "dq = dqr"),
+    ("backward ignores the mask", "        if causal:\n            S[future] = -np.inf\n        e = np.exp",
+     "        e = np.exp"),
+    ("backward positions do not restart per sequence",
+     "_one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,\n"
+     "                                                      base, style)",
+     "(lambda r: (r[0][a:], r[1][a:], r[2][a:]))(_one_sequence_bwd(q[:b], k[:b], v[:b], dout[:b],"
+     " causal, scale, base, style))"),
 ]
 
 
