@@ -4,8 +4,9 @@ Argument marshalling only. Every step of the computation runs in the HIP
 kernels of ``libcgr.so``; torch supplies device memory and the current
 stream. The functions carry the names of the C entry points declared in
 ``include/cgr.h`` (``cgr_rope_tables``, ``cgr_gqa_rope_attn_fwd``,
-``cgr_gqa_rope_attn_fwd_varlen``, ...); the short names (``rope_tables``,
-``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``) are the same functions.
+``cgr_gqa_rope_attn_fwd_varlen``, ``cgr_gqa_rope_attn_bwd``, ...); the short
+names (``rope_tables``, ``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``,
+``gqa_rope_attn_bwd``) are the same functions.
 
 The library leaves the HIP runtime's symbols unresolved; before loading it,
 the binding makes the runtime torch already loaded globally visible, so the
@@ -30,10 +31,13 @@ __all__ = [
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_varlen_device_status",
+    "cgr_attn_bwd_workspace_size",
+    "cgr_gqa_rope_attn_bwd",
     "cgr_version",
     "rope_tables",
     "gqa_rope_attn_fwd",
     "gqa_rope_attn_fwd_varlen",
+    "gqa_rope_attn_bwd",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -54,6 +58,8 @@ EXPORTED_SYMBOLS = (
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_varlen_device_status",
+    "cgr_attn_bwd_workspace_size",
+    "cgr_gqa_rope_attn_bwd",
     "cgr_last_error",
     "cgr_version",
 )
@@ -101,6 +107,11 @@ def library() -> ctypes.CDLL:
                                                  i32, i32, vp, vp, i32, i32, i32, f32, i32, vp,
                                                  ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd_varlen.restype = i32
+    lib.cgr_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.cgr_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_gqa_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, vp, vp, i32, i32, i32, f32, i32, vp, ctypes.c_size_t, vp]
+    lib.cgr_gqa_rope_attn_bwd.restype = i32
     lib.cgr_varlen_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.cgr_varlen_device_status.restype = i32
     lib.cgr_last_error.argtypes = []
@@ -258,6 +269,61 @@ def cgr_varlen_device_status(workspace: torch.Tensor) -> int:
     return int(st.value)
 
 
+def cgr_attn_bwd_workspace_size(B: int, T: int, n_head: int, n_kv_head: int, head_dim: int) -> int:
+    return int(library().cgr_attn_bwd_workspace_size(int(B), int(T), int(n_head), int(n_kv_head),
+                                                      int(head_dim)))
+
+
+def cgr_gqa_rope_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          lse: torch.Tensor, dout: torch.Tensor, rope_cos: torch.Tensor,
+                          rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
+                          softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                          dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Dense backward: the forward's q, k, v, o [B,T,.,d], lse [B,H,T] and dL/dO -> (dq, dk, dv).
+
+    Every argument that the forward also takes must be the same as in that
+    forward call (bf16 tensors only).
+    """
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(n, t, torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 4-D [B, T, heads, head_dim]")
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "o and dout must have q's shape")
+    _dev_tensor("lse", lse, torch.float32)
+    if tuple(lse.shape) != (B, H, T):
+        raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _dev_tensor(n, t, torch.bfloat16)
+        if t.shape != ref.shape:
+            raise CgrError(CGR_ERR_INVALID_ARG, f"{n} must have shape {tuple(ref.shape)}")
+    need = lib.cgr_attn_bwd_workspace_size(B, T, H, k.shape[2], D)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_bwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, T, H, k.shape[2], D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+            _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
 rope_tables = cgr_rope_tables
 gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
+gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd

@@ -31,6 +31,9 @@ SOURCES = [
     "attn_fwd_d32.hip",
     "attn_fwd_d64.hip",
     "attn_fwd_d128.hip",
+    "attn_bwd_d32.hip",
+    "attn_bwd_d64.hip",
+    "attn_bwd_d128.hip",
 ]
 
 ARCH = os.environ.get("CGR_OFFLOAD_ARCH", "gfx950")

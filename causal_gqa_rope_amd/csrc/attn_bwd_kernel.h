@@ -1,0 +1,663 @@
+// Backward of the fused causal GQA + RoPE attention for gfx950 (internal to
+// libcgr).
+//
+// What is computed: the chain rule through the forward's definition ("Attention
+// from Scratch", section "Attention, the math"; "Train It & Run for Real",
+// section "Coming from CUDA: where's .backward()?": every op of the model,
+// attention and RoPE included, carries its backward). Per sequence and query
+// head h with K/V head h / G, in the rotated frame (q~ = R q, k~ = R k):
+//   P_ij  = exp(scale q~_i.k~_j - lse_i)      (the forward's log-sum-exp)
+//   dP_ij = dO_i . v_j,  D_i = dO_i . O_i = sum_j P_ij dP_ij
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dv_j += sum_i P_ij dO_i
+//   dk~_j += scale sum_i dS_ij q~_i,   dq~_i = scale sum_j dS_ij k~_j
+//   dq = R^T dq~,  dk = R^T dk~   (the transposed rotation, at the row's position)
+// dk and dv sum over the G query heads that share the K/V head.
+//
+// Three kernels:
+//   * bwd_prep_kernel: q~ * scale*log2(e) and k~ in the Q.K^T operand type (so
+//     the rotation is done once, not once per tile that reads them), and per
+//     32-row tile of every (sequence, head) the two accumulator starting
+//     values -lse*log2(e) and -D.
+//   * attn_bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128 keys).
+//     Each wave keeps 32 keys' k~ and v in registers as matrix-core operands
+//     and accumulates dk~^T and dv^T for them over every query row and every
+//     query head of the group; S = q~ k~^T puts one key per lane column, so P
+//     and dS feed dv^T += dO^T P and dk~^T += q~^T dS straight from registers.
+//   * attn_bwd_dq_kernel: one workgroup per (sequence, query head, 256 rows),
+//     the forward's layout: S^T = k~ q~^T puts one query per lane column and
+//     dq~^T += k~^T dS^T takes dS^T from registers.
+// Recomputing S and dP in both kernels costs two extra matrix products per
+// tile against sharing dS through memory, and buys a backward without atomics
+// or a dS round trip: every output element is written once, by one lane, in a
+// fixed order (bit-for-bit repeatable).
+#pragma once
+
+#include "attn_fwd_kernel.h"
+
+namespace cgr {
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, H, T], natural log (the forward's)
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* rope_cos;  // [P, D/2]
+  const float* rope_sin;
+  // Workspace (written by bwd_prep_kernel).
+  void* qr;   // [B, T, H, D] operand type: R q * scale * log2(e)
+  void* kr;   // [B, T, KV, D] operand type: R k
+  float* ld;  // [B, H, NT][64]: per 32-row tile, -lse*log2(e) (rows 0..31) then -D
+  int B, T, H, KV, NT;
+  float qscale;  // scale * log2(e)
+  float scale;
+};
+
+constexpr int kBwdTileRows = 32;  // rows per ld tile
+
+// ---------------------------------------------------------------------------
+// Operand tiles in LDS: rows of 2*D bytes (16-bit elements), 16-byte chunks
+// XOR-swizzled per row. The swizzle serves both ways the tiles are read:
+//   * row reads (operand row m = lane%32, 16 bytes): the 16 lanes that share a
+//     bank cycle read 16 consecutive rows at one logical chunk, which the
+//     swizzle spreads over all 16 bank slots of a 256-byte line;
+//   * transposing reads (ds_read_b64_tr_b16): a half-wave reads 4 consecutive
+//     rows x 64 bytes, which the swizzle puts on 4 distinct 64-byte windows.
+// Tiles are written by direct global->LDS loads (16 bytes per lane, lane order),
+// so the swizzle is applied to the global address each lane fetches.
+template <int D>
+__device__ __forceinline__ int tswz(int r) {
+  if constexpr (D == 128)
+    return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+  else if constexpr (D == 64)
+    return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
+  else
+    return (r >> 2) & 3;
+}
+template <int D>
+__device__ __forceinline__ int toff(int r, int c) {
+  return r * 2 * D + 16 * (c ^ tswz<D>(r));
+}
+
+// Load `rows` rows (row r of the tile at global byte offset r * gstride + soff)
+// into an LDS tile, by the `nw` waves of a group; `wig` is this wave's index in
+// the group. Rows past the buffer's range read as zeros.
+template <int D, int ROWS>
+__device__ __forceinline__ void tile_to_lds(rsrc_t rs, char* lds, int gstride, int soff, int wig,
+                                            int nw, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int NI = ROWS * NCH / 64;  // 1 KiB wave loads
+  static_assert(ROWS * NCH % 64 == 0, "whole wave loads");
+  for (int u = wig; u < NI; u += nw) {
+    const int slot = u * 64 + lane, r = slot / NCH, pc = slot % NCH;
+    buf_load16_lds(rs, lds + u * 1024, r * gstride + 16 * (pc ^ tswz<D>(r)), soff);
+  }
+}
+
+// Operand fragment k-step s of row r (lane half hh): elements 16s + 8hh .. +7.
+template <int D>
+__device__ __forceinline__ u32x4 row_frag(const char* tile, int r, int s, int hh) {
+  return *(const u32x4*)(tile + toff<D>(r, 2 * s + hh));
+}
+
+// Per-lane offsets of the transposing reads. For 16 tile rows starting at a
+// multiple of 16 and the 32-wide column block db, lane (hh, gi, li) reads row
+// 4hh + li/4 (first half) and 8 rows further (second half), 8 bytes at logical
+// chunk 4db + 2(gi&1) + (li&3)/2, half li&1. The pair of reads is the
+// operand fragment A[m][k] = X[row(k)][32db + m]: with k-slot 8hh + j it
+// holds row 8(j/4) + 4hh + j%4 of the 16, the row order of the accumulator
+// registers 8t..8t+7 that the B operand comes from.
+template <int D>
+struct TrOffsets {
+  int a[D / 32], b[D / 32];
+  __device__ __forceinline__ TrOffsets(int lane) {
+    const int hh = lane >> 5, gi = lane >> 4, li = lane & 15;
+    const int ra = 4 * hh + (li >> 2), rb = ra + 8;
+    const int cs = 2 * (gi & 1) + ((li & 3) >> 1), half = 8 * (li & 1);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      a[db] = ra * 2 * D + 16 * ((4 * db + cs) ^ tswz<D>(ra)) + half;
+      b[db] = rb * 2 * D + 16 * ((4 * db + cs) ^ tswz<D>(rb)) + half;
+    }
+  }
+};
+template <int D>
+__device__ __forceinline__ u32x4 tr_frag(const char* tile, int row16, int db, const TrOffsets<D>& o) {
+  const char* p = tile + row16 * 2 * D;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + o.a[db]));
+  const s16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + o.b[db]));
+  const u32x2 ux = __builtin_bit_cast(u32x2, x), uy = __builtin_bit_cast(u32x2, y);
+  return (u32x4){ux[0], ux[1], uy[0], uy[1]};
+}
+
+template <typename Op>
+__device__ __forceinline__ Frag<Op> frag(u32x4 v) {
+  Frag<Op> f;
+  f.v = v;
+  return f;
+}
+
+// The transposed rotation applied to an accumulator whose lane column sits at
+// position `pos` and whose registers hold rows d = 32db + 8(i/4) + 4hh + i%4:
+// pair (a, b) with angle t becomes (a cos t + b sin t, -a sin t + b cos t).
+// Pairs lie inside the lane for both pairings: (d, d+1) are registers i, i+1;
+// (d, d + D/2) are the same register of block db + D/64 (or, for D = 32, of
+// row group i/4 + 2).
+template <int D, int STYLE>
+__device__ __forceinline__ void rope_transpose_acc(f32x16 (&acc)[D / 32], const float* cs,
+                                                   const float* sn, int pos, int hh) {
+  const float* c = cs + (long)pos * (D / 2);
+  const float* s = sn + (long)pos * (D / 2);
+  if constexpr (STYLE == STYLE_INTERLEAVED) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int p = (32 * db + 8 * g + 4 * hh) / 2;
+        const f32x2 cc = *(const f32x2*)(c + p), ss = *(const f32x2*)(s + p);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const float a = acc[db][4 * g + 2 * m], b = acc[db][4 * g + 2 * m + 1];
+          acc[db][4 * g + 2 * m] = a * cc[m] + b * ss[m];
+          acc[db][4 * g + 2 * m + 1] = -a * ss[m] + b * cc[m];
+        }
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hh;
+        if (d >= D / 2) continue;  // compile-time per (db, g) up to hh
+        const int db2 = D >= 64 ? db + D / 64 : db, g2 = D >= 64 ? g : g + 2;
+        const f32x4 cc = *(const f32x4*)(c + d), ss = *(const f32x4*)(s + d);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float a = acc[db][4 * g + m], b = acc[db2][4 * g2 + m];
+          acc[db][4 * g + m] = a * cc[m] + b * ss[m];
+          acc[db2][4 * g2 + m] = -a * ss[m] + b * cc[m];
+        }
+      }
+  }
+}
+
+// Round an accumulator (lane column = row `pos` of a [.., D] bf16 tensor) to
+// bf16 and store it: 8 bytes (4 consecutive elements) per (db, row group).
+template <int D>
+__device__ __forceinline__ void store_acc_bf16(const f32x16 (&acc)[D / 32], float mul, rsrc_t r,
+                                               int row_off, int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hh;
+      const u32x2 w = {pack2(OpBF16{}, acc[db][4 * g] * mul, acc[db][4 * g + 1] * mul),
+                       pack2(OpBF16{}, acc[db][4 * g + 2] * mul, acc[db][4 * g + 3] * mul)};
+      __builtin_amdgcn_raw_buffer_store_b64(w, r, row_off + d * 2, 0, 0);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prepass. Item = (row, group g < D/16), covering the chunk pair (g, g + D/16)
+// so that both pairings find their partners (as the forward's K loader). The
+// query part runs over rows padded to whole 32-row tiles; padding rows get
+// -lse = -inf (no probability) and -D = 0.
+template <int D, typename QK, int STYLE>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
+  constexpr int IPR = D / 16;  // items per row
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  const int Tp = a.NT * kBwdTileRows;
+  const long nq = (long)a.B * Tp * a.H * IPR;
+  const long nk = (long)a.B * a.T * a.KV * IPR;
+  const int g = (int)(tid % IPR);
+  if (tid < nq) {
+    const long row = tid / IPR;  // ((b * Tp + t) * H + h)
+    const int h = (int)(row % a.H);
+    const long bt = row / a.H;
+    const int t = (int)(bt % Tp), b = (int)(bt / Tp);
+    const bool ok = t < a.T;
+    float dot = 0.f;
+    if (ok) {
+      const long e0 = (((long)b * a.T + t) * a.H + h) * D;
+      const uint16_t* qp = (const uint16_t*)a.q + e0;
+      u32x4 w0[1] = {*(const u32x4*)(qp + 8 * g)}, w1[1] = {*(const u32x4*)(qp + 8 * g + D / 2)};
+      float x0[8], x1[8];
+      raw_to_f32<uint16_t>(w0, x0);
+      raw_to_f32<uint16_t>(w1, x1);
+      f32x4 c[2], s[2];
+      load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
+      rope_pair<STYLE>(x0, x1, c, s);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x0[j] *= a.qscale;
+        x1[j] *= a.qscale;
+      }
+      uint16_t* qo = (uint16_t*)a.qr + e0;
+      *(u32x4*)(qo + 8 * g) = to_frag<QK>(x0).v;
+      *(u32x4*)(qo + 8 * g + D / 2) = to_frag<QK>(x1).v;
+      // D_i over this item's 16 elements.
+      const uint16_t* op = (const uint16_t*)a.o + e0;
+      const uint16_t* dp = (const uint16_t*)a.dout + e0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int off = 8 * g + half * (D / 2);
+        u32x4 wo[1] = {*(const u32x4*)(op + off)}, wd[1] = {*(const u32x4*)(dp + off)};
+        float xo[8], xd[8];
+        raw_to_f32<uint16_t>(wo, xo);
+        raw_to_f32<uint16_t>(wd, xd);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot += xo[j] * xd[j];
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < IPR; m <<= 1) dot += __shfl_xor(dot, m, 64);
+    if (g == 0) {
+      float* l = a.ld + (((long)b * a.H + h) * a.NT + t / kBwdTileRows) * 64 + t % kBwdTileRows;
+      l[0] = ok ? -a.lse[((long)b * a.H + h) * a.T + t] * 1.4426950408889634f : -INFINITY;
+      l[32] = ok ? -dot : 0.f;
+    }
+  } else if (tid < nq + nk) {
+    const long row = (tid - nq) / IPR;  // ((b * T + t) * KV + kv)
+    const long bt = row / a.KV;
+    const int t = (int)(bt % a.T);
+    const long e0 = row * D;
+    const uint16_t* kp = (const uint16_t*)a.k + e0;
+    u32x4 w0[1] = {*(const u32x4*)(kp + 8 * g)}, w1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
+    float x0[8], x1[8];
+    raw_to_f32<uint16_t>(w0, x0);
+    raw_to_f32<uint16_t>(w1, x1);
+    f32x4 c[2], s[2];
+    load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
+    rope_pair<STYLE>(x0, x1, c, s);
+    uint16_t* ko = (uint16_t*)a.kr + e0;
+    *(u32x4*)(ko + 8 * g) = to_frag<QK>(x0).v;
+    *(u32x4*)(ko + 8 * g + D / 2) = to_frag<QK>(x1).v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dk, dv. Workgroup = 8 waves = two groups of 4; wave w holds keys
+// k0 + 32(w%4) .. +31 of the workgroup's 128. The group's work items are
+// (query head of the K/V group, 32-row query step); group 0 takes the even
+// items and group 1 the odd ones, so the two waves of a SIMD (w and w+4, same
+// keys) split the rows, and their partial sums meet in LDS at the end.
+// Per item and wave (32 query rows x 32 keys):
+//   S  = q~ k~^T - lse        (rows = queries, lane column = key; log2 units)
+//   dP = dO v^T - D
+//   P = 2^S;  dS = P dP
+//   dv^T += dO^T P            (dO^T by transposing LDS reads)
+//   dk~^T += q~^T dS
+template <int D_, typename QK_, bool CAUSAL_, int STYLE_>
+struct BwdCfg {
+  static constexpr int D = D_;
+  using QK = QK_;
+  static constexpr bool CAUSAL = CAUSAL_;
+  static constexpr int STYLE = STYLE_;
+  static constexpr int KSTEPS = D / 16;
+  static constexpr int DB = D / 32;
+  static constexpr int TILE = 32 * 2 * D;                // one 32-row operand tile
+  static constexpr int GSTAGE = 2 * TILE + 256;          // q~, dO, ld of one group
+  static constexpr int KV_STAGE = 2 * GSTAGE;            // both groups
+  static constexpr int BK = 128;                         // keys per dk/dv workgroup
+  static constexpr int BQ = 256;                         // rows per dq workgroup
+  static constexpr int BN = 64;                          // keys per dq tile
+  static constexpr int KT = BN * 2 * D;                  // one dq key tile
+};
+
+template <class C>
+__global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int D = C::D, KSTEPS = C::KSTEPS, DB = C::DB;
+  using QK = typename C::QK;
+  __shared__ __attribute__((aligned(16))) char st0[C::KV_STAGE], st1[C::KV_STAGE];
+  __shared__ __attribute__((aligned(16))) char vk[C::BK * 2 * C::D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, wig = wave & 3;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int G = a.H / a.KV;
+  const int nK = (a.T + C::BK - 1) / C::BK;
+  // Heavy blocks first (causal: the first keys see the most queries); when
+  // the (batch, K/V head) groups divide evenly over the 8 XCDs, each XCD keeps
+  // whole groups, whose queries it then streams through one L2.
+  const int u = blockIdx.x, groups = a.B * a.KV;
+  int rank, gsel;
+  if ((groups & 7) == 0) {
+    const int x = u & 7, i = u >> 3, per = groups >> 3;
+    rank = i / per;
+    gsel = (i - rank * per) * 8 + x;
+  } else {
+    rank = u / groups;
+    gsel = u - rank * groups;
+  }
+  const int kb = rank;
+  const int b = gsel / a.KV, kvh = gsel - b * a.KV;
+  const int L = a.T, tok0 = b * a.T;
+  const int k0 = kb * C::BK, kw0 = k0 + 32 * wig;
+  const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
+
+  // This wave's keys: k~ as the B operand of S in registers (k-step s of lane
+  // (key l32, hh) = elements 16s + 8hh .. +7); v, the B operand of dP, is read
+  // from the workgroup's LDS copy (registers are short: the two accumulators
+  // take half of them).
+  const rsrc_t rkr = make_rsrc((const uint16_t*)a.kr + ((long)tok0 * ks + kvh * D),
+                               (uint32_t)(((L - 1) * ks + D) * 2));
+  const rsrc_t rv = make_rsrc((const uint16_t*)a.v + ((long)tok0 * ks + kvh * D),
+                              (uint32_t)(((L - 1) * ks + D) * 2));
+  u32x4 kf[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) kf[s] = buf_load16(rkr, (kw0 + l32) * ks * 2 + (2 * s + hh) * 16, 0);
+  tile_to_lds<D, C::BK>(rv, vk, ks * 2, k0 * ks * 2, wave, 8, lane);
+  const int vrow = 32 * wig + l32;
+
+  const int q_first = C::CAUSAL ? k0 : 0;
+  const int n_steps = (L - q_first + 31) / 32;
+  const int n_items = G * n_steps;
+  const int n_iter = (n_items + 1) / 2;
+  const rsrc_t rld = make_rsrc(a.ld, (uint32_t)((long)a.B * a.H * a.NT * 256));
+
+  // Loads of iteration i (this group's item 2i + grp) into a stage.
+  auto issue = [&](int i, char* st) {
+    const int n = 2 * i + grp;
+    if (n >= n_items) return;
+    const int g = n / n_steps, sidx = n - g * n_steps;
+    const int h = kvh * G + g, qrow0 = q_first + 32 * sidx;
+    char* gs = st + grp * C::GSTAGE;
+    const long hoff = (long)tok0 * qs + (long)h * D;
+    const rsrc_t rq = make_rsrc((const uint16_t*)a.qr + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
+    const rsrc_t rd = make_rsrc((const uint16_t*)a.dout + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
+    tile_to_lds<D, 32>(rq, gs, qs * 2, qrow0 * qs * 2, wig, 4, lane);
+    tile_to_lds<D, 32>(rd, gs + C::TILE, qs * 2, qrow0 * qs * 2, wig, 4, lane);
+    if (wig == 0) {
+      const long t = ((long)b * a.H + h) * a.NT + qrow0 / 32;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_void*)(gs + 2 * C::TILE), 4, lane * 4,
+                                               (int)(t * 256), 0, 0);
+    }
+  };
+
+  const TrOffsets<D> tro(lane);
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dk[db] = dv[db] = (f32x16){};
+
+  auto compute = [&](int i, const char* st) {
+    const int n = 2 * i + grp;
+    if (n >= n_items) return;
+    const int g = n / n_steps, sidx = n - g * n_steps;
+    const int qrow0 = q_first + 32 * sidx;
+    if (C::CAUSAL && qrow0 < kw0) return;  // every key of the wave is later than every row
+    const char* gs = st + grp * C::GSTAGE;
+    const char* Qt = gs;
+    const char* Ot = gs + C::TILE;
+    const float* ldt = (const float*)(gs + 2 * C::TILE);
+    f32x16 sacc, dpacc;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const f32x4 x = *(const f32x4*)(ldt + 8 * r + 4 * hh);
+      const f32x4 y = *(const f32x4*)(ldt + 32 + 8 * r + 4 * hh);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        sacc[4 * r + m] = x[m];
+        dpacc[4 * r + m] = y[m];
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      sacc = mma32(frag<QK>(row_frag<D>(Qt, l32, s, hh)), frag<QK>(kf[s]), sacc);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s)
+      dpacc = mma32(frag<OpBF16>(row_frag<D>(Ot, l32, s, hh)), frag<OpBF16>(row_frag<D>(vk, vrow, s, hh)),
+                    dpacc);
+    if (C::CAUSAL && qrow0 == kw0) {
+      // Diagonal block: key l32 is visible to row 8(i/4) + 4hh + i%4 iff key <= row.
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (l32 > 8 * (r >> 2) + 4 * hh + (r & 3)) sacc[r] = -INFINITY;
+    }
+    u32x4 pb[2], sb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int r = 8 * t + 2 * m;
+        const float p0 = fast_exp2(sacc[r]), p1 = fast_exp2(sacc[r + 1]);
+        pb[t][m] = pack2(OpBF16{}, p0, p1);
+        sb[t][m] = pack2(QK{}, p0 * dpacc[r], p1 * dpacc[r + 1]);
+      }
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        dv[db] = mma32(frag<OpBF16>(tr_frag<D>(Ot, 16 * t, db, tro)), frag<OpBF16>(pb[t]), dv[db]);
+        dk[db] = mma32(frag<QK>(tr_frag<D>(Qt, 16 * t, db, tro)), frag<QK>(sb[t]), dk[db]);
+      }
+  };
+
+  issue(0, st0);
+  wait_vmem();
+  __syncthreads();
+  int i = 0;
+  for (; i + 1 < n_iter; i += 2) {
+    issue(i + 1, st1);
+    compute(i, st0);
+    wait_vmem();
+    __syncthreads();
+    issue(i + 2, st0);
+    compute(i + 1, st1);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (i < n_iter) {
+    compute(i, st0);
+    __syncthreads();
+  }
+
+  // Group 1 hands its partial sums to group 0 through LDS, RR registers of
+  // one 32-wide block at a time, alternating between the two stage arrays (a
+  // piece is written only after the barrier that follows the previous piece,
+  // by which time group 0 has read the piece before that). Word (wig, r) of
+  // lane l sits at (wig * RR + r) * 64 + l.
+  constexpr int RR = C::KV_STAGE >= 16 * 1024 ? 16 : 8;
+  static_assert(C::KV_STAGE >= RR * 1024, "a reduction piece fits a stage");
+  auto reduce = [&](f32x16 (&acc)[DB], int p0) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int hf = 0; hf < 16 / RR; ++hf) {
+        const int p = p0 + db * (16 / RR) + hf;
+        float* red = (float*)((p & 1) ? st1 : st0);
+        if (grp == 1) {
+#pragma unroll
+          for (int r = 0; r < RR; ++r) red[(wig * RR + r) * 64 + lane] = acc[db][hf * RR + r];
+        }
+        __syncthreads();
+        if (grp == 0) {
+#pragma unroll
+          for (int r = 0; r < RR; ++r) acc[db][hf * RR + r] += red[(wig * RR + r) * 64 + lane];
+        }
+      }
+  };
+  reduce(dv, 0);
+  reduce(dk, DB * (16 / RR));
+  if (grp != 0) return;
+
+  const int key = kw0 + l32;
+  const rsrc_t rdv = make_rsrc((uint16_t*)a.dv + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
+  const rsrc_t rdk = make_rsrc((uint16_t*)a.dk + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
+  store_acc_bf16<D>(dv, 1.f, rdv, key * ks * 2, hh);
+  // dk~ = scale * sum dS q~ and the q~ operand carried scale*log2(e): one ln 2.
+  if (key < L) rope_transpose_acc<D, C::STYLE>(dk, a.rope_cos, a.rope_sin, key, hh);
+  store_acc_bf16<D>(dk, 0.69314718055994531f, rdk, key * ks * 2, hh);
+}
+
+// ---------------------------------------------------------------------------
+// dq. Workgroup = 8 waves x 32 query rows of one query head; key tiles of 64
+// stream through LDS (k~ and v, double-buffered, direct loads). Per tile and
+// wave:
+//   S^T  = k~ q~^T - lse      (rows = keys, lane column = query)
+//   dP^T = v dO^T - D
+//   P^T = 2^S^T;  dS^T = P^T dP^T
+//   dq~^T += k~^T dS^T        (k~^T by transposing LDS reads)
+template <class C>
+__global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int D = C::D, KSTEPS = C::KSTEPS, DB = C::DB, BN = C::BN;
+  using QK = typename C::QK;
+  __shared__ __attribute__((aligned(16))) char kt0s[C::KT], kt1s[C::KT];
+  __shared__ __attribute__((aligned(16))) char vt0s[C::KT], vt1s[C::KT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int G = a.H / a.KV;
+  const int nQ = (a.T + C::BQ - 1) / C::BQ;
+  const int u = blockIdx.x, groups = a.B * a.KV;
+  int rank, gsel, hq;
+  if ((groups & 7) == 0) {
+    const int x = u & 7, i = u >> 3, per = (groups >> 3) * G;
+    rank = i / per;
+    const int rem = i - rank * per;
+    gsel = (rem / G) * 8 + x;
+    hq = rem % G;
+  } else {
+    const int per = groups * G;
+    rank = u / per;
+    const int rem = u - rank * per;
+    gsel = rem / G;
+    hq = rem % G;
+  }
+  const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
+  const int b = gsel / a.KV, kvh = gsel - b * a.KV, head = kvh * G + hq;
+  const int L = a.T, tok0 = b * a.T;
+  const int qs = a.H * D, ks = a.KV * D;
+  const int q0 = qb * C::BQ, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
+  const bool wave_has_rows = qw0 < L;
+  const int wave_last = min(qw0 + 31, L - 1);
+  const int q_hi = min(q0 + C::BQ, L);
+  const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
+
+  // This lane's query row as B operands: q~ (for S^T) and dO (for dP^T).
+  const long hoff = (long)tok0 * qs + (long)head * D;
+  const rsrc_t rq = make_rsrc((const uint16_t*)a.qr + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
+  const rsrc_t rd = make_rsrc((const uint16_t*)a.dout + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
+  u32x4 qf[KSTEPS], df[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int off = my_q * qs * 2 + (2 * s + hh) * 16;
+    qf[s] = buf_load16(rq, off, 0);
+    df[s] = buf_load16(rd, off, 0);
+  }
+  float neg_lse = -INFINITY, neg_d = 0.f;
+  if (my_q < L) {
+    const float* l = a.ld + (((long)b * a.H + head) * a.NT + my_q / 32) * 64 + my_q % 32;
+    neg_lse = l[0];
+    neg_d = l[32];
+  }
+
+  const rsrc_t rkr = make_rsrc((const uint16_t*)a.kr + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
+  const rsrc_t rv = make_rsrc((const uint16_t*)a.v + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
+  auto issue = [&](int j, char* kt, char* vt) {
+    if (j >= n_tiles) return;
+    tile_to_lds<D, BN>(rkr, kt, ks * 2, j * BN * ks * 2, wave, 8, lane);
+    tile_to_lds<D, BN>(rv, vt, ks * 2, j * BN * ks * 2, wave, 8, lane);
+  };
+
+  const TrOffsets<D> tro(lane);
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
+
+  auto compute = [&](int j, const char* Kt, const char* Vt) {
+    if (!wave_has_rows || (C::CAUSAL && j * BN > wave_last)) return;
+    const bool domask = C::CAUSAL && j * BN + BN - 1 > qw0;
+    const int lim = my_q - j * BN - 4 * hh;  // key offset in the tile must be <= lim
+#pragma unroll
+    for (int kb = 0; kb < BN / 32; ++kb) {
+      f32x16 sacc = (f32x16){} + neg_lse, dpacc = (f32x16){} + neg_d;
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        sacc = mma32(frag<QK>(row_frag<D>(Kt, 32 * kb + l32, s, hh)), frag<QK>(qf[s]), sacc);
+#pragma unroll
+      for (int s = 0; s < KSTEPS; ++s)
+        dpacc = mma32(frag<OpBF16>(row_frag<D>(Vt, 32 * kb + l32, s, hh)), frag<OpBF16>(df[s]), dpacc);
+      if (domask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[r] = -INFINITY;
+      }
+      u32x4 sb[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int r = 8 * t + 2 * m;
+          const float p0 = fast_exp2(sacc[r]), p1 = fast_exp2(sacc[r + 1]);
+          sb[t][m] = pack2(QK{}, p0 * dpacc[r], p1 * dpacc[r + 1]);
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          dq[db] = mma32(frag<QK>(tr_frag<D>(Kt, 32 * kb + 16 * t, db, tro)), frag<QK>(sb[t]), dq[db]);
+    }
+  };
+
+  issue(0, kt0s, vt0s);
+  wait_vmem();
+  __syncthreads();
+  int j = 0;
+  for (; j + 1 < n_tiles; j += 2) {
+    issue(j + 1, kt1s, vt1s);
+    compute(j, kt0s, vt0s);
+    wait_vmem();
+    __syncthreads();
+    issue(j + 2, kt0s, vt0s);
+    compute(j + 1, kt1s, vt1s);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (j < n_tiles) compute(j, kt0s, vt0s);
+
+  if (!wave_has_rows) return;
+  if (my_q < L) rope_transpose_acc<D, C::STYLE>(dq, a.rope_cos, a.rope_sin, my_q, hh);
+  const rsrc_t rdq = make_rsrc((uint16_t*)a.dq + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
+  store_acc_bf16<D>(dq, a.scale, rdq, my_q * qs * 2, hh);
+}
+
+// Launch the three kernels of one instance (arguments validated by the caller).
+template <class C>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  constexpr int D = C::D;
+  const long items = ((long)a.B * a.NT * kBwdTileRows * a.H + (long)a.B * a.T * a.KV) * (D / 16);
+  hipLaunchKernelGGL((bwd_prep_kernel<D, typename C::QK, C::STYLE>), dim3((unsigned)((items + 255) / 256)),
+                     dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nK = (a.T + C::BK - 1) / C::BK, nQ = (a.T + C::BQ - 1) / C::BQ;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3(nK * a.B * a.KV), dim3(512), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3(nQ * a.B * a.H), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_attn_bwd_d(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream) {
+#define CGR_BL(QK, CAU, STY) return launch_bwd<BwdCfg<D, QK, CAU, STY>>(a, stream)
+#define CGR_BS(QK, CAU) \
+  if (style == STYLE_HALF) { CGR_BL(QK, CAU, STYLE_HALF); } else { CGR_BL(QK, CAU, STYLE_INTERLEAVED); }
+#define CGR_BM(QK) \
+  if (causal) { CGR_BS(QK, true) } else { CGR_BS(QK, false) }
+  if (qk_bf16) {
+    CGR_BM(OpBF16)
+  } else {
+    CGR_BM(OpF16)
+  }
+#undef CGR_BM
+#undef CGR_BS
+#undef CGR_BL
+}
+
+}  // namespace cgr

@@ -10,6 +10,7 @@
 #include <cstdio>
 #include <string>
 
+#include "attn_bwd_kernel.h"
 #include "attn_fwd_kernel.h"
 #include "cgr.h"
 #include "launch.h"
@@ -136,6 +137,22 @@ long varlen_max_items(int num_seqs, int total_tokens) {
   return ((long)total_tokens + 63) / 64 + (long)num_seqs;
 }
 
+// Backward workspace: the rotated q (operand type) and k, then the per-tile
+// accumulator starting values; each part starts on a 256-byte boundary.
+struct BwdLayout {
+  size_t qr, kr, ld, total;
+};
+BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const int nt = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
+  BwdLayout l;
+  l.qr = 0;
+  l.kr = up((size_t)B * T * n_head * head_dim * 2);
+  l.ld = l.kr + up((size_t)B * T * n_kv_head * head_dim * 2);
+  l.total = l.ld + (size_t)B * n_head * nt * 64 * 4;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -237,6 +254,76 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   if (grid < 1) grid = 1;
   e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
   if (e != hipSuccess) return hip_fail("attention launch", e);
+  return CGR_OK;
+}
+
+size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_head, int head_dim) {
+  if (B < 1 || T < 1 || n_head < 1 || n_kv_head < 1 || head_dim < 2) return 0;
+  return bwd_layout(B, T, n_head, n_kv_head, head_dim).total;
+}
+
+cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 int B, int T, int n_head, int n_kv_head, int head_dim,
+                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
+  cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
+                               rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
+  if (st != CGR_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv)
+    return fail(CGR_ERR_INVALID_ARG, "lse, dout, dq, dk and dv must be non-null");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(CGR_ERR_ALIGNMENT, "dout, dq, dk and dv must be 16-byte aligned");
+  if (dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "the backward takes bf16 tensors only (dtype %d)", (int)dtype);
+  if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
+  const BwdLayout lay = bwd_layout(B, T, n_head, n_kv_head, head_dim);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 256)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
+                lay.total);
+  const int nt = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
+  // The kernels address the per-tile values with one 32-bit buffer range.
+  if (lay.total - lay.ld > (size_t)UINT32_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "B * n_head * T is too large for one call");
+  const long grid_q = (long)((T + 255) / 256) * B * n_head;
+  if (grid_q > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  cgr::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.qr = (char*)workspace + lay.qr;
+  a.kr = (char*)workspace + lay.kr;
+  a.ld = (float*)((char*)workspace + lay.ld);
+  a.B = B;
+  a.T = T;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  a.NT = nt;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  a.scale = (float)scale;
+  a.qscale = (float)(scale * 1.4426950408889634074);
+  const int qkb = qk_operand == CGR_QK_BF16, sty = (int)style, cau = mask == CGR_MASK_CAUSAL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (head_dim) {
+    case 32: e = cgr::launch_attn_bwd_d32(a, qkb, sty, cau, s); break;
+    case 64: e = cgr::launch_attn_bwd_d64(a, qkb, sty, cau, s); break;
+    default: e = cgr::launch_attn_bwd_d128(a, qkb, sty, cau, s); break;
+  }
+  if (e != hipSuccess) return hip_fail("backward launch", e);
   return CGR_OK;
 }
 

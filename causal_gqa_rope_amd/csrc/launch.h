@@ -7,6 +7,7 @@
 namespace cgr {
 
 struct AttnArgs;
+struct BwdArgs;
 
 hipError_t launch_attn_d32(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                            bool varlen, int grid, hipStream_t stream);
@@ -14,6 +15,10 @@ hipError_t launch_attn_d64(const AttnArgs& a, int f32_io, int qk_bf16, int style
                            bool varlen, int grid, hipStream_t stream);
 hipError_t launch_attn_d128(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                             bool varlen, int grid, hipStream_t stream);
+
+hipError_t launch_attn_bwd_d32(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);
+hipError_t launch_attn_bwd_d64(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);
+hipError_t launch_attn_bwd_d128(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);
 
 hipError_t launch_rope_tables(int max_pos, int head_dim, double base, float* cos_out,
                               float* sin_out, hipStream_t stream);

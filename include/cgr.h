@@ -1,6 +1,7 @@
 /*
  * cgr.h -- fused causal grouped-query attention with rotary position
- * embedding (RoPE), forward pass, for AMD Instinct MI355X (gfx950).
+ * embedding (RoPE), forward and backward passes, for AMD Instinct MI355X
+ * (gfx950).
  *
  * The operation, as the pages define it:
  *   - RoPE tables: "Embeddings & the Residual Stream", section "Positional
@@ -56,7 +57,7 @@ typedef enum {
   CGR_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, n_head % n_kv_head != 0, ... */
   CGR_ERR_UNSUPPORTED = 2, /* head_dim not in {32, 64, 128}, unknown dtype/style/mask */
   CGR_ERR_ALIGNMENT = 3,   /* a tensor pointer is not 16-byte aligned */
-  CGR_ERR_WORKSPACE = 4,   /* varlen workspace missing or too small */
+  CGR_ERR_WORKSPACE = 4,   /* workspace missing or too small */
   CGR_ERR_HIP = 5          /* a HIP call failed; cgr_last_error() holds its message */
 } cgr_status;
 
@@ -151,6 +152,48 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, co
                                         int rope_max_pos, cgr_rope_style style, cgr_mask mask,
                                         float softmax_scale, cgr_qk_operand qk_operand,
                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace cgr_gqa_rope_attn_bwd needs for these sizes
+ * (0 for invalid sizes): the rotated q and k in the Q.K^T operand type plus
+ * two floats per query row and head.
+ */
+CGR_API size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_head, int head_dim);
+
+/*
+ * Dense batch backward: the gradients of a loss L with respect to q, k and v,
+ * given dL/dO, by the chain rule through the forward above ("Train It & Run
+ * for Real", section "Coming from CUDA: where's .backward()?": RoPE and
+ * attention each carry their backward). With q~ = R q and k~ = R k rotated at
+ * their positions, P the forward's softmax weights and D_i = dO_i . O_i:
+ *   dv_j = sum_i P_ij dO_i;   dS_ij = P_ij (dO_i . v_j - D_i)
+ *   dq_i = R_i^T scale sum_j dS_ij k~_j;   dk_j = R_j^T scale sum_i dS_ij q~_i
+ * where dk and dv sum over the n_head / n_kv_head query heads sharing the K/V
+ * head.
+ *   q, k, v, rope tables, sizes, style, mask, softmax_scale, qk_operand: as
+ *     given to cgr_gqa_rope_attn_fwd.
+ *   o: device [B, T, n_head, head_dim], lse: device float32 [B, n_head, T] --
+ *     the forward's outputs for these inputs (P is recomputed from q, k and
+ *     lse; D from o).
+ *   dout: device [B, T, n_head, head_dim], dL/dO.
+ *   dq: device [B, T, n_head, head_dim]; dk, dv: device [B, T, n_kv_head,
+ *     head_dim]; all written in full, none may overlap an input.
+ *   dtype: CGR_BF16 only (CGR_F32 returns CGR_ERR_UNSUPPORTED). The products
+ *     that involve q~ or k~ use the qk_operand type (dS is rounded to it), the
+ *     ones that involve dO use bf16 (P is rounded to bf16); all accumulate in
+ *     f32, and each gradient is rounded once to bf16.
+ *   workspace: device memory of at least cgr_attn_bwd_workspace_size(...)
+ *     bytes, 256-byte aligned, scratch for this call only.
+ * Every output element is written once, in a fixed order: repeated calls give
+ * identical bits.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 int B, int T, int n_head, int n_kv_head, int head_dim,
+                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Reads the device error word the last varlen call on `workspace` left:

@@ -58,6 +58,7 @@ __all__ = [
     "apply_rope_transpose",
     "attention_dense_bwd",
     "attention_varlen_bwd",
+    "attention_bwd_group",
 ]
 
 
@@ -341,4 +342,49 @@ def attention_varlen_bwd(q, k, v, dout, cu_seqlens, *, causal: bool = True, base
         a, b = cu[s], cu[s + 1]
         dq[a:b], dk[a:b], dv[a:b] = _one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,
                                                       base, style)
+    return dq, dk, dv
+
+
+def attention_bwd_group(q, k, v, dout, b: int, kv: int, *, causal: bool = True, base: float = 10000.0,
+                        style: str = "interleaved", scale: Optional[float] = None, rows_per_block: int = 512):
+    """Gradients that involve one K/V head of one dense batch entry, for long sequences.
+
+    Same arithmetic as ``_one_sequence_bwd`` restricted to batch entry b, K/V
+    head kv and its query heads, with the score matrix built a block of query
+    rows at a time (every row whole, so each row's softmax is exact) to bound
+    memory. Under the causal mask a block of rows ending at r1 only needs keys
+    below r1: the others have weight exactly 0.
+    Returns dq [T, G, d] (the group's query heads, in order), dk [T, d], dv [T, d].
+    """
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, T, H, d = q.shape
+    KV = k.shape[2]
+    _check_heads(H, KV)
+    G = H // KV
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    pos = np.arange(T)
+    kr = apply_rope(k[b, :, kv], pos, base, style)
+    vv = v[b, :, kv]
+    dqr = np.zeros((T, G, d))
+    dkr = np.zeros((T, d))
+    dv = np.zeros((T, d))
+    for g in range(G):
+        h = kv * G + g
+        qr = apply_rope(q[b, :, h], pos, base, style)
+        do = dout[b, :, h]
+        for r0 in range(0, T, rows_per_block):
+            r1 = min(T, r0 + rows_per_block)
+            n = r1 if causal else T
+            S = (qr[r0:r1] @ kr[:n].T) * scale
+            if causal:
+                S[np.arange(r0, r1)[:, None] < np.arange(n)[None, :]] = -np.inf
+            e = np.exp(S - S.max(axis=1)[:, None])
+            P = e / e.sum(axis=1)[:, None]
+            dv[:n] += P.T @ do[r0:r1]
+            dP = do[r0:r1] @ vv[:n].T
+            dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+            dqr[r0:r1, g] = (dS @ kr[:n]) * scale
+            dkr[:n] += (dS.T @ qr[r0:r1]) * scale
+    dq = apply_rope_transpose(dqr, pos, base, style)
+    dk = apply_rope_transpose(dkr, pos, base, style)
     return dq, dk, dv

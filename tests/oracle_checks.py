@@ -539,6 +539,22 @@ def check_bwd_varlen_is_concat_of_dense():
             assert np.array_equal(dv[a:a + L], r[2][0])
 
 
+def check_bwd_group_matches_full():
+    # The blocked one-group backward is the full backward restricted to that group.
+    rng = RNG(37)
+    q = rng.standard_normal((2, 45, 6, 8))
+    k = rng.standard_normal((2, 45, 2, 8))
+    v = rng.standard_normal((2, 45, 2, 8))
+    W = rng.standard_normal((2, 45, 6, 8))
+    for causal, style in ((True, "interleaved"), (False, "half")):
+        dq, dk, dv = oracle.attention_dense_bwd(q, k, v, W, causal=causal, style=style)
+        for b, kv in ((0, 1), (1, 0)):
+            gq, gk, gv = oracle.attention_bwd_group(q, k, v, W, b, kv, causal=causal, style=style,
+                                                    rows_per_block=16)
+            assert np.allclose(gq, dq[b, :, 3 * kv:3 * kv + 3], atol=1e-12)
+            assert np.allclose(gk, dk[b, :, kv], atol=1e-12) and np.allclose(gv, dv[b, :, kv], atol=1e-12)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -565,4 +581,5 @@ ALL_CHECKS = [
     check_bwd_invariants,
     check_bwd_closed_forms,
     check_bwd_varlen_is_concat_of_dense,
+    check_bwd_group_matches_full,
 ]

@@ -155,3 +155,47 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 4, 2, 64)
     with pytest.raises(cgr.CgrError):
         cgr.gqa_rope_attn_fwd(x, x, x, torch.zeros(4, 32), torch.zeros(4, 32))
+
+
+def test_backward_workspace_size():
+    lib = cgr.library()
+    assert lib.cgr_attn_bwd_workspace_size(0, 16, 4, 2, 64) == 0
+    assert lib.cgr_attn_bwd_workspace_size(1, 16, 4, 0, 64) == 0
+    # rotated q and k (2 bytes each) on 256-byte boundaries, then 2 floats per
+    # (head, row) over rows padded to 32
+    n = lib.cgr_attn_bwd_workspace_size(2, 100, 8, 2, 128)
+    assert n == 2 * 100 * 8 * 128 * 2 + 2 * 100 * 2 * 128 * 2 + 2 * 8 * 4 * 64 * 4
+
+
+def backward(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, T=16, H=4, KV=2, D=64,
+             dtype=1, cos=P, sin=P, P=16, style=0, mask=1, scale=0.0, qk=0, ws=ctypes.c_void_p(0x10000),
+             wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
+                                   a["dk"], a["dv"], a["B"], a["T"], a["H"], a["KV"], a["D"],
+                                   a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["mask"],
+                                   a["scale"], a["qk"], a["ws"], a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), 1, "non-null"),
+    (dict(dout=None), 1, "non-null"),
+    (dict(dk=None), 1, "non-null"),
+    (dict(dtype=0), 2, "bf16"),
+    (dict(dq=PMIS), 3, "aligned"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(wsb=100), 4, "needs"),
+    (dict(ws=ctypes.c_void_p(0x10010)), 3, "256-byte"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(D=80), 2, "not one of"),
+    (dict(T=0), 1, ">= 1"),
+    (dict(P=15), 1, "positions"),
+])
+def test_backward_rejects_bad_arguments(kw, status, needle):
+    st, msg = backward(**kw)
+    assert st == status, msg
+    assert needle in msg

@@ -62,6 +62,10 @@ MUTANTS = [
     ("dq left rotated", "dq = apply_rope_transpose(dqr, pos, base, style)", "dq = dqr"),
     ("backward ignores the mask", "        if causal:\n            S[future] = -np.inf\n        e = np.exp",
      "        e = np.exp"),
+    ("group backward drops the last row", "r1 = min(T, r0 + rows_per_block)",
+     "r1 = min(T - 1, r0 + rows_per_block)"),
+    ("group backward sees one key too few", "            n = r1 if causal else T",
+     "            n = r1 - 1 if causal else T"),
     ("backward positions do not restart per sequence",
      "_one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,\n"
      "                                                      base, style)",

@@ -39,7 +39,9 @@ __all__ = [
     "get",
     "make_inputs",
     "varlen_lengths",
+    "make_dout",
     "algorithmic_flops",
+    "algorithmic_flops_bwd",
 ]
 
 
@@ -184,3 +186,25 @@ def algorithmic_flops(n_head: int, head_dim: int, lengths, causal: bool) -> int:
     """
     pairs = sum((int(L) * (int(L) + 1)) // 2 if causal else int(L) * int(L) for L in lengths)
     return 4 * head_dim * n_head * pairs
+
+
+# Seed offset of the upstream gradient dL/dO, so it is a stream of its own and
+# the workload's q, k, v stay what they are without it.
+DOUT_SEED_OFFSET = 1_000_003
+
+
+def make_dout(w: Workload, like: torch.Tensor) -> torch.Tensor:
+    """dL/dO for a workload: N(0,1) iid in the I/O dtype, q's shape, from seed + 1000003."""
+    gen = torch.Generator("cpu").manual_seed(w.seed + DOUT_SEED_OFFSET)
+    return torch.randn(tuple(like.shape), generator=gen, dtype=torch.float32).to(_io_dtype(w.dtype))
+
+
+def algorithmic_flops_bwd(n_head: int, head_dim: int, lengths, causal: bool) -> int:
+    """FLOPs credited to one backward: 10*d per allowed (query, key) pair per query head.
+
+    Five products of 2*d each per pair: the recomputed scores q.k, dO.v, and
+    the three gradient sums dv += p dO, dk += ds q, dq += ds k (2.5 times the
+    forward's count). The recomputation that splitting dq from dk/dv costs is
+    not credited.
+    """
+    return algorithmic_flops(n_head, head_dim, lengths, causal) // 4 * 10
