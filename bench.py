@@ -20,6 +20,8 @@ bounded sample of the same workload on this host's cores.
   python bench.py --copy-calibration   (plain copies, for counter scaling)
   python bench.py --all-configs        (one JSON line per workload configuration,
                                         attention call only; not the headline line)
+  python bench.py --backward           (one JSON line for the backward on the same
+                                        workload; not the headline line)
 """
 
 from __future__ import annotations
@@ -156,6 +158,107 @@ def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
                           "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2)}), flush=True)
 
 
+BWD_METRIC = "causal GQA+RoPE attention bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+
+
+def cpu_baseline_bwd(inputs, dout, w) -> dict:
+    """The float64 oracle's backward, as it stands, on one of the 8 K/V groups
+    (its 4 query heads) at the full T = 8192: an eighth of the workload."""
+    import oracle
+    import workloads as W
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or None
+    except Exception:
+        pass
+    G = w.n_head // w.n_kv_head
+    t0 = time.perf_counter()
+    oracle.attention_bwd_group(inputs["q"], inputs["k"], inputs["v"], dout, 0, 0, causal=True,
+                               base=w.base, style=w.rope_style)
+    dt = time.perf_counter() - t0
+    flops = W.algorithmic_flops_bwd(G, w.head_dim, [w.T], True)
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle backward, B=1 T={w.T}, K/V head 0 and its {G} query "
+                  f"heads, causal: 1/{w.n_kv_head} of the workload, {dt:.1f} s",
+    }
+
+
+def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
+    """One step = one backward call (prepass, dk/dv kernel, dq kernel) on the
+    long-context workload; o and lse come from one forward before timing."""
+    w = W.get(WORKLOAD)
+    inputs = W.make_inputs(w)
+    q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
+    dout_cpu = W.make_dout(w, inputs["q"])
+    dout = dout_cpu.to(dev)
+    cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
+    o, lse = cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(cgr.cgr_attn_bwd_workspace_size(w.B, w.T, w.n_head, w.n_kv_head, w.head_dim),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        cgr.gqa_rope_attn_bwd(q, k, v, o, lse, dout, cos, sin, causal=True, rope_style=w.rope_style,
+                              dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, [w.T] * w.B, True)
+    ms_step = wall * 1e3 / steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": BWD_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16/bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+            "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
+            "io": "bf16", "qk_operand": "f16", "accumulate": "f32", "step": "gqa_rope_attn_bwd",
+            "flops_per_step": flops,
+            "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "the backward call: bwd_prep_kernel + attn_bwd_dkdv_kernel + attn_bwd_dq_kernel "
+                      "(head_dim 128, f16 QK, causal, interleaved)",
+            "kernel_ms": round(call_ms, 5),
+        },
+        "cpu_baseline": cpu_baseline_bwd(inputs, dout_cpu, w) if with_cpu else None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -164,6 +267,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--backward", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -183,6 +287,9 @@ def main() -> int:
         return 0
     if args.all_configs:
         all_configs(torch, cgr, W, dev, args.steps, args.warmup)
+        return 0
+    if args.backward:
+        backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
         return 0
 
     w = W.get(WORKLOAD)

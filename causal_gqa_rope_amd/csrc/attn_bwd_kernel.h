@@ -282,10 +282,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dk, dv. Workgroup = 8 waves = two groups of 4; wave w holds keys
-// k0 + 32(w%4) .. +31 of the workgroup's 128. The group's work items are
-// (query head of the K/V group, 32-row query step); group 0 takes the even
-// items and group 1 the odd ones, so the two waves of a SIMD (w and w+4, same
-// keys) split the rows, and their partial sums meet in LDS at the end.
+// k0 + 32(w%4) .. +31 of the workgroup's 128. The work items are (32-row
+// query step, query head of the K/V group); group 0 takes the even items and
+// group 1 the odd ones, so the two waves of a SIMD (w and w+4, same keys)
+// split the work, and their partial sums meet in LDS at the end.
 // Per item and wave (32 query rows x 32 keys):
 //   S  = q~ k~^T - lse        (rows = queries, lane column = key; log2 units)
 //   dP = dO v^T - D
@@ -360,12 +360,22 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int n_iter = (n_items + 1) / 2;
   const rsrc_t rld = make_rsrc(a.ld, (uint32_t)((long)a.B * a.H * a.NT * 256));
 
+  // Item n = (query step, head g) with the heads innermost and the steps from
+  // the last rows back: the workgroups of one K/V head (which share an XCD)
+  // then stream the same query rows at about the same time, and both groups
+  // of a workgroup work on the same rows, so most reloads hit L2.
+  auto item = [&](int n, int& g, int& qrow0) {
+    const int sidx = n / G;
+    g = n - sidx * G;
+    qrow0 = q_first + 32 * (n_steps - 1 - sidx);
+  };
   // Loads of iteration i (this group's item 2i + grp) into a stage.
   auto issue = [&](int i, char* st) {
     const int n = 2 * i + grp;
     if (n >= n_items) return;
-    const int g = n / n_steps, sidx = n - g * n_steps;
-    const int h = kvh * G + g, qrow0 = q_first + 32 * sidx;
+    int g, qrow0;
+    item(n, g, qrow0);
+    const int h = kvh * G + g;
     char* gs = st + grp * C::GSTAGE;
     const long hoff = (long)tok0 * qs + (long)h * D;
     const rsrc_t rq = make_rsrc((const uint16_t*)a.qr + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
@@ -387,8 +397,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   auto compute = [&](int i, const char* st) {
     const int n = 2 * i + grp;
     if (n >= n_items) return;
-    const int g = n / n_steps, sidx = n - g * n_steps;
-    const int qrow0 = q_first + 32 * sidx;
+    int g, qrow0;
+    item(n, g, qrow0);
     if (C::CAUSAL && qrow0 < kw0) return;  // every key of the wave is later than every row
     const char* gs = st + grp * C::GSTAGE;
     const char* Qt = gs;
