@@ -31,6 +31,12 @@ Real", section "Coming from CUDA: where's .backward()?": backprop is the
 chain rule through every op, RoPE and attention included): from dL/dO it
 returns dL/dq, dL/dk, dL/dv of the un-rotated inputs.
 
+Decode against a KV cache (``attention_decode``): the new queries of a
+sequence are its last positions, so the causal mask aligns them with the end
+of the cache ("Attention from Scratch", section "Attention, the math": GQA
+shares each K/V head among several query heads so that the cache of keys and
+values kept for generation shrinks by that factor).
+
 Packed variable-length batches (the kohakutt page, Highlights: "packed
 variable-length batches") are the concatenation of independent sequences:
 positions restart at 0 in every sequence and the mask never crosses a
@@ -59,6 +65,7 @@ __all__ = [
     "attention_dense_bwd",
     "attention_varlen_bwd",
     "attention_bwd_group",
+    "attention_decode",
 ]
 
 
@@ -388,3 +395,43 @@ def attention_bwd_group(q, k, v, dout, b: int, kv: int, *, causal: bool = True, 
     dq = apply_rope_transpose(dqr, pos, base, style)
     dk = apply_rope_transpose(dkr, pos, base, style)
     return dq, dk, dv
+
+
+def attention_decode(q, k, v, cache_seqlens, *, base: float = 10000.0, style: str = "interleaved",
+                     scale: Optional[float] = None):
+    """New queries against a KV cache.
+
+    q [B, Tq, H, d]: the Tq newest tokens of each sequence; k, v [B, S, KV, d]:
+    the cache, un-rotated, of which batch entry b uses rows 0 .. L_b - 1 with
+    L_b = cache_seqlens[b] >= Tq (the new tokens' own keys are its last Tq
+    rows). Query i of entry b sits at position L_b - Tq + i and sees the keys
+    at positions j <= L_b - Tq + i (the causal mask aligned with the end of the
+    cache). Returns O [B, Tq, H, d] and lse [B, H, Tq] (float64).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Tq, H, d = q.shape
+    KV = k.shape[2]
+    _check_heads(H, KV)
+    G = H // KV
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lens = [int(x) for x in np.asarray(cache_seqlens).reshape(-1)]
+    O = np.empty_like(q)
+    lse = np.empty((B, H, Tq), dtype=np.float64)
+    for b in range(B):
+        L = lens[b]
+        if not (Tq <= L <= k.shape[1]):
+            raise ValueError(f"cache length {L} of entry {b} must lie in [Tq, S]")
+        qpos = np.arange(L - Tq, L)
+        qr = apply_rope(q[b], qpos, base, style)
+        kr = apply_rope(k[b, :L], np.arange(L), base, style)
+        future = qpos[:, None] < np.arange(L)[None, :]
+        for h in range(H):
+            kv = h // G
+            S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
+            S[future] = -np.inf
+            m = S.max(axis=1)
+            e = np.exp(S - m[:, None])
+            den = e.sum(axis=1)
+            lse[b, h] = m + np.log(den)
+            O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :]
+    return O, lse

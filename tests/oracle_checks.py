@@ -555,6 +555,62 @@ def check_bwd_group_matches_full():
             assert np.allclose(gk, dk[b, :, kv], atol=1e-12) and np.allclose(gv, dv[b, :, kv], atol=1e-12)
 
 
+# -------------------------------------------------------------------------- decode
+
+def check_decode_is_the_end_of_the_causal_forward():
+    # The Tq new queries of a sequence of length L are rows L-Tq .. L-1 of the
+    # causal forward over its first L tokens, whatever sits in the query rows
+    # before them and in the cache rows past L.
+    rng = RNG(40)
+    B, S, H, KV, d, Tq = 3, 40, 6, 2, 8, 3
+    lens = [3, 17, 40]
+    q = rng.standard_normal((B, Tq, H, d))
+    k = rng.standard_normal((B, S, KV, d))
+    v = rng.standard_normal((B, S, KV, d))
+    for style, base in (("interleaved", 10000.0), ("half", 500000.0)):
+        o, lse = oracle.attention_decode(q, k, v, lens, base=base, style=style)
+        for b, L in enumerate(lens):
+            qf = rng.standard_normal((1, L, H, d))
+            qf[0, L - Tq:] = q[b]
+            of, lf = oracle.attention_dense(qf, k[None, b, :L], v[None, b, :L], causal=True, base=base,
+                                            style=style)
+            assert np.allclose(o[b], of[0, L - Tq:], atol=1e-12)
+            assert np.allclose(lse[b], lf[0, :, L - Tq:], atol=1e-12)
+    # brute force on one entry
+    ob, lb = brute_force(np.concatenate([np.zeros((1, lens[1] - Tq, H, d)), q[1:2]], axis=1).tolist(),
+                         k[1:2, :lens[1]].tolist(), v[1:2, :lens[1]].tolist(), True, 10000.0, "interleaved")
+    o, lse = oracle.attention_decode(q, k, v, lens, base=10000.0)
+    assert np.allclose(o[1], ob[0, lens[1] - Tq:], atol=1e-12) and np.allclose(lse[1], lb[0, :, lens[1] - Tq:], atol=1e-12)
+
+
+def check_decode_special_cases():
+    rng = RNG(41)
+    B, S, H, KV, d = 2, 16, 4, 1, 8
+    q = rng.standard_normal((B, 1, H, d))
+    k = rng.standard_normal((B, S, KV, d))
+    v = rng.standard_normal((B, S, KV, d))
+    # A cache of one token: every head returns that token's value, lse = its score.
+    o, lse = oracle.attention_decode(q, k, v, [1, 1])
+    assert np.array_equal(o[:, 0, 2], v[:, 0, 0])
+    assert np.allclose(lse[:, 3, 0], np.einsum("bd,bd->b", q[:, 0, 3], k[:, 0, 0]) / math.sqrt(d), atol=1e-14)
+    # Cache rows past the length do not matter.
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 9:] = 1e3
+    v2[:, 9:] = np.nan
+    a = oracle.attention_decode(q, k, v, [9, 5])
+    b = oracle.attention_decode(q, k2, v2, [9, 5])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # Tq = L is the whole causal forward.
+    q3 = rng.standard_normal((1, 12, H, d))
+    o3, l3 = oracle.attention_decode(q3, k[:1], v[:1], [12])
+    od, ld = oracle.attention_dense(q3, k[:1, :12], v[:1, :12], causal=True)
+    assert np.allclose(o3, od, atol=1e-13) and np.allclose(l3, ld, atol=1e-13)
+    # q = 0: the one new query averages every cached value.
+    o4, l4 = oracle.attention_decode(np.zeros((B, 1, H, d)), k, v, [16, 7])
+    assert np.allclose(o4[1, 0, 0], v[1, :7, 0].mean(axis=0), atol=1e-14)
+    assert np.allclose(l4[1], math.log(7), atol=1e-14)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -582,4 +638,6 @@ ALL_CHECKS = [
     check_bwd_closed_forms,
     check_bwd_varlen_is_concat_of_dense,
     check_bwd_group_matches_full,
+    check_decode_is_the_end_of_the_causal_forward,
+    check_decode_special_cases,
 ]

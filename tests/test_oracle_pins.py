@@ -66,6 +66,13 @@ MUTANTS = [
      "r1 = min(T - 1, r0 + rows_per_block)"),
     ("group backward sees one key too few", "            n = r1 if causal else T",
      "            n = r1 - 1 if causal else T"),
+    ("decode queries at positions 0..Tq-1", "qpos = np.arange(L - Tq, L)", "qpos = np.arange(0, Tq)"),
+    ("decode mask aligned with the start", "future = qpos[:, None] < np.arange(L)[None, :]",
+     "future = np.arange(Tq)[:, None] < np.arange(L)[None, :]"),
+    ("decode keys unrotated", "kr = apply_rope(k[b, :L], np.arange(L), base, style)", "kr = k[b, :L]"),
+    ("decode sees cache rows past the length", "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :]",
+     "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :] + 0.0 * v[b, L - 1:L, kv, :].sum() + "
+     "(v[b, L:, kv, :].sum() if L < v.shape[1] else 0.0)"),
     ("backward positions do not restart per sequence",
      "_one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,\n"
      "                                                      base, style)",
