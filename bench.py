@@ -22,6 +22,8 @@ bounded sample of the same workload on this host's cores.
                                         attention call only; not the headline line)
   python bench.py --backward           (one JSON line for the backward on the same
                                         workload; not the headline line)
+  python bench.py --decode             (one JSON line for decode against a KV cache,
+                                        16 sequences x 1 new token; not the headline line)
 """
 
 from __future__ import annotations
@@ -259,6 +261,113 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
     print(json.dumps(result), flush=True)
 
 
+DECODE_WORKLOAD = "decode_B16_Tq1_cache4096to8192_H32_KV8_d128"
+DECODE_METRIC = "causal GQA+RoPE decode against a KV cache, GB/s moved on 1 MI355X; % of HBM peak"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def cpu_baseline_decode(x, w) -> dict:
+    """The float64 oracle's decode, as it stands, on 4 of the 16 sequences."""
+    import oracle
+    import workloads as W
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or None
+    except Exception:
+        pass
+    n = 4
+    lens = x["cache_seqlens"][:n].numpy()
+    t0 = time.perf_counter()
+    oracle.attention_decode(x["q"][:n], x["k"][:n], x["v"][:n], lens, base=w.base, style=w.rope_style)
+    dt = time.perf_counter() - t0
+    nbytes = W.decode_bytes(w.replace(B=n), lens)
+    return {
+        "value": round(nbytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle decode, sequences 0-{n - 1} of {w.B} (cache lengths "
+                  f"{', '.join(str(int(L)) for L in lens)}), {dt:.1f} s",
+    }
+
+
+def decode(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
+    """One step = one decode call; the cache is filled (keys rotated by
+    cgr_rope_rotate) before timing."""
+    w = W.DECODE_WORKLOADS[DECODE_WORKLOAD]
+    x = W.make_decode_inputs(w)
+    B, S, KV, D = x["k"].shape
+    cos, sin = cgr.rope_tables(w.capacity, D, w.base, device=dev)
+    pos = torch.arange(S, dtype=torch.int32, device=dev).repeat(B)
+    kc = cgr.rope_rotate(x["k"].to(dev).reshape(B * S, KV, D), pos, cos, sin,
+                         rope_style=w.rope_style).reshape(B, S, KV, D)
+    vc = x["v"].to(dev)
+    q = x["q"].to(dev)
+    lens = x["cache_seqlens"].to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, w.n_head, w.Tq), dtype=torch.float32, device=dev)
+    ws = torch.empty(cgr.cgr_attn_decode_workspace_size(B, w.Tq, x["max_seqlen"], w.n_head, KV, D),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        cgr.gqa_rope_attn_decode(q, kc, vc, lens, x["max_seqlen"], cos, sin, rope_style=w.rope_style,
+                                 out=o, lse=lse, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    nbytes = W.decode_bytes(w, x["cache_seqlens"].tolist())
+    ms_step = wall * 1e3 / steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    result = {
+        "metric": DECODE_METRIC,
+        "value": round(nbytes / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": DECODE_WORKLOAD, "B": B, "Tq": w.Tq, "cache_capacity": S,
+            "cache_lengths": f"U[{w.len_lo}, {w.len_hi}], sum {int(x['cache_seqlens'].sum())}",
+            "n_head": w.n_head, "n_kv_head": KV, "head_dim": D, "rope_base": w.base,
+            "rope_pairs": w.rope_style, "mask": "causal, aligned with the cache end", "io": "bf16",
+            "step": "gqa_rope_attn_decode", "bytes_per_step": nbytes,
+            "tokens_per_s": round(B * w.Tq / (ms_step * 1e-3), 1),
+            "pct_of_peak": round(100.0 * nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "the decode call: attn_decode_kernel + decode_combine_kernel (head_dim 128, interleaved)",
+            "kernel_ms": round(call_ms, 5),
+        },
+        "cpu_baseline": cpu_baseline_decode(x, w) if with_cpu else None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +377,7 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--decode", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -290,6 +400,9 @@ def main() -> int:
         return 0
     if args.backward:
         backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
+        return 0
+    if args.decode:
+        decode(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
         return 0
 
     w = W.get(WORKLOAD)

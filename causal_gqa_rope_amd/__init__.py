@@ -4,9 +4,11 @@ Argument marshalling only. Every step of the computation runs in the HIP
 kernels of ``libcgr.so``; torch supplies device memory and the current
 stream. The functions carry the names of the C entry points declared in
 ``include/cgr.h`` (``cgr_rope_tables``, ``cgr_gqa_rope_attn_fwd``,
-``cgr_gqa_rope_attn_fwd_varlen``, ``cgr_gqa_rope_attn_bwd``, ...); the short
-names (``rope_tables``, ``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``,
-``gqa_rope_attn_bwd``) are the same functions.
+``cgr_gqa_rope_attn_fwd_varlen``, ``cgr_gqa_rope_attn_bwd``,
+``cgr_rope_rotate``, ``cgr_gqa_rope_attn_decode``, ...); the short names
+(``rope_tables``, ``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``,
+``gqa_rope_attn_bwd``, ``rope_rotate``, ``gqa_rope_attn_decode``) are the same
+functions.
 
 The library leaves the HIP runtime's symbols unresolved; before loading it,
 the binding makes the runtime torch already loaded globally visible, so the
@@ -33,11 +35,16 @@ __all__ = [
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
+    "cgr_rope_rotate",
+    "cgr_attn_decode_workspace_size",
+    "cgr_gqa_rope_attn_decode",
     "cgr_version",
     "rope_tables",
     "gqa_rope_attn_fwd",
     "gqa_rope_attn_fwd_varlen",
     "gqa_rope_attn_bwd",
+    "rope_rotate",
+    "gqa_rope_attn_decode",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -60,6 +67,9 @@ EXPORTED_SYMBOLS = (
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
+    "cgr_rope_rotate",
+    "cgr_attn_decode_workspace_size",
+    "cgr_gqa_rope_attn_decode",
     "cgr_last_error",
     "cgr_version",
 )
@@ -112,6 +122,14 @@ def library() -> ctypes.CDLL:
     lib.cgr_gqa_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                           i32, vp, vp, i32, i32, i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_bwd.restype = i32
+    lib.cgr_rope_rotate.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp]
+    lib.cgr_rope_rotate.restype = i32
+    lib.cgr_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.cgr_attn_decode_workspace_size.restype = ctypes.c_size_t
+    i64 = ctypes.c_int64
+    lib.cgr_gqa_rope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i64, i32, i32,
+                                             i32, i32, i32, vp, vp, i32, i32, f32, vp, ctypes.c_size_t, vp]
+    lib.cgr_gqa_rope_attn_decode.restype = i32
     lib.cgr_varlen_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.cgr_varlen_device_status.restype = i32
     lib.cgr_last_error.argtypes = []
@@ -323,7 +341,98 @@ def cgr_gqa_rope_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
     return dq, dk, dv
 
 
+def cgr_rope_rotate(x: torch.Tensor, positions: torch.Tensor, rope_cos: torch.Tensor,
+                    rope_sin: torch.Tensor, *, rope_style: str = "interleaved",
+                    out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None):
+    """out[t, h] = R(positions[t]) x[t, h] for x [N, n_heads, d] (bf16 or f32); out may be x."""
+    lib = library()
+    _dev_tensor("x", x)
+    if x.dim() != 3:
+        raise CgrError(CGR_ERR_INVALID_ARG, "x must be [n_tokens, n_heads, head_dim]")
+    if x.dtype not in _DTYPES:
+        raise CgrError(CGR_ERR_UNSUPPORTED, "x must be float32 or bfloat16")
+    _dev_tensor("positions", positions, torch.int32)
+    if positions.numel() != x.shape[0]:
+        raise CgrError(CGR_ERR_INVALID_ARG, "positions must have one entry per token")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != x.shape[2] // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    out = torch.empty_like(x) if out is None else out
+    _dev_tensor("out", out, x.dtype)
+    if out.shape != x.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "out must have x's shape")
+    if status is not None:
+        _dev_tensor("status", status, torch.int32)
+    with torch.cuda.device(x.device):
+        _check(lib.cgr_rope_rotate(_ptr(x), _ptr(out), _ptr(positions), x.shape[0], x.shape[1], x.shape[2],
+                                   _DTYPES[x.dtype], _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+                                   _STYLES[rope_style], _ptr(status), _stream(x.device)))
+    return out
+
+
+def cgr_attn_decode_workspace_size(B: int, Tq: int, max_seqlen: int, n_head: int, n_kv_head: int,
+                                   head_dim: int) -> int:
+    return int(library().cgr_attn_decode_workspace_size(int(B), int(Tq), int(max_seqlen), int(n_head),
+                                                        int(n_kv_head), int(head_dim)))
+
+
+def cgr_gqa_rope_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                             cache_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
+                             rope_sin: torch.Tensor, *, rope_style: str = "interleaved",
+                             softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                             lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                             workspace: Optional[torch.Tensor] = None):
+    """Decode: q [B,Tq,H,d] against caches k/v indexed [B,S,KV,d] (keys rotated) with
+    lengths cache_seqlens int32 [B] (device). The caches may be strided views (a
+    head-major [B,KV,S,d] buffer viewed as [B,S,KV,d] with .transpose(1, 2)), with
+    head_dim contiguous and the same strides for k and v.
+    Returns (o [B,Tq,H,d], lse [B,H,Tq] float32 or None)."""
+    lib = library()
+    _dev_tensor("q", q, torch.bfloat16)
+    for n, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.bfloat16:
+            raise CgrError(CGR_ERR_INVALID_ARG, f"{n} must be a bfloat16 CUDA/HIP tensor")
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise CgrError(CGR_ERR_INVALID_ARG, f"{n} must be 4-D [B,S,KV,d] with head_dim contiguous")
+    if k_cache.stride() != v_cache.stride() or v_cache.shape != k_cache.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "k_cache and v_cache must share shape and strides")
+    _dev_tensor("cache_seqlens", cache_seqlens, torch.int32)
+    if q.dim() != 4:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q must be [B,Tq,H,d]")
+    B, Tq, H, D = q.shape
+    S, KV = k_cache.shape[1], k_cache.shape[2]
+    sb, st, sh = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or cache_seqlens.numel() != B:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, caches and cache_seqlens disagree on B or head_dim")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    out = torch.empty_like(q) if out is None else out
+    _dev_tensor("out", out, torch.bfloat16)
+    if out.shape != q.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev_tensor("lse", lse, torch.float32)
+    need = lib.cgr_attn_decode_workspace_size(B, Tq, int(max_seqlen), H, KV, D)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_decode(
+            _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Tq, S,
+            sb, st, sh, int(max_seqlen), H, KV, D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+            _STYLES[rope_style], 0.0 if softmax_scale is None else float(softmax_scale),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return out, lse
+
+
 rope_tables = cgr_rope_tables
 gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd
+rope_rotate = cgr_rope_rotate
+gqa_rope_attn_decode = cgr_gqa_rope_attn_decode

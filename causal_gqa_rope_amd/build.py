@@ -34,6 +34,9 @@ SOURCES = [
     "attn_bwd_d32.hip",
     "attn_bwd_d64.hip",
     "attn_bwd_d128.hip",
+    "attn_decode_d32.hip",
+    "attn_decode_d64.hip",
+    "attn_decode_d128.hip",
 ]
 
 ARCH = os.environ.get("CGR_OFFLOAD_ARCH", "gfx950")

@@ -1,0 +1,14 @@
+// Instances of the decode and row-rotation kernels for head_dim 32.
+#include "attn_decode_kernel.h"
+#include "launch.h"
+
+namespace cgr {
+hipError_t launch_decode_d32(const DecodeArgs& a, int style, hipStream_t stream) {
+  return launch_decode_d<32>(a, style, stream);
+}
+hipError_t launch_rope_rotate_d32(const void* x, void* out, const int32_t* positions, long n_rows, int nh,
+                                 int f32_io, const float* cs, const float* sn, int P, int style,
+                                 int32_t* status, hipStream_t stream) {
+  return launch_rope_rotate_d<32>(x, out, positions, n_rows, nh, f32_io, cs, sn, P, style, status, stream);
+}
+}  // namespace cgr

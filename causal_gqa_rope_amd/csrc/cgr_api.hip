@@ -11,6 +11,7 @@
 #include <string>
 
 #include "attn_bwd_kernel.h"
+#include "attn_decode_kernel.h"
 #include "attn_fwd_kernel.h"
 #include "cgr.h"
 #include "launch.h"
@@ -151,6 +152,34 @@ BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
   l.ld = l.kr + up((size_t)B * T * n_kv_head * head_dim * 2);
   l.total = l.ld + (size_t)B * n_head * nt * 64 * 4;
   return l;
+}
+
+// Decode split policy, a function of the sizes alone (so the workspace size
+// needs no device): about 2048 single-wave workgroups (eight per CU are
+// resident at once, so every chunk starts in the first wave of them), chunks
+// a multiple of the 32-key tile, no more chunks than tiles.
+struct DecodePlan {
+  int rg, ns, ch;
+  size_t lse_off, o_off, total;
+};
+DecodePlan decode_plan(int B, int Tq, int max_seqlen, int n_head, int n_kv_head, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  DecodePlan p;
+  const int G = n_head / n_kv_head;
+  p.rg = (G * Tq + 31) / 32;
+  const long pairs = (long)B * n_kv_head * p.rg;
+  const int tiles = (max_seqlen + cgr::kDecodeBN - 1) / cgr::kDecodeBN;
+  long ns = (2048 + pairs - 1) / pairs;
+  if (ns > tiles) ns = tiles;
+  if (ns < 1) ns = 1;
+  const int per = (int)((max_seqlen + ns - 1) / ns);
+  p.ch = ((per + cgr::kDecodeBN - 1) / cgr::kDecodeBN) * cgr::kDecodeBN;
+  p.ns = (max_seqlen + p.ch - 1) / p.ch;
+  const size_t rows = (size_t)B * n_head * Tq * p.ns;
+  p.lse_off = 256;  // int32 header: [2] is the error word
+  p.o_off = p.lse_off + up(rows * 4);
+  p.total = p.o_off + rows * head_dim * 4;
+  return p;
 }
 
 }  // namespace
@@ -324,6 +353,122 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
     default: e = cgr::launch_attn_bwd_d128(a, qkb, sty, cau, s); break;
   }
   if (e != hipSuccess) return hip_fail("backward launch", e);
+  return CGR_OK;
+}
+
+size_t cgr_attn_decode_workspace_size(int B, int Tq, int max_seqlen, int n_head, int n_kv_head,
+                                      int head_dim) {
+  if (B < 1 || Tq < 1 || max_seqlen < Tq || n_head < 1 || n_kv_head < 1 || n_head % n_kv_head ||
+      head_dim < 2)
+    return 0;
+  return decode_plan(B, Tq, max_seqlen, n_head, n_kv_head, head_dim).total;
+}
+
+cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Tq,
+                                    int cache_capacity, int64_t cache_batch_stride,
+                                    int64_t cache_token_stride, int64_t cache_head_stride,
+                                    int max_seqlen, int n_head, int n_kv_head, int head_dim,
+                                    cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                    int rope_max_pos, cgr_rope_style style, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 1 || Tq < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and Tq (%d) must be >= 1", B, Tq);
+  if (!cache_seqlens) return fail(CGR_ERR_INVALID_ARG, "cache_seqlens must be non-null");
+  if (!aligned(cache_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cache_seqlens must be 4-byte aligned");
+  if (max_seqlen < Tq || max_seqlen > cache_capacity)
+    return fail(CGR_ERR_INVALID_ARG, "need Tq (%d) <= max_seqlen (%d) <= cache_capacity (%d)", Tq,
+                max_seqlen, cache_capacity);
+  cgr_status st = check_common(q, k_cache, v_cache, o, lse, n_head, n_kv_head, head_dim, dtype,
+                               rope_cos, rope_sin, rope_max_pos, max_seqlen, style, CGR_MASK_CAUSAL,
+                               softmax_scale, CGR_QK_BF16);
+  if (st != CGR_OK) return st;
+  if (dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "decode takes bf16 tensors only (dtype %d)", (int)dtype);
+  if (cache_batch_stride < 0 || cache_token_stride < head_dim || cache_head_stride < head_dim ||
+      cache_batch_stride % 8 || cache_token_stride % 8 || cache_head_stride % 8)
+    return fail(CGR_ERR_INVALID_ARG,
+                "cache strides must be non-negative multiples of 8 elements, token and head strides "
+                ">= head_dim");
+  // One (entry, K/V head) is addressed with 32-bit byte offsets.
+  if (((long)cache_capacity - 1) * cache_token_stride * 2 + head_dim * 2 > (long)INT_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "one cache entry of %d tokens spans more than 2 GiB", cache_capacity);
+  const DecodePlan plan = decode_plan(B, Tq, max_seqlen, n_head, n_kv_head, head_dim);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 256)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < plan.total)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
+                plan.total);
+  if ((long)B * n_kv_head * plan.rg * plan.ns > INT_MAX || (long)B * n_head * Tq * head_dim > INT_MAX)
+    return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  cgr::DecodeArgs a{};
+  a.q = q;
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.sb = cache_batch_stride;
+  a.st = cache_token_stride;
+  a.sh = cache_head_stride;
+  a.seqlens = cache_seqlens;
+  a.o = o;
+  a.lse = lse;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.status = (int32_t*)workspace + 2;
+  a.part_lse = (float*)((char*)workspace + plan.lse_off);
+  a.part_o = (float*)((char*)workspace + plan.o_off);
+  a.B = B;
+  a.Tq = Tq;
+  a.S = cache_capacity;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  a.NS = plan.ns;
+  a.CH = plan.ch;
+  a.RG = plan.rg;
+  a.M = max_seqlen;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  a.qscale = (float)(scale * 1.4426950408889634074);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (head_dim) {
+    case 32: e = cgr::launch_decode_d32(a, (int)style, s); break;
+    case 64: e = cgr::launch_decode_d64(a, (int)style, s); break;
+    default: e = cgr::launch_decode_d128(a, (int)style, s); break;
+  }
+  if (e != hipSuccess) return hip_fail("decode launch", e);
+  return CGR_OK;
+}
+
+cgr_status cgr_rope_rotate(const void* x, void* out, const int32_t* positions, int n_tokens,
+                           int n_heads, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                           const float* rope_sin, int rope_max_pos, cgr_rope_style style,
+                           int32_t* device_status, void* stream) {
+  if (!x || !out || !positions || !rope_cos || !rope_sin)
+    return fail(CGR_ERR_INVALID_ARG, "x, out, positions, rope_cos and rope_sin must be non-null");
+  if (n_tokens < 0 || n_heads < 1)
+    return fail(CGR_ERR_INVALID_ARG, "n_tokens (%d) must be >= 0 and n_heads (%d) >= 1", n_tokens,
+                n_heads);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(CGR_ERR_UNSUPPORTED, "head_dim %d is not one of 32, 64, 128", head_dim);
+  if (dtype != CGR_F32 && dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "dtype %d is not CGR_F32 or CGR_BF16", (int)dtype);
+  if (style != CGR_ROPE_INTERLEAVED && style != CGR_ROPE_HALF)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown rope style %d", (int)style);
+  if (rope_max_pos < 1) return fail(CGR_ERR_INVALID_ARG, "rope_max_pos must be >= 1");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16) ||
+      !aligned(positions, 4) || (device_status && !aligned(device_status, 4)))
+    return fail(CGR_ERR_ALIGNMENT, "x, out and the tables must be 16-byte aligned, positions 4-byte");
+  if (n_tokens == 0) return CGR_OK;
+  const long rows = (long)n_tokens * n_heads;
+  if (rows * (head_dim / 16) > (long)UINT32_MAX * 256)
+    return fail(CGR_ERR_INVALID_ARG, "too many rows");
+  hipStream_t s = (hipStream_t)stream;
+  const int f32 = dtype == CGR_F32;
+  hipError_t e;
+  switch (head_dim) {
+    case 32: e = cgr::launch_rope_rotate_d32(x, out, positions, rows, n_heads, f32, rope_cos, rope_sin, rope_max_pos, (int)style, device_status, s); break;
+    case 64: e = cgr::launch_rope_rotate_d64(x, out, positions, rows, n_heads, f32, rope_cos, rope_sin, rope_max_pos, (int)style, device_status, s); break;
+    default: e = cgr::launch_rope_rotate_d128(x, out, positions, rows, n_heads, f32, rope_cos, rope_sin, rope_max_pos, (int)style, device_status, s); break;
+  }
+  if (e != hipSuccess) return hip_fail("rope_rotate launch", e);
   return CGR_OK;
 }
 

@@ -1,7 +1,7 @@
 /*
  * cgr.h -- fused causal grouped-query attention with rotary position
- * embedding (RoPE), forward and backward passes, for AMD Instinct MI355X
- * (gfx950).
+ * embedding (RoPE) for AMD Instinct MI355X (gfx950): forward (dense and packed
+ * batches), backward, and decode against a KV cache.
  *
  * The operation, as the pages define it:
  *   - RoPE tables: "Embeddings & the Residual Stream", section "Positional
@@ -196,10 +196,79 @@ CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const voi
                                  size_t workspace_bytes, void* stream);
 
 /*
- * Reads the device error word the last varlen call on `workspace` left:
- * waits for `stream`, then stores 0 (cu_seqlens was well formed) or a
- * positive code (1: cu_seqlens[0] != 0, 2: decreasing, 3: a sequence longer
- * than max_seqlen, 4: cu_seqlens[num_seqs] != total_tokens) in *host_status.
+ * RoPE on rows at given positions ("Embeddings & the Residual Stream",
+ * "Positional information: RoPE"): out[t, h, :] = R(positions[t]) x[t, h, :]
+ * for x, out device [n_tokens, n_heads, head_dim] (dtype; out may equal x).
+ * The step that appends new keys to a KV cache for cgr_gqa_rope_attn_decode,
+ * which expects keys already rotated at their positions.
+ *   positions: device int32 [n_tokens]; a row whose position is outside
+ *     [0, rope_max_pos) is left unwritten and sets *device_status to 1 (when
+ *     device_status, a device int32, is non-null; it is never cleared here).
+ *   head_dim in {32, 64, 128}; tables as for the forward.
+ */
+CGR_API cgr_status cgr_rope_rotate(const void* x, void* out, const int32_t* positions, int n_tokens,
+                           int n_heads, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                           const float* rope_sin, int rope_max_pos, cgr_rope_style style,
+                           int32_t* device_status, void* stream);
+
+/*
+ * Bytes of device workspace cgr_gqa_rope_attn_decode needs (0 for invalid
+ * sizes): a 256-byte header, then one partial output and log-sum-exp per
+ * (batch entry, head, query, key chunk); the chunking depends on the sizes
+ * only.
+ */
+CGR_API size_t cgr_attn_decode_workspace_size(int B, int Tq, int max_seqlen, int n_head, int n_kv_head,
+                                      int head_dim);
+
+/*
+ * Decode: the Tq newest tokens of each of B sequences attend to that
+ * sequence's KV cache ("Attention from Scratch", "Attention, the math": GQA
+ * lets n_head / n_kv_head query heads share one cached K/V head).
+ * Batch entry b has L_b = cache_seqlens[b] cached tokens at positions
+ * 0 .. L_b - 1, the Tq new ones being the last Tq; query i is at position
+ * L_b - Tq + i and sees keys j <= L_b - Tq + i (causal, aligned with the end
+ * of the cache).
+ *   q: device bf16 [B, Tq, n_head, head_dim], rotated here at its position.
+ *   k_cache, v_cache: device bf16 caches with room for cache_capacity tokens
+ *     per entry; token t of K/V head kv of entry b starts at element
+ *     b * cache_batch_stride + t * cache_token_stride + kv * cache_head_stride
+ *     (head_dim contiguous elements; the same layout for both caches). A
+ *     contiguous [B, cache_capacity, n_kv_head, head_dim] cache has strides
+ *     (cache_capacity * n_kv_head * head_dim, n_kv_head * head_dim, head_dim);
+ *     a head-major [B, n_kv_head, cache_capacity, head_dim] one
+ *     (n_kv_head * cache_capacity * head_dim, head_dim, cache_capacity *
+ *     head_dim). Strides are multiples of 8 elements. Rows 0 .. L_b - 1 of
+ *     entry b are used; the keys are stored already rotated at their
+ *     positions (cgr_rope_rotate), the values as they are.
+ *   cache_seqlens: device int32 [B], each in [Tq, max_seqlen]; max_seqlen <=
+ *     cache_capacity and <= rope_max_pos.
+ *   o: device bf16 [B, Tq, n_head, head_dim]; lse: device float32
+ *     [B, n_head, Tq] (natural log-sum-exp), or NULL.
+ *   dtype: CGR_BF16 only. Scores are products of the bf16 keys with the
+ *     rotated, scaled query carried as two bf16 parts (16 significant bits);
+ *     P.V multiplies bf16 P by bf16 V; f32 accumulation.
+ *   workspace: at least cgr_attn_decode_workspace_size(B, Tq, max_seqlen,
+ *     n_head, n_kv_head, head_dim) bytes, 256-byte aligned, for this call only.
+ * cache_seqlens lives on the device and is checked there: entries outside
+ * [Tq, max_seqlen] are left unwritten and the call's error word (read with
+ * cgr_varlen_device_status on the workspace) becomes 1; otherwise 0.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_seqlens, void* o, float* lse, int B, int Tq,
+                                    int cache_capacity, int64_t cache_batch_stride,
+                                    int64_t cache_token_stride, int64_t cache_head_stride,
+                                    int max_seqlen, int n_head, int n_kv_head, int head_dim,
+                                    cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                    int rope_max_pos, cgr_rope_style style, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Reads the device error word the last varlen or decode call on `workspace` left:
+ * waits for `stream`, then stores 0 (the device-side sizes were well formed)
+ * or a positive code in *host_status. Varlen: 1: cu_seqlens[0] != 0,
+ * 2: decreasing, 3: a sequence longer than max_seqlen, 4:
+ * cu_seqlens[num_seqs] != total_tokens. Decode: 1: a cache length outside
+ * [Tq, max_seqlen].
  */
 CGR_API cgr_status cgr_varlen_device_status(const void* workspace, void* stream, int32_t* host_status);
 

@@ -199,3 +199,69 @@ def test_backward_rejects_bad_arguments(kw, status, needle):
     st, msg = backward(**kw)
     assert st == status, msg
     assert needle in msg
+
+
+def test_decode_workspace_size():
+    lib = cgr.library()
+    assert lib.cgr_attn_decode_workspace_size(0, 1, 10, 4, 2, 64) == 0
+    assert lib.cgr_attn_decode_workspace_size(2, 5, 4, 4, 2, 64) == 0   # max_seqlen < Tq
+    assert lib.cgr_attn_decode_workspace_size(2, 1, 10, 6, 4, 64) == 0  # heads not divisible
+    small = lib.cgr_attn_decode_workspace_size(1, 1, 32, 4, 2, 64)
+    big = lib.cgr_attn_decode_workspace_size(16, 1, 8192, 32, 8, 128)
+    assert 256 < small < big
+
+
+def decode_call(**kw):
+    a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Tq=1, S=64, sb=64 * 2 * 64, st=2 * 64, sh=64,
+             M=64, H=4, KV=2, D=64, dtype=1, cos=P, sin=P, P=64, style=0, scale=0.0,
+             ws=ctypes.c_void_p(0x10000), wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Tq"],
+                                      a["S"], a["sb"], a["st"], a["sh"], a["M"], a["H"], a["KV"], a["D"],
+                                      a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["scale"], a["ws"],
+                                      a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lens=None), 1, "cache_seqlens"),
+    (dict(B=0), 1, ">= 1"),
+    (dict(Tq=0), 1, ">= 1"),
+    (dict(M=65), 1, "cache_capacity"),
+    (dict(Tq=3, M=2), 1, "max_seqlen"),
+    (dict(P=63), 1, "positions"),
+    (dict(dtype=0), 2, "bf16"),
+    (dict(st=60), 1, "multiples of 8"),
+    (dict(sh=32), 1, "head_dim"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(wsb=300), 4, "needs"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(D=48), 2, "not one of"),
+])
+def test_decode_rejects_bad_arguments(kw, status, needle):
+    st, msg = decode_call(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(x=None), 1, "non-null"),
+    (dict(pos=None), 1, "non-null"),
+    (dict(n=-1), 1, ">= 0"),
+    (dict(nh=0), 1, ">= 1"),
+    (dict(d=48), 2, "not one of"),
+    (dict(dtype=5), 2, "dtype"),
+    (dict(style=2), 2, "style"),
+    (dict(x=PMIS), 3, "aligned"),
+])
+def test_rope_rotate_rejects_bad_arguments(kw, status, needle):
+    a = dict(x=P, out=P, pos=P, n=4, nh=2, d=64, dtype=1, cos=P, sin=P, P=16, style=0, status=None)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_rope_rotate(a["x"], a["out"], a["pos"], a["n"], a["nh"], a["d"], a["dtype"], a["cos"],
+                             a["sin"], a["P"], a["style"], a["status"], None)
+    assert st == status, lib.cgr_last_error().decode()
+    assert needle in lib.cgr_last_error().decode()

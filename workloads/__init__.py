@@ -42,6 +42,10 @@ __all__ = [
     "make_dout",
     "algorithmic_flops",
     "algorithmic_flops_bwd",
+    "DecodeWorkload",
+    "DECODE_WORKLOADS",
+    "make_decode_inputs",
+    "decode_bytes",
 ]
 
 
@@ -208,3 +212,58 @@ def algorithmic_flops_bwd(n_head: int, head_dim: int, lengths, causal: bool) -> 
     not credited.
     """
     return algorithmic_flops(n_head, head_dim, lengths, causal) // 4 * 10
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    """New queries against a KV cache: B sequences with cache lengths drawn
+    uniformly from [len_lo, len_hi] (inclusive) by the seed, the Tq newest
+    tokens of each as queries; the cache has room for `capacity` tokens."""
+
+    name: str
+    B: int
+    Tq: int
+    capacity: int
+    n_head: int
+    n_kv_head: int
+    head_dim: int
+    base: float
+    seed: int
+    len_lo: int
+    len_hi: int
+    rope_style: str = "interleaved"
+
+    def replace(self, **kw) -> "DecodeWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+DECODE_WORKLOADS = {
+    w.name: w
+    for w in [
+        # One serving step of the long-context model's attention: 16 sequences,
+        # one new token each, caches of 4096 to 8192 tokens.
+        DecodeWorkload("decode_B16_Tq1_cache4096to8192_H32_KV8_d128", B=16, Tq=1, capacity=8192,
+                       n_head=32, n_kv_head=8, head_dim=128, base=500000.0, seed=20, len_lo=4096,
+                       len_hi=8192),
+    ]
+}
+
+
+def make_decode_inputs(w: DecodeWorkload) -> dict:
+    """Seeded CPU tensors: cache lengths first (int32 [B]), then q [B, Tq, H, d] and the
+    un-rotated k, v caches [B, capacity, KV, d], all N(0,1), cast once to bf16."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    lens = torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=gen).to(torch.int32)
+    q = torch.randn((w.B, w.Tq, w.n_head, w.head_dim), generator=gen, dtype=torch.float32)
+    k = torch.randn((w.B, w.capacity, w.n_kv_head, w.head_dim), generator=gen, dtype=torch.float32)
+    v = torch.randn((w.B, w.capacity, w.n_kv_head, w.head_dim), generator=gen, dtype=torch.float32)
+    return dict(q=q.to(torch.bfloat16), k=k.to(torch.bfloat16), v=v.to(torch.bfloat16), cache_seqlens=lens,
+                max_seqlen=int(lens.max()))
+
+
+def decode_bytes(w: DecodeWorkload, lens) -> int:
+    """Bytes one decode call must move at least: the used K and V cache rows
+    (bf16), the queries in, the outputs out (bf16) and their log-sum-exp (f32)."""
+    cache = sum(int(L) for L in lens) * w.n_kv_head * w.head_dim * 2 * 2
+    qo = 2 * w.B * w.Tq * w.n_head * w.head_dim * 2
+    return cache + qo + w.B * w.n_head * w.Tq * 4
