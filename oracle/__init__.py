@@ -135,7 +135,28 @@ def apply_rope(x, positions, base: float, style: str = "interleaved") -> np.ndar
     return y
 
 
-def _one_sequence(q, k, v, causal: bool, scale: float, base: float, style: str):
+def _hidden(qpos, kpos, causal: bool, window: int) -> np.ndarray:
+    """[len(qpos), len(kpos)]: True where the query at position qpos[i] may not
+    see the key at kpos[j] -- a later key (causal), or, with window W > 0, a
+    key W or more positions back (sliding window: 0 <= i - j < W is visible)."""
+    qp = np.asarray(qpos)[:, None]
+    kp = np.asarray(kpos)[None, :]
+    hide = np.zeros((qp.shape[0], kp.shape[1]), dtype=bool)
+    if causal:
+        hide |= kp > qp
+    if window > 0:
+        hide |= qp - kp >= window
+    return hide
+
+
+def _check_window(causal: bool, window: int):
+    if window < 0:
+        raise ValueError("window must be >= 0 (0: no window)")
+    if window > 0 and not causal:
+        raise ValueError("a sliding window needs the causal mask")
+
+
+def _one_sequence(q, k, v, causal: bool, scale: float, base: float, style: str, window: int = 0):
     """Attention for one sequence. q [L, H, d], k/v [L, KV, d] float64.
 
     Returns O [L, H, d] and lse [H, L]. The score matrix of every head is
@@ -152,12 +173,11 @@ def _one_sequence(q, k, v, causal: bool, scale: float, base: float, style: str):
     lse = np.empty((H, L), dtype=np.float64)
     if L == 0:
         return O, lse
-    future = np.triu(np.ones((L, L), dtype=bool), k=1) if causal else None
+    hidden = _hidden(pos, pos, causal, window)
     for h in range(H):
         kv = h // G  # repeat_interleave: heads of one group are adjacent
         S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
-        if causal:
-            S[future] = -np.inf
+        S[hidden] = -np.inf
         m = S.max(axis=1)
         e = np.exp(S - m[:, None])
         den = e.sum(axis=1)
@@ -173,8 +193,11 @@ def _check_heads(n_head: int, n_kv_head: int):
 
 
 def attention_dense(q, k, v, *, causal: bool = True, base: float = 10000.0,
-                    style: str = "interleaved", scale: Optional[float] = None):
-    """Dense batch: q [B,T,H,d], k/v [B,T,KV,d]. Returns O [B,T,H,d], lse [B,H,T] (float64)."""
+                    style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
+    """Dense batch: q [B,T,H,d], k/v [B,T,KV,d]. Returns O [B,T,H,d], lse [B,H,T] (float64).
+
+    window W > 0 (with the causal mask) keeps only keys 0 <= i - j < W."""
+    _check_window(causal, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, T, H, d = q.shape
     _check_heads(H, k.shape[2])
@@ -182,17 +205,18 @@ def attention_dense(q, k, v, *, causal: bool = True, base: float = 10000.0,
     O = np.empty_like(q)
     lse = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
-        O[b], lse[b] = _one_sequence(q[b], k[b], v[b], causal, scale, base, style)
+        O[b], lse[b] = _one_sequence(q[b], k[b], v[b], causal, scale, base, style, window)
     return O, lse
 
 
 def attention_varlen(q, k, v, cu_seqlens, *, causal: bool = True, base: float = 10000.0,
-                     style: str = "interleaved", scale: Optional[float] = None):
+                     style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
     """Packed batch: q [total,H,d], k/v [total,KV,d], cu_seqlens [n+1].
 
     Each sequence s occupies tokens cu[s]..cu[s+1]-1 and is attended to on its
     own, positions restarting at 0. Returns O [total,H,d], lse [H,total].
     """
+    _check_window(causal, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
     total, H, d = q.shape
@@ -202,13 +226,13 @@ def attention_varlen(q, k, v, cu_seqlens, *, causal: bool = True, base: float = 
     lse = np.empty((H, total), dtype=np.float64)
     for s in range(len(cu) - 1):
         a, b = cu[s], cu[s + 1]
-        O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style)
+        O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style, window)
     return O, lse
 
 
 def attention_rows(q, k, v, rows: Sequence, *, causal: bool = True, base: float = 10000.0,
                    style: str = "interleaved", scale: Optional[float] = None,
-                   cu_seqlens=None):
+                   cu_seqlens=None, window: int = 0):
     """O and lse of selected output rows only, one row at a time.
 
     ``rows`` lists (b, t, h) for a dense batch (q [B,T,H,d]) or (s, t, h) for a
@@ -217,6 +241,7 @@ def attention_rows(q, k, v, rows: Sequence, *, causal: bool = True, base: float 
     its sequence that the mask allows; nothing else is computed, so sampled
     checks at full size stay cheap. Returns (O [n, d], lse [n]) float64.
     """
+    _check_window(causal, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     d = q.shape[-1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -239,13 +264,14 @@ def attention_rows(q, k, v, rows: Sequence, *, causal: bool = True, base: float 
             qrow = q[a + t, h]
             keys, vals = k[a:a + L, h // G], v[a:a + L, h // G]
         n = t + 1 if causal else L
+        lo = max(0, t - window + 1) if window > 0 else 0
         qr = apply_rope(qrow[None, :], [t], base, style)[0]
-        kr = apply_rope(keys[:n], np.arange(n), base, style)
+        kr = apply_rope(keys[lo:n], np.arange(lo, n), base, style)
         s = (kr @ qr) * scale
         m = s.max()
         e = np.exp(s - m)
         den = e.sum()
-        outs.append((e / den) @ vals[:n])
+        outs.append((e / den) @ vals[lo:n])
         lses.append(m + math.log(den))
     return np.array(outs).reshape(len(rows), d), np.array(lses)
 
@@ -280,7 +306,8 @@ def apply_rope_transpose(g, positions, base: float, style: str = "interleaved") 
     return x
 
 
-def _one_sequence_bwd(q, k, v, dout, causal: bool, scale: float, base: float, style: str):
+def _one_sequence_bwd(q, k, v, dout, causal: bool, scale: float, base: float, style: str,
+                      window: int = 0):
     """Gradients for one sequence: q, dout [L, H, d], k/v [L, KV, d] float64.
 
     Reverse of ``_one_sequence``, op by op, for every head:
@@ -304,12 +331,11 @@ def _one_sequence_bwd(q, k, v, dout, causal: bool, scale: float, base: float, st
     kr = apply_rope(k, pos, base, style)
     dqr = np.zeros_like(q)
     dkr = np.zeros_like(k)
-    future = np.triu(np.ones((L, L), dtype=bool), k=1) if causal else None
+    hidden = _hidden(pos, pos, causal, window)
     for h in range(H):
         kv = h // G
         S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
-        if causal:
-            S[future] = -np.inf
+        S[hidden] = -np.inf
         e = np.exp(S - S.max(axis=1)[:, None])
         P = e / e.sum(axis=1)[:, None]
         dv[:, kv, :] += P.T @ dout[:, h, :]
@@ -323,22 +349,25 @@ def _one_sequence_bwd(q, k, v, dout, causal: bool, scale: float, base: float, st
 
 
 def attention_dense_bwd(q, k, v, dout, *, causal: bool = True, base: float = 10000.0,
-                        style: str = "interleaved", scale: Optional[float] = None):
+                        style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
     """Dense batch backward: q/dout [B,T,H,d], k/v [B,T,KV,d] -> dq, dk, dv (float64, same shapes)."""
+    _check_window(causal, window)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, T, H, d = q.shape
     _check_heads(H, k.shape[2])
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
     for b in range(B):
-        dq[b], dk[b], dv[b] = _one_sequence_bwd(q[b], k[b], v[b], dout[b], causal, scale, base, style)
+        dq[b], dk[b], dv[b] = _one_sequence_bwd(q[b], k[b], v[b], dout[b], causal, scale, base, style,
+                                                window)
     return dq, dk, dv
 
 
 def attention_varlen_bwd(q, k, v, dout, cu_seqlens, *, causal: bool = True, base: float = 10000.0,
-                         style: str = "interleaved", scale: Optional[float] = None):
+                         style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
     """Packed batch backward: q/dout [total,H,d], k/v [total,KV,d], cu_seqlens [n+1]; each sequence
     on its own, positions restarting at 0. Returns dq, dk, dv (float64, same shapes)."""
+    _check_window(causal, window)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
     total, H, d = q.shape
@@ -348,21 +377,24 @@ def attention_varlen_bwd(q, k, v, dout, cu_seqlens, *, causal: bool = True, base
     for s in range(len(cu) - 1):
         a, b = cu[s], cu[s + 1]
         dq[a:b], dk[a:b], dv[a:b] = _one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,
-                                                      base, style)
+                                                      base, style, window)
     return dq, dk, dv
 
 
 def attention_bwd_group(q, k, v, dout, b: int, kv: int, *, causal: bool = True, base: float = 10000.0,
-                        style: str = "interleaved", scale: Optional[float] = None, rows_per_block: int = 512):
+                        style: str = "interleaved", scale: Optional[float] = None, rows_per_block: int = 512,
+                        window: int = 0):
     """Gradients that involve one K/V head of one dense batch entry, for long sequences.
 
     Same arithmetic as ``_one_sequence_bwd`` restricted to batch entry b, K/V
     head kv and its query heads, with the score matrix built a block of query
     rows at a time (every row whole, so each row's softmax is exact) to bound
     memory. Under the causal mask a block of rows ending at r1 only needs keys
-    below r1: the others have weight exactly 0.
+    below r1, and with a window W only keys from r0 - W + 1 on: the others
+    have weight exactly 0.
     Returns dq [T, G, d] (the group's query heads, in order), dk [T, d], dv [T, d].
     """
+    _check_window(causal, window)
     q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, T, H, d = q.shape
     KV = k.shape[2]
@@ -382,23 +414,23 @@ def attention_bwd_group(q, k, v, dout, b: int, kv: int, *, causal: bool = True, 
         for r0 in range(0, T, rows_per_block):
             r1 = min(T, r0 + rows_per_block)
             n = r1 if causal else T
-            S = (qr[r0:r1] @ kr[:n].T) * scale
-            if causal:
-                S[np.arange(r0, r1)[:, None] < np.arange(n)[None, :]] = -np.inf
+            lo = max(0, r0 - window + 1) if window > 0 else 0
+            S = (qr[r0:r1] @ kr[lo:n].T) * scale
+            S[_hidden(np.arange(r0, r1), np.arange(lo, n), causal, window)] = -np.inf
             e = np.exp(S - S.max(axis=1)[:, None])
             P = e / e.sum(axis=1)[:, None]
-            dv[:n] += P.T @ do[r0:r1]
-            dP = do[r0:r1] @ vv[:n].T
+            dv[lo:n] += P.T @ do[r0:r1]
+            dP = do[r0:r1] @ vv[lo:n].T
             dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
-            dqr[r0:r1, g] = (dS @ kr[:n]) * scale
-            dkr[:n] += (dS.T @ qr[r0:r1]) * scale
+            dqr[r0:r1, g] = (dS @ kr[lo:n]) * scale
+            dkr[lo:n] += (dS.T @ qr[r0:r1]) * scale
     dq = apply_rope_transpose(dqr, pos, base, style)
     dk = apply_rope_transpose(dkr, pos, base, style)
     return dq, dk, dv
 
 
 def attention_decode(q, k, v, cache_seqlens, *, base: float = 10000.0, style: str = "interleaved",
-                     scale: Optional[float] = None):
+                     scale: Optional[float] = None, window: int = 0):
     """New queries against a KV cache.
 
     q [B, Tq, H, d]: the Tq newest tokens of each sequence; k, v [B, S, KV, d]:
@@ -406,8 +438,10 @@ def attention_decode(q, k, v, cache_seqlens, *, base: float = 10000.0, style: st
     L_b = cache_seqlens[b] >= Tq (the new tokens' own keys are its last Tq
     rows). Query i of entry b sits at position L_b - Tq + i and sees the keys
     at positions j <= L_b - Tq + i (the causal mask aligned with the end of the
-    cache). Returns O [B, Tq, H, d] and lse [B, H, Tq] (float64).
+    cache); with window W > 0 only keys 0 <= position - j < W. Returns
+    O [B, Tq, H, d] and lse [B, H, Tq] (float64).
     """
+    _check_window(True, window)
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, Tq, H, d = q.shape
     KV = k.shape[2]
@@ -424,11 +458,11 @@ def attention_decode(q, k, v, cache_seqlens, *, base: float = 10000.0, style: st
         qpos = np.arange(L - Tq, L)
         qr = apply_rope(q[b], qpos, base, style)
         kr = apply_rope(k[b, :L], np.arange(L), base, style)
-        future = qpos[:, None] < np.arange(L)[None, :]
+        hidden = _hidden(qpos, np.arange(L), True, window)
         for h in range(H):
             kv = h // G
             S = (qr[:, h, :] @ kr[:, kv, :].T) * scale
-            S[future] = -np.inf
+            S[hidden] = -np.inf
             m = S.max(axis=1)
             e = np.exp(S - m[:, None])
             den = e.sum(axis=1)

@@ -138,7 +138,7 @@ def check_rope_styles_related_by_permutation():
 
 # ------------------------------------------------------------------------ attention
 
-def brute_force(q, k, v, causal, base, style, scale=None):
+def brute_force(q, k, v, causal, base, style, scale=None, window=0):
     """Scalar loops over Python floats: rotate, share, score, mask, softmax, gather.
 
     Follows the six steps of "Attention from Scratch", section "Attention, the
@@ -169,7 +169,7 @@ def brute_force(q, k, v, causal, base, style, scale=None):
                 qi = rot(q[b][i][h], i)
                 w = []
                 for j in range(T):
-                    if causal and j > i:
+                    if (causal and j > i) or (window > 0 and i - j >= window):
                         w.append(0.0)
                         continue
                     kj = rot(k[b][j][g], j)
@@ -611,6 +611,97 @@ def check_decode_special_cases():
     assert np.allclose(l4[1], math.log(7), atol=1e-14)
 
 
+# ------------------------------------------------------------------ sliding window
+
+def check_window_is_causal_attention_on_a_slice():
+    # With a window W, row i sees keys i-W+1 .. i. RoPE scores depend on i - j
+    # only, so row i equals the last row of plain causal attention over the
+    # tokens i-W+1 .. i with positions restarting at 0.
+    rng = RNG(50)
+    T, H, KV, d = 40, 4, 2, 8
+    q = rng.standard_normal((1, T, H, d))
+    k = rng.standard_normal((1, T, KV, d))
+    v = rng.standard_normal((1, T, KV, d))
+    for W, style in ((7, "interleaved"), (16, "half"), (1, "interleaved")):
+        o, lse = oracle.attention_dense(q, k, v, causal=True, base=10000.0, style=style, window=W)
+        for i in (0, 3, W - 1, W, 25, T - 1):
+            if i >= T:
+                continue
+            a = max(0, i - W + 1)
+            os_, ls = oracle.attention_dense(q[:, a:i + 1], k[:, a:i + 1], v[:, a:i + 1], causal=True,
+                                             base=10000.0, style=style)
+            assert np.allclose(o[0, i], os_[0, -1], atol=1e-9) and np.allclose(lse[0, :, i], ls[0, :, -1], atol=1e-9)
+
+
+def check_window_special_cases():
+    rng = RNG(51)
+    T = 24
+    q = rng.standard_normal((2, T, 4, 8))
+    k = rng.standard_normal((2, T, 1, 8))
+    v = rng.standard_normal((2, T, 1, 8))
+    a = oracle.attention_dense(q, k, v, causal=True)
+    b = oracle.attention_dense(q, k, v, causal=True, window=T)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # W = 1: each row sees itself only.
+    o, lse = oracle.attention_dense(q, k, v, causal=True, window=1, base=10000.0)
+    assert np.array_equal(o[:, :, 2], v[:, :, 0])
+    qr = oracle.apply_rope(q[0, :, 3], np.arange(T), 10000.0)
+    kr = oracle.apply_rope(k[0, :, 0], np.arange(T), 10000.0)
+    assert np.allclose(lse[0, 3], np.einsum("td,td->t", qr, kr) / math.sqrt(8), atol=1e-12)
+    # brute force
+    ob, lb = brute_force(q[:1, :12].tolist(), k[:1, :12].tolist(), v[:1, :12].tolist(), True, 500000.0,
+                         "half", window=5)
+    o5, l5 = oracle.attention_dense(q[:1, :12], k[:1, :12], v[:1, :12], causal=True, base=500000.0,
+                                    style="half", window=5)
+    assert np.allclose(o5, ob, atol=1e-12) and np.allclose(l5, lb, atol=1e-12)
+    # sampled rows, packed batch, decode
+    rows = [(0, 0, 0), (1, 23, 3), (0, 9, 1), (1, 4, 2)]
+    o9, l9 = oracle.attention_dense(q, k, v, causal=True, window=9)
+    ro, rl = oracle.attention_rows(q, k, v, rows, causal=True, window=9)
+    for n, (bb, t, h) in enumerate(rows):
+        assert np.allclose(ro[n], o9[bb, t, h], atol=1e-13) and abs(rl[n] - l9[bb, h, t]) < 1e-13
+    cu = np.array([0, 10, 10, 24], dtype=np.int32)
+    ov, lv = oracle.attention_varlen(q[0], k[0], v[0], cu, causal=True, window=4)
+    for s0, s1 in ((0, 10), (10, 24)):
+        od, ld = oracle.attention_dense(q[None, 0, s0:s1], k[None, 0, s0:s1], v[None, 0, s0:s1], causal=True,
+                                        window=4)
+        assert np.array_equal(ov[s0:s1], od[0]) and np.array_equal(lv[:, s0:s1], ld[0])
+    Tq = 3
+    od, ld = oracle.attention_decode(q[:, T - Tq:], k, v, [T, T], window=6)
+    ow, lw = oracle.attention_dense(q, k, v, causal=True, window=6)
+    assert np.allclose(od, ow[:, T - Tq:], atol=1e-12) and np.allclose(ld, lw[:, :, T - Tq:], atol=1e-12)
+
+
+def check_window_backward():
+    # Finite differences of sum(O * W) through the windowed forward, and the
+    # blocked one-group backward against the full one.
+    rng = RNG(52)
+    B, T, H, KV, d, Wn = 1, 9, 2, 1, 4, 3
+    q = rng.standard_normal((B, T, H, d))
+    k = rng.standard_normal((B, T, KV, d))
+    v = rng.standard_normal((B, T, KV, d))
+    Wt = rng.standard_normal((B, T, H, d))
+    eps = 1e-5
+    dq, dk, dv = oracle.attention_dense_bwd(q, k, v, Wt, causal=True, window=Wn)
+    for which, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for idx in list(np.ndindex(*x.shape))[::3]:
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args = {"q": lambda y: (y, k, v), "k": lambda y: (q, y, v), "v": lambda y: (q, k, y)}[which]
+            fp = np.sum(oracle.attention_dense(*args(xp), causal=True, window=Wn)[0] * Wt)
+            fm = np.sum(oracle.attention_dense(*args(xm), causal=True, window=Wn)[0] * Wt)
+            assert abs((fp - fm) / (2 * eps) - g[idx]) < 1e-7, (which, idx)
+    q2 = rng.standard_normal((1, 37, 4, 8))
+    k2 = rng.standard_normal((1, 37, 2, 8))
+    v2 = rng.standard_normal((1, 37, 2, 8))
+    W2 = rng.standard_normal((1, 37, 4, 8))
+    fq, fk, fv = oracle.attention_dense_bwd(q2, k2, v2, W2, causal=True, window=10)
+    gq, gk, gv = oracle.attention_bwd_group(q2, k2, v2, W2, 0, 1, causal=True, window=10, rows_per_block=8)
+    assert np.allclose(gq, fq[0, :, 2:4], atol=1e-12) and np.allclose(gk, fk[0, :, 1], atol=1e-12)
+    assert np.allclose(gv, fv[0, :, 1], atol=1e-12)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -640,4 +731,7 @@ ALL_CHECKS = [
     check_bwd_group_matches_full,
     check_decode_is_the_end_of_the_causal_forward,
     check_decode_special_cases,
+    check_window_is_causal_attention_on_a_slice,
+    check_window_special_cases,
+    check_window_backward,
 ]

@@ -26,17 +26,20 @@ MUTANTS = [
     ("dropped sin term", "y[..., 1::2] = a * s + b * c", "y[..., 1::2] = b * c"),
     ("half pairing swapped", "y[..., d // 2:] = a * s + b * c", "y[..., d // 2:] = a * c + b * s"),
     ("GQA repeat instead of repeat_interleave", "kv = h // G  #", "kv = h % KV  #"),
-    ("mask includes diagonal", "np.triu(np.ones((L, L), dtype=bool), k=1)",
-     "np.triu(np.ones((L, L), dtype=bool), k=2)"),
+    ("mask hides the diagonal", "hide |= kp > qp", "hide |= kp >= qp"),
+    ("sliding window one key too wide", "hide |= qp - kp >= window", "hide |= qp - kp > window"),
+    ("sliding window ignored", "    if window > 0:\n        hide |=", "    if window < 0:\n        hide |="),
+    ("sampled row ignores the window", "lo = max(0, t - window + 1) if window > 0 else 0",
+     "lo = 0"),
     ("no softmax scale", "S = (qr[:, h, :] @ kr[:, kv, :].T) * scale",
      "S = (qr[:, h, :] @ kr[:, kv, :].T)"),
     ("transposed P", "O[:, h, :] = P @ v[:, kv, :]", "O[:, h, :] = P.T @ v[:, kv, :]"),
     ("lse without max", "lse[h] = m + np.log(den)", "lse[h] = np.log(den)"),
     ("K not rotated", "kr = apply_rope(k, pos, base, style)", "kr = k"),
     ("positions do not restart per sequence",
-     "O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style)",
-     "O[a:b], lse[:, a:b] = _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style)[0][a:b],"
-     " _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style)[1][:, a:b]"),
+     "O[a:b], lse[:, a:b] = _one_sequence(q[a:b], k[a:b], v[a:b], causal, scale, base, style, window)",
+     "O[a:b], lse[:, a:b] = _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style, window)[0][a:b],"
+     " _one_sequence(q[:b], k[:b], v[:b], causal, scale, base, style, window)[1][:, a:b]"),
     ("sampled row sees one key too few", "n = t + 1 if causal else L", "n = t if causal else L"),
     ("sampled row uses wrong KV head", "keys, vals = k[b, :, h // G], v[b, :, h // G]",
      "keys, vals = k[b, :, h % KV], v[b, :, h % KV]"),
@@ -60,24 +63,26 @@ MUTANTS = [
     ("dP against the wrong K/V head", "dP = dout[:, h, :] @ v[:, kv, :].T",
      "dP = dout[:, h, :] @ v[:, h % KV, :].T"),
     ("dq left rotated", "dq = apply_rope_transpose(dqr, pos, base, style)", "dq = dqr"),
-    ("backward ignores the mask", "        if causal:\n            S[future] = -np.inf\n        e = np.exp",
+    ("backward ignores the mask", "        S[hidden] = -np.inf\n        e = np.exp",
      "        e = np.exp"),
+    ("group backward ignores the window", "lo = max(0, r0 - window + 1) if window > 0 else 0",
+     "lo = max(0, r0 - window + 2) if window > 0 else 0"),
     ("group backward drops the last row", "r1 = min(T, r0 + rows_per_block)",
      "r1 = min(T - 1, r0 + rows_per_block)"),
     ("group backward sees one key too few", "            n = r1 if causal else T",
      "            n = r1 - 1 if causal else T"),
     ("decode queries at positions 0..Tq-1", "qpos = np.arange(L - Tq, L)", "qpos = np.arange(0, Tq)"),
-    ("decode mask aligned with the start", "future = qpos[:, None] < np.arange(L)[None, :]",
-     "future = np.arange(Tq)[:, None] < np.arange(L)[None, :]"),
+    ("decode mask aligned with the start", "hidden = _hidden(qpos, np.arange(L), True, window)",
+     "hidden = _hidden(np.arange(Tq), np.arange(L), True, window)"),
     ("decode keys unrotated", "kr = apply_rope(k[b, :L], np.arange(L), base, style)", "kr = k[b, :L]"),
     ("decode sees cache rows past the length", "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :]",
      "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :] + 0.0 * v[b, L - 1:L, kv, :].sum() + "
      "(v[b, L:, kv, :].sum() if L < v.shape[1] else 0.0)"),
     ("backward positions do not restart per sequence",
      "_one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,\n"
-     "                                                      base, style)",
+     "                                                      base, style, window)",
      "(lambda r: (r[0][a:], r[1][a:], r[2][a:]))(_one_sequence_bwd(q[:b], k[:b], v[:b], dout[:b],"
-     " causal, scale, base, style))"),
+     " causal, scale, base, style, window))"),
 ]
 
 
