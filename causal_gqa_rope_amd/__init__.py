@@ -109,18 +109,19 @@ def library() -> ctypes.CDLL:
     lib.cgr_rope_tables.argtypes = [i32, i32, f64, vp, vp, vp]
     lib.cgr_rope_tables.restype = i32
     lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                          i32, i32, i32, f32, i32, vp]
+                                          i32, i32, i32, i32, f32, i32, vp]
     lib.cgr_gqa_rope_attn_fwd.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                                 i32, i32, vp, vp, i32, i32, i32, f32, i32, vp,
+                                                 i32, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp,
                                                  ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd_varlen.restype = i32
     lib.cgr_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.cgr_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
-                                          i32, vp, vp, i32, i32, i32, f32, i32, vp, ctypes.c_size_t, vp]
+                                          i32, vp, vp, i32, i32, i32, i32, f32, i32, vp, ctypes.c_size_t,
+                                          vp]
     lib.cgr_gqa_rope_attn_bwd.restype = i32
     lib.cgr_rope_rotate.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp]
     lib.cgr_rope_rotate.restype = i32
@@ -128,7 +129,8 @@ def library() -> ctypes.CDLL:
     lib.cgr_attn_decode_workspace_size.restype = ctypes.c_size_t
     i64 = ctypes.c_int64
     lib.cgr_gqa_rope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i64, i64, i64, i32, i32,
-                                             i32, i32, i32, vp, vp, i32, i32, f32, vp, ctypes.c_size_t, vp]
+                                             i32, i32, i32, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t,
+                                             vp]
     lib.cgr_gqa_rope_attn_decode.restype = i32
     lib.cgr_varlen_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.cgr_varlen_device_status.restype = i32
@@ -188,7 +190,7 @@ def cgr_rope_tables(max_pos: int, head_dim: int, base: float,
 
 def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope_cos: torch.Tensor,
                           rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
-                          softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                          window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                           return_lse: bool = True):
     """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None)."""
@@ -221,7 +223,7 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
         _check(lib.cgr_gqa_rope_attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
             _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
-            CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
             0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _stream(q.device)))
     return out, lse
 
@@ -233,7 +235,8 @@ def cgr_attn_fwd_varlen_workspace_size(num_seqs: int, total_tokens: int) -> int:
 def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  cu_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
                                  rope_sin: torch.Tensor, *, causal: bool = True,
-                                 rope_style: str = "interleaved", softmax_scale: Optional[float] = None,
+                                 rope_style: str = "interleaved", window: int = 0,
+                                 softmax_scale: Optional[float] = None,
                                  qk_operand: str = "f16", out: Optional[torch.Tensor] = None,
                                  lse: Optional[torch.Tensor] = None, return_lse: bool = True,
                                  workspace: Optional[torch.Tensor] = None):
@@ -273,7 +276,7 @@ def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), nseq, total,
             int(max_seqlen), H, k.shape[1], D, _DTYPES[q.dtype], _ptr(rope_cos), _ptr(rope_sin),
             rope_cos.shape[0], _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
-            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
+            int(window), 0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out, lse
 
@@ -295,7 +298,7 @@ def cgr_attn_bwd_workspace_size(B: int, T: int, n_head: int, n_kv_head: int, hea
 def cgr_gqa_rope_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                           lse: torch.Tensor, dout: torch.Tensor, rope_cos: torch.Tensor,
                           rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
-                          softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                          window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
                           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
                           dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
     """Dense backward: the forward's q, k, v, o [B,T,.,d], lse [B,H,T] and dL/dO -> (dq, dk, dv).
@@ -335,7 +338,7 @@ def cgr_gqa_rope_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
         _check(lib.cgr_gqa_rope_attn_bwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
             B, T, H, k.shape[2], D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
-            _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
             0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return dq, dk, dv
@@ -379,7 +382,7 @@ def cgr_attn_decode_workspace_size(B: int, Tq: int, max_seqlen: int, n_head: int
 
 def cgr_gqa_rope_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                              cache_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
-                             rope_sin: torch.Tensor, *, rope_style: str = "interleaved",
+                             rope_sin: torch.Tensor, *, rope_style: str = "interleaved", window: int = 0,
                              softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                              lse: Optional[torch.Tensor] = None, return_lse: bool = True,
                              workspace: Optional[torch.Tensor] = None):
@@ -425,7 +428,7 @@ def cgr_gqa_rope_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
         _check(lib.cgr_gqa_rope_attn_decode(
             _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(out), _ptr(lse), B, Tq, S,
             sb, st, sh, int(max_seqlen), H, KV, D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
-            _STYLES[rope_style], 0.0 if softmax_scale is None else float(softmax_scale),
+            _STYLES[rope_style], int(window), 0.0 if softmax_scale is None else float(softmax_scale),
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out, lse
 

@@ -54,6 +54,7 @@ struct BwdArgs {
   void* kr;   // [B, T, KV, D] operand type: R k
   float* ld;  // [B, H, NT][64]: per 32-row tile, -lse*log2(e) (rows 0..31) then -D
   int B, T, H, KV, NT;
+  int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
   float qscale;  // scale * log2(e)
   float scale;
 };
@@ -150,12 +151,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
 //   P = 2^S;  dS = P dP
 //   dv^T += dO^T P            (dO^T by transposing LDS reads)
 //   dk~^T += q~^T dS
-template <int D_, typename QK_, bool CAUSAL_, int STYLE_>
+template <int D_, typename QK_, bool CAUSAL_, int STYLE_, bool WIN_ = false>
 struct BwdCfg {
   static constexpr int D = D_;
   using QK = QK_;
   static constexpr bool CAUSAL = CAUSAL_;
   static constexpr int STYLE = STYLE_;
+  static constexpr bool WIN = WIN_ && CAUSAL_;  // sliding-window instances are separate
   static constexpr int KSTEPS = D / 16;
   static constexpr int DB = D / 32;
   static constexpr int TILE = 32 * 2 * D;                // one 32-row operand tile
@@ -212,8 +214,12 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   tile_to_lds<D, C::BK>(rv, vk, ks * 2, k0 * ks * 2, wave, 8, lane);
   const int vrow = 32 * wig + l32;
 
+  // Rows that can see these keys: from the first key on (causal), up to the
+  // last key + W - 1 (sliding window).
+  const int W = C::WIN ? a.window : 0;
   const int q_first = C::CAUSAL ? k0 : 0;
-  const int n_steps = (L - q_first + 31) / 32;
+  const int q_end = W > 0 ? min(L, k0 + C::BK - 1 + W) : L;
+  const int n_steps = (q_end - q_first + 31) / 32;
   const int n_items = G * n_steps;
   const int n_iter = (n_items + 1) / 2;
   const rsrc_t rld = make_rsrc(a.ld, (uint32_t)((long)a.B * a.H * a.NT * 256));
@@ -258,6 +264,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
     int g, qrow0;
     item(n, g, qrow0);
     if (C::CAUSAL && qrow0 < kw0) return;  // every key of the wave is later than every row
+    if (W > 0 && qrow0 - (kw0 + 31) >= W) return;  // every row is past every key's window
     const char* gs = st + grp * C::GSTAGE;
     const char* Qt = gs;
     const char* Ot = gs + C::TILE;
@@ -285,6 +292,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (l32 > 8 * (r >> 2) + 4 * hh + (r & 3)) sacc[r] = -INFINITY;
+    }
+    if (W > 0 && qrow0 + 31 - kw0 >= W) {
+      // Window's far edge: row - key >= W is hidden.
+      const int lim = W - 1 + kw0 + l32 - qrow0 - 4 * hh;  // row offset must be <= lim
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) sacc[r] = -INFINITY;
     }
     u32x4 pb[2], sb[2];
 #pragma unroll
@@ -405,6 +419,9 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave_last = min(qw0 + 31, L - 1);
   const int q_hi = min(q0 + C::BQ, L);
   const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
+  // Sliding window: from the tile holding the first row's earliest visible key.
+  const int W = C::WIN ? a.window : 0;
+  const int j0 = W > 0 ? max(0, q0 - W + 1) / BN : 0;
 
   // This lane's query row as B operands: q~ (for S^T) and dO (for dP^T).
   const long hoff = (long)tok0 * qs + (long)head * D;
@@ -439,8 +456,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   auto compute = [&](int j, const char* Kt, const char* Vt) {
     if (!wave_has_rows || (C::CAUSAL && j * BN > wave_last)) return;
+    if (W > 0 && j * BN + BN - 1 < qw0 - W + 1) return;  // left of every row's window
     const bool domask = C::CAUSAL && j * BN + BN - 1 > qw0;
+    const bool wmask = W > 0 && j * BN < wave_last - W + 1;
     const int lim = my_q - j * BN - 4 * hh;  // key offset in the tile must be <= lim
+    const int lo = my_q - W + 1 - j * BN - 4 * hh;  // ... and >= lo under a window
 #pragma unroll
     for (int kb = 0; kb < BN / 32; ++kb) {
       f32x16 sacc = (f32x16){} + neg_lse, dpacc = (f32x16){} + neg_d;
@@ -454,6 +474,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) sacc[r] = -INFINITY;
+      }
+      if (wmask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + 8 * (r >> 2) + (r & 3) < lo) sacc[r] = -INFINITY;
       }
       u32x4 sb[2];
 #pragma unroll
@@ -472,10 +497,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  issue(0, kt0s, vt0s);
+  // Tile j0 + 2m uses stage 0, j0 + 2m + 1 stage 1.
+  issue(j0, kt0s, vt0s);
   wait_vmem();
   __syncthreads();
-  int j = 0;
+  int j = j0;
   for (; j + 1 < n_tiles; j += 2) {
     issue(j + 1, kt1s, vt1s);
     compute(j, kt0s, vt0s);
@@ -513,11 +539,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t launch_attn_bwd_d(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream) {
-#define CGR_BL(QK, CAU, STY) return launch_bwd<BwdCfg<D, QK, CAU, STY>>(a, stream)
-#define CGR_BS(QK, CAU) \
-  if (style == STYLE_HALF) { CGR_BL(QK, CAU, STYLE_HALF); } else { CGR_BL(QK, CAU, STYLE_INTERLEAVED); }
-#define CGR_BM(QK) \
-  if (causal) { CGR_BS(QK, true) } else { CGR_BS(QK, false) }
+#define CGR_BL(QK, CAU, STY, WIN) return launch_bwd<BwdCfg<D, QK, CAU, STY, WIN>>(a, stream)
+#define CGR_BS(QK, CAU, WIN) \
+  if (style == STYLE_HALF) { CGR_BL(QK, CAU, STYLE_HALF, WIN); } else { CGR_BL(QK, CAU, STYLE_INTERLEAVED, WIN); }
+#define CGR_BM(QK)                                                                               \
+  if (causal && a.window > 0) { CGR_BS(QK, true, true) }                                        \
+  else if (causal) { CGR_BS(QK, true, false) } else { CGR_BS(QK, false, false) }
   if (qk_bf16) {
     CGR_BM(OpBF16)
   } else {

@@ -39,6 +39,7 @@ struct DecodeArgs {
   int32_t* status;          // device error word
   long sb, st, sh;          // cache strides (elements): batch entry, token, K/V head
   int B, Tq, S, H, KV, NS, CH, RG, M;  // M: the largest cache length the call allows
+  int window;               // > 0: keys 0 <= position - j < window; 0: none
   float qscale;             // scale * log2(e)
 };
 
@@ -78,6 +79,9 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(DecodeArgs a) {
   const int k0 = split * a.CH;
   if (k0 >= L) return;
   const int k1 = min(L, k0 + a.CH);
+  // Sliding window: a chunk that ends before every query's window starts has
+  // nothing to do (the merge skips the same chunks).
+  if (a.window > 0 && k1 <= L - a.Tq - a.window + 1) return;
   const int G = a.H / a.KV;
   const int r = rg * 32 + l32;
   const bool row_ok = r < G * a.Tq;
@@ -167,6 +171,7 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(DecodeArgs a) {
   // Key of accumulator register i: tile start + 8(i/4) + 4hh + i%4; visible
   // to this column iff below k1 and at or before the query's position.
   const int lim_all = min(k1 - 1, pos) - 4 * hh;
+  const int lo_all = a.window > 0 ? pos - a.window + 1 - 4 * hh : -(1 << 30);  // and from here on
 
   auto tile = [&](int j, const u32x4 (&kt)[KSTEPS], const char* Vt) {
     f32x16 sacc = (f32x16){};
@@ -176,10 +181,12 @@ __global__ __launch_bounds__(64) void attn_decode_kernel(DecodeArgs a) {
       sacc = mma32(kf, frag<OpBF16>(qhi[s]), sacc);
       sacc = mma32(kf, frag<OpBF16>(qlo[s]), sacc);
     }
-    const int lim = lim_all - (k0 + j * BN);
+    const int lim = lim_all - (k0 + j * BN), lo = lo_all - (k0 + j * BN);
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (8 * (i >> 2) + (i & 3) > lim) sacc[i] = -INFINITY;
+    for (int i = 0; i < 16; ++i) {
+      const int off = 8 * (i >> 2) + (i & 3);
+      if (off > lim || off < lo) sacc[i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
@@ -269,14 +276,16 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(DecodeArgs a) {
   const int L = a.seqlens[b];
   if (bad(L)) return;
   const int ns = (L + a.CH - 1) / a.CH;
+  // The chunks the decode kernel skipped under a sliding window.
+  const int s0 = a.window > 0 ? max(0, L - a.Tq - a.window + 1) / a.CH : 0;
   const float* pl = a.part_lse + row * a.NS;
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, pl[s]);
+  for (int s = s0; s < ns; ++s) mx = fmaxf(mx, pl[s]);
   float den = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const f32x4* po = (const f32x4*)(a.part_o + row * a.NS * D) + c;
 #pragma unroll 4
-  for (int s = 0; s < ns; ++s) {
+  for (int s = s0; s < ns; ++s) {
     const float w = fast_exp2(pl[s] - mx);  // chunks with no visible key have lse -inf: w = 0
     den += w;
     acc += w * po[s * (D / 4)];

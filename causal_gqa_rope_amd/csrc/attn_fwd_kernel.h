@@ -60,6 +60,7 @@ struct AttnArgs {
   int32_t* sched;             // packed batches: [0] items, [1] queue counter, [2] error, then items
   int B, T, H, KV;
   int total_tokens;
+  int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
   float qscale;  // softmax_scale * log2(e), folded into Q
 };
 
@@ -84,7 +85,7 @@ constexpr int v_stride_dwords(int row_dwords) {
   return s;
 }
 
-template <int D_, typename IO_, typename QK_, bool CAUSAL_, int STYLE_>
+template <int D_, typename IO_, typename QK_, bool CAUSAL_, int STYLE_, bool WIN_ = false>
 struct Cfg {
   static constexpr int D = D_;
   using IO = IO_;  // float, or uint16_t holding bf16 bits
@@ -93,6 +94,9 @@ struct Cfg {
   using PV = typename std::conditional<F32, OpF32, OpBF16>::type;
   static constexpr bool CAUSAL = CAUSAL_;
   static constexpr int STYLE = STYLE_;
+  // Sliding-window instances (causal only) are separate: the others compile
+  // without any of the window's code.
+  static constexpr bool WIN = WIN_ && CAUSAL_;
 
 #ifndef CGR_NW
 #define CGR_NW 8
@@ -339,6 +343,10 @@ struct Unit {
     const int wave_last = min(qw0 + 31, L - 1);
     const int q_hi = min(q0 + C::BM, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
+    // Sliding window: the unit starts at the tile holding its first row's
+    // earliest visible key.
+    const int W = C::WIN ? a.window : 0;
+    const int j0 = W > 0 ? max(0, q0 - W + 1) / BN : 0;
 
     // ---- Q: rotate at position my_q, fold in scale*log2(e), round once.
     Frag<typename C::QK> qf[C::KSTEPS];
@@ -380,16 +388,17 @@ struct Unit {
 
     TileRegs<C> regs;
     __syncthreads();  // the previous unit of this workgroup is done with LDS
-    load_tile(regs, kp, vp, ks, 0, L, a.rope_cos, a.rope_sin);
-    store_tile(regs, ks0, vs0);
+    load_tile(regs, kp, vp, ks, j0 * BN, L, a.rope_cos, a.rope_sin);
+    store_tile(regs, stage_of(j0, ks0, ks1), stage_of(j0, vs0, vs1));
     __syncthreads();
 
-    for (int j = 0; j < n_tiles; ++j) {
+    for (int j = j0; j < n_tiles; ++j) {
       const int kt0 = j * BN;
       if (j + 1 < n_tiles) load_tile(regs, kp, vp, ks, kt0 + BN, L, a.rope_cos, a.rope_sin);
       const char* Ks = stage_of(j, ks0, ks1);
       const char* Vs = stage_of(j, vs0, vs1);
-      const bool active = wave_has_rows && (!C::CAUSAL || kt0 <= wave_last);
+      const bool active = wave_has_rows && (!C::CAUSAL || kt0 <= wave_last) &&
+                          (W <= 0 || kt0 + BN - 1 >= qw0 - W + 1);
       if (active) {
         // S^T = K Q^T for the BN keys of this tile (log2 units, scale folded in).
         f32x16 sacc[C::NKB];
@@ -401,19 +410,23 @@ struct Unit {
           for (int kb = 0; kb < C::NKB; ++kb)
             sacc[kb] = mma32(k_frag(Ks, kb * 32 + l32, s, hh), qf[s], sacc[kb]);
         }
-        // Mask: only tiles that straddle the diagonal or the sequence end.
-        const bool need_mask = C::CAUSAL ? (kt0 + BN - 1 > qw0) : (kt0 + BN > L);
+        // Mask: only tiles that straddle the diagonal, the sequence end or the
+        // window's left edge.
+        const bool need_mask = (C::CAUSAL ? (kt0 + BN - 1 > qw0) : (kt0 + BN > L)) ||
+                               (W > 0 && kt0 < wave_last - W + 1);
         if (need_mask) {
 #pragma unroll
           for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
               const int key = kt0 + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
-              if ((C::CAUSAL && key > my_q) || key >= L) sacc[kb][i] = -INFINITY;
+              if ((C::CAUSAL && key > my_q) || key >= L || (W > 0 && key < my_q - W + 1))
+                sacc[kb][i] = -INFINITY;
             }
         }
-        // Online softmax. Tile 0 always holds key 0, which every row may see,
-        // so m_new is finite from the first tile on.
+        // Online softmax. Without a window tile 0 holds key 0, which every
+        // row may see; with one, a row may see nothing in its first tiles, and
+        // then m stays -inf and p = 0 (m_use keeps exp2 away from -inf - -inf).
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
@@ -421,14 +434,15 @@ struct Unit {
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
         mx = pair_max(mx);
         const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - m_new);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
         m_run = m_new;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(sacc[kb][i] - m_new);
+            const float p = fast_exp2(sacc[kb][i] - m_use);
             sacc[kb][i] = p;
             rs += p;
           }
@@ -553,6 +567,11 @@ struct UnitFast {
     const int wave_last = min(qw0 + 31, L - 1);
     const int q_hi = min(q0 + C::BM, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
+    // Sliding window: such units run the rescaling loop below (the fast
+    // path's reference comes from tile 0, which a window may hide), from the
+    // tile holding their first row's earliest visible key.
+    const int W = C::WIN ? a.window : 0;
+    const int j0 = W > 0 ? max(0, q0 - W + 1) / BN : 0;
 
     // ---- Q. A lane of the matrix-core operand holds one query row, so loading
     // Q (and its cos/sin rows) straight into that layout would touch 32 rows
@@ -713,14 +732,14 @@ struct UnitFast {
     f32x4 kc[KI][2], ksn[KI][2];
     u32x4 vw[VU_REG];
 
-    // Stage tile 0 (K rotated, V) in LDS.
-    auto start = [&](char* kst, char* vst) {
+    // Stage tile j (K rotated, V) in LDS.
+    auto start = [&](int j, char* kst, char* vst) {
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
       l_run = 0.f;
       __syncthreads();  // earlier users of this workgroup's LDS are done
-      issue_loads(0, vst, kw, kc, ksn, vw);
-      store_k(0, kst, kw, kc, ksn, vw);
+      issue_loads(j * BN, vst, kw, kc, ksn, vw);
+      store_k(j * BN, kst, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
     };
@@ -748,6 +767,18 @@ struct UnitFast {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim) sacc[kb][i] = -INFINITY;
+    };
+    // The window's left edge as well: keys before my_q - W + 1 get -inf too.
+    auto mask_window = [&](int j, f32x16 (&sacc)[C::NKB]) {
+      const int lim = min(my_q, L - 1) - j * BN - 4 * hh;
+      const int lo = my_q - W + 1 - j * BN - 4 * hh;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int off = kb * 32 + 8 * (i >> 2) + (i & 3);
+          if (off > lim || off < lo) sacc[kb][i] = -INFINITY;
+        }
     };
     auto rowmax = [&](const f32x16 (&sacc)[C::NKB]) {
       float mx = -INFINITY;
@@ -834,121 +865,163 @@ struct UnitFast {
     // of V: at the top of iteration j, stage (j+1)&1 has K_{j+1} and stage
     // j&1 has V_j; the loads of iteration j fill V_{j+1} and, through
     // registers, K_{j+2}.
-    float m_ref = 0.f;
-    {
-      auto active = [&](int t) { return wave_has_rows && (!C::CAUSAL || t * BN <= wave_last); };
-      // Stage K_0, V_0 and K_1, with the loads of Q, K_0 and K_1 all in
-      // flight before the first wait.
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
-      l_run = 0.f;
-      load_k(0, kw, kc, ksn);
-      u32x4 kw1[KI][2];
-      f32x4 kc1[KI][2], ksn1[KI][2];
-      if (n_tiles > 1) load_k(BN, kw1, kc1, ksn1);
-      __syncthreads();  // earlier users of this workgroup's LDS are done
-      load_v(0, vs0, vw);
-      stage_q();
-      store_k(0, ks0, kw, kc, ksn, vw);
-      wait_vmem();
-      __syncthreads();
-      // S_0 and the reference; K_1 into LDS.
-      f32x16 s_cur[C::NKB];
-      if (wave_has_rows) {
-        scores(ks0, s_cur, (f32x16){});
-        mask(0, s_cur);
-        m_ref = rowmax(s_cur);
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
-      }
-      if (n_tiles > 1) store_k(BN, ks1, kw1, kc1, ksn1, vw);
-      wait_vmem();
-      __syncthreads();
-      const f32x16 negm = (f32x16){} - m_ref;
-
-      // kj/vj: the stages of tile j; kj1/vj1: those of tile j+1.
-      auto iter = [&](int j, auto mask_tag, char* kj, char* kj1, char* vj, char* vj1) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        // Loads for V_{j+1} (LDS, stage (j+1)&1) and K_{j+2} (registers).
-        if (j + 1 < n_tiles) load_v((j + 1) * BN, vj1, vw);
-        if (j + 2 < n_tiles) load_k((j + 2) * BN, kw, kc, ksn);
-        f32x16 s_next[C::NKB];
-        if (j + 1 < n_tiles && active(j + 1)) scores(kj1, s_next, negm);
-        if (active(j)) {
-          if constexpr (MASK) mask(j, s_cur);
-          softmax_pv(vj, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
-        }
-        if (j + 2 < n_tiles) store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
-        wait_vmem();
-        __syncthreads();
-#pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
-      };
-      // Steady state: tiles j+1 and j+2 exist, tile j needs no mask and the
-      // wave has rows. Unrolled by two so every LDS stage is fixed at compile
-      // time (the direct V load into one stage then needs no wait before the
-      // reads of the others) and S alternates between two register sets; the
-      // iteration is one straight-line block in which the matrix-core and
-      // vector work of the two tiles can interleave.
-      f32x16 s_alt[C::NKB];
-      auto iter_steady = [&](int j, f32x16 (&s_in)[C::NKB], f32x16 (&s_out)[C::NKB], char* kj,
-                             char* kj1, char* vj, char* vj1) {
-        load_v((j + 1) * BN, vj1, vw);
-        load_k((j + 2) * BN, kw, kc, ksn);
-        // Waves w and w+4 share a SIMD. At equal priority the older one wins
-        // every issue tie, finishes the tile first and then idles at the
-        // barrier while the younger one runs alone; raising the younger
-        // wave's priority for the tile evens the two out.
-        if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
-        // Keep the global loads at the top of the block, a whole block ahead
-        // of their use (left alone, the scheduler sinks them next to it).
-        __builtin_amdgcn_sched_barrier(0);
-        scores(kj1, s_out, negm);
-        softmax_pv(vj, s_in, std::false_type{}, 0.f, std::false_type{}, 1.f);
-        store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
-        wait_vmem();
-        __syncthreads();
-        __builtin_amdgcn_s_setprio(0);
-      };
-      int j = 0;
-      if (wave_has_rows) {
-        const int n_steady = min(n_plain, n_tiles - 2);
-        for (; j + 1 < n_steady; j += 2) {
-          iter_steady(j, s_cur, s_alt, ks0, ks1, vs0, vs1);
-          iter_steady(j + 1, s_alt, s_cur, ks1, ks0, vs1, vs0);
-        }
-      }
-      for (; j < n_plain; ++j)
-        iter(j, std::false_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
-             stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
-      for (; j < n_tiles; ++j)
-        iter(j, std::true_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
-             stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
-    }
-    float m_fin = m_ref;
-    const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
-
     // ---- Rescaling path (classic online softmax: m' = max(m, tile max), O
-    // and l scaled by 2^(m - m') every tile), for units whose scores grow too
-    // far beyond the first tile. The whole workgroup redoes the unit.
-    if (__syncthreads_or(overflow)) {
+    // and l scaled by 2^(m - m') every tile): every windowed unit, and units
+    // whose scores grow too far beyond the first tile (the whole workgroup
+    // then redoes the unit). Returns the final row max. WIN selects the
+    // window's tile range and mask at compile time, so the fallback of the
+    // unwindowed path carries none of that code.
+    auto rescale_pass = [&](auto win_tag) -> float {
+      constexpr bool WIN = decltype(win_tag)::value;
+      const int jb = WIN ? j0 : 0;
       float m_run = -INFINITY;
-      start(ks0, vs0);
-      for (int j = 0; j < n_tiles; ++j) {
+      start(jb, stage_of(jb, ks0, ks1), stage_of(jb, vs0, vs1));
+      for (int j = jb; j < n_tiles; ++j) {
         prefetch(j, stage_of(j + 1, vs0, vs1));
-        if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last)) {
+        if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last) &&
+            (!WIN || j * BN + BN - 1 >= qw0 - W + 1)) {
           f32x16 sacc[C::NKB];
           scores(stage_of(j, ks0, ks1), sacc, (f32x16){});
-          mask(j, sacc);
+          if constexpr (WIN)
+            mask_window(j, sacc);
+          else
+            mask(j, sacc);
+          // A row may see no key of its first tiles under a window: m stays
+          // -inf and p = 0 (m_use keeps exp2 away from -inf - -inf).
           const float m_new = fmaxf(m_run, rowmax(sacc));
-          const float alpha = fast_exp2(m_run - m_new);
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = fast_exp2(m_run - m_use);
           m_run = m_new;
           l_run *= alpha;
-          softmax_pv(stage_of(j, vs0, vs1), sacc, std::true_type{}, m_new, std::true_type{}, alpha);
+          softmax_pv(stage_of(j, vs0, vs1), sacc, std::true_type{}, m_use, std::true_type{}, alpha);
         }
         finish(j, stage_of(j + 1, ks0, ks1));
       }
-      m_fin = m_run;
+      return m_run;
+    };
+    float m_fin;
+    if (W > 0) {
+      // Q fragments straight from global memory, each lane its own row (the
+      // staged path's registers belong to the fast path alone: giving them
+      // a second consumer here costs the fast path dozens of spills).
+      const bool ok = my_q < L;
+      const long tq = (long)(ok ? my_q : 0);
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) {
+        const int g = 2 * s2 + hh;  // k-step s2 holds group g; k-step s2 + D/32 holds g + D/16
+        u32x4 w0[1], w1[1];
+        load8_raw<uint16_t>(qbase + tq * qs + 8 * g, ok, w0);
+        load8_raw<uint16_t>(qbase + tq * qs + 8 * g + D / 2, ok, w1);
+        f32x4 c[2], s[2];
+        load_tab<D, C::STYLE>(a.rope_cos + tq * (D / 2), a.rope_sin + tq * (D / 2), g, ok, c, s);
+        float x0[8], x1[8];
+        raw_to_f32<uint16_t>(w0, x0);
+        raw_to_f32<uint16_t>(w1, x1);
+        rope_pair<C::STYLE>(x0, x1, c, s);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x0[j] *= a.qscale;
+          x1[j] *= a.qscale;
+        }
+        qf[s2] = to_frag<QK>(x0);
+        qf[s2 + D / 32] = to_frag<QK>(x1);
+      }
+      m_fin = rescale_pass(std::true_type{});
+    } else {
+      float m_ref = 0.f;
+      {
+        auto active = [&](int t) { return wave_has_rows && (!C::CAUSAL || t * BN <= wave_last); };
+        // Stage K_0, V_0 and K_1, with the loads of Q, K_0 and K_1 all in
+        // flight before the first wait.
+  #pragma unroll
+        for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+        l_run = 0.f;
+        load_k(0, kw, kc, ksn);
+        u32x4 kw1[KI][2];
+        f32x4 kc1[KI][2], ksn1[KI][2];
+        if (n_tiles > 1) load_k(BN, kw1, kc1, ksn1);
+        __syncthreads();  // earlier users of this workgroup's LDS are done
+        load_v(0, vs0, vw);
+        stage_q();
+        store_k(0, ks0, kw, kc, ksn, vw);
+        wait_vmem();
+        __syncthreads();
+        // S_0 and the reference; K_1 into LDS.
+        f32x16 s_cur[C::NKB];
+        if (wave_has_rows) {
+          scores(ks0, s_cur, (f32x16){});
+          mask(0, s_cur);
+          m_ref = rowmax(s_cur);
+  #pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
+        }
+        if (n_tiles > 1) store_k(BN, ks1, kw1, kc1, ksn1, vw);
+        wait_vmem();
+        __syncthreads();
+        const f32x16 negm = (f32x16){} - m_ref;
+
+        // kj/vj: the stages of tile j; kj1/vj1: those of tile j+1.
+        auto iter = [&](int j, auto mask_tag, char* kj, char* kj1, char* vj, char* vj1) {
+          constexpr bool MASK = decltype(mask_tag)::value;
+          // Loads for V_{j+1} (LDS, stage (j+1)&1) and K_{j+2} (registers).
+          if (j + 1 < n_tiles) load_v((j + 1) * BN, vj1, vw);
+          if (j + 2 < n_tiles) load_k((j + 2) * BN, kw, kc, ksn);
+          f32x16 s_next[C::NKB];
+          if (j + 1 < n_tiles && active(j + 1)) scores(kj1, s_next, negm);
+          if (active(j)) {
+            if constexpr (MASK) mask(j, s_cur);
+            softmax_pv(vj, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
+          }
+          if (j + 2 < n_tiles) store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
+          wait_vmem();
+          __syncthreads();
+  #pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
+        };
+        // Steady state: tiles j+1 and j+2 exist, tile j needs no mask and the
+        // wave has rows. Unrolled by two so every LDS stage is fixed at compile
+        // time (the direct V load into one stage then needs no wait before the
+        // reads of the others) and S alternates between two register sets; the
+        // iteration is one straight-line block in which the matrix-core and
+        // vector work of the two tiles can interleave.
+        f32x16 s_alt[C::NKB];
+        auto iter_steady = [&](int j, f32x16 (&s_in)[C::NKB], f32x16 (&s_out)[C::NKB], char* kj,
+                               char* kj1, char* vj, char* vj1) {
+          load_v((j + 1) * BN, vj1, vw);
+          load_k((j + 2) * BN, kw, kc, ksn);
+          // Waves w and w+4 share a SIMD. At equal priority the older one wins
+          // every issue tie, finishes the tile first and then idles at the
+          // barrier while the younger one runs alone; raising the younger
+          // wave's priority for the tile evens the two out.
+          if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
+          // Keep the global loads at the top of the block, a whole block ahead
+          // of their use (left alone, the scheduler sinks them next to it).
+          __builtin_amdgcn_sched_barrier(0);
+          scores(kj1, s_out, negm);
+          softmax_pv(vj, s_in, std::false_type{}, 0.f, std::false_type{}, 1.f);
+          store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
+          wait_vmem();
+          __syncthreads();
+          __builtin_amdgcn_s_setprio(0);
+        };
+        int j = 0;
+        if (wave_has_rows) {
+          const int n_steady = min(n_plain, n_tiles - 2);
+          for (; j + 1 < n_steady; j += 2) {
+            iter_steady(j, s_cur, s_alt, ks0, ks1, vs0, vs1);
+            iter_steady(j + 1, s_alt, s_cur, ks1, ks0, vs1, vs0);
+          }
+        }
+        for (; j < n_plain; ++j)
+          iter(j, std::false_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
+               stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
+        for (; j < n_tiles; ++j)
+          iter(j, std::true_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
+               stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
+      }
+      m_fin = m_ref;
+      const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
+      if (__syncthreads_or(overflow)) m_fin = rescale_pass(std::false_type{});
     }
 
     // ---- Epilogue: O = O^T / l, rounded to bf16, goes through the wave's
@@ -1065,11 +1138,13 @@ constexpr int kBN = CGR_BN;  // keys per tile (all instances)
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                          bool varlen, int grid, hipStream_t stream) {
-#define CGR_LAUNCH(IO, QK, CAU, STY) return launch_attn<Cfg<D, IO, QK, CAU, STY>>(a, varlen, grid, stream)
-#define CGR_BY_STYLE(IO, QK, CAU) \
-  if (style == STYLE_HALF) { CGR_LAUNCH(IO, QK, CAU, STYLE_HALF); } else { CGR_LAUNCH(IO, QK, CAU, STYLE_INTERLEAVED); }
-#define CGR_BY_MASK(IO, QK) \
-  if (causal) { CGR_BY_STYLE(IO, QK, true) } else { CGR_BY_STYLE(IO, QK, false) }
+#define CGR_LAUNCH(IO, QK, CAU, STY, WIN) \
+  return launch_attn<Cfg<D, IO, QK, CAU, STY, WIN>>(a, varlen, grid, stream)
+#define CGR_BY_STYLE(IO, QK, CAU, WIN) \
+  if (style == STYLE_HALF) { CGR_LAUNCH(IO, QK, CAU, STYLE_HALF, WIN); } else { CGR_LAUNCH(IO, QK, CAU, STYLE_INTERLEAVED, WIN); }
+#define CGR_BY_MASK(IO, QK)                                                                           \
+  if (causal && a.window > 0) { CGR_BY_STYLE(IO, QK, true, true) }                                   \
+  else if (causal) { CGR_BY_STYLE(IO, QK, true, false) } else { CGR_BY_STYLE(IO, QK, false, false) }
   if (f32_io) {
     CGR_BY_MASK(float, OpF32)
   } else if (qk_bf16) {

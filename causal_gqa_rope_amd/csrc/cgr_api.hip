@@ -100,6 +100,13 @@ cgr_status check_common(const void* q, const void* k, const void* v, const void*
   return CGR_OK;
 }
 
+cgr_status check_window(int window, cgr_mask mask) {
+  if (window < 0) return fail(CGR_ERR_INVALID_ARG, "window (%d) must be >= 0 (0: none)", window);
+  if (window > 0 && mask != CGR_MASK_CAUSAL)
+    return fail(CGR_ERR_INVALID_ARG, "a sliding window needs CGR_MASK_CAUSAL");
+  return CGR_OK;
+}
+
 cgr::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, float* lse,
                         const float* cs, const float* sn, int n_head, int n_kv_head, int head_dim,
                         float softmax_scale) {
@@ -207,12 +214,13 @@ cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float* cos_ou
 cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
                                  float softmax_scale, cgr_qk_operand qk_operand, void* stream) {
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
   if (st != CGR_OK) return st;
+  if ((st = check_window(window, mask)) != CGR_OK) return st;
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
   const long grid = (long)((T + cgr::kBM - 1) / cgr::kBM) * B * n_head;
   if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
@@ -221,6 +229,7 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
   a.B = B;
   a.T = T;
   a.total_tokens = B * T;
+  a.window = window;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("attention launch", e);
@@ -238,7 +247,7 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
                                         int n_kv_head, int head_dim, cgr_dtype dtype,
                                         const float* rope_cos, const float* rope_sin,
                                         int rope_max_pos, cgr_rope_style style, cgr_mask mask,
-                                        float softmax_scale, cgr_qk_operand qk_operand,
+                                        int window, float softmax_scale, cgr_qk_operand qk_operand,
                                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!cu_seqlens) return fail(CGR_ERR_INVALID_ARG, "cu_seqlens must be non-null");
   if (!aligned(cu_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cu_seqlens must be 4-byte aligned");
@@ -252,6 +261,7 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
                                rope_sin, rope_max_pos, max_seqlen, style, mask, softmax_scale,
                                qk_operand);
   if (st != CGR_OK) return st;
+  if ((st = check_window(window, mask)) != CGR_OK) return st;
   const size_t need = cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens);
   if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
   if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
@@ -277,6 +287,7 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   a.B = num_seqs;
   a.T = max_seqlen;
   a.total_tokens = total_tokens;
+  a.window = window;
   // Persistent grid: two workgroups per compute unit, never more than the units.
   long grid = 2L * cus;
   if (grid > max_items * n_head) grid = max_items * n_head;
@@ -295,13 +306,14 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
                                  float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
                                  size_t workspace_bytes, void* stream) {
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
   if (st != CGR_OK) return st;
+  if ((st = check_window(window, mask)) != CGR_OK) return st;
   if (!lse || !dout || !dq || !dk || !dv)
     return fail(CGR_ERR_INVALID_ARG, "lse, dout, dq, dk and dv must be non-null");
   if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
@@ -341,6 +353,7 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
   a.H = n_head;
   a.KV = n_kv_head;
   a.NT = nt;
+  a.window = window;
   const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
   a.scale = (float)scale;
   a.qscale = (float)(scale * 1.4426950408889634074);
@@ -370,8 +383,9 @@ cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const vo
                                     int64_t cache_token_stride, int64_t cache_head_stride,
                                     int max_seqlen, int n_head, int n_kv_head, int head_dim,
                                     cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                    int rope_max_pos, cgr_rope_style style, float softmax_scale,
-                                    void* workspace, size_t workspace_bytes, void* stream) {
+                                    int rope_max_pos, cgr_rope_style style, int window,
+                                    float softmax_scale, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
   if (B < 1 || Tq < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and Tq (%d) must be >= 1", B, Tq);
   if (!cache_seqlens) return fail(CGR_ERR_INVALID_ARG, "cache_seqlens must be non-null");
   if (!aligned(cache_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cache_seqlens must be 4-byte aligned");
@@ -384,6 +398,7 @@ cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const vo
   if (st != CGR_OK) return st;
   if (dtype != CGR_BF16)
     return fail(CGR_ERR_UNSUPPORTED, "decode takes bf16 tensors only (dtype %d)", (int)dtype);
+  if ((st = check_window(window, CGR_MASK_CAUSAL)) != CGR_OK) return st;
   if (cache_batch_stride < 0 || cache_token_stride < head_dim || cache_head_stride < head_dim ||
       cache_batch_stride % 8 || cache_token_stride % 8 || cache_head_stride % 8)
     return fail(CGR_ERR_INVALID_ARG,
@@ -424,6 +439,7 @@ cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const vo
   a.CH = plan.ch;
   a.RG = plan.rg;
   a.M = max_seqlen;
+  a.window = window;
   const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
   a.qscale = (float)(scale * 1.4426950408889634074);
   hipStream_t s = (hipStream_t)stream;

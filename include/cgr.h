@@ -72,7 +72,11 @@ typedef enum { CGR_F32 = 0, CGR_BF16 = 1 } cgr_dtype;
 typedef enum { CGR_ROPE_INTERLEAVED = 0, CGR_ROPE_HALF = 1 } cgr_rope_style;
 
 /* CGR_MASK_CAUSAL: key j is visible to query i iff j <= i (positions within
- * the sequence). CGR_MASK_NONE: every key of the sequence is visible. */
+ * the sequence). CGR_MASK_NONE: every key of the sequence is visible.
+ * The entry points that take a `window` argument add a sliding window to the
+ * causal mask: window W > 0 keeps only keys with 0 <= i - j < W (each query
+ * sees itself and the W - 1 tokens before it); 0 means no window. A window
+ * requires CGR_MASK_CAUSAL. */
 typedef enum { CGR_MASK_NONE = 0, CGR_MASK_CAUSAL = 1 } cgr_mask;
 
 /* Operand type of the Q.K^T matrix product (bf16 I/O only; f32 I/O always
@@ -108,6 +112,7 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
  *   rope_cos, rope_sin: device float32 [rope_max_pos, head_dim/2] as written by
  *     cgr_rope_tables; rope_max_pos >= T (token t of every batch entry is at
  *     position t).
+ *   window: sliding window (see cgr_mask), 0 for none.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   qk_operand: see cgr_qk_operand (ignored for CGR_F32).
  * o and lse must not overlap the inputs.
@@ -115,7 +120,7 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
 CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
                                  float softmax_scale, cgr_qk_operand qk_operand, void* stream);
 
 /*
@@ -150,7 +155,7 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, co
                                         int n_kv_head, int head_dim, cgr_dtype dtype,
                                         const float* rope_cos, const float* rope_sin,
                                         int rope_max_pos, cgr_rope_style style, cgr_mask mask,
-                                        float softmax_scale, cgr_qk_operand qk_operand,
+                                        int window, float softmax_scale, cgr_qk_operand qk_operand,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -170,8 +175,8 @@ CGR_API size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_he
  *   dq_i = R_i^T scale sum_j dS_ij k~_j;   dk_j = R_j^T scale sum_i dS_ij q~_i
  * where dk and dv sum over the n_head / n_kv_head query heads sharing the K/V
  * head.
- *   q, k, v, rope tables, sizes, style, mask, softmax_scale, qk_operand: as
- *     given to cgr_gqa_rope_attn_fwd.
+ *   q, k, v, rope tables, sizes, style, mask, window, softmax_scale,
+ *     qk_operand: as given to cgr_gqa_rope_attn_fwd.
  *   o: device [B, T, n_head, head_dim], lse: device float32 [B, n_head, T] --
  *     the forward's outputs for these inputs (P is recomputed from q, k and
  *     lse; D from o).
@@ -191,7 +196,7 @@ CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const voi
                                  const float* lse, const void* dout, void* dq, void* dk, void* dv,
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
                                  float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
@@ -242,6 +247,7 @@ CGR_API size_t cgr_attn_decode_workspace_size(int B, int Tq, int max_seqlen, int
  *     positions (cgr_rope_rotate), the values as they are.
  *   cache_seqlens: device int32 [B], each in [Tq, max_seqlen]; max_seqlen <=
  *     cache_capacity and <= rope_max_pos.
+ *   window: W > 0 keeps only keys with 0 <= (L_b - Tq + i) - j < W; 0: none.
  *   o: device bf16 [B, Tq, n_head, head_dim]; lse: device float32
  *     [B, n_head, Tq] (natural log-sum-exp), or NULL.
  *   dtype: CGR_BF16 only. Scores are products of the bf16 keys with the
@@ -259,8 +265,9 @@ CGR_API cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, 
                                     int64_t cache_token_stride, int64_t cache_head_stride,
                                     int max_seqlen, int n_head, int n_kv_head, int head_dim,
                                     cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                    int rope_max_pos, cgr_rope_style style, float softmax_scale,
-                                    void* workspace, size_t workspace_bytes, void* stream);
+                                    int rope_max_pos, cgr_rope_style style, int window,
+                                    float softmax_scale, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /*
  * Reads the device error word the last varlen or decode call on `workspace` left:

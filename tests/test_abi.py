@@ -67,12 +67,12 @@ PMIS = ctypes.c_void_p(0x10002)   # misaligned placeholder
 
 def dense(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
-             P=16, style=0, mask=1, scale=0.0, qk=0)
+             P=16, style=0, mask=1, window=0, scale=0.0, qk=0)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"],
                                    a["KV"], a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
-                                   a["style"], a["mask"], a["scale"], a["qk"], None)
+                                   a["style"], a["mask"], a["window"], a["scale"], a["qk"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -95,6 +95,8 @@ def dense(**kw):
     (dict(q=PMIS), 3, "aligned"),
     (dict(sin=PMIS), 3, "aligned"),
     (dict(P=15), 1, "positions"),
+    (dict(window=-1), 1, "window"),
+    (dict(window=8, mask=0), 1, "CGR_MASK_CAUSAL"),
 ])
 def test_dense_rejects_bad_arguments(kw, status, needle):
     st, msg = dense(**kw)
@@ -104,14 +106,14 @@ def test_dense_rejects_bad_arguments(kw, status, needle):
 
 def varlen(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, cu=P, nseq=2, total=100, maxlen=60, H=4, KV=1, D=128,
-             dtype=1, cos=P, sin=P, P=60, style=0, mask=1, scale=0.0, qk=0, ws=P, wsb=1 << 20)
+             dtype=1, cos=P, sin=P, P=60, style=0, mask=1, window=0, scale=0.0, qk=0, ws=P, wsb=1 << 20)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"],
                                           a["nseq"], a["total"], a["maxlen"], a["H"], a["KV"],
                                           a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
-                                          a["style"], a["mask"], a["scale"], a["qk"], a["ws"],
-                                          a["wsb"], None)
+                                          a["style"], a["mask"], a["window"], a["scale"], a["qk"],
+                                          a["ws"], a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -169,14 +171,14 @@ def test_backward_workspace_size():
 
 def backward(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, B=1, T=16, H=4, KV=2, D=64,
-             dtype=1, cos=P, sin=P, P=16, style=0, mask=1, scale=0.0, qk=0, ws=ctypes.c_void_p(0x10000),
-             wsb=1 << 20)
+             dtype=1, cos=P, sin=P, P=16, style=0, mask=1, window=0, scale=0.0, qk=0,
+             ws=ctypes.c_void_p(0x10000), wsb=1 << 20)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"],
                                    a["dk"], a["dv"], a["B"], a["T"], a["H"], a["KV"], a["D"],
                                    a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["mask"],
-                                   a["scale"], a["qk"], a["ws"], a["wsb"], None)
+                                   a["window"], a["scale"], a["qk"], a["ws"], a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -194,6 +196,7 @@ def backward(**kw):
     (dict(D=80), 2, "not one of"),
     (dict(T=0), 1, ">= 1"),
     (dict(P=15), 1, "positions"),
+    (dict(window=4, mask=0), 1, "CGR_MASK_CAUSAL"),
 ])
 def test_backward_rejects_bad_arguments(kw, status, needle):
     st, msg = backward(**kw)
@@ -213,14 +216,14 @@ def test_decode_workspace_size():
 
 def decode_call(**kw):
     a = dict(q=P, k=P, v=P, lens=P, o=P, lse=None, B=2, Tq=1, S=64, sb=64 * 2 * 64, st=2 * 64, sh=64,
-             M=64, H=4, KV=2, D=64, dtype=1, cos=P, sin=P, P=64, style=0, scale=0.0,
+             M=64, H=4, KV=2, D=64, dtype=1, cos=P, sin=P, P=64, style=0, window=0, scale=0.0,
              ws=ctypes.c_void_p(0x10000), wsb=1 << 20)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_decode(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["Tq"],
                                       a["S"], a["sb"], a["st"], a["sh"], a["M"], a["H"], a["KV"], a["D"],
-                                      a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["scale"], a["ws"],
-                                      a["wsb"], None)
+                                      a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["window"],
+                                      a["scale"], a["ws"], a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -239,6 +242,7 @@ def decode_call(**kw):
     (dict(wsb=300), 4, "needs"),
     (dict(H=6, KV=4), 1, "divisible"),
     (dict(D=48), 2, "not one of"),
+    (dict(window=-2), 1, "window"),
 ])
 def test_decode_rejects_bad_arguments(kw, status, needle):
     st, msg = decode_call(**kw)
