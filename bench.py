@@ -24,6 +24,8 @@ bounded sample of the same workload on this host's cores.
                                         workload; not the headline line)
   python bench.py --decode             (one JSON line for decode against a KV cache,
                                         16 sequences x 1 new token; not the headline line)
+  python bench.py --window W           (the forward or --backward line with a causal
+                                        sliding window of W keys; not the headline line)
 """
 
 from __future__ import annotations
@@ -191,7 +193,7 @@ def cpu_baseline_bwd(inputs, dout, w) -> dict:
     }
 
 
-def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
+def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window: int = 0) -> None:
     """One step = one backward call (prepass, dk/dv kernel, dq kernel) on the
     long-context workload; o and lse come from one forward before timing."""
     w = W.get(WORKLOAD)
@@ -200,7 +202,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
     dout_cpu = W.make_dout(w, inputs["q"])
     dout = dout_cpu.to(dev)
     cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
-    o, lse = cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style)
+    o, lse = cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=window)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(cgr.cgr_attn_bwd_workspace_size(w.B, w.T, w.n_head, w.n_kv_head, w.head_dim),
                      dtype=torch.uint8, device=dev)
@@ -208,7 +210,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
 
     def call():
         cgr.gqa_rope_attn_bwd(q, k, v, o, lse, dout, cos, sin, causal=True, rope_style=w.rope_style,
-                              dq=dq, dk=dk, dv=dv, workspace=ws)
+                              window=window, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(warmup):
         call()
@@ -221,7 +223,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, [w.T] * w.B, True)
+    flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, [w.T] * w.B, True, window)
     ms_step = wall * 1e3 / steps
     call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     achieved = flops / (call_ms * 1e-3) / 1e12
@@ -242,7 +244,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
             "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
             "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
             "io": "bf16", "qk_operand": "f16", "accumulate": "f32", "step": "gqa_rope_attn_bwd",
-            "flops_per_step": flops,
+            "window": window, "flops_per_step": flops,
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
         "roofline": {
@@ -256,7 +258,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> Non
                       "(head_dim 128, f16 QK, causal, interleaved)",
             "kernel_ms": round(call_ms, 5),
         },
-        "cpu_baseline": cpu_baseline_bwd(inputs, dout_cpu, w) if with_cpu else None,
+        "cpu_baseline": cpu_baseline_bwd(inputs, dout_cpu, w) if with_cpu and window == 0 else None,
     }
     print(json.dumps(result), flush=True)
 
@@ -378,6 +380,7 @@ def main() -> int:
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--decode", action="store_true")
+    ap.add_argument("--window", type=int, default=0)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -399,7 +402,7 @@ def main() -> int:
         all_configs(torch, cgr, W, dev, args.steps, args.warmup)
         return 0
     if args.backward:
-        backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
+        backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline, args.window)
         return 0
     if args.decode:
         decode(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
@@ -422,7 +425,8 @@ def main() -> int:
         cgr._check(lib.cgr_rope_tables(w.T, w.head_dim, w.base, cgr._ptr(cos), cgr._ptr(sin), sptr))
 
     def attention():
-        cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, out=o, lse=lse)
+        cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=args.window,
+                              out=o, lse=lse)
 
     for _ in range(args.warmup):
         tables()
@@ -441,11 +445,11 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True)
+    flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True, args.window)
     ms_step = wall * 1e3 / args.steps
     kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    traffic = read_traffic() if args.window == 0 else None
 
     result = {
         "metric": METRIC,
@@ -464,7 +468,7 @@ def main() -> int:
             "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
             "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
             "io": "bf16", "qk_operand": "f16", "pv_operand": "bf16", "accumulate": "f32",
-            "step": "rope_tables + gqa_rope_attn_fwd", "flops_per_step": flops,
+            "step": "rope_tables + gqa_rope_attn_fwd", "window": args.window, "flops_per_step": flops,
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
         "roofline": {
@@ -477,7 +481,7 @@ def main() -> int:
             "kernel": "attn_fwd_dense_kernel (head_dim 128, bf16 I/O, f16 QK, causal, interleaved)",
             "kernel_ms": round(kernel_ms, 5),
         },
-        "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline(inputs, w),
+        "cpu_baseline": None if args.no_cpu_baseline or args.window else cpu_baseline(inputs, w),
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -40,6 +40,7 @@ __all__ = [
     "make_inputs",
     "varlen_lengths",
     "make_dout",
+    "visible_pairs",
     "algorithmic_flops",
     "algorithmic_flops_bwd",
     "DecodeWorkload",
@@ -181,15 +182,24 @@ def custom(name: str = "custom", **kw) -> Workload:
     return Workload(name, **defaults)
 
 
-def algorithmic_flops(n_head: int, head_dim: int, lengths, causal: bool) -> int:
+def visible_pairs(L: int, causal: bool, window: int = 0) -> int:
+    """Allowed (query, key) pairs of one sequence of length L: L(L+1)/2 causal,
+    L^2 unmasked; with a sliding window W, row i sees min(i + 1, W) keys."""
+    L = int(L)
+    if not causal:
+        return L * L
+    if window <= 0 or window >= L:
+        return L * (L + 1) // 2
+    return window * (window + 1) // 2 + (L - window) * window
+
+
+def algorithmic_flops(n_head: int, head_dim: int, lengths, causal: bool, window: int = 0) -> int:
     """FLOPs credited to one forward: 4*d per allowed (query, key) pair per query head.
 
-    2*d for the score dot product and 2*d for the weighted sum of V. A causal
-    sequence of length L has L(L+1)/2 allowed pairs, an unmasked one L^2.
+    2*d for the score dot product and 2*d for the weighted sum of V.
     Exponentials, RoPE and rescaling are not counted.
     """
-    pairs = sum((int(L) * (int(L) + 1)) // 2 if causal else int(L) * int(L) for L in lengths)
-    return 4 * head_dim * n_head * pairs
+    return 4 * head_dim * n_head * sum(visible_pairs(L, causal, window) for L in lengths)
 
 
 # Seed offset of the upstream gradient dL/dO, so it is a stream of its own and
@@ -203,7 +213,7 @@ def make_dout(w: Workload, like: torch.Tensor) -> torch.Tensor:
     return torch.randn(tuple(like.shape), generator=gen, dtype=torch.float32).to(_io_dtype(w.dtype))
 
 
-def algorithmic_flops_bwd(n_head: int, head_dim: int, lengths, causal: bool) -> int:
+def algorithmic_flops_bwd(n_head: int, head_dim: int, lengths, causal: bool, window: int = 0) -> int:
     """FLOPs credited to one backward: 10*d per allowed (query, key) pair per query head.
 
     Five products of 2*d each per pair: the recomputed scores q.k, dO.v, and
@@ -211,7 +221,7 @@ def algorithmic_flops_bwd(n_head: int, head_dim: int, lengths, causal: bool) -> 
     forward's count). The recomputation that splitting dq from dk/dv costs is
     not credited.
     """
-    return algorithmic_flops(n_head, head_dim, lengths, causal) // 4 * 10
+    return algorithmic_flops(n_head, head_dim, lengths, causal, window) // 4 * 10
 
 
 @dataclasses.dataclass(frozen=True)
