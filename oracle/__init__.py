@@ -37,6 +37,12 @@ of the cache ("Attention from Scratch", section "Attention, the math": GQA
 shares each K/V head among several query heads so that the cache of keys and
 values kept for generation shrinks by that factor).
 
+The neighbours of attention in the block (``rmsnorm``, ``rmsnorm_qkv_rope``):
+pre-norm RMSNorm ("The Transformer Block & the Model", section "RMSNorm:
+normalizing before every sub-layer": x / sqrt(mean(x^2) + eps) * weight), then
+the bias-free q, k, v projections and RoPE on q and k ("Attention from
+Scratch", "Attention, the math": project, then rotate).
+
 Packed variable-length batches (the kohakutt page, Highlights: "packed
 variable-length batches") are the concatenation of independent sequences:
 positions restart at 0 in every sequence and the mask never crosses a
@@ -66,6 +72,8 @@ __all__ = [
     "attention_varlen_bwd",
     "attention_bwd_group",
     "attention_decode",
+    "rmsnorm",
+    "rmsnorm_qkv_rope",
 ]
 
 
@@ -469,3 +477,38 @@ def attention_decode(q, k, v, cache_seqlens, *, base: float = 10000.0, style: st
             lse[b, h] = m + np.log(den)
             O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :]
     return O, lse
+
+
+def rmsnorm(x, weight, eps: float) -> np.ndarray:
+    """x [..., C] -> x / sqrt(mean(x^2 over C) + eps) * weight (float64)."""
+    x = _f64(x)
+    w = _f64(weight)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * w
+
+
+def rmsnorm_qkv_rope(x, norm_weight, eps: float, w_qkv, positions, n_head: int, n_kv_head: int,
+                     *, base: float = 10000.0, style: str = "interleaved", rotate_q: bool = True,
+                     rotate_k: bool = True):
+    """The block's pre-attention steps for N tokens: xn = rmsnorm(x), then
+    q = xn W_q^T, k = xn W_k^T, v = xn W_v^T (no bias), and RoPE on q and/or k
+    at each token's position.
+
+    x [N, C]; w_qkv [(n_head + 2 n_kv_head) * d, C]: the rows of W_q, then W_k,
+    then W_v (nn.Linear's [out, in] layout); positions [N].
+    Returns q [N, n_head, d], k [N, n_kv_head, d], v [N, n_kv_head, d] (float64).
+    """
+    x = _f64(x)
+    W = _f64(w_qkv)
+    N = x.shape[0]
+    d = W.shape[0] // (n_head + 2 * n_kv_head)
+    if d * (n_head + 2 * n_kv_head) != W.shape[0]:
+        raise ValueError("w_qkv rows must be (n_head + 2 n_kv_head) * head_dim")
+    y = rmsnorm(x, norm_weight, eps) @ W.T
+    q = y[:, : n_head * d].reshape(N, n_head, d)
+    k = y[:, n_head * d:(n_head + n_kv_head) * d].reshape(N, n_kv_head, d)
+    v = y[:, (n_head + n_kv_head) * d:].reshape(N, n_kv_head, d)
+    if rotate_q:
+        q = apply_rope(q, positions, base, style)
+    if rotate_k:
+        k = apply_rope(k, positions, base, style)
+    return q, k, v

@@ -702,6 +702,61 @@ def check_window_backward():
     assert np.allclose(gv, fv[0, :, 1], atol=1e-12)
 
 
+# ----------------------------------------------------------- RMSNorm + QKV + RoPE
+
+def check_rmsnorm_closed_forms():
+    rng = RNG(60)
+    x = rng.standard_normal((7, 48)) * 3.0
+    # weight 1, eps 0: every row has root-mean-square exactly 1.
+    y = oracle.rmsnorm(x, np.ones(48), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, atol=1e-14)
+    # Scale invariance (eps 0) and the weight as a per-feature factor.
+    assert np.allclose(oracle.rmsnorm(5.0 * x, np.ones(48), 0.0), y, atol=1e-13)
+    w = rng.standard_normal(48)
+    assert np.allclose(oracle.rmsnorm(x, w, 0.0), y * w, atol=1e-13)
+    # eps: mean(y^2) = m / (m + eps) for m = mean(x^2).
+    m = np.mean(x * x, axis=1)
+    ye = oracle.rmsnorm(x, np.ones(48), 0.5)
+    assert np.allclose(np.mean(ye * ye, axis=1), m / (m + 0.5), atol=1e-13)
+    # A constant row c: x / |c| (eps 0).
+    assert np.allclose(oracle.rmsnorm(np.full((1, 8), -3.0), np.ones(8), 0.0), -1.0, atol=1e-15)
+    # Against torch's own RMSNorm.
+    tn = torch.nn.functional.rms_norm(torch.from_numpy(x), (48,), torch.from_numpy(w), eps=1e-6)
+    assert np.allclose(oracle.rmsnorm(x, w, 1e-6), tn.numpy(), atol=1e-12)
+
+
+def check_rmsnorm_qkv_rope_structure():
+    rng = RNG(61)
+    N, H, KV, d = 9, 4, 2, 8
+    C = H * d
+    x = rng.standard_normal((N, C))
+    pos = rng.integers(0, 100, N)
+    # Identity projections (W_q = I, W_k = W_v = the first KV*d rows of I),
+    # weight 1, eps 0: q is RoPE of the unit-RMS row itself.
+    W = np.concatenate([np.eye(C), np.eye(C)[: KV * d], np.eye(C)[: KV * d]])
+    q, k, v = oracle.rmsnorm_qkv_rope(x, np.ones(C), 0.0, W, pos, H, KV, base=10000.0)
+    xn = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True))
+    assert np.allclose(q, oracle.apply_rope(xn.reshape(N, H, d), pos, 10000.0), atol=1e-13)
+    assert np.allclose(v, xn[:, : KV * d].reshape(N, KV, d), atol=1e-14)
+    assert np.allclose(k, oracle.apply_rope(xn[:, : KV * d].reshape(N, KV, d), pos, 10000.0), atol=1e-13)
+    # Random weights: each output is the normalised row times its slice of W,
+    # rotated (or not) as asked; positions 0 leave q, k unrotated.
+    W = rng.standard_normal(((H + 2 * KV) * d, 24))
+    x2 = rng.standard_normal((N, 24))
+    g = rng.standard_normal(24)
+    q, k, v = oracle.rmsnorm_qkv_rope(x2, g, 1e-6, W, np.zeros(N, int), H, KV, style="half")
+    xn2 = x2 / np.sqrt(np.mean(x2 * x2, axis=1, keepdims=True) + 1e-6) * g
+    for n in range(N):
+        for h in range(H):
+            assert np.allclose(q[n, h], W[h * d:(h + 1) * d] @ xn2[n], atol=1e-12)
+        for j in range(KV):
+            assert np.allclose(k[n, j], W[(H + j) * d:(H + j + 1) * d] @ xn2[n], atol=1e-12)
+            assert np.allclose(v[n, j], W[(H + KV + j) * d:(H + KV + j + 1) * d] @ xn2[n], atol=1e-12)
+    q2, k2, _ = oracle.rmsnorm_qkv_rope(x2, g, 1e-6, W, pos, H, KV, style="half", rotate_q=False)
+    assert np.allclose(k2, oracle.apply_rope(k, pos, 10000.0, "half"), atol=1e-12)
+    assert np.allclose(q2, q, atol=1e-13)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -734,4 +789,6 @@ ALL_CHECKS = [
     check_window_is_causal_attention_on_a_slice,
     check_window_special_cases,
     check_window_backward,
+    check_rmsnorm_closed_forms,
+    check_rmsnorm_qkv_rope_structure,
 ]

@@ -78,6 +78,15 @@ MUTANTS = [
     ("decode sees cache rows past the length", "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :]",
      "O[b, :, h, :] = (e / den[:, None]) @ v[b, :L, kv, :] + 0.0 * v[b, L - 1:L, kv, :].sum() + "
      "(v[b, L:, kv, :].sum() if L < v.shape[1] else 0.0)"),
+    ("rmsnorm without the mean", "np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+     "np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)"),
+    ("rmsnorm eps outside the root", "np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+     "(np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)"),
+    ("projection not transposed", "y = rmsnorm(x, norm_weight, eps) @ W.T",
+     "y = rmsnorm(x, norm_weight, eps) @ W.reshape(W.shape[1], W.shape[0])"),
+    ("k and v slices swapped", "k = y[:, n_head * d:(n_head + n_kv_head) * d].reshape(N, n_kv_head, d)",
+     "k = y[:, (n_head + n_kv_head) * d:].reshape(N, n_kv_head, d)"),
+    ("v rotated", "    return q, k, v\n", "    return q, k, apply_rope(v, positions, base, style)\n"),
     ("backward positions do not restart per sequence",
      "_one_sequence_bwd(q[a:b], k[a:b], v[a:b], dout[a:b], causal, scale,\n"
      "                                                      base, style, window)",
