@@ -26,6 +26,8 @@ bounded sample of the same workload on this host's cores.
                                         16 sequences x 1 new token; not the headline line)
   python bench.py --window W           (the forward or --backward line with a causal
                                         sliding window of W keys; not the headline line)
+  python bench.py --qkv                (one JSON line for the fused RMSNorm + q/k/v projection
+                                        + RoPE step of the same model; not the headline line)
 """
 
 from __future__ import annotations
@@ -370,6 +372,103 @@ def decode(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
     print(json.dumps(result), flush=True)
 
 
+QKV_WORKLOAD = "qkv_long_context_T8192_C4096_H32_KV8_d128"
+QKV_METRIC = "fused RMSNorm + q/k/v projection + RoPE TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
+
+
+def cpu_baseline_qkv(x, w) -> dict:
+    """The float64 oracle, as it stands, on the first 512 of the 8192 tokens."""
+    import oracle
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(i["num_threads"] for i in threadpool_info()) or None
+    except Exception:
+        pass
+    n = 512
+    t0 = time.perf_counter()
+    oracle.rmsnorm_qkv_rope(x["x"][:n], x["norm_weight"], w.eps, x["w_qkv"], x["positions"][:n].numpy(),
+                            w.n_head, w.n_kv_head, base=w.base, style=w.rope_style)
+    dt = time.perf_counter() - t0
+    O = (w.n_head + 2 * w.n_kv_head) * w.head_dim
+    return {
+        "value": round(2.0 * n * w.n_embd * O / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads or len(os.sched_getaffinity(0)),
+        "kind": "oracle",
+        "sample": f"float64 numpy oracle, tokens 0-{n - 1} of {w.B * w.T}, {dt:.2f} s",
+    }
+
+
+def qkv(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
+    """One step = one cgr_rmsnorm_qkv_rope call (q and k rotated)."""
+    w = W.QKV_WORKLOADS[QKV_WORKLOAD]
+    x = W.make_qkv_inputs(w)
+    N, C = x["x"].shape
+    O = x["w_qkv"].shape[0]
+    xs, g, wq, pos = (x[n].to(dev) for n in ("x", "norm_weight", "w_qkv", "positions"))
+    cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
+    q = torch.empty((N, w.n_head, w.head_dim), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((N, w.n_kv_head, w.head_dim), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    ws = torch.empty(cgr.cgr_rmsnorm_qkv_rope_workspace_size(N, C, w.n_head, w.n_kv_head, w.head_dim),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        cgr.rmsnorm_qkv_rope(xs, g, w.eps, wq, pos, w.n_head, w.n_kv_head, cos, sin, rope_style=w.rope_style,
+                             q=q, k=k, v=v, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = 2 * N * C * O
+    ms_step = wall * 1e3 / steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": QKV_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": QKV_WORKLOAD, "tokens": N, "n_embd": C, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+            "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "eps": w.eps,
+            "rotate": "q and k", "step": "rmsnorm_qkv_rope", "flops_per_step": flops,
+            "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "the call: qkv_prep_kernel + qkv_gemm_kernel (head_dim 128, interleaved)",
+            "kernel_ms": round(call_ms, 5),
+        },
+        "cpu_baseline": cpu_baseline_qkv(x, w) if with_cpu else None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -381,6 +480,7 @@ def main() -> int:
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
+    ap.add_argument("--qkv", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -406,6 +506,9 @@ def main() -> int:
         return 0
     if args.decode:
         decode(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
+        return 0
+    if args.qkv:
+        qkv(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
         return 0
 
     w = W.get(WORKLOAD)

@@ -38,6 +38,8 @@ __all__ = [
     "cgr_rope_rotate",
     "cgr_attn_decode_workspace_size",
     "cgr_gqa_rope_attn_decode",
+    "cgr_rmsnorm_qkv_rope_workspace_size",
+    "cgr_rmsnorm_qkv_rope",
     "cgr_version",
     "rope_tables",
     "gqa_rope_attn_fwd",
@@ -45,6 +47,7 @@ __all__ = [
     "gqa_rope_attn_bwd",
     "rope_rotate",
     "gqa_rope_attn_decode",
+    "rmsnorm_qkv_rope",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -70,6 +73,8 @@ EXPORTED_SYMBOLS = (
     "cgr_rope_rotate",
     "cgr_attn_decode_workspace_size",
     "cgr_gqa_rope_attn_decode",
+    "cgr_rmsnorm_qkv_rope_workspace_size",
+    "cgr_rmsnorm_qkv_rope",
     "cgr_last_error",
     "cgr_version",
 )
@@ -132,6 +137,11 @@ def library() -> ctypes.CDLL:
                                              i32, i32, i32, vp, vp, i32, i32, i32, f32, vp, ctypes.c_size_t,
                                              vp]
     lib.cgr_gqa_rope_attn_decode.restype = i32
+    lib.cgr_rmsnorm_qkv_rope_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.cgr_rmsnorm_qkv_rope_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_rmsnorm_qkv_rope.argtypes = [vp, vp, f32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp,
+                                         vp, i32, i32, i32, vp, ctypes.c_size_t, vp]
+    lib.cgr_rmsnorm_qkv_rope.restype = i32
     lib.cgr_varlen_device_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
     lib.cgr_varlen_device_status.restype = i32
     lib.cgr_last_error.argtypes = []
@@ -433,9 +443,62 @@ def cgr_gqa_rope_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: to
     return out, lse
 
 
+def cgr_rmsnorm_qkv_rope_workspace_size(n_tokens: int, n_embd: int, n_head: int, n_kv_head: int,
+                                        head_dim: int) -> int:
+    return int(library().cgr_rmsnorm_qkv_rope_workspace_size(int(n_tokens), int(n_embd), int(n_head),
+                                                             int(n_kv_head), int(head_dim)))
+
+
+def cgr_rmsnorm_qkv_rope(x: torch.Tensor, norm_weight: torch.Tensor, eps: float, w_qkv: torch.Tensor,
+                         positions: torch.Tensor, n_head: int, n_kv_head: int, rope_cos: torch.Tensor,
+                         rope_sin: torch.Tensor, *, rope_style: str = "interleaved", rotate_q: bool = True,
+                         rotate_k: bool = True, q: Optional[torch.Tensor] = None,
+                         k: Optional[torch.Tensor] = None, v: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None):
+    """x [N, C] (bf16), norm_weight [C], w_qkv [(H + 2 KV) d, C], positions int32 [N] (device)
+    -> q [N, H, d], k [N, KV, d], v [N, KV, d]: RMSNorm, projections, RoPE on q and/or k."""
+    lib = library()
+    for n, tns in (("x", x), ("norm_weight", norm_weight), ("w_qkv", w_qkv)):
+        _dev_tensor(n, tns, torch.bfloat16)
+    _dev_tensor("positions", positions, torch.int32)
+    if x.dim() != 2 or norm_weight.dim() != 1 or w_qkv.dim() != 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "x must be [N, C], norm_weight [C], w_qkv [O, C]")
+    N, C = x.shape
+    O = w_qkv.shape[0]
+    if norm_weight.shape[0] != C or w_qkv.shape[1] != C or positions.numel() != N:
+        raise CgrError(CGR_ERR_INVALID_ARG, "x, norm_weight, w_qkv and positions disagree on sizes")
+    heads = int(n_head) + 2 * int(n_kv_head)
+    if O % heads:
+        raise CgrError(CGR_ERR_INVALID_ARG, "w_qkv rows must be (n_head + 2 n_kv_head) * head_dim")
+    D = O // heads
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    q = torch.empty((N, n_head, D), dtype=torch.bfloat16, device=x.device) if q is None else q
+    k = torch.empty((N, n_kv_head, D), dtype=torch.bfloat16, device=x.device) if k is None else k
+    v = torch.empty((N, n_kv_head, D), dtype=torch.bfloat16, device=x.device) if v is None else v
+    for n, tns, shp in (("q", q, (N, n_head, D)), ("k", k, (N, n_kv_head, D)), ("v", v, (N, n_kv_head, D))):
+        _dev_tensor(n, tns, torch.bfloat16)
+        if tuple(tns.shape) != shp:
+            raise CgrError(CGR_ERR_INVALID_ARG, f"{n} must have shape {shp}")
+    need = lib.cgr_rmsnorm_qkv_rope_workspace_size(N, C, int(n_head), int(n_kv_head), D)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=x.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(x.device):
+        _check(lib.cgr_rmsnorm_qkv_rope(
+            _ptr(x), _ptr(norm_weight), float(eps), _ptr(w_qkv), _ptr(positions), _ptr(q), _ptr(k), _ptr(v),
+            N, C, int(n_head), int(n_kv_head), D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+            _STYLES[rope_style], int(bool(rotate_q)) | (int(bool(rotate_k)) << 1), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(x.device)))
+    return q, k, v
+
+
 rope_tables = cgr_rope_tables
 gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd
 rope_rotate = cgr_rope_rotate
 gqa_rope_attn_decode = cgr_gqa_rope_attn_decode
+rmsnorm_qkv_rope = cgr_rmsnorm_qkv_rope

@@ -37,6 +37,9 @@ SOURCES = [
     "attn_decode_d32.hip",
     "attn_decode_d64.hip",
     "attn_decode_d128.hip",
+    "qkv_d32.hip",
+    "qkv_d64.hip",
+    "qkv_d128.hip",
 ]
 
 ARCH = os.environ.get("CGR_OFFLOAD_ARCH", "gfx950")

@@ -13,6 +13,7 @@
 #include "attn_bwd_kernel.h"
 #include "attn_decode_kernel.h"
 #include "attn_fwd_kernel.h"
+#include "qkv_kernel.h"
 #include "cgr.h"
 #include "launch.h"
 
@@ -485,6 +486,79 @@ cgr_status cgr_rope_rotate(const void* x, void* out, const int32_t* positions, i
     default: e = cgr::launch_rope_rotate_d128(x, out, positions, rows, n_heads, f32, rope_cos, rope_sin, rope_max_pos, (int)style, device_status, s); break;
   }
   if (e != hipSuccess) return hip_fail("rope_rotate launch", e);
+  return CGR_OK;
+}
+
+size_t cgr_rmsnorm_qkv_rope_workspace_size(int n_tokens, int n_embd, int n_head, int n_kv_head,
+                                            int head_dim) {
+  if (n_tokens < 1 || n_embd < 1 || n_head < 1 || n_kv_head < 1 || head_dim < 2) return 0;
+  const size_t O = (size_t)(n_head + 2 * n_kv_head) * head_dim;
+  return 256 + (((size_t)n_tokens * 4 + 255) & ~(size_t)255) + O * n_embd * 2;
+}
+
+cgr_status cgr_rmsnorm_qkv_rope(const void* x, const void* norm_weight, float eps, const void* w_qkv,
+                                const int32_t* positions, void* q, void* k, void* v, int n_tokens,
+                                int n_embd, int n_head, int n_kv_head, int head_dim, cgr_dtype dtype,
+                                const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                                cgr_rope_style style, int rotate, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (!x || !norm_weight || !w_qkv || !positions || !q || !k || !v || !rope_cos || !rope_sin)
+    return fail(CGR_ERR_INVALID_ARG, "every tensor pointer must be non-null");
+  if (n_tokens < 1 || n_embd < 1 || n_head < 1 || n_kv_head < 1)
+    return fail(CGR_ERR_INVALID_ARG, "n_tokens, n_embd, n_head and n_kv_head must be >= 1");
+  if (n_head % n_kv_head != 0)
+    return fail(CGR_ERR_INVALID_ARG, "n_head (%d) must be divisible by n_kv_head (%d)", n_head, n_kv_head);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(CGR_ERR_UNSUPPORTED, "head_dim %d is not one of 32, 64, 128", head_dim);
+  if (n_embd % 32 != 0) return fail(CGR_ERR_UNSUPPORTED, "n_embd (%d) must be a multiple of 32", n_embd);
+  if (dtype != CGR_BF16) return fail(CGR_ERR_UNSUPPORTED, "bf16 tensors only (dtype %d)", (int)dtype);
+  if (style != CGR_ROPE_INTERLEAVED && style != CGR_ROPE_HALF)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown rope style %d", (int)style);
+  if (rotate < 0 || rotate > 3) return fail(CGR_ERR_INVALID_ARG, "rotate must be 0..3 (bit 0: q, bit 1: k)");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(CGR_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (rope_max_pos < 1) return fail(CGR_ERR_INVALID_ARG, "rope_max_pos must be >= 1");
+  if (!aligned(x, 16) || !aligned(norm_weight, 16) || !aligned(w_qkv, 16) || !aligned(q, 16) ||
+      !aligned(k, 16) || !aligned(v, 16) || !aligned(rope_cos, 16) || !aligned(rope_sin, 16) ||
+      !aligned(positions, 4))
+    return fail(CGR_ERR_ALIGNMENT, "tensors must be 16-byte aligned (positions 4-byte)");
+  const long O = (long)(n_head + 2 * n_kv_head) * head_dim;
+  if ((long)n_tokens * n_embd * 2 > (long)INT_MAX || O * n_embd * 2 > (long)INT_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "x or the projection weight spans more than 2 GiB");
+  const size_t need = cgr_rmsnorm_qkv_rope_workspace_size(n_tokens, n_embd, n_head, n_kv_head, head_dim);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 256)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
+  cgr::QkvArgs a{};
+  a.x = x;
+  a.norm_w = norm_weight;
+  a.w = w_qkv;
+  a.positions = positions;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.status = (int32_t*)workspace + 2;
+  a.rstd = (float*)((char*)workspace + 256);
+  a.wn = (char*)workspace + 256 + (((size_t)n_tokens * 4 + 255) & ~(size_t)255);
+  a.N = n_tokens;
+  a.C = n_embd;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  a.O = (int)O;
+  a.P = rope_max_pos;
+  a.rot_q = rotate & 1;
+  a.rot_k = (rotate >> 1) & 1;
+  a.eps = eps;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (head_dim) {
+    case 32: e = cgr::launch_qkv_d32(a, (int)style, s); break;
+    case 64: e = cgr::launch_qkv_d64(a, (int)style, s); break;
+    default: e = cgr::launch_qkv_d128(a, (int)style, s); break;
+  }
+  if (e != hipSuccess) return hip_fail("rmsnorm_qkv_rope launch", e);
   return CGR_OK;
 }
 

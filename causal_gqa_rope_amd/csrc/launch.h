@@ -9,6 +9,7 @@ namespace cgr {
 struct AttnArgs;
 struct BwdArgs;
 struct DecodeArgs;
+struct QkvArgs;
 
 hipError_t launch_attn_d32(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                            bool varlen, int grid, hipStream_t stream);
@@ -33,6 +34,10 @@ hipError_t launch_rope_rotate_d64(const void* x, void* out, const int32_t* posit
 hipError_t launch_rope_rotate_d128(const void* x, void* out, const int32_t* positions, long n_rows, int nh,
                                    int f32_io, const float* cs, const float* sn, int P, int style,
                                    int32_t* status, hipStream_t stream);
+
+hipError_t launch_qkv_d32(const QkvArgs& a, int style, hipStream_t stream);
+hipError_t launch_qkv_d64(const QkvArgs& a, int style, hipStream_t stream);
+hipError_t launch_qkv_d128(const QkvArgs& a, int style, hipStream_t stream);
 
 hipError_t launch_rope_tables(int max_pos, int head_dim, double base, float* cos_out,
                               float* sin_out, hipStream_t stream);

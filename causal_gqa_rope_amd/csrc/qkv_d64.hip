@@ -1,0 +1,9 @@
+// Instances of the fused RMSNorm + q/k/v projection + RoPE kernels for head_dim 64.
+#include "launch.h"
+#include "qkv_kernel.h"
+
+namespace cgr {
+hipError_t launch_qkv_d64(const QkvArgs& a, int style, hipStream_t stream) {
+  return launch_qkv_d<64>(a, style, stream);
+}
+}  // namespace cgr

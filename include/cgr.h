@@ -1,7 +1,8 @@
 /*
  * cgr.h -- fused causal grouped-query attention with rotary position
  * embedding (RoPE) for AMD Instinct MI355X (gfx950): forward (dense and packed
- * batches), backward, and decode against a KV cache.
+ * batches), backward, decode against a KV cache, and the fused RMSNorm + q/k/v
+ * projection + RoPE step that feeds them.
  *
  * The operation, as the pages define it:
  *   - RoPE tables: "Embeddings & the Residual Stream", section "Positional
@@ -270,12 +271,53 @@ CGR_API cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, 
                                     void* stream);
 
 /*
- * Reads the device error word the last varlen or decode call on `workspace` left:
+ * Bytes of device workspace cgr_rmsnorm_qkv_rope needs (0 for invalid sizes):
+ * a 256-byte header, one float per token, and the projection weight with the
+ * norm's weight folded in (bf16).
+ */
+CGR_API size_t cgr_rmsnorm_qkv_rope_workspace_size(int n_tokens, int n_embd, int n_head, int n_kv_head,
+                                           int head_dim);
+
+/*
+ * The block's steps before attention, fused: pre-norm RMSNorm ("The
+ * Transformer Block & the Model", "RMSNorm: normalizing before every
+ * sub-layer"), the bias-free q, k, v projections and RoPE ("Attention from
+ * Scratch", "Attention, the math": project, then rotate). For token t:
+ *   xn = x[t] / sqrt(mean(x[t]^2) + eps) * norm_weight
+ *   q[t] = xn W_q^T,  k[t] = xn W_k^T,  v[t] = xn W_v^T
+ * then q[t] (rotate bit 0) and k[t] (rotate bit 1) are rotated at position
+ * positions[t]. rotate = 0 leaves RoPE to the attention call (which rotates
+ * q and k itself); 2 gives the rotated keys a KV cache stores; 3 rotates both.
+ *   x: device bf16 [n_tokens, n_embd], n_embd a multiple of 32.
+ *   norm_weight: device bf16 [n_embd].
+ *   w_qkv: device bf16 [(n_head + 2 n_kv_head) * head_dim, n_embd]: the rows of
+ *     W_q, then W_k, then W_v (the [out, in] layout of a linear layer).
+ *   positions: device int32 [n_tokens]; a token whose position lies outside
+ *     [0, rope_max_pos) is left unwritten and sets the call's error word to 1
+ *     (read it with cgr_varlen_device_status on the workspace).
+ *   q: device bf16 [n_tokens, n_head, head_dim]; k, v: device bf16
+ *     [n_tokens, n_kv_head, head_dim]; written in full otherwise.
+ *   head_dim in {32, 64, 128}; tables and style as for the forward.
+ *   workspace: at least cgr_rmsnorm_qkv_rope_workspace_size(...) bytes,
+ *     256-byte aligned, for this call only.
+ * Numerics: W diag(norm_weight) is rounded once to bf16, products on bf16
+ * matrix cores with f32 sums, the 1/rms factor and RoPE in f32, one rounding
+ * of each output to bf16.
+ */
+CGR_API cgr_status cgr_rmsnorm_qkv_rope(const void* x, const void* norm_weight, float eps, const void* w_qkv,
+                                const int32_t* positions, void* q, void* k, void* v, int n_tokens,
+                                int n_embd, int n_head, int n_kv_head, int head_dim, cgr_dtype dtype,
+                                const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                                cgr_rope_style style, int rotate, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+/*
+ * Reads the device error word the last varlen, decode or rmsnorm_qkv_rope call on `workspace` left:
  * waits for `stream`, then stores 0 (the device-side sizes were well formed)
  * or a positive code in *host_status. Varlen: 1: cu_seqlens[0] != 0,
  * 2: decreasing, 3: a sequence longer than max_seqlen, 4:
  * cu_seqlens[num_seqs] != total_tokens. Decode: 1: a cache length outside
- * [Tq, max_seqlen].
+ * [Tq, max_seqlen]. rmsnorm_qkv_rope: 1: a position outside [0, rope_max_pos).
  */
 CGR_API cgr_status cgr_varlen_device_status(const void* workspace, void* stream, int32_t* host_status);
 

@@ -47,6 +47,9 @@ __all__ = [
     "DECODE_WORKLOADS",
     "make_decode_inputs",
     "decode_bytes",
+    "QkvWorkload",
+    "QKV_WORKLOADS",
+    "make_qkv_inputs",
 ]
 
 
@@ -277,3 +280,51 @@ def decode_bytes(w: DecodeWorkload, lens) -> int:
     cache = sum(int(L) for L in lens) * w.n_kv_head * w.head_dim * 2 * 2
     qo = 2 * w.B * w.Tq * w.n_head * w.head_dim * 2
     return cache + qo + w.B * w.n_head * w.Tq * 4
+
+
+@dataclasses.dataclass(frozen=True)
+class QkvWorkload:
+    """The block's pre-attention step: RMSNorm, q/k/v projections, RoPE, for
+    B sequences of T tokens of width n_embd (positions 0 .. T-1 in each)."""
+
+    name: str
+    B: int
+    T: int
+    n_embd: int
+    n_head: int
+    n_kv_head: int
+    head_dim: int
+    base: float
+    seed: int
+    eps: float = 1e-6
+    rope_style: str = "interleaved"
+
+    def replace(self, **kw) -> "QkvWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+QKV_WORKLOADS = {
+    w.name: w
+    for w in [
+        # The long-context model (n_embd = n_head * head_dim) over one 8192-token sequence.
+        QkvWorkload("qkv_long_context_T8192_C4096_H32_KV8_d128", B=1, T=8192, n_embd=4096, n_head=32,
+                    n_kv_head=8, head_dim=128, base=500000.0, seed=30),
+        # The pages' nanollama3 block: n_embd 384, 6 heads, 3 KV groups, theta 500000, B8 x T256.
+        QkvWorkload("qkv_nanollama3_B8_T256_C384_H6_KV3_d64", B=8, T=256, n_embd=384, n_head=6,
+                    n_kv_head=3, head_dim=64, base=500000.0, seed=31),
+    ]
+}
+
+
+def make_qkv_inputs(w: QkvWorkload) -> dict:
+    """Seeded CPU tensors in bf16: x [N, C] ~ N(0,1); norm_weight [C] ~ 1 + 0.1 N(0,1);
+    w_qkv [(H + 2 KV) d, C] ~ N(0,1) / sqrt(C); positions int32 [N] = t mod T."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    N, C = w.B * w.T, w.n_embd
+    O = (w.n_head + 2 * w.n_kv_head) * w.head_dim
+    x = torch.randn((N, C), generator=gen)
+    g = 1.0 + 0.1 * torch.randn((C,), generator=gen)
+    W = torch.randn((O, C), generator=gen) / (C ** 0.5)
+    pos = (torch.arange(N) % w.T).to(torch.int32)
+    return dict(x=x.to(torch.bfloat16), norm_weight=g.to(torch.bfloat16), w_qkv=W.to(torch.bfloat16),
+                positions=pos)
