@@ -45,15 +45,6 @@ struct DecodeArgs {
 
 constexpr int kDecodeBN = 32;  // keys per tile
 
-// Waits until at most n of this wave's vector-memory operations are
-// outstanding (n < 64), then keeps later code from moving above the wait.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 template <int D, int STYLE>
 __global__ __launch_bounds__(64) void attn_decode_kernel(DecodeArgs a) {
   constexpr int BN = kDecodeBN, KSTEPS = D / 16, DB = D / 32;

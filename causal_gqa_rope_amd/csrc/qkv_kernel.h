@@ -124,13 +124,30 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
   constexpr int BO = 128, BT = 256, KB = 32;
   constexpr int AT = BO * KB * 2, BTB = BT * KB * 2;
   static_assert(BO % D == 0, "whole heads per tile");
-  __shared__ __attribute__((aligned(16))) char a0[AT], a1[AT];
-  __shared__ __attribute__((aligned(16))) char b0[BTB], b1[BTB];
+  // Three stages (separate arrays, named at compile time in the unrolled
+  // loop): tile j + 2 loads while tile j is multiplied, so each load has two
+  // steps of matrix work to arrive in.
+  __shared__ __attribute__((aligned(16))) char a0[AT], a1[AT], a2[AT];
+  __shared__ __attribute__((aligned(16))) char b0[BTB], b1[BTB], b2[BTB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  const int n_ot = (a.O + BO - 1) / BO;
-  const int ot = blockIdx.x % n_ot, tt = blockIdx.x / n_ot;
+  // Tile order: consecutive workgroups go to the 8 XCDs in turn. When the
+  // token tiles split evenly over the XCDs, XCD x takes token tiles
+  // [x n_tt/8, (x+1) n_tt/8), walked token-fastest, so the workgroups it runs
+  // at once share both their weight rows and their token rows through its L2
+  // (each weight tile is fetched once per n_tt/8 token tiles instead of once
+  // per token tile).
+  const int n_ot = (a.O + BO - 1) / BO, n_tt = (a.N + BT - 1) / BT;
+  int ot, tt;
+  if ((n_tt & 7) == 0) {
+    const int x = blockIdx.x & 7, kk = blockIdx.x >> 3, per = n_tt >> 3;
+    ot = kk / per;
+    tt = x * per + kk % per;
+  } else {
+    ot = blockIdx.x % n_ot;
+    tt = blockIdx.x / n_ot;
+  }
   const int o0 = ot * BO, t0 = tt * BT;
   const rsrc_t rw = make_rsrc(a.wn, (uint32_t)((long)a.O * a.C * 2));
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)((long)a.N * a.C * 2));
@@ -156,21 +173,26 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
         for (int tb = 0; tb < 2; ++tb) acc[ob][tb] = mma32(af[ob], bf[tb], acc[ob][tb]);
     }
   };
+  // Step j: wait for this wave's loads of tile j (tile j + 1's may still be in
+  // flight), barrier (tile j complete in LDS, and every wave done with tile
+  // j - 1, whose stage tile j + 2 then takes), issue tile j + 2, multiply j.
+  constexpr int LOADS = (AT / 1024 + BTB / 1024) / 4;  // this wave's loads per tile
+  auto step = [&](int j, const char* at, const char* bt, char* an, char* bn) {
+    if (j + 1 < nk)
+      wait_vmem_le<LOADS>();
+    else
+      wait_vmem_le<0>();
+    __syncthreads();
+    if (j + 2 < nk) issue(j + 2, an, bn);
+    compute(at, bt);
+  };
   issue(0, a0, b0);
-  wait_vmem();
-  __syncthreads();
-  int j = 0;
-  for (; j + 1 < nk; j += 2) {
-    issue(j + 1, a1, b1);
-    compute(a0, b0);
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < nk) issue(j + 2, a0, b0);
-    compute(a1, b1);
-    wait_vmem();
-    __syncthreads();
+  if (1 < nk) issue(1, a1, b1);
+  for (int j = 0; j < nk; j += 3) {
+    step(j, a0, b0, a2, b2);
+    if (j + 1 < nk) step(j + 1, a1, b1, a0, b0);
+    if (j + 2 < nk) step(j + 2, a2, b2, a1, b1);
   }
-  if (j < nk) compute(a0, b0);
 
   // Epilogue: lane column = token; block ob = features o0 + 32 ob ...
 #pragma unroll

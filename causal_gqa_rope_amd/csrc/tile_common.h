@@ -32,6 +32,15 @@ __device__ __forceinline__ int toff(int r, int c) {
   return r * 2 * D + 16 * (c ^ tswz<D>(r));
 }
 
+// Waits until at most n of this wave's vector-memory operations are
+// outstanding (n < 64), then keeps later code from moving above the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Load `rows` rows (row r of the tile at global byte offset r * gstride + soff)
 // into an LDS tile, by the `nw` waves of a group; `wig` is this wave's index in
 // the group. Rows past the buffer's range read as zeros.
