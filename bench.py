@@ -8,6 +8,8 @@ Inputs are already resident in HBM when the timed region starts.
 
 Prints one JSON line. `value` is algorithmic TFLOP/s of the step (causal
 FLOPs counted exactly: 4*d per visible (query, key) pair per query head).
+The forward is given a workspace, so the keys are rotated once by a small
+kernel before the attention kernel; both run inside the timed step.
 `roofline` reports the attention kernel itself: its average launch duration
 measured with HIP events on the stream it is launched on, against the MI355X
 dense f16/bf16 MFMA peak; `traffic` is HBM bytes per launch from rocprofv3
@@ -143,10 +145,12 @@ def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
         else:
             lengths = [w.T] * w.B
             lse = torch.empty((w.B, w.n_head, w.T), dtype=torch.float32, device=dev)
+            ws = torch.empty(cgr.cgr_attn_fwd_workspace_size(w.B, w.T, w.n_kv_head, w.head_dim),
+                             dtype=torch.uint8, device=dev) if w.dtype == "bf16" else False
 
             def call():
                 cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=w.causal, rope_style=w.rope_style,
-                                      out=o, lse=lse)
+                                      out=o, lse=lse, workspace=ws)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
@@ -527,9 +531,12 @@ def main() -> int:
     def tables():
         cgr._check(lib.cgr_rope_tables(w.T, w.head_dim, w.base, cgr._ptr(cos), cgr._ptr(sin), sptr))
 
+    ws = torch.empty(cgr.cgr_attn_fwd_workspace_size(w.B, w.T, w.n_kv_head, w.head_dim), dtype=torch.uint8,
+                     device=dev)
+
     def attention():
         cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=args.window,
-                              out=o, lse=lse)
+                              out=o, lse=lse, workspace=ws)
 
     for _ in range(args.warmup):
         tables()
@@ -581,7 +588,8 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_fwd_dense_kernel (head_dim 128, bf16 I/O, f16 QK, causal, interleaved)",
+            "kernel": "the attention call: krot_kernel (keys rotated once) + attn_fwd_dense_kernel "
+                      "(head_dim 128, bf16 I/O, f16 QK, causal, interleaved); HIP events around the call",
             "kernel_ms": round(kernel_ms, 5),
         },
         "cpu_baseline": None if args.no_cpu_baseline or args.window else cpu_baseline(inputs, w),

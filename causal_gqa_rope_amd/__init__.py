@@ -30,6 +30,7 @@ __all__ = [
     "library_path",
     "cgr_rope_tables",
     "cgr_gqa_rope_attn_fwd",
+    "cgr_attn_fwd_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_varlen_device_status",
@@ -65,6 +66,7 @@ CGR_QK_F16, CGR_QK_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "cgr_rope_tables",
     "cgr_gqa_rope_attn_fwd",
+    "cgr_attn_fwd_workspace_size",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_varlen_device_status",
@@ -113,8 +115,10 @@ def library() -> ctypes.CDLL:
     vp, i32, f32, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
     lib.cgr_rope_tables.argtypes = [i32, i32, f64, vp, vp, vp]
     lib.cgr_rope_tables.restype = i32
+    lib.cgr_attn_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.cgr_attn_fwd_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                          i32, i32, i32, i32, f32, i32, vp]
+                                          i32, i32, i32, i32, f32, i32, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
@@ -202,8 +206,13 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
                           rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
                           window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          return_lse: bool = True):
-    """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None)."""
+                          return_lse: bool = True, workspace=None):
+    """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None).
+
+    workspace: None allocates one (bf16 I/O: the keys are then rotated once up
+    front), a uint8 device tensor of cgr_attn_fwd_workspace_size bytes is used
+    as given, and False passes none (the keys are rotated on every tile).
+    """
     lib = library()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(n, t)
@@ -229,13 +238,26 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
         _dev_tensor("lse", lse, torch.float32)
         if tuple(lse.shape) != (B, H, T):
             raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    if workspace is None and q.dtype == torch.bfloat16:
+        workspace = torch.empty(int(lib.cgr_attn_fwd_workspace_size(B, T, k.shape[2], D)), dtype=torch.uint8,
+                                device=q.device)
+    if workspace is False or workspace is None:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        _dev_tensor("workspace", workspace)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
         _check(lib.cgr_gqa_rope_attn_fwd(
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
             _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
             CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
-            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _stream(q.device)))
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], ws_ptr, ws_bytes,
+            _stream(q.device)))
     return out, lse
+
+
+def cgr_attn_fwd_workspace_size(B: int, T: int, n_kv_head: int, head_dim: int) -> int:
+    return int(library().cgr_attn_fwd_workspace_size(int(B), int(T), int(n_kv_head), int(head_dim)))
 
 
 def cgr_attn_fwd_varlen_workspace_size(num_seqs: int, total_tokens: int) -> int:

@@ -58,6 +58,7 @@ struct AttnArgs {
   const float* rope_sin;
   const int32_t* cu_seqlens;  // packed batches
   int32_t* sched;             // packed batches: [0] items, [1] queue counter, [2] error, then items
+  void* krot;                 // dense batches with a workspace: k rotated, in the Q.K^T operand type
   int B, T, H, KV;
   int total_tokens;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
@@ -85,7 +86,8 @@ constexpr int v_stride_dwords(int row_dwords) {
   return s;
 }
 
-template <int D_, typename IO_, typename QK_, bool CAUSAL_, int STYLE_, bool WIN_ = false>
+template <int D_, typename IO_, typename QK_, bool CAUSAL_, int STYLE_, bool WIN_ = false,
+          bool KPRE_ = false>
 struct Cfg {
   static constexpr int D = D_;
   using IO = IO_;  // float, or uint16_t holding bf16 bits
@@ -97,6 +99,9 @@ struct Cfg {
   // Sliding-window instances (causal only) are separate: the others compile
   // without any of the window's code.
   static constexpr bool WIN = WIN_ && CAUSAL_;
+  // K already rotated and rounded to the operand type by krot_kernel (a
+  // workspace was given): the tiles only copy it into LDS.
+  static constexpr bool KPRE = KPRE_ && !std::is_same<IO_, float>::value;
 
 #ifndef CGR_NW
 #define CGR_NW 8
@@ -188,6 +193,11 @@ __device__ __forceinline__ void load_tab(const float* cs, const float* sn, int g
 }
 
 // Rotate the group pair in place: (a, b) -> (a cos - b sin, a sin + b cos).
+// Each output is one rounded product and one fused multiply-add, written out
+// so that every kernel that rotates keys (per tile, or once up front) rounds
+// them identically, whatever contractions the compiler would choose.
+__device__ __forceinline__ float rot_a(float a, float b, float c, float s) { return __builtin_fmaf(a, c, -(b * s)); }
+__device__ __forceinline__ float rot_b(float a, float b, float c, float s) { return __builtin_fmaf(a, s, b * c); }
 template <int STYLE>
 __device__ __forceinline__ void rope_pair(float (&x0)[8], float (&x1)[8], const f32x4 (&c)[2],
                                           const f32x4 (&s)[2]) {
@@ -195,20 +205,20 @@ __device__ __forceinline__ void rope_pair(float (&x0)[8], float (&x1)[8], const 
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       float a = x0[2 * m], b = x0[2 * m + 1];
-      x0[2 * m] = a * c[0][m] - b * s[0][m];
-      x0[2 * m + 1] = a * s[0][m] + b * c[0][m];
+      x0[2 * m] = rot_a(a, b, c[0][m], s[0][m]);
+      x0[2 * m + 1] = rot_b(a, b, c[0][m], s[0][m]);
       a = x1[2 * m];
       b = x1[2 * m + 1];
-      x1[2 * m] = a * c[1][m] - b * s[1][m];
-      x1[2 * m + 1] = a * s[1][m] + b * c[1][m];
+      x1[2 * m] = rot_a(a, b, c[1][m], s[1][m]);
+      x1[2 * m + 1] = rot_b(a, b, c[1][m], s[1][m]);
     }
   } else {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float cj = c[j >> 2][j & 3], sj = s[j >> 2][j & 3];
       const float a = x0[j], b = x1[j];
-      x0[j] = a * cj - b * sj;
-      x1[j] = a * sj + b * cj;
+      x0[j] = rot_a(a, b, cj, sj);
+      x1[j] = rot_b(a, b, cj, sj);
     }
   }
 }
@@ -552,7 +562,7 @@ struct UnitFast {
     const int G = a.H / a.KV, kvh = head / G;
     const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
     const uint16_t* qbase = (const uint16_t*)a.q + (long)tok0 * qs + (long)head * D;
-    const uint16_t* kbase = (const uint16_t*)a.k + (long)tok0 * ks + (long)kvh * D;
+    const uint16_t* kbase = (const uint16_t*)(C::KPRE ? a.krot : a.k) + (long)tok0 * ks + (long)kvh * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (long)tok0 * ks + (long)kvh * D;
     const rsrc_t rq = make_rsrc(qbase, (uint32_t)(((L - 1) * qs + D) * 2));
     const rsrc_t rk = make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
@@ -684,11 +694,13 @@ struct UnitFast {
           const int so = (kt0 + u * RPU) * ks * 2;
           kw[u][0] = buf_load16(rk, k_vo, so);
           kw[u][1] = buf_load16(rk, k_vo + D, so);
-          const int st = (kt0 + u * RPU) * (D / 2) * 4;
-          kc[u][0] = buf_load16f(rc, t_vo, st);
-          kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
-          ksn[u][0] = buf_load16f(rs, t_vo, st);
-          ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
+          if constexpr (!C::KPRE) {
+            const int st = (kt0 + u * RPU) * (D / 2) * 4;
+            kc[u][0] = buf_load16f(rc, t_vo, st);
+            kc[u][1] = buf_load16f(rc, t_vo + TAB_O1, st);
+            ksn[u][0] = buf_load16f(rs, t_vo, st);
+            ksn[u][1] = buf_load16f(rs, t_vo + TAB_O1, st);
+          }
         }
       }
     };
@@ -703,14 +715,19 @@ struct UnitFast {
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
         if (has_k(u)) {
-          float x0[8], x1[8];
-          const u32x4 w0[1] = {kw[u][0]}, w1[1] = {kw[u][1]};
-          raw_to_f32<uint16_t>(w0, x0);
-          raw_to_f32<uint16_t>(w1, x1);
-          rope_pair<C::STYLE>(x0, x1, kc[u], ksn[u]);
           char* dst = kst + k_lds + u * RPU * C::K_STRIDE;
-          *(u32x4*)dst = to_frag<QK>(x0).v;
-          *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+          if constexpr (C::KPRE) {
+            *(u32x4*)dst = kw[u][0];
+            *(u32x4*)(dst + D) = kw[u][1];
+          } else {
+            float x0[8], x1[8];
+            const u32x4 w0[1] = {kw[u][0]}, w1[1] = {kw[u][1]};
+            raw_to_f32<uint16_t>(w0, x0);
+            raw_to_f32<uint16_t>(w1, x1);
+            rope_pair<C::STYLE>(x0, x1, kc[u], ksn[u]);
+            *(u32x4*)dst = to_frag<QK>(x0).v;
+            *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+          }
         }
       }
     };
@@ -1120,6 +1137,31 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varle
   }
 }
 
+// K rotated once at its positions (token t of a dense batch entry is at
+// position t mod T) and rounded to the Q.K^T operand type, for the tile loops
+// to copy. Item = (row, group g < D/16) carrying the chunk pair (g, g + D/16),
+// as in the K loader.
+template <int D, typename QK, int STYLE>
+__global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
+  constexpr int IPR = D / 16;
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long row = tid / IPR;  // (token * KV + kv)
+  if (row >= (long)a.B * a.T * a.KV) return;
+  const int g = (int)(tid % IPR);
+  const int t = (int)((row / a.KV) % a.T);
+  const uint16_t* kp = (const uint16_t*)a.k + row * D;
+  u32x4 w0[1] = {*(const u32x4*)(kp + 8 * g)}, w1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
+  float x0[8], x1[8];
+  raw_to_f32<uint16_t>(w0, x0);
+  raw_to_f32<uint16_t>(w1, x1);
+  f32x4 c[2], s[2];
+  load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
+  rope_pair<STYLE>(x0, x1, c, s);
+  uint16_t* out = (uint16_t*)a.krot + row * D;
+  *(u32x4*)(out + 8 * g) = to_frag<QK>(x0).v;
+  *(u32x4*)(out + 8 * g + D / 2) = to_frag<QK>(x1).v;
+}
+
 // Launch one instance. Host-side, after the arguments are validated.
 template <class C>
 hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t stream) {
@@ -1132,13 +1174,29 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
   return hipGetLastError();
 }
 
+// Dense batch with the K rotation done once up front (a.krot set).
+template <class C>
+hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
+  const long items = (long)a.B * a.T * a.KV * (C::D / 16);
+  hipLaunchKernelGGL((krot_kernel<C::D, typename C::QK, C::STYLE>), dim3((unsigned)((items + 255) / 256)),
+                     dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+  return hipGetLastError();
+}
+
 constexpr int kBM = 32 * CGR_NW;  // query rows per unit (all instances)
 constexpr int kBN = CGR_BN;  // keys per tile (all instances)
 
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                          bool varlen, int grid, hipStream_t stream) {
-#define CGR_LAUNCH(IO, QK, CAU, STY, WIN) \
+#define CGR_LAUNCH(IO, QK, CAU, STY, WIN)                                                       \
+  if constexpr (!std::is_same<IO, float>::value) {                                               \
+    if (!varlen && a.krot != nullptr)                                                             \
+      return launch_attn_kpre<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream);             \
+  }                                                                                               \
   return launch_attn<Cfg<D, IO, QK, CAU, STY, WIN>>(a, varlen, grid, stream)
 #define CGR_BY_STYLE(IO, QK, CAU, WIN) \
   if (style == STYLE_HALF) { CGR_LAUNCH(IO, QK, CAU, STYLE_HALF, WIN); } else { CGR_LAUNCH(IO, QK, CAU, STYLE_INTERLEAVED, WIN); }

@@ -216,12 +216,20 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
                                  int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
-                                 float softmax_scale, cgr_qk_operand qk_operand, void* stream) {
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
   if (st != CGR_OK) return st;
   if ((st = check_window(window, mask)) != CGR_OK) return st;
+  const bool use_ws = workspace != nullptr && dtype == CGR_BF16;
+  if (use_ws) {
+    if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+    const size_t need = cgr_attn_fwd_workspace_size(B, T, n_kv_head, head_dim);
+    if (workspace_bytes < need)
+      return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
+  }
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
   const long grid = (long)((T + cgr::kBM - 1) / cgr::kBM) * B * n_head;
   if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
@@ -231,10 +239,16 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
   a.T = T;
   a.total_tokens = B * T;
   a.window = window;
+  a.krot = use_ws ? workspace : nullptr;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
                                      (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   return CGR_OK;
+}
+
+size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim) {
+  if (B < 1 || T < 1 || n_kv_head < 1 || head_dim < 2) return 0;
+  return (size_t)B * T * n_kv_head * head_dim * 2;
 }
 
 size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens) {

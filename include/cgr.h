@@ -103,6 +103,13 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
                            float* sin_out, void* stream);
 
 /*
+ * Bytes of the optional workspace of cgr_gqa_rope_attn_fwd (bf16 I/O): the
+ * rotated keys in the Q.K^T operand type, B * T * n_kv_head * head_dim * 2.
+ * Returns 0 for invalid sizes.
+ */
+CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim);
+
+/*
  * Dense batch forward.
  *   q: device [B, T, n_head, head_dim]      (dtype)
  *   k, v: device [B, T, n_kv_head, head_dim] (dtype)
@@ -116,13 +123,19 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
  *   window: sliding window (see cgr_mask), 0 for none.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   qk_operand: see cgr_qk_operand (ignored for CGR_F32).
+ *   workspace: NULL, or (bf16 I/O) device memory of at least
+ *     cgr_attn_fwd_workspace_size(B, T, n_kv_head, head_dim) bytes, 16-byte
+ *     aligned, scratch for this call only. With it the keys are rotated
+ *     once, before the attention kernel, instead of on every tile that reads
+ *     them (the results are the same bits either way). Ignored for CGR_F32.
  * o and lse must not overlap the inputs.
  */
 CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
                                  int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
-                                 float softmax_scale, cgr_qk_operand qk_operand, void* stream);
+                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace cgr_gqa_rope_attn_fwd_varlen needs for a packed

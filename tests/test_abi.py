@@ -49,6 +49,8 @@ def test_library_leaves_the_hip_runtime_to_the_process():
 def test_version_and_workspace_size():
     assert cgr.cgr_version() == 10000
     lib = cgr.library()
+    assert lib.cgr_attn_fwd_workspace_size(0, 16, 2, 64) == 0
+    assert lib.cgr_attn_fwd_workspace_size(2, 100, 8, 128) == 2 * 100 * 8 * 128 * 2
     assert lib.cgr_attn_fwd_varlen_workspace_size(0, 10) == 0
     assert lib.cgr_attn_fwd_varlen_workspace_size(1, -1) == 0
     small = lib.cgr_attn_fwd_varlen_workspace_size(1, 1)
@@ -67,12 +69,13 @@ PMIS = ctypes.c_void_p(0x10002)   # misaligned placeholder
 
 def dense(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
-             P=16, style=0, mask=1, window=0, scale=0.0, qk=0)
+             P=16, style=0, mask=1, window=0, scale=0.0, qk=0, ws=None, wsb=0)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"],
                                    a["KV"], a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
-                                   a["style"], a["mask"], a["window"], a["scale"], a["qk"], None)
+                                   a["style"], a["mask"], a["window"], a["scale"], a["qk"], a["ws"],
+                                   a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -97,6 +100,8 @@ def dense(**kw):
     (dict(P=15), 1, "positions"),
     (dict(window=-1), 1, "window"),
     (dict(window=8, mask=0), 1, "CGR_MASK_CAUSAL"),
+    (dict(ws=P, wsb=100), 4, "needs"),
+    (dict(ws=PMIS, wsb=1 << 20), 3, "aligned"),
 ])
 def test_dense_rejects_bad_arguments(kw, status, needle):
     st, msg = dense(**kw)

@@ -332,3 +332,20 @@ def test_first_tile_dominates(gpu):
     o, lse = run_gpu(w, to_dev(x, gpu), gpu)
     ro, rl = run_oracle(w, x)
     assert_close("sink", f64(o), ro, f64(lse), rl, "bf16")
+
+
+@pytest.mark.parametrize("T,H,KV,d,causal,style", [(300, 8, 2, 128, True, "interleaved"),
+                                                   (129, 4, 1, 64, False, "half"),
+                                                   (1000, 6, 3, 32, True, "half")])
+def test_pre_rotated_keys_give_the_same_bits(gpu, T, H, KV, d, causal, style):
+    """With a workspace the keys are rotated once up front; without, on every
+    tile: the same arithmetic in the same order, so the same bits."""
+    w = W.custom("prerot", B=2, T=T, n_head=H, n_kv_head=KV, head_dim=d, causal=causal, rope_style=style,
+                 seed=T + d)
+    x = to_dev(W.make_inputs(w), gpu)
+    cos, sin = cgr.rope_tables(T, d, w.base, device=gpu)
+    o1, l1 = cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, causal=causal, rope_style=style,
+                                   workspace=False)
+    o2, l2 = cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, causal=causal, rope_style=style)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
