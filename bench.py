@@ -30,6 +30,11 @@ bounded sample of the same workload on this host's cores.
                                         sliding window of W keys; not the headline line)
   python bench.py --qkv                (one JSON line for the fused RMSNorm + q/k/v projection
                                         + RoPE step of the same model; not the headline line)
+  python bench.py --wide               (the forward line at head_dim 256: T=8192, 16 query and
+                                        8 K/V heads; not the headline line)
+  python bench.py --padded             (the forward line on a right-padded batch of 4 x 8192
+                                        tokens, valid lengths U[2048, 8192]; FLOPs over the
+                                        valid tokens; not the headline line)
 """
 
 from __future__ import annotations
@@ -47,6 +52,8 @@ if ROOT not in sys.path:
 
 METRIC = "causal GQA+RoPE attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 WORKLOAD = "long_context_T8192_H32_KV8_d128"
+PADDED_WORKLOAD = "padded_B4_T8192_len2048to8192_H32_KV8_d128"
+WIDE_WORKLOAD = "long_context_T8192_H16_KV8_d256"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 KERNEL_SOURCES = ["attn_fwd_kernel.h", "device_common.h", "attn_fwd_d128.hip"]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", f"attn_fwd_{WORKLOAD}.counters.txt")
@@ -485,6 +492,10 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
     ap.add_argument("--qkv", action="store_true")
+    ap.add_argument("--wide", action="store_true",
+                    help="head_dim 256: B=1 T=8192 H=16 KV=8 (the long-context width in wider heads)")
+    ap.add_argument("--padded", action="store_true",
+                    help="right-padded dense batch: B=4 entries of T=8192, valid lengths U[2048, 8192]")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -515,7 +526,13 @@ def main() -> int:
         qkv(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
         return 0
 
-    w = W.get(WORKLOAD)
+    w = W.get(WIDE_WORKLOAD if args.wide else WORKLOAD)
+    seqlens, lens = None, [w.T] * w.B
+    if args.padded:
+        w = W.custom(PADDED_WORKLOAD, B=4, T=w.T, n_head=w.n_head, n_kv_head=w.n_kv_head, head_dim=w.head_dim,
+                     base=w.base, seed=21)
+        lens = W.padded_lengths(w.B, 2048, w.T, seed=21)
+        seqlens = torch.tensor(lens, dtype=torch.int32, device=dev)
     inputs = W.make_inputs(w)
     q = inputs["q"].to(dev)
     k = inputs["k"].to(dev)
@@ -536,7 +553,7 @@ def main() -> int:
 
     def attention():
         cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=args.window,
-                              out=o, lse=lse, workspace=ws)
+                              out=o, lse=lse, workspace=ws, seqlens=seqlens)
 
     for _ in range(args.warmup):
         tables()
@@ -555,11 +572,12 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True, args.window)
+    flops = W.algorithmic_flops(w.n_head, w.head_dim, lens, True, args.window)
     ms_step = wall * 1e3 / args.steps
     kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    traffic = read_traffic() if args.window == 0 else None
+    headline = args.window == 0 and not args.padded and not args.wide
+    traffic = read_traffic() if headline else None
 
     result = {
         "metric": METRIC,
@@ -575,9 +593,10 @@ def main() -> int:
         "dtype": "f16/bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+            "workload": w.name, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
             "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
             "io": "bf16", "qk_operand": "f16", "pv_operand": "bf16", "accumulate": "f32",
+            **({"valid_lengths": lens} if args.padded else {}),
             "step": "rope_tables + gqa_rope_attn_fwd", "window": args.window, "flops_per_step": flops,
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
@@ -589,10 +608,10 @@ def main() -> int:
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
             "kernel": "the attention call: krot_kernel (keys rotated once) + attn_fwd_dense_kernel "
-                      "(head_dim 128, bf16 I/O, f16 QK, causal, interleaved); HIP events around the call",
+                      f"(head_dim {w.head_dim}, bf16 I/O, f16 QK, causal, interleaved); HIP events around the call",
             "kernel_ms": round(kernel_ms, 5),
         },
-        "cpu_baseline": None if args.no_cpu_baseline or args.window else cpu_baseline(inputs, w),
+        "cpu_baseline": None if args.no_cpu_baseline or not headline else cpu_baseline(inputs, w),
     }
     print(json.dumps(result), flush=True)
     return 0

@@ -118,7 +118,7 @@ def library() -> ctypes.CDLL:
     lib.cgr_attn_fwd_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.cgr_attn_fwd_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
-                                          i32, i32, i32, i32, f32, i32, vp, ctypes.c_size_t, vp]
+                                          i32, i32, i32, i32, f32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
@@ -206,12 +206,14 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
                           rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
                           window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          return_lse: bool = True, workspace=None):
+                          return_lse: bool = True, workspace=None, seqlens: Optional[torch.Tensor] = None):
     """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None).
 
     workspace: None allocates one (bf16 I/O: the keys are then rotated once up
     front), a uint8 device tensor of cgr_attn_fwd_workspace_size bytes is used
     as given, and False passes none (the keys are rotated on every tile).
+    seqlens: optional int32 device tensor [B] of valid tokens per entry (right
+    padding): keys past them are hidden, rows past them are left unwritten.
     """
     lib = library()
     for n, t in (("q", q), ("k", k), ("v", v)):
@@ -238,6 +240,10 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
         _dev_tensor("lse", lse, torch.float32)
         if tuple(lse.shape) != (B, H, T):
             raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    if seqlens is not None:
+        _dev_tensor("seqlens", seqlens, torch.int32)
+        if tuple(seqlens.shape) != (B,):
+            raise CgrError(CGR_ERR_INVALID_ARG, "seqlens must be [B]")
     if workspace is None and q.dtype == torch.bfloat16:
         workspace = torch.empty(int(lib.cgr_attn_fwd_workspace_size(B, T, k.shape[2], D)), dtype=torch.uint8,
                                 device=q.device)
@@ -251,8 +257,8 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
             _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
             CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
-            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], ws_ptr, ws_bytes,
-            _stream(q.device)))
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _ptr(seqlens), ws_ptr,
+            ws_bytes, _stream(q.device)))
     return out, lse
 
 

@@ -57,6 +57,7 @@ struct AttnArgs {
   const float* rope_cos;  // [P, D/2]
   const float* rope_sin;
   const int32_t* cu_seqlens;  // packed batches
+  const int32_t* seqlens;     // dense batches: valid tokens per entry (right padding), or null
   int32_t* sched;             // packed batches: [0] items, [1] queue counter, [2] error, then items
   void* krot;                 // dense batches with a workspace: k rotated, in the Q.K^T operand type
   int B, T, H, KV;
@@ -106,13 +107,18 @@ struct Cfg {
 #ifndef CGR_NW
 #define CGR_NW 8
 #endif
-  static constexpr int NW = CGR_NW;
-  static constexpr int THREADS = 64 * NW;
-  static constexpr int BM = 32 * NW;  // query rows per unit
 #ifndef CGR_BN
 #define CGR_BN 64
 #endif
-  static constexpr int BN = CGR_BN;   // keys per tile
+  // head_dim 256 (bf16 I/O): one wave per SIMD, each with the whole register
+  // file (its O accumulator alone is 128 registers per lane), four waves per
+  // workgroup and 32-key tiles, so K, V and the Q staging fit in LDS.
+  static constexpr bool WIDE = D_ == 256;
+  static constexpr int NW = WIDE ? 4 : CGR_NW;
+  static constexpr int WPS = WIDE ? 1 : CGR_WAVES_PER_SIMD;  // waves per SIMD
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BM = 32 * NW;  // query rows per unit
+  static constexpr int BN = WIDE ? 32 : CGR_BN;   // keys per tile
   static constexpr int ESZ = F32 ? 4 : 2;
   static constexpr int KSTEPS = D / 16;  // 32x32x16 k-steps over the head dim
   static constexpr int DB = D / 32;      // 32-wide blocks of the head dim
@@ -146,7 +152,8 @@ struct Cfg {
   static constexpr int V_ITEMS = BN * V_CHUNKS;
   static constexpr int VU = (V_ITEMS + THREADS - 1) / THREADS;
 
-  static_assert(D == 32 || D == 64 || D == 128, "head_dim");
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head_dim");
+  static_assert(!(WIDE && F32), "head_dim 256 is built for bf16 I/O only");
 };
 
 // Eight consecutive elements from global memory as floats (zeros when !ok).
@@ -547,7 +554,7 @@ struct UnitFast {
 
   // XOR swizzle of the 16-byte chunks of V row r (an involution).
   static __device__ __forceinline__ int vswz_mask(int r) {
-    if constexpr (D == 128) return (r & 3) << 2;
+    if constexpr (D >= 128) return (r & 3) << 2;
     else if constexpr (D == 64) return ((r >> 1) & 1) << 2;
     else return 0;
   }
@@ -619,6 +626,33 @@ struct UnitFast {
       }
     }
     Frag<QK> qf[C::KSTEPS];
+    // Q fragments straight from global memory (the windowed path): each lane
+    // loads its own row's groups, k-step s2 holding group g = 2 s2 + hh and
+    // k-step s2 + D/32 group g + D/16.
+    auto load_q_direct = [&]() {
+      const bool ok = my_q < L;
+      const long tq = (long)(ok ? my_q : 0);
+#pragma unroll
+      for (int s2 = 0; s2 < D / 32; ++s2) {
+        const int g = 2 * s2 + hh;
+        u32x4 w0[1], w1[1];
+        load8_raw<uint16_t>(qbase + tq * qs + 8 * g, ok, w0);
+        load8_raw<uint16_t>(qbase + tq * qs + 8 * g + D / 2, ok, w1);
+        f32x4 c[2], s[2];
+        load_tab<D, C::STYLE>(a.rope_cos + tq * (D / 2), a.rope_sin + tq * (D / 2), g, ok, c, s);
+        float x0[8], x1[8];
+        raw_to_f32<uint16_t>(w0, x0);
+        raw_to_f32<uint16_t>(w1, x1);
+        rope_pair<C::STYLE>(x0, x1, c, s);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          x0[j] *= a.qscale;
+          x1[j] *= a.qscale;
+        }
+        qf[s2] = to_frag<QK>(x0);
+        qf[s2 + D / 32] = to_frag<QK>(x1);
+      }
+    };
     auto stage_q = [&]() {
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
@@ -669,12 +703,15 @@ struct UnitFast {
     constexpr int TAB_O1 = C::STYLE == STYLE_INTERLEAVED ? D : 16;  // bytes from o0 to o1
     const int t_vo = (row0 * (D / 2) + (C::STYLE == STYLE_INTERLEAVED ? 4 * g0 : 8 * g0)) * 4;
     const int k_lds = row0 * C::K_STRIDE + g0 * 16;
-    // V: 1 KiB per wave load = VROWS rows; the lane's row within the block and
-    // its swizzled chunk do not depend on the block.
+    // V: 1 KiB per wave load = VROWS rows. The swizzle follows the row within
+    // the tile, blk * VROWS + v_r, and repeats every 4 rows: with 4 or more
+    // rows per load the lane's chunk does not depend on the block; with 2
+    // (head_dim 256) it depends on the block's parity.
     constexpr int VWL = C::V_WAVE_LOADS;
     constexpr int VROWS = 1024 / (2 * D);
     const int v_r = lane / (2 * D / 16), v_pch = lane % (2 * D / 16);
     const int v_vo = v_r * ks * 2 + 16 * (v_pch ^ vswz_mask(v_r));
+    const int v_vo_odd = VROWS >= 4 ? v_vo : v_r * ks * 2 + 16 * (v_pch ^ vswz_mask(VROWS + v_r));
 
     // K (to registers) and V (straight to LDS) of the tile at kt0; the K
     // registers are consumed by store_k once this tile's products are issued.
@@ -684,7 +721,7 @@ struct UnitFast {
       for (int u = 0; u < VWL; ++u) {
         const int blk = wave * VWL + u;
         if (C::V_BYTES == NW * VWL * 1024 || blk * 1024 < C::V_BYTES)
-          buf_load16_lds(rv, vs + blk * 1024, v_vo, (kt0 + blk * VROWS) * ks * 2);
+          buf_load16_lds(rv, vs + blk * 1024, (blk & 1) ? v_vo_odd : v_vo, (kt0 + blk * VROWS) * ks * 2);
       }
     };
     auto load_k = [&](int kt0, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
@@ -735,7 +772,7 @@ struct UnitFast {
     // Lane offsets of the K fragment reads and of the transposing V reads.
     const int k_rd = l32 * C::K_STRIDE + hh * 16;
     const int gi = lane >> 4, li = lane & 15;
-    const int vx = D == 128 ? (li >> 2) : (D == 64 ? (((4 * hh + (li >> 2)) >> 1) & 1) : 0);
+    const int vx = D >= 128 ? (li >> 2) : (D == 64 ? (((4 * hh + (li >> 2)) >> 1) & 1) : 0);
     const int v_lane = (4 * hh + (li >> 2)) * (2 * D) + 16 * (2 * (gi & 1) + ((li & 3) >> 1)) +
                        8 * (li & 1);
     int v_rd[C::DB];
@@ -918,31 +955,8 @@ struct UnitFast {
     };
     float m_fin;
     if (W > 0) {
-      // Q fragments straight from global memory, each lane its own row (the
-      // staged path's registers belong to the fast path alone: giving them
-      // a second consumer here costs the fast path dozens of spills).
-      const bool ok = my_q < L;
-      const long tq = (long)(ok ? my_q : 0);
-#pragma unroll
-      for (int s2 = 0; s2 < D / 32; ++s2) {
-        const int g = 2 * s2 + hh;  // k-step s2 holds group g; k-step s2 + D/32 holds g + D/16
-        u32x4 w0[1], w1[1];
-        load8_raw<uint16_t>(qbase + tq * qs + 8 * g, ok, w0);
-        load8_raw<uint16_t>(qbase + tq * qs + 8 * g + D / 2, ok, w1);
-        f32x4 c[2], s[2];
-        load_tab<D, C::STYLE>(a.rope_cos + tq * (D / 2), a.rope_sin + tq * (D / 2), g, ok, c, s);
-        float x0[8], x1[8];
-        raw_to_f32<uint16_t>(w0, x0);
-        raw_to_f32<uint16_t>(w1, x1);
-        rope_pair<C::STYLE>(x0, x1, c, s);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          x0[j] *= a.qscale;
-          x1[j] *= a.qscale;
-        }
-        qf[s2] = to_frag<QK>(x0);
-        qf[s2 + D / 32] = to_frag<QK>(x1);
-      }
+      // Q fragments straight from global memory, each lane its own row.
+      load_q_direct();
       m_fin = rescale_pass(std::true_type{});
     } else {
       float m_ref = 0.f;
@@ -1046,6 +1060,8 @@ struct UnitFast {
     // the sequence end fall outside the buffer range and are dropped.
     const float l_tot = pair_sum(l_run);
     const float inv = 1.f / l_tot;
+    uint16_t* obase = (uint16_t*)a.o + (long)tok0 * qs + (long)head * D;
+    const rsrc_t ro = make_rsrc(obase, (uint32_t)(((L - 1) * qs + D) * 2));
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -1057,8 +1073,6 @@ struct UnitFast {
             (u32x2){pack2(OpBF16{}, o0, o1), pack2(OpBF16{}, o2, o3)};
       }
     {
-      uint16_t* obase = (uint16_t*)a.o + (long)tok0 * qs + (long)head * D;
-      const rsrc_t ro = make_rsrc(obase, (uint32_t)(((L - 1) * qs + D) * 2));
 #pragma unroll
       for (int i = 0; i < 32 * QCH / 64; ++i) {
         const int flat = i * 64 + lane, r = flat / QCH, c = flat % QCH;
@@ -1085,7 +1099,7 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int
 // (batch, kv-head) groups divide evenly over the 8 XCDs, each XCD takes whole
 // groups so the query heads that share a K/V head share that XCD's L2.
 template <class C>
-__global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
@@ -1109,13 +1123,17 @@ __global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_dense
   const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
   const int head = kvh * G + hq;
-  run_unit<C>(a, b * a.T, a.T, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1, qst);
+  // A padded entry is its first L tokens: the unit sees only those keys and
+  // writes only those rows; units past them have nothing to do.
+  const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
+  if (qb * C::BM >= L) return;
+  run_unit<C>(a, b * a.T, L, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1, qst);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
 // schedule in order (most expensive first); each item expands to all heads.
 template <class C>
-__global__ __launch_bounds__(C::THREADS, CGR_WAVES_PER_SIMD) void attn_fwd_varlen_kernel(AttnArgs a) {
+__global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
@@ -1148,7 +1166,9 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
   const long row = tid / IPR;  // (token * KV + kv)
   if (row >= (long)a.B * a.T * a.KV) return;
   const int g = (int)(tid % IPR);
-  const int t = (int)((row / a.KV) % a.T);
+  const long tok = row / a.KV;
+  const int t = (int)(tok % a.T);
+  if (a.seqlens != nullptr && t >= a.seqlens[tok / a.T]) return;  // padding: never read
   const uint16_t* kp = (const uint16_t*)a.k + row * D;
   u32x4 w0[1] = {*(const u32x4*)(kp + 8 * g)}, w1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
   float x0[8], x1[8];
@@ -1186,8 +1206,10 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kBM = 32 * CGR_NW;  // query rows per unit (all instances)
-constexpr int kBN = CGR_BN;  // keys per tile (all instances)
+// Query rows per unit and keys per tile of the forward instances of a head_dim.
+constexpr int fwd_block_rows(int head_dim) { return head_dim == 256 ? 128 : 32 * CGR_NW; }
+constexpr int fwd_tile_keys(int head_dim) { return head_dim == 256 ? 32 : CGR_BN; }
+constexpr int kMinBM = 32 * CGR_NW < 128 ? 32 * CGR_NW : 128;  // smallest of them
 
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
@@ -1204,7 +1226,8 @@ hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, 
   if (causal && a.window > 0) { CGR_BY_STYLE(IO, QK, true, true) }                                   \
   else if (causal) { CGR_BY_STYLE(IO, QK, true, false) } else { CGR_BY_STYLE(IO, QK, false, false) }
   if (f32_io) {
-    CGR_BY_MASK(float, OpF32)
+    if constexpr (D == 256) return hipErrorInvalidValue;  // rejected by the host checks first
+    else { CGR_BY_MASK(float, OpF32) }
   } else if (qk_bf16) {
     CGR_BY_MASK(uint16_t, OpBF16)
   } else {

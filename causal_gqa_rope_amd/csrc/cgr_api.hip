@@ -75,10 +75,12 @@ cgr_status check_common(const void* q, const void* k, const void* v, const void*
                 n_kv_head);
   if (head_dim < 2 || head_dim % 2 != 0)
     return fail(CGR_ERR_INVALID_ARG, "head_dim (%d) must be even: RoPE rotates pairs", head_dim);
-  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
-    return fail(CGR_ERR_UNSUPPORTED, "head_dim %d is not one of 32, 64, 128", head_dim);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(CGR_ERR_UNSUPPORTED, "head_dim %d is not one of 32, 64, 128, 256", head_dim);
   if (dtype != CGR_F32 && dtype != CGR_BF16)
     return fail(CGR_ERR_UNSUPPORTED, "dtype %d is not CGR_F32 or CGR_BF16", (int)dtype);
+  if (head_dim == 256 && dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "head_dim 256 is supported for CGR_BF16 only");
   if (style != CGR_ROPE_INTERLEAVED && style != CGR_ROPE_HALF)
     return fail(CGR_ERR_UNSUPPORTED, "unknown rope style %d", (int)style);
   if (mask != CGR_MASK_NONE && mask != CGR_MASK_CAUSAL)
@@ -134,7 +136,8 @@ hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, 
   switch (head_dim) {
     case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s);
     case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s);
-    default: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s);
+    case 128: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s);
+    default: return cgr::launch_attn_d256(a, f32, qkb, sty, cau, varlen, grid, s);
   }
 }
 
@@ -142,7 +145,7 @@ hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, 
 // sum_s ceil(L_s / BM) <= total / BM + num_seqs. The workspace is sized for
 // blocks of 64 rows, which covers every block height the kernels use.
 long varlen_max_items(int num_seqs, int total_tokens) {
-  static_assert(cgr::kBM >= 64, "workspace bound assumes query blocks of >= 64 rows");
+  static_assert(cgr::kMinBM >= 64, "workspace bound assumes query blocks of >= 64 rows");
   return ((long)total_tokens + 63) / 64 + (long)num_seqs;
 }
 
@@ -216,8 +219,11 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
                                  int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
-                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
+                                 float softmax_scale, cgr_qk_operand qk_operand,
+                                 const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (seqlens != nullptr && !aligned(seqlens, 4))
+    return fail(CGR_ERR_ALIGNMENT, "seqlens must be 4-byte aligned");
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
@@ -231,7 +237,8 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
       return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
   }
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
-  const long grid = (long)((T + cgr::kBM - 1) / cgr::kBM) * B * n_head;
+  const int bm = cgr::fwd_block_rows(head_dim);
+  const long grid = (long)((T + bm - 1) / bm) * B * n_head;
   if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
                               softmax_scale);
@@ -239,6 +246,7 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
   a.T = T;
   a.total_tokens = B * T;
   a.window = window;
+  a.seqlens = seqlens;
   a.krot = use_ws ? workspace : nullptr;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
                                      (hipStream_t)stream);
@@ -292,7 +300,8 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   hipStream_t s = (hipStream_t)stream;
   int32_t* sched = (int32_t*)workspace;
   hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
-                                             cgr::kBM, cgr::kBN, mask == CGR_MASK_CAUSAL, sched,
+                                             cgr::fwd_block_rows(head_dim), cgr::fwd_tile_keys(head_dim),
+                                             mask == CGR_MASK_CAUSAL, sched,
                                              (int)max_items, s);
   if (e != hipSuccess) return hip_fail("schedule launch", e);
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
@@ -328,6 +337,7 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
   if (st != CGR_OK) return st;
+  if (head_dim == 256) return fail(CGR_ERR_UNSUPPORTED, "the backward is built for head_dim 32, 64, 128");
   if ((st = check_window(window, mask)) != CGR_OK) return st;
   if (!lse || !dout || !dq || !dk || !dv)
     return fail(CGR_ERR_INVALID_ARG, "lse, dout, dq, dk and dv must be non-null");
@@ -413,6 +423,7 @@ cgr_status cgr_gqa_rope_attn_decode(const void* q, const void* k_cache, const vo
   if (st != CGR_OK) return st;
   if (dtype != CGR_BF16)
     return fail(CGR_ERR_UNSUPPORTED, "decode takes bf16 tensors only (dtype %d)", (int)dtype);
+  if (head_dim == 256) return fail(CGR_ERR_UNSUPPORTED, "decode is built for head_dim 32, 64, 128");
   if ((st = check_window(window, CGR_MASK_CAUSAL)) != CGR_OK) return st;
   if (cache_batch_stride < 0 || cache_token_stride < head_dim || cache_head_stride < head_dim ||
       cache_batch_stride % 8 || cache_token_stride % 8 || cache_head_stride % 8)

@@ -114,6 +114,7 @@ CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head
  *   q: device [B, T, n_head, head_dim]      (dtype)
  *   k, v: device [B, T, n_kv_head, head_dim] (dtype)
  *   o: device [B, T, n_head, head_dim]      (dtype), written in full
+ *     (without seqlens)
  *   lse: device float32 [B, n_head, T], or NULL to skip it
  *   B, T, n_head, n_kv_head >= 1; n_head % n_kv_head == 0;
  *   head_dim in {32, 64, 128}.
@@ -123,6 +124,13 @@ CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head
  *   window: sliding window (see cgr_mask), 0 for none.
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
  *   qk_operand: see cgr_qk_operand (ignored for CGR_F32).
+ *   seqlens: NULL (every entry holds T tokens), or device int32 [B], 4-byte
+ *     aligned: entry b holds L_b valid tokens followed by T - L_b padding
+ *     tokens (right padding; a padding mask, one of the masks of the
+ *     Kohaku-TT feature list). Keys at or past L_b are hidden from every
+ *     query on top of `mask`, and rows at or past L_b of o and lse are left
+ *     as they were. The kernel clamps each L_b to [0, T]; no error is
+ *     reported for values outside it.
  *   workspace: NULL, or (bf16 I/O) device memory of at least
  *     cgr_attn_fwd_workspace_size(B, T, n_kv_head, head_dim) bytes, 16-byte
  *     aligned, scratch for this call only. With it the keys are rotated
@@ -134,8 +142,9 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const voi
                                  int B, int T, int n_head, int n_kv_head, int head_dim,
                                  cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
                                  int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
-                                 float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
-                                 size_t workspace_bytes, void* stream);
+                                 float softmax_scale, cgr_qk_operand qk_operand,
+                                 const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 
 /*
  * Bytes of device workspace cgr_gqa_rope_attn_fwd_varlen needs for a packed

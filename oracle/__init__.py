@@ -217,6 +217,30 @@ def attention_dense(q, k, v, *, causal: bool = True, base: float = 10000.0,
     return O, lse
 
 
+def attention_padded(q, k, v, seqlens, *, causal: bool = True, base: float = 10000.0,
+                     style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
+    """Dense batch with right padding (a padding mask; "masks" in the Kohaku-TT
+    feature list): entry b holds seqlens[b] tokens followed by padding. The
+    padding keys are hidden from every query, so the first seqlens[b] rows are
+    the attention of that prefix on its own, positions from 0; the padding rows
+    have no output and are NaN here. Returns O [B,T,H,d], lse [B,H,T]."""
+    _check_window(causal, window)
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, d = q.shape
+    _check_heads(H, k.shape[2])
+    lens = [int(x) for x in np.asarray(seqlens).reshape(-1)]
+    if len(lens) != B or any(n < 0 or n > T for n in lens):
+        raise ValueError("seqlens must hold B values in [0, T]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    O = np.full_like(q, np.nan)
+    lse = np.full((B, H, T), np.nan, dtype=np.float64)
+    for b, n in enumerate(lens):
+        if n > 0:
+            O[b, :n], lse[b, :, :n] = _one_sequence(q[b, :n], k[b, :n], v[b, :n], causal, scale, base, style,
+                                                    window)
+    return O, lse
+
+
 def attention_varlen(q, k, v, cu_seqlens, *, causal: bool = True, base: float = 10000.0,
                      style: str = "interleaved", scale: Optional[float] = None, window: int = 0):
     """Packed batch: q [total,H,d], k/v [total,KV,d], cu_seqlens [n+1].

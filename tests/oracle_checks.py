@@ -757,6 +757,54 @@ def check_rmsnorm_qkv_rope_structure():
     assert np.allclose(q2, q, atol=1e-13)
 
 
+def check_padding_mask():
+    """Right-padded dense batches: the valid rows against scalar brute force on
+    each entry's prefix and against torch's SDPA with an explicit key mask
+    (after float64 RoPE); the padding tokens' values change nothing; padding
+    rows are NaN (no output); full lengths give the dense result."""
+    import torch
+    rng = RNG(67)
+    B, T, H, KV, d = 4, 11, 4, 2, 8
+    lens = [11, 5, 1, 0]
+    for causal, style in ((True, "interleaved"), (False, "half")):
+        q = rng.standard_normal((B, T, H, d))
+        k = rng.standard_normal((B, T, KV, d))
+        v = rng.standard_normal((B, T, KV, d))
+        o, lse = oracle.attention_padded(q, k, v, lens, causal=causal, base=1e4, style=style)
+        for b, n in enumerate(lens):
+            assert np.isnan(o[b, n:]).all() and np.isnan(lse[b, :, n:]).all()
+            if n == 0:
+                continue
+            ob, lb = brute_force(q[b:b + 1, :n].tolist(), k[b:b + 1, :n].tolist(), v[b:b + 1, :n].tolist(),
+                                 causal, 1e4, style)
+            assert np.allclose(o[b, :n], ob[0], atol=1e-12, rtol=0)
+            assert np.allclose(lse[b, :, :n], lb[0], atol=1e-12, rtol=0)
+            # SDPA over all T keys with the padding keys (and the future) masked out.
+            pos = np.arange(T)
+            qr = torch.from_numpy(oracle.apply_rope(q[b], pos, 1e4, style)).permute(1, 0, 2)
+            kr = torch.from_numpy(oracle.apply_rope(k[b], pos, 1e4, style)).permute(1, 0, 2)
+            vv = torch.from_numpy(v[b]).permute(1, 0, 2)
+            kr = kr.repeat_interleave(H // KV, 0)
+            vv = vv.repeat_interleave(H // KV, 0)
+            allow = torch.arange(T)[None, :] < n
+            if causal:
+                allow = allow & (torch.arange(T)[None, :] <= torch.arange(T)[:, None])
+            ref = torch.nn.functional.scaled_dot_product_attention(qr, kr, vv, attn_mask=allow)
+            assert np.allclose(o[b, :n], ref.permute(1, 0, 2).numpy()[:n], atol=1e-12, rtol=0)
+        # The padding tokens carry no information.
+        q2, k2, v2 = q.copy(), k.copy(), v.copy()
+        for b, n in enumerate(lens):
+            q2[b, n:] = 1e3 * rng.standard_normal(q2[b, n:].shape)
+            k2[b, n:] = 1e3 * rng.standard_normal(k2[b, n:].shape)
+            v2[b, n:] = 1e3 * rng.standard_normal(v2[b, n:].shape)
+        o2, l2 = oracle.attention_padded(q2, k2, v2, lens, causal=causal, base=1e4, style=style)
+        assert np.array_equal(np.isnan(o2), np.isnan(o)) and np.allclose(o2, o, atol=0, rtol=0, equal_nan=True)
+        assert np.allclose(l2, lse, atol=0, rtol=0, equal_nan=True)
+        of, lf = oracle.attention_padded(q, k, v, [T] * B, causal=causal, base=1e4, style=style)
+        od, ld = oracle.attention_dense(q, k, v, causal=causal, base=1e4, style=style)
+        assert np.array_equal(of, od) and np.array_equal(lf, ld)
+
+
 ALL_CHECKS = [
     check_inv_freq_closed_forms,
     check_tables_closed_forms,
@@ -791,4 +839,5 @@ ALL_CHECKS = [
     check_window_backward,
     check_rmsnorm_closed_forms,
     check_rmsnorm_qkv_rope_structure,
+    check_padding_mask,
 ]

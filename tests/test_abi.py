@@ -69,13 +69,13 @@ PMIS = ctypes.c_void_p(0x10002)   # misaligned placeholder
 
 def dense(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
-             P=16, style=0, mask=1, window=0, scale=0.0, qk=0, ws=None, wsb=0)
+             P=16, style=0, mask=1, window=0, scale=0.0, qk=0, seqlens=None, ws=None, wsb=0)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"],
                                    a["KV"], a["D"], a["dtype"], a["cos"], a["sin"], a["P"],
-                                   a["style"], a["mask"], a["window"], a["scale"], a["qk"], a["ws"],
-                                   a["wsb"], None)
+                                   a["style"], a["mask"], a["window"], a["scale"], a["qk"], a["seqlens"],
+                                   a["ws"], a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -89,7 +89,8 @@ def dense(**kw):
     (dict(H=6, KV=4), 1, "divisible"),
     (dict(D=63), 1, "even"),
     (dict(D=96), 2, "not one of"),
-    (dict(D=256), 2, "not one of"),
+    (dict(D=512), 2, "not one of"),
+    (dict(D=256, dtype=0), 2, "256"),
     (dict(dtype=7), 2, "dtype"),
     (dict(style=3), 2, "style"),
     (dict(mask=2), 2, "mask"),
@@ -101,6 +102,7 @@ def dense(**kw):
     (dict(window=-1), 1, "window"),
     (dict(window=8, mask=0), 1, "CGR_MASK_CAUSAL"),
     (dict(ws=P, wsb=100), 4, "needs"),
+    (dict(seqlens=PMIS), 3, "seqlens"),
     (dict(ws=PMIS, wsb=1 << 20), 3, "aligned"),
 ])
 def test_dense_rejects_bad_arguments(kw, status, needle):
@@ -199,6 +201,7 @@ def backward(**kw):
     (dict(ws=ctypes.c_void_p(0x10010)), 3, "256-byte"),
     (dict(H=6, KV=4), 1, "divisible"),
     (dict(D=80), 2, "not one of"),
+    (dict(D=256), 2, "backward is built for"),
     (dict(T=0), 1, ">= 1"),
     (dict(P=15), 1, "positions"),
     (dict(window=4, mask=0), 1, "CGR_MASK_CAUSAL"),
@@ -247,6 +250,7 @@ def decode_call(**kw):
     (dict(wsb=300), 4, "needs"),
     (dict(H=6, KV=4), 1, "divisible"),
     (dict(D=48), 2, "not one of"),
+    (dict(D=256), 2, "decode is built for"),
     (dict(window=-2), 1, "window"),
 ])
 def test_decode_rejects_bad_arguments(kw, status, needle):

@@ -20,6 +20,10 @@ def test_oracle_pin(check):
 # Each mutant is one plausible mistake, planted by editing the oracle's source
 # text in memory: (what it breaks, text to find, replacement).
 MUTANTS = [
+    ("padding rows written as zeros", "O = np.full_like(q, np.nan)", "O = np.zeros_like(q)"),
+    ("length-1 entries dropped", "        if n > 0:\n            O[b, :n]", "        if n > 1:\n            O[b, :n]"),
+    ("padding keys visible", "_one_sequence(q[b, :n], k[b, :n], v[b, :n]",
+     "_one_sequence(q[b], k[b], v[b]"),
     ("exponent -i/d", "-2.0 * i / head_dim", "-1.0 * i / head_dim"),
     ("base^(+2i/d)", "-2.0 * i / head_dim", "2.0 * i / head_dim"),
     ("rotation sign", "y[..., 0::2] = a * c - b * s", "y[..., 0::2] = a * c + b * s"),

@@ -49,6 +49,8 @@ __all__ = [
     "decode_bytes",
     "QkvWorkload",
     "QKV_WORKLOADS",
+    "WIDE_WORKLOADS",
+    "padded_lengths",
     "make_qkv_inputs",
 ]
 
@@ -127,10 +129,22 @@ PARITY_EXTRAS = {
 }
 
 
+# head_dim 256: the long-context workload's width (n_head * head_dim = 4096)
+# in half as many, twice as wide heads (a parity case and its own bench line).
+WIDE_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("long_context_T8192_H16_KV8_d256", B=1, T=8192, n_head=16, n_kv_head=8, head_dim=256,
+                 base=500000.0, dtype="bf16", seed=5),
+    ]
+}
+
+
 def get(name: str) -> Workload:
-    if name in WORKLOADS:
-        return WORKLOADS[name]
-    return PARITY_EXTRAS[name]
+    for table in (WORKLOADS, PARITY_EXTRAS, WIDE_WORKLOADS):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 def varlen_lengths(w: Workload, gen: Optional[torch.Generator] = None) -> torch.Tensor:
@@ -183,6 +197,13 @@ def custom(name: str = "custom", **kw) -> Workload:
                     seed=0)
     defaults.update(kw)
     return Workload(name, **defaults)
+
+
+def padded_lengths(B: int, lo: int, hi: int, seed: int) -> list:
+    """Valid lengths of a right-padded dense batch: B draws, uniform in [lo, hi]
+    (inclusive), from a generator of its own seed."""
+    gen = torch.Generator("cpu").manual_seed(seed + 7919)
+    return [int(x) for x in torch.randint(lo, hi + 1, (B,), generator=gen)]
 
 
 def visible_pairs(L: int, causal: bool, window: int = 0) -> int:
