@@ -30,6 +30,8 @@ bounded sample of the same workload on this host's cores.
                                         sliding window of W keys; not the headline line)
   python bench.py --qkv                (one JSON line for the fused RMSNorm + q/k/v projection
                                         + RoPE step of the same model; not the headline line)
+  python bench.py --fp8                (the long-context forward with e4m3 q/k/v and e4m3 matrix
+                                        products, against the fp8 peak; not the headline line)
   python bench.py --wide               (the forward line at head_dim 256: T=8192, 16 query and
                                         8 K/V heads; not the headline line)
   python bench.py --padded             (the forward line on a right-padded batch of 4 x 8192
@@ -383,6 +385,80 @@ def decode(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
     print(json.dumps(result), flush=True)
 
 
+FP8_WORKLOAD = "fp8_long_context_T8192_H32_KV8_d128"
+FP8_METRIC = "causal GQA+RoPE attention fwd with fp8 (e4m3) operands, TFLOP/s on 1 MI355X; % of fp8 MFMA peak"
+FP8_PEAK_TFLOPS = 5000.0  # MI355X dense fp8 MFMA, published
+
+
+def fp8(torch, cgr, W, dev, steps: int, warmup: int) -> None:
+    """One step = one cgr_gqa_rope_attn_fwd_fp8 call (the key/value tile
+    preparation and the attention kernel) on the long-context workload with its
+    q, k, v quantized per tensor to e4m3; the RoPE tables are built once."""
+    w = W.get(FP8_WORKLOAD)
+    x = W.make_fp8_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.B, w.n_head, w.T), dtype=torch.float32, device=dev)
+    ws = torch.empty(cgr.cgr_attn_fwd_fp8_workspace_size(w.B, w.T, w.n_kv_head, w.head_dim), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        cgr.gqa_rope_attn_fwd_fp8(q, k, v, x["q_descale"], x["k_descale"], x["v_descale"], cos, sin, out=o, lse=lse,
+                                  workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        call()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True)
+    ms_step = wall * 1e3 / steps
+    call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    result = {
+        "metric": FP8_METRIC,
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": FP8_WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
+            "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
+            "io": "e4m3 q/k/v (per-tensor descales), bf16 o", "qk_operand": "e4m3", "pv_operand": "e4m3",
+            "accumulate": "f32", "step": "gqa_rope_attn_fwd_fp8", "flops_per_step": flops,
+            "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "the fp8 call: fp8_prep_kernel (keys rotated, tile images) + attn_fwd_fp8_kernel "
+                      "(head_dim 128, causal, interleaved); HIP events around the call",
+            "kernel_ms": round(call_ms, 5),
+        },
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+
+
 QKV_WORKLOAD = "qkv_long_context_T8192_C4096_H32_KV8_d128"
 QKV_METRIC = "fused RMSNorm + q/k/v projection + RoPE TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 
@@ -492,6 +568,8 @@ def main() -> int:
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
     ap.add_argument("--qkv", action="store_true")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the long-context forward with e4m3 q/k/v and e4m3 matrix products")
     ap.add_argument("--wide", action="store_true",
                     help="head_dim 256: B=1 T=8192 H=16 KV=8 (the long-context width in wider heads)")
     ap.add_argument("--padded", action="store_true",
@@ -524,6 +602,9 @@ def main() -> int:
         return 0
     if args.qkv:
         qkv(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)
+        return 0
+    if args.fp8:
+        fp8(torch, cgr, W, dev, args.steps, args.warmup)
         return 0
 
     w = W.get(WIDE_WORKLOAD if args.wide else WORKLOAD)

@@ -77,6 +77,8 @@ EXPORTED_SYMBOLS = (
     "cgr_gqa_rope_attn_decode",
     "cgr_rmsnorm_qkv_rope_workspace_size",
     "cgr_rmsnorm_qkv_rope",
+    "cgr_attn_fwd_fp8_workspace_size",
+    "cgr_gqa_rope_attn_fwd_fp8",
     "cgr_last_error",
     "cgr_version",
 )
@@ -120,6 +122,11 @@ def library() -> ctypes.CDLL:
     lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                           i32, i32, i32, i32, f32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd.restype = i32
+    lib.cgr_attn_fwd_fp8_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.cgr_attn_fwd_fp8_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_gqa_rope_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, vp, vp,
+                                              i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
+    lib.cgr_gqa_rope_attn_fwd_fp8.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -259,6 +266,54 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
             CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
             0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _ptr(seqlens), ws_ptr,
             ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def cgr_attn_fwd_fp8_workspace_size(B: int, T: int, n_kv_head: int, head_dim: int) -> int:
+    return int(library().cgr_attn_fwd_fp8_workspace_size(int(B), int(T), int(n_kv_head), int(head_dim)))
+
+
+def cgr_gqa_rope_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_descale: float, k_descale: float,
+                              v_descale: float, rope_cos: torch.Tensor, rope_sin: torch.Tensor, *,
+                              causal: bool = True, rope_style: str = "interleaved",
+                              softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None, return_lse: bool = True, workspace=None):
+    """fp8 forward: q [B,T,H,128], k/v [B,T,KV,128] as torch.float8_e4m3fn (the real inputs are the
+    codes times the descales) -> (o [B,T,H,128] bfloat16, lse [B,H,T] float32 or None)."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t, torch.float8_e4m3fn)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 4-D [B, T, heads, head_dim]")
+    B, T, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != T or k.shape[3] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    _dev_tensor("out", out, torch.bfloat16)
+    if out.shape != q.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "out must have q's shape")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev_tensor("lse", lse, torch.float32)
+        if tuple(lse.shape) != (B, H, T):
+            raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    if workspace is None:
+        workspace = torch.empty(max(16, int(lib.cgr_attn_fwd_fp8_workspace_size(B, T, k.shape[2], D))),
+                                dtype=torch.uint8, device=q.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_fwd_fp8(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, float(q_descale),
+            float(k_descale), float(v_descale), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+            _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            0.0 if softmax_scale is None else float(softmax_scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out, lse
 
 
@@ -525,6 +580,7 @@ def cgr_rmsnorm_qkv_rope(x: torch.Tensor, norm_weight: torch.Tensor, eps: float,
 
 rope_tables = cgr_rope_tables
 gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
+gqa_rope_attn_fwd_fp8 = cgr_gqa_rope_attn_fwd_fp8
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd
 rope_rotate = cgr_rope_rotate

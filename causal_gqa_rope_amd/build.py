@@ -32,6 +32,7 @@ SOURCES = [
     "attn_fwd_d64.hip",
     "attn_fwd_d128.hip",
     "attn_fwd_d256.hip",
+    "attn_fp8.hip",
     "attn_bwd_d32.hip",
     "attn_bwd_d64.hip",
     "attn_bwd_d128.hip",

@@ -12,6 +12,7 @@
 
 #include "attn_bwd_kernel.h"
 #include "attn_decode_kernel.h"
+#include "attn_fp8_kernel.h"
 #include "attn_fwd_kernel.h"
 #include "qkv_kernel.h"
 #include "cgr.h"
@@ -257,6 +258,84 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
 size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim) {
   if (B < 1 || T < 1 || n_kv_head < 1 || head_dim < 2) return 0;
   return (size_t)B * T * n_kv_head * head_dim * 2;
+}
+
+size_t cgr_attn_fwd_fp8_workspace_size(int B, int T, int n_kv_head, int head_dim) {
+  if (B < 1 || T < 1 || n_kv_head < 1 || head_dim != cgr::kFp8D) return 0;
+  const size_t nt = ((size_t)T + cgr::kFp8BN - 1) / cgr::kFp8BN;
+  return 2 * (size_t)B * n_kv_head * nt * cgr::kFp8Tile;
+}
+
+cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int T, int n_head, int n_kv_head, int head_dim,
+                                     float q_descale, float k_descale, float v_descale,
+                                     const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                                     cgr_rope_style style, cgr_mask mask, float softmax_scale,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o) return fail(CGR_ERR_INVALID_ARG, "q, k, v and o must be non-null");
+  if (!rope_cos || !rope_sin) return fail(CGR_ERR_INVALID_ARG, "rope_cos and rope_sin must be non-null");
+  if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
+  if (n_head < 1 || n_kv_head < 1)
+    return fail(CGR_ERR_INVALID_ARG, "n_head (%d) and n_kv_head (%d) must be >= 1", n_head, n_kv_head);
+  if (n_head % n_kv_head != 0)
+    return fail(CGR_ERR_INVALID_ARG, "n_head (%d) must be divisible by n_kv_head (%d)", n_head, n_kv_head);
+  if (head_dim != cgr::kFp8D)
+    return fail(CGR_ERR_UNSUPPORTED, "the fp8 forward is built for head_dim 128 (got %d)", head_dim);
+  if (style != CGR_ROPE_INTERLEAVED && style != CGR_ROPE_HALF)
+    return fail(CGR_ERR_UNSUPPORTED, "unknown rope style %d", (int)style);
+  if (mask != CGR_MASK_NONE && mask != CGR_MASK_CAUSAL) return fail(CGR_ERR_UNSUPPORTED, "unknown mask %d", (int)mask);
+  if (!std::isfinite(softmax_scale)) return fail(CGR_ERR_INVALID_ARG, "softmax_scale must be finite");
+  if (!(q_descale > 0.f) || !(k_descale > 0.f) || !(v_descale > 0.f) || !std::isfinite(q_descale) ||
+      !std::isfinite(k_descale) || !std::isfinite(v_descale))
+    return fail(CGR_ERR_INVALID_ARG, "the descales must be finite and > 0");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(rope_cos, 16) ||
+      !aligned(rope_sin, 16))
+    return fail(CGR_ERR_ALIGNMENT, "q, k, v, o, rope_cos and rope_sin must be 16-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(CGR_ERR_ALIGNMENT, "lse must be 4-byte aligned");
+  if (rope_max_pos < T)
+    return fail(CGR_ERR_INVALID_ARG, "rope tables cover %d positions, the call needs %d", rope_max_pos, T);
+  if ((long)(T + 256) * n_head * head_dim * 2 > (long)INT_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "a sequence of %d tokens x %d heads x %d exceeds 2 GiB", T, n_head, head_dim);
+  if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
+  const size_t need = cgr_attn_fwd_fp8_workspace_size(B, T, n_kv_head, head_dim);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
+  // score in log2 units = (sum of Q~ K~) * c / gamma with Q~ = rot(q8) gamma,
+  // K~ = rot(k8) / 2: c = q_descale * 2 k_descale * scale * log2(e) = f 2^e,
+  // f in [1/2, 1); gamma = f / 2 and the block scale 2^(e + 1).
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  const double c = (double)q_descale * 2.0 * (double)k_descale * scale * 1.4426950408889634074;
+  int e = 0;
+  const double f = std::frexp(c, &e);
+  const int E = e + 1;
+  if (E < -127 || E > 127) return fail(CGR_ERR_INVALID_ARG, "q_descale * k_descale * softmax_scale is out of range");
+  const long nt = ((long)T + cgr::kFp8BN - 1) / cgr::kFp8BN;
+  const long grid = ((long)T + cgr::kFp8BM - 1) / cgr::kFp8BM * B * n_head;
+  if (grid > INT_MAX || (long)B * n_kv_head * nt > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  cgr::Fp8Args a{};
+  a.q = (const uint8_t*)q;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.kimg = (uint8_t*)workspace;
+  a.vimg = (uint8_t*)workspace + need / 2;
+  a.o = o;
+  a.lse = lse;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.B = B;
+  a.T = T;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  a.NT = (int)nt;
+  a.qgamma = (float)(f * 0.5);
+  const uint32_t byte = (uint32_t)(127 + E);
+  a.kscale = (int)(byte * 0x01010101u);
+  a.vdescale = v_descale;
+  const hipError_t err = cgr::launch_attn_fp8(a, (int)style, mask == CGR_MASK_CAUSAL, (hipStream_t)stream);
+  if (err != hipSuccess) return hip_fail("fp8 attention launch", err);
+  return CGR_OK;
 }
 
 size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens) {

@@ -10,6 +10,7 @@ struct AttnArgs;
 struct BwdArgs;
 struct DecodeArgs;
 struct QkvArgs;
+struct Fp8Args;
 
 hipError_t launch_attn_d32(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                            bool varlen, int grid, hipStream_t stream);
@@ -19,6 +20,7 @@ hipError_t launch_attn_d128(const AttnArgs& a, int f32_io, int qk_bf16, int styl
                             bool varlen, int grid, hipStream_t stream);
 hipError_t launch_attn_d256(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
                             bool varlen, int grid, hipStream_t stream);
+hipError_t launch_attn_fp8(const Fp8Args& a, int style, int causal, hipStream_t stream);
 
 hipError_t launch_attn_bwd_d32(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);
 hipError_t launch_attn_bwd_d64(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);

@@ -147,6 +147,43 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const voi
                                  void* stream);
 
 /*
+ * Bytes of the workspace of cgr_gqa_rope_attn_fwd_fp8: the rotated keys and
+ * the transposed values as 64-key tile images, 2 * B * n_kv_head *
+ * ceil(T / 64) * 64 * head_dim. Returns 0 for invalid sizes (head_dim must be
+ * 128).
+ */
+CGR_API size_t cgr_attn_fwd_fp8_workspace_size(int B, int T, int n_kv_head, int head_dim);
+
+/*
+ * Dense batch forward with fp8 operands ("fp8 operands" of the masks/GQA/
+ * packed-batch flash attention listed in the Kohaku-TT feature list; the
+ * attention itself as in "Attention from Scratch", "Attention, the math").
+ *   q: device [B, T, n_head, 128], k, v: device [B, T, n_kv_head, 128], all
+ *     OCP fp8 e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
+ *     0x7f / 0xff are NaN; largest finite 448). The real inputs are the
+ *     codes times q_descale, k_descale, v_descale (finite, > 0).
+ *   o: device bf16 [B, T, n_head, 128], written in full.
+ *   lse: device float32 [B, n_head, T], or NULL.
+ *   head_dim must be 128; mask CGR_MASK_CAUSAL or CGR_MASK_NONE; RoPE tables
+ *     as for cgr_gqa_rope_attn_fwd (rope_max_pos >= T).
+ *   workspace: device memory of cgr_attn_fwd_fp8_workspace_size(...) bytes,
+ *     16-byte aligned, scratch for this call only (required).
+ * Arithmetic: q and k are rotated in f32 and rounded back to e4m3 (q scaled
+ * into [1/4, 1/2) of its range, k halved, so no rotated value overflows);
+ * both products run on the e4m3 matrix cores with f32 accumulation, the
+ * probabilities rounded to e4m3. Expect errors of a few 1e-2 relative to the
+ * exact attention of the dequantized inputs (about 10x those of the bf16
+ * path). If the softmax scale times the descales is outside 2^-127 .. 2^127
+ * the call returns CGR_ERR_INVALID_ARG.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int T, int n_head, int n_kv_head, int head_dim,
+                                     float q_descale, float k_descale, float v_descale,
+                                     const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                                     cgr_rope_style style, cgr_mask mask, float softmax_scale,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace cgr_gqa_rope_attn_fwd_varlen needs for a packed
  * batch of num_seqs sequences holding total_tokens tokens. Returns 0 for
  * invalid sizes (num_seqs < 1 or total_tokens < 0).

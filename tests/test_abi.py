@@ -111,6 +111,47 @@ def test_dense_rejects_bad_arguments(kw, status, needle):
     assert needle in msg
 
 
+def fp8(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=128, qd=0.01, kd=0.01, vd=0.01, cos=P, sin=P,
+             P=16, style=0, mask=1, scale=0.0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"], a["KV"],
+                                       a["D"], a["qd"], a["kd"], a["vd"], a["cos"], a["sin"], a["P"], a["style"],
+                                       a["mask"], a["scale"], a["ws"], a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(q=None), 1, "non-null"),
+    (dict(T=0), 1, ">= 1"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(D=64), 2, "head_dim 128"),
+    (dict(qd=0.0), 1, "descales"),
+    (dict(vd=float("inf")), 1, "descales"),
+    (dict(style=5), 2, "style"),
+    (dict(mask=3), 2, "mask"),
+    (dict(k=PMIS), 3, "aligned"),
+    (dict(P=15), 1, "positions"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(wsb=100), 4, "needs"),
+    (dict(qd=1e30, kd=1e30), 1, "out of range"),
+])
+def test_fp8_rejects_bad_arguments(kw, status, needle):
+    st, msg = fp8(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
+def test_fp8_workspace_size():
+    lib = cgr.library()
+    assert lib.cgr_attn_fwd_fp8_workspace_size(1, 16, 2, 64) == 0
+    assert lib.cgr_attn_fwd_fp8_workspace_size(0, 16, 2, 128) == 0
+    # two 8 KiB tile images (64 keys x 128 bytes) per (entry, K/V head, tile)
+    assert lib.cgr_attn_fwd_fp8_workspace_size(2, 100, 3, 128) == 2 * 2 * 3 * 2 * 8192
+
+
 def varlen(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, cu=P, nseq=2, total=100, maxlen=60, H=4, KV=1, D=128,
              dtype=1, cos=P, sin=P, P=60, style=0, mask=1, window=0, scale=0.0, qk=0, ws=P, wsb=1 << 20)

@@ -50,6 +50,9 @@ __all__ = [
     "QkvWorkload",
     "QKV_WORKLOADS",
     "WIDE_WORKLOADS",
+    "FP8_WORKLOADS",
+    "quantize_fp8",
+    "make_fp8_inputs",
     "padded_lengths",
     "make_qkv_inputs",
 ]
@@ -129,6 +132,16 @@ PARITY_EXTRAS = {
 }
 
 
+# fp8 operands: the long-context workload with its q, k, v quantized per
+# tensor to e4m3 (make_fp8_inputs); a bench line against the fp8 peak.
+FP8_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("fp8_long_context_T8192_H32_KV8_d128", B=1, T=8192, n_head=32, n_kv_head=8, head_dim=128,
+                 base=500000.0, dtype="f32", seed=3),
+    ]
+}
+
 # head_dim 256: the long-context workload's width (n_head * head_dim = 4096)
 # in half as many, twice as wide heads (a parity case and its own bench line).
 WIDE_WORKLOADS = {
@@ -141,7 +154,7 @@ WIDE_WORKLOADS = {
 
 
 def get(name: str) -> Workload:
-    for table in (WORKLOADS, PARITY_EXTRAS, WIDE_WORKLOADS):
+    for table in (WORKLOADS, PARITY_EXTRAS, WIDE_WORKLOADS, FP8_WORKLOADS):
         if name in table:
             return table[name]
     raise KeyError(name)
@@ -188,6 +201,30 @@ def make_inputs(w: Workload) -> dict:
         k = torch.where(sel, k * w.outlier_factor, k)
     dt = _io_dtype(w.dtype)
     out.update(q=q.to(dt), k=k.to(dt), v=v.to(dt))
+    return out
+
+
+def quantize_fp8(x: torch.Tensor):
+    """Per-tensor e4m3 quantization of a float tensor: descale = amax / 448
+    (rounded to float32), codes = x / descale rounded to the nearest e4m3
+    (torch's conversion). Returns (codes as torch.float8_e4m3fn, descale)."""
+    amax = float(x.abs().max())
+    descale = float(torch.tensor(amax / 448.0 if amax > 0 else 1.0, dtype=torch.float32))
+    return (x.to(torch.float32) / descale).to(torch.float8_e4m3fn), descale
+
+
+def make_fp8_inputs(w: Workload) -> dict:
+    """The workload's q, k, v drawn as for make_inputs (float32, same seed and
+    order), then quantized per tensor to e4m3 (quantize_fp8). Returns q, k, v
+    (torch.float8_e4m3fn, CPU), their descales, and the dequantized float64
+    numpy arrays q64, k64, v64 that the exact attention is taken of."""
+    x = make_inputs(dataclasses.replace(w, dtype="f32"))
+    out = {}
+    for n in ("q", "k", "v"):
+        codes, ds = quantize_fp8(x[n])
+        out[n] = codes
+        out[n + "_descale"] = ds
+        out[n + "64"] = codes.to(torch.float64).numpy() * ds
     return out
 
 
