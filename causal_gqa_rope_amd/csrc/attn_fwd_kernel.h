@@ -1020,11 +1020,6 @@ struct UnitFast {
                                char* kj1, char* vj, char* vj1) {
           load_v((j + 1) * BN, vj1, vw);
           load_k((j + 2) * BN, kw, kc, ksn);
-          // Waves w and w+4 share a SIMD. At equal priority the older one wins
-          // every issue tie, finishes the tile first and then idles at the
-          // barrier while the younger one runs alone; raising the younger
-          // wave's priority for the tile evens the two out.
-          if (wave >= NW / 2) __builtin_amdgcn_s_setprio(1);
           // Keep the global loads at the top of the block, a whole block ahead
           // of their use (left alone, the scheduler sinks them next to it).
           __builtin_amdgcn_sched_barrier(0);
@@ -1033,7 +1028,6 @@ struct UnitFast {
           store_k((j + 2) * BN, kj, kw, kc, ksn, vw);
           wait_vmem();
           __syncthreads();
-          __builtin_amdgcn_s_setprio(0);
         };
         int j = 0;
         if (wave_has_rows) {

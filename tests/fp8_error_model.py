@@ -11,7 +11,7 @@ e4m3 operands alone move the result:
     of two; the row reference m is the row's max over the first 64 keys;
   * p = 2^(s - m) rounded to e4m3 for the P.V product, the row sum over the
     unrounded p; O = (P V codes) * v_descale / row sum;
-  * rows go in blocks of 256 (the library's work unit): if some p of a
+  * rows go in blocks of 128 (the library's work unit): if some p of a
     block would leave e4m3's range (above 464, which rounds to NaN), the block
     is redone as the classic online softmax over 64-key tiles: the running
     max is updated per tile, p = 2^(s - running max) is rounded, and O and
@@ -32,7 +32,7 @@ def e4m3(x) -> np.ndarray:
     return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
 
 
-def model_forward(q8, k8, v8, q_ds, k_ds, v_ds, *, base, style="interleaved", causal=True, tile=64, block=256):
+def model_forward(q8, k8, v8, q_ds, k_ds, v_ds, *, base, style="interleaved", causal=True, tile=64, block=128):
     """q8 [T,H,d], k8/v8 [T,KV,d] float64 e4m3 code values -> O [T,H,d], lse [H,T]."""
     T, H, d = q8.shape
     G = H // k8.shape[1]
