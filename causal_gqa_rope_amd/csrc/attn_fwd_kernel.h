@@ -130,6 +130,9 @@ struct Cfg {
   // global->LDS loads.
   static constexpr int V_STRIDE = F32 ? D * 4 + 16 : 2 * D;
   static constexpr int K_BYTES = BN * K_STRIDE;
+  // A tile image of once-rotated keys: BN unpadded rows of 2*D bytes with
+  // XOR-swizzled 16-byte chunks (tswz), copied into the K stage as is.
+  static constexpr int K_IMG = BN * 2 * D;
   static constexpr int V_BYTES = BN * V_STRIDE;
   static constexpr int STAGE = K_BYTES + V_BYTES;
   static constexpr int SMEM = 2 * STAGE;
@@ -569,10 +572,16 @@ struct UnitFast {
     const int G = a.H / a.KV, kvh = head / G;
     const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
     const uint16_t* qbase = (const uint16_t*)a.q + (long)tok0 * qs + (long)head * D;
-    const uint16_t* kbase = (const uint16_t*)(C::KPRE ? a.krot : a.k) + (long)tok0 * ks + (long)kvh * D;
+    const uint16_t* kbase = (const uint16_t*)a.k + (long)tok0 * ks + (long)kvh * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (long)tok0 * ks + (long)kvh * D;
     const rsrc_t rq = make_rsrc(qbase, (uint32_t)(((L - 1) * qs + D) * 2));
-    const rsrc_t rk = make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
+    // Once-rotated keys (dense batches): tile images of K_IMG bytes per
+    // (entry, K/V head); one unit's images are one range.
+    const int n_img = (a.T + BN - 1) / BN;
+    const rsrc_t rk = C::KPRE
+        ? make_rsrc((const char*)a.krot + ((long)(tok0 / a.T) * a.KV + kvh) * n_img * C::K_IMG,
+                    (uint32_t)(n_img * C::K_IMG))
+        : make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
     const rsrc_t rv = make_rsrc(vbase, (uint32_t)(((L - 1) * ks + D) * 2));
     const rsrc_t rc = make_rsrc(a.rope_cos, (uint32_t)(L * (D / 2) * 4));
     const rsrc_t rs = make_rsrc(a.rope_sin, (uint32_t)(L * (D / 2) * 4));
@@ -724,7 +733,20 @@ struct UnitFast {
           buf_load16_lds(rv, vs + blk * 1024, (blk & 1) ? v_vo_odd : v_vo, (kt0 + blk * VROWS) * ks * 2);
       }
     };
-    auto load_k = [&](int kt0, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
+    // K of the tile at kt0: rotated in registers (store_k writes it to LDS
+    // later), or, once-rotated, its tile image straight into LDS at kdst.
+    auto load_k = [&](int kt0, char* kdst, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2], f32x4 (&ksn)[KI][2]) {
+      if constexpr (C::KPRE) {
+        constexpr int NBLK = C::K_IMG / 1024;
+        static_assert(C::K_IMG % 1024 == 0, "whole 1-KiB loads");
+        const int soff = (kt0 / BN) * C::K_IMG;
+#pragma unroll
+        for (int u = 0; u < (NBLK + NW - 1) / NW; ++u) {
+          const int blk = wave + u * NW;
+          if (NBLK % NW == 0 || blk < NBLK) buf_load16_lds(rk, kdst + blk * 1024, lane * 16, soff + blk * 1024);
+        }
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < KI; ++u) {
         if (has_k(u)) {
@@ -741,10 +763,10 @@ struct UnitFast {
         }
       }
     };
-    auto issue_loads = [&](int kt0, char* vs, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
+    auto issue_loads = [&](int kt0, char* ks_, char* vs, u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
                            f32x4 (&ksn)[KI][2], u32x4 (&vw)[VU_REG]) {
       load_v(kt0, vs, vw);
-      load_k(kt0, kw, kc, ksn);
+      load_k(kt0, ks_, kw, kc, ksn);
     };
     // Rotate K at the key positions and write it to LDS.
     auto store_k = [&](int kt0, char* kst, const u32x4 (&kw)[KI][2], f32x4 (&kc)[KI][2],
@@ -754,8 +776,7 @@ struct UnitFast {
         if (has_k(u)) {
           char* dst = kst + k_lds + u * RPU * C::K_STRIDE;
           if constexpr (C::KPRE) {
-            *(u32x4*)dst = kw[u][0];
-            *(u32x4*)(dst + D) = kw[u][1];
+            // loaded straight into LDS by load_k
           } else {
             float x0[8], x1[8];
             const u32x4 w0[1] = {kw[u][0]}, w1[1] = {kw[u][1]};
@@ -771,6 +792,13 @@ struct UnitFast {
 
     // Lane offsets of the K fragment reads and of the transposing V reads.
     const int k_rd = l32 * C::K_STRIDE + hh * 16;
+    // Swizzled images: chunk 2s + hh of row kb*32 + l32 (the swizzle repeats
+    // every 16 rows, so it depends on l32 only).
+    int k_rds[C::KPRE ? C::KSTEPS : 1];
+    if constexpr (C::KPRE) {
+#pragma unroll
+      for (int s = 0; s < C::KSTEPS; ++s) k_rds[s] = l32 * 2 * D + 16 * ((2 * s + hh) ^ tswz<D>(l32));
+    }
     const int gi = lane >> 4, li = lane & 15;
     const int vx = D >= 128 ? (li >> 2) : (D == 64 ? (((4 * hh + (li >> 2)) >> 1) & 1) : 0);
     const int v_lane = (4 * hh + (li >> 2)) * (2 * D) + 16 * (2 * (gi & 1) + ((li & 3) >> 1)) +
@@ -792,14 +820,14 @@ struct UnitFast {
       for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
       l_run = 0.f;
       __syncthreads();  // earlier users of this workgroup's LDS are done
-      issue_loads(j * BN, vst, kw, kc, ksn, vw);
+      issue_loads(j * BN, kst, vst, kw, kc, ksn, vw);
       store_k(j * BN, kst, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
     };
     // Start loading tile j+1 (every wave, every tile).
-    auto prefetch = [&](int j, char* vnext) {
-      if (j + 1 < n_tiles) issue_loads((j + 1) * BN, vnext, kw, kc, ksn, vw);
+    auto prefetch = [&](int j, char* knext, char* vnext) {
+      if (j + 1 < n_tiles) issue_loads((j + 1) * BN, knext, vnext, kw, kc, ksn, vw);
     };
     // S^T = K Q^T + cinit (log2 units, scale folded in).
     auto scores = [&](const char* Ks, f32x16 (&sacc)[C::NKB], const f32x16& cinit) {
@@ -808,7 +836,10 @@ struct UnitFast {
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) {
           Frag<QK> kf;
-          kf.v = *(const u32x4*)(Ks + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
+          if constexpr (C::KPRE)
+            kf.v = *(const u32x4*)(Ks + k_rds[s] + kb * 32 * 2 * D);
+          else
+            kf.v = *(const u32x4*)(Ks + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
           sacc[kb] = mma32(kf, qf[s], s == 0 ? cinit : sacc[kb]);
         }
     };
@@ -931,7 +962,7 @@ struct UnitFast {
       float m_run = -INFINITY;
       start(jb, stage_of(jb, ks0, ks1), stage_of(jb, vs0, vs1));
       for (int j = jb; j < n_tiles; ++j) {
-        prefetch(j, stage_of(j + 1, vs0, vs1));
+        prefetch(j, stage_of(j + 1, ks0, ks1), stage_of(j + 1, vs0, vs1));
         if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last) &&
             (!WIN || j * BN + BN - 1 >= qw0 - W + 1)) {
           f32x16 sacc[C::NKB];
@@ -967,11 +998,17 @@ struct UnitFast {
   #pragma unroll
         for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
         l_run = 0.f;
-        load_k(0, kw, kc, ksn);
         u32x4 kw1[KI][2];
         f32x4 kc1[KI][2], ksn1[KI][2];
-        if (n_tiles > 1) load_k(BN, kw1, kc1, ksn1);
+        if constexpr (!C::KPRE) {
+          load_k(0, ks0, kw, kc, ksn);
+          if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
+        }
         __syncthreads();  // earlier users of this workgroup's LDS are done
+        if constexpr (C::KPRE) {
+          load_k(0, ks0, kw, kc, ksn);
+          if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
+        }
         load_v(0, vs0, vw);
         stage_q();
         store_k(0, ks0, kw, kc, ksn, vw);
@@ -996,7 +1033,7 @@ struct UnitFast {
           constexpr bool MASK = decltype(mask_tag)::value;
           // Loads for V_{j+1} (LDS, stage (j+1)&1) and K_{j+2} (registers).
           if (j + 1 < n_tiles) load_v((j + 1) * BN, vj1, vw);
-          if (j + 2 < n_tiles) load_k((j + 2) * BN, kw, kc, ksn);
+          if (j + 2 < n_tiles) load_k((j + 2) * BN, kj, kw, kc, ksn);
           f32x16 s_next[C::NKB];
           if (j + 1 < n_tiles && active(j + 1)) scores(kj1, s_next, negm);
           if (active(j)) {
@@ -1019,7 +1056,7 @@ struct UnitFast {
         auto iter_steady = [&](int j, f32x16 (&s_in)[C::NKB], f32x16 (&s_out)[C::NKB], char* kj,
                                char* kj1, char* vj, char* vj1) {
           load_v((j + 1) * BN, vj1, vw);
-          load_k((j + 2) * BN, kw, kc, ksn);
+          load_k((j + 2) * BN, kj, kw, kc, ksn);
           // Keep the global loads at the top of the block, a whole block ahead
           // of their use (left alone, the scheduler sinks them next to it).
           __builtin_amdgcn_sched_barrier(0);
@@ -1150,30 +1187,42 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
 }
 
 // K rotated once at its positions (token t of a dense batch entry is at
-// position t mod T) and rounded to the Q.K^T operand type, for the tile loops
-// to copy. Item = (row, group g < D/16) carrying the chunk pair (g, g + D/16),
-// as in the K loader.
-template <int D, typename QK, int STYLE>
+// position t) and rounded to the Q.K^T operand type, written as tile images:
+// per (entry, K/V head, tile of BN keys), the tile exactly as the unit's LDS
+// stage will hold it (rows of 2*D bytes, 16-byte chunks swizzled by tswz), so
+// the unit copies each tile into LDS with 1-KiB direct loads. Keys past the
+// entry's length are zeros. Item = (image row, group g < D/16) carrying the
+// chunk pair (g, g + D/16), as in the K loader.
+template <class C>
 __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
-  constexpr int IPR = D / 16;
+  constexpr int D = C::D, BN = C::BN, IPR = D / 16;
+  const int n_img = (a.T + BN - 1) / BN;
   const long tid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long row = tid / IPR;  // (token * KV + kv)
-  if (row >= (long)a.B * a.T * a.KV) return;
-  const int g = (int)(tid % IPR);
-  const long tok = row / a.KV;
-  const int t = (int)(tok % a.T);
-  if (a.seqlens != nullptr && t >= a.seqlens[tok / a.T]) return;  // padding: never read
-  const uint16_t* kp = (const uint16_t*)a.k + row * D;
-  u32x4 w0[1] = {*(const u32x4*)(kp + 8 * g)}, w1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
-  float x0[8], x1[8];
-  raw_to_f32<uint16_t>(w0, x0);
-  raw_to_f32<uint16_t>(w1, x1);
-  f32x4 c[2], s[2];
-  load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
-  rope_pair<STYLE>(x0, x1, c, s);
-  uint16_t* out = (uint16_t*)a.krot + row * D;
-  *(u32x4*)(out + 8 * g) = to_frag<QK>(x0).v;
-  *(u32x4*)(out + 8 * g + D / 2) = to_frag<QK>(x1).v;
+  const long item = tid / IPR;
+  if (item >= (long)a.B * a.KV * n_img * BN) return;
+  const int g = (int)(tid % IPR), r = (int)(item % BN);
+  const long img = item / BN;  // (b * KV + kv) * n_img + tile
+  const int tile = (int)(img % n_img);
+  const long bk = img / n_img;
+  const int kv = (int)(bk % a.KV), b = (int)(bk / a.KV);
+  const int t = tile * BN + r;
+  const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
+  u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+  if (t < L) {
+    const uint16_t* kp = (const uint16_t*)a.k + (((long)b * a.T + t) * a.KV + kv) * D;
+    u32x4 i0[1] = {*(const u32x4*)(kp + 8 * g)}, i1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
+    float x0[8], x1[8];
+    raw_to_f32<uint16_t>(i0, x0);
+    raw_to_f32<uint16_t>(i1, x1);
+    f32x4 c[2], s[2];
+    load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
+    rope_pair<C::STYLE>(x0, x1, c, s);
+    w0 = to_frag<typename C::QK>(x0).v;
+    w1 = to_frag<typename C::QK>(x1).v;
+  }
+  char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
+  *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
+  *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
 }
 
 // Launch one instance. Host-side, after the arguments are validated.
@@ -1191,9 +1240,8 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
 // Dense batch with the K rotation done once up front (a.krot set).
 template <class C>
 hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
-  const long items = (long)a.B * a.T * a.KV * (C::D / 16);
-  hipLaunchKernelGGL((krot_kernel<C::D, typename C::QK, C::STYLE>), dim3((unsigned)((items + 255) / 256)),
-                     dim3(256), 0, stream, a);
+  const long items = (long)a.B * a.KV * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
+  hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
@@ -1204,6 +1252,8 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
 constexpr int fwd_block_rows(int head_dim) { return head_dim == 256 ? 128 : 32 * CGR_NW; }
 constexpr int fwd_tile_keys(int head_dim) { return head_dim == 256 ? 32 : CGR_BN; }
 constexpr int kMinBM = 32 * CGR_NW < 128 ? 32 * CGR_NW : 128;  // smallest of them
+// Bytes of one K tile image of the once-rotated keys (16-bit operands).
+constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_dim) * 2 * head_dim; }
 
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,

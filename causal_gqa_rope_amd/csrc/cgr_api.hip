@@ -256,8 +256,10 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
 }
 
 size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim) {
-  if (B < 1 || T < 1 || n_kv_head < 1 || head_dim < 2) return 0;
-  return (size_t)B * T * n_kv_head * head_dim * 2;
+  if (B < 1 || T < 1 || n_kv_head < 1) return 0;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return 0;
+  const int bn = cgr::fwd_tile_keys(head_dim);
+  return (size_t)B * n_kv_head * ((T + bn - 1) / bn) * cgr::fwd_kimg_bytes(head_dim);
 }
 
 size_t cgr_attn_fwd_fp8_workspace_size(int B, int T, int n_kv_head, int head_dim) {

@@ -8,30 +8,6 @@
 
 namespace cgr {
 
-// ---------------------------------------------------------------------------
-// Operand tiles in LDS: rows of 2*D bytes (16-bit elements), 16-byte chunks
-// XOR-swizzled per row. The swizzle serves both ways the tiles are read:
-//   * row reads (operand row m = lane%32, 16 bytes): the 16 lanes that share a
-//     bank cycle read 16 consecutive rows at one logical chunk, which the
-//     swizzle spreads over all 16 bank slots of a 256-byte line;
-//   * transposing reads (ds_read_b64_tr_b16): a half-wave reads 4 consecutive
-//     rows x 64 bytes, which the swizzle puts on 4 distinct 64-byte windows.
-// Tiles are written by direct global->LDS loads (16 bytes per lane, lane order),
-// so the swizzle is applied to the global address each lane fetches.
-template <int D>
-__device__ __forceinline__ int tswz(int r) {
-  if constexpr (D == 128)
-    return (((r >> 1) & 1) << 3) | ((r & 1) << 2) | (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
-  else if constexpr (D == 64)
-    return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1);
-  else
-    return (r >> 2) & 3;
-}
-template <int D>
-__device__ __forceinline__ int toff(int r, int c) {
-  return r * 2 * D + 16 * (c ^ tswz<D>(r));
-}
-
 // Waits until at most n of this wave's vector-memory operations are
 // outstanding (n < 64), then keeps later code from moving above the wait.
 template <int N>

@@ -104,8 +104,10 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
 
 /*
  * Bytes of the optional workspace of cgr_gqa_rope_attn_fwd (bf16 I/O): the
- * rotated keys in the Q.K^T operand type, B * T * n_kv_head * head_dim * 2.
- * Returns 0 for invalid sizes.
+ * rotated keys in the Q.K^T operand type as tiles of BN keys (BN = 64, 32 for
+ * head_dim 256) in the layout the kernel's LDS holds them:
+ * B * n_kv_head * ceil(T / BN) * BN * head_dim * 2. Returns 0 for invalid
+ * sizes.
  */
 CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim);
 

@@ -50,7 +50,11 @@ def test_version_and_workspace_size():
     assert cgr.cgr_version() == 10000
     lib = cgr.library()
     assert lib.cgr_attn_fwd_workspace_size(0, 16, 2, 64) == 0
-    assert lib.cgr_attn_fwd_workspace_size(2, 100, 8, 128) == 2 * 100 * 8 * 128 * 2
+    # whole tiles of 64 keys (32 for head_dim 256), 2 bytes per element
+    assert lib.cgr_attn_fwd_workspace_size(2, 100, 8, 128) == 2 * 8 * 2 * 64 * 128 * 2
+    assert lib.cgr_attn_fwd_workspace_size(1, 64, 1, 32) == 64 * 32 * 2
+    assert lib.cgr_attn_fwd_workspace_size(1, 33, 2, 256) == 2 * 2 * 32 * 256 * 2
+    assert lib.cgr_attn_fwd_workspace_size(1, 16, 2, 96) == 0
     assert lib.cgr_attn_fwd_varlen_workspace_size(0, 10) == 0
     assert lib.cgr_attn_fwd_varlen_workspace_size(1, -1) == 0
     small = lib.cgr_attn_fwd_varlen_workspace_size(1, 1)
