@@ -63,6 +63,8 @@ struct AttnArgs {
   int B, T, H, KV;
   int total_tokens;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
+  int hp;        // query heads per unit (divides NW and the group): wave w takes
+                 // head head0 + w % hp and rows 32 (w / hp) .. of the unit's block
   float qscale;  // softmax_scale * log2(e), folded into Q
 };
 
@@ -344,24 +346,28 @@ struct Unit {
     return f;
   }
 
-  // One work unit: query rows qb*BM .. of a sequence of L tokens starting at
-  // token tok0, query head `head`. lse_base indexes lse[] for local row 0.
-  static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                             long lse_base, CGR_LDS_PARAMS) {
+  // One work unit: query rows qb*bm .. (bm = 32 NW / hp) of a sequence of L
+  // tokens starting at token tok0, query heads head0 .. head0 + hp - 1 of one
+  // K/V group. lse[] of local row 0 of head h is at lse_b + h * lse_h.
+  static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head0,
+                                             long lse_b, long lse_h, CGR_LDS_PARAMS) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
+    const int hp = a.hp, bm = 32 * C::NW / hp;
+    const int head = head0 + wave % hp;
+    const long lse_base = lse_b + (long)head * lse_h;
     const int G = a.H / a.KV, kvh = head / G;
     const long qs = (long)a.H * D, ks = (long)a.KV * D;
     const IO* qp = (const IO*)a.q + (long)tok0 * qs + (long)head * D;
     const IO* kp = (const IO*)a.k + (long)tok0 * ks + (long)kvh * D;
     const IO* vp = (const IO*)a.v + (long)tok0 * ks + (long)kvh * D;
 
-    const int q0 = qb * C::BM;
-    const int qw0 = q0 + wave * 32;
+    const int q0 = qb * bm;
+    const int qw0 = q0 + (wave / hp) * 32;
     const int my_q = qw0 + l32;
     const bool wave_has_rows = qw0 < L;
     const int wave_last = min(qw0 + 31, L - 1);
-    const int q_hi = min(q0 + C::BM, L);
+    const int q_hi = min(q0 + bm, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
     // Sliding window: the unit starts at the tile holding its first row's
     // earliest visible key.
@@ -562,12 +568,17 @@ struct UnitFast {
     else return 0;
   }
 
-  static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                             long lse_base, CGR_LDS_PARAMS) {
+  static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head0,
+                                             long lse_b, long lse_h, CGR_LDS_PARAMS) {
     // `wave` is the same in every lane: keeping it scalar makes every wave-level
     // decision below (active tiles, masking, V blocks) a scalar branch.
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // The unit's waves split over hp query heads of one K/V group x 32-row
+    // blocks: each K/V tile in LDS serves all of them.
+    const int hp = a.hp, bm = 32 * NW / hp;
+    const int head = head0 + wave % hp, wrow = wave / hp;
+    const long lse_base = lse_b + (long)head * lse_h;
     const int l32 = lane & 31, hh = lane >> 5;
     const int G = a.H / a.KV, kvh = head / G;
     const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
@@ -586,12 +597,12 @@ struct UnitFast {
     const rsrc_t rc = make_rsrc(a.rope_cos, (uint32_t)(L * (D / 2) * 4));
     const rsrc_t rs = make_rsrc(a.rope_sin, (uint32_t)(L * (D / 2) * 4));
 
-    const int q0 = qb * C::BM;
-    const int qw0 = q0 + wave * 32;
+    const int q0 = qb * bm;
+    const int qw0 = q0 + wrow * 32;
     const int my_q = qw0 + l32;
     const bool wave_has_rows = qw0 < L;
     const int wave_last = min(qw0 + 31, L - 1);
-    const int q_hi = min(q0 + C::BM, L);
+    const int q_hi = min(q0 + bm, L);
     const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
     // Sliding window: such units run the rescaling loop below (the fast
     // path's reference comes from tile 0, which a window may hide), from the
@@ -1117,48 +1128,50 @@ struct UnitFast {
 };
 
 template <class C>
-__device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head,
-                                         long lse_base, CGR_LDS_PARAMS) {
+__device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head0, long lse_b,
+                                         long lse_h, CGR_LDS_PARAMS) {
   if constexpr (C::F32)
-    Unit<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1, qst);
+    Unit<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, ks0, ks1, vs0, vs1, qst);
   else
-    UnitFast<C>::run(a, tok0, L, qb, head, lse_base, ks0, ks1, vs0, vs1, qst);
+    UnitFast<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, ks0, ks1, vs0, vs1, qst);
 }
 
-// Dense batch: one workgroup per unit. Heavy units (late query blocks, which
-// see the most keys under the causal mask) are issued first, and when the
-// (batch, kv-head) groups divide evenly over the 8 XCDs, each XCD takes whole
-// groups so the query heads that share a K/V head share that XCD's L2.
+// Dense batch: one workgroup per unit (entry, K/V group, hp heads of the
+// group, query block). Heavy units (late query blocks, which see the most
+// keys under the causal mask) are issued first, and when the (batch, kv-head)
+// groups divide evenly over the 8 XCDs, each XCD takes whole groups so the
+// query heads that share a K/V head share that XCD's L2.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
-  const int nQ = (a.T + C::BM - 1) / C::BM;
-  const int G = a.H / a.KV, groups = a.B * a.KV;
+  const int bm = 32 * C::NW / a.hp;
+  const int nQ = (a.T + bm - 1) / bm;
+  const int G = a.H / a.KV, GH = G / a.hp, groups = a.B * a.KV;
   const int u = blockIdx.x;
   int rank, g, hq;
   if ((groups & 7) == 0) {
-    const int x = u & 7, i = u >> 3, per = (groups >> 3) * G;
+    const int x = u & 7, i = u >> 3, per = (groups >> 3) * GH;
     rank = i / per;
     const int rem = i - rank * per;
-    g = (rem / G) * 8 + x;
-    hq = rem % G;
+    g = (rem / GH) * 8 + x;
+    hq = rem % GH;
   } else {
-    const int per = groups * G;
+    const int per = groups * GH;
     rank = u / per;
     const int rem = u - rank * per;
-    g = rem / G;
-    hq = rem % G;
+    g = rem / GH;
+    hq = rem % GH;
   }
   const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
-  const int head = kvh * G + hq;
+  const int head0 = kvh * G + hq * a.hp;
   // A padded entry is its first L tokens: the unit sees only those keys and
   // writes only those rows; units past them have nothing to do.
   const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
-  if (qb * C::BM >= L) return;
-  run_unit<C>(a, b * a.T, L, qb, head, ((long)b * a.H + head) * a.T, k0, k1, v0, v1, qst);
+  if (qb * bm >= L) return;
+  run_unit<C>(a, b * a.T, L, qb, head0, (long)b * a.H * a.T, a.T, k0, k1, v0, v1, qst);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
@@ -1169,7 +1182,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
   __shared__ int s_unit;
-  const int n_units = a.sched[0] * a.H;
+  const int HG = a.H / a.hp;  // head groups of hp heads
+  const int n_units = a.sched[0] * HG;
   int* counter = a.sched + 1;
   const int2* items = (const int2*)(a.sched + kSchedHeaderInts);
   for (;;) {
@@ -1178,11 +1192,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
     const int u = s_unit;
     __syncthreads();
     if (u >= n_units) break;
-    const int it = u / a.H, head = u - it * a.H;
+    const int it = u / HG, hg = u - it * HG;
     const int2 sq = items[it];
     const int tok0 = a.cu_seqlens[sq.x];
     const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    run_unit<C>(a, tok0, L, sq.y, head, (long)head * a.total_tokens + tok0, k0, k1, v0, v1, qst);
+    run_unit<C>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, k0, k1, v0, v1, qst);
   }
 }
 
@@ -1248,10 +1262,21 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Query rows per unit and keys per tile of the forward instances of a head_dim.
-constexpr int fwd_block_rows(int head_dim) { return head_dim == 256 ? 128 : 32 * CGR_NW; }
+#ifndef CGR_MAX_HP
+#define CGR_MAX_HP 8
+#endif
+// Waves per workgroup, query heads per unit (the largest power of two that
+// divides both the waves and the group size G), query rows per unit and keys
+// per tile of the forward instances of a head_dim.
+constexpr int fwd_waves(int head_dim) { return head_dim == 256 ? 4 : CGR_NW; }
+constexpr int fwd_heads_per_unit(int head_dim, int G) {
+  int hp = 1;
+  while (2 * hp <= fwd_waves(head_dim) && 2 * hp <= CGR_MAX_HP && G % (2 * hp) == 0) hp *= 2;
+  return hp;
+}
+constexpr int fwd_block_rows(int head_dim, int hp) { return 32 * fwd_waves(head_dim) / hp; }
 constexpr int fwd_tile_keys(int head_dim) { return head_dim == 256 ? 32 : CGR_BN; }
-constexpr int kMinBM = 32 * CGR_NW < 128 ? 32 * CGR_NW : 128;  // smallest of them
+constexpr int kMinBM = 32;  // smallest query block of any unit
 // Bytes of one K tile image of the once-rotated keys (16-bit operands).
 constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_dim) * 2 * head_dim; }
 

@@ -144,10 +144,10 @@ hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, 
 
 // Upper bound on the (sequence, query block) items of a packed batch:
 // sum_s ceil(L_s / BM) <= total / BM + num_seqs. The workspace is sized for
-// blocks of 64 rows, which covers every block height the kernels use.
+// blocks of 32 rows, which covers every block height the kernels use.
 long varlen_max_items(int num_seqs, int total_tokens) {
-  static_assert(cgr::kMinBM >= 64, "workspace bound assumes query blocks of >= 64 rows");
-  return ((long)total_tokens + 63) / 64 + (long)num_seqs;
+  static_assert(cgr::kMinBM >= 32, "workspace bound assumes query blocks of >= 32 rows");
+  return ((long)total_tokens + 31) / 32 + (long)num_seqs;
 }
 
 // Backward workspace: the rotated q (operand type) and k, then the per-tile
@@ -238,8 +238,9 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
       return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
   }
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
-  const int bm = cgr::fwd_block_rows(head_dim);
-  const long grid = (long)((T + bm - 1) / bm) * B * n_head;
+  const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
+  const int bm = cgr::fwd_block_rows(head_dim, hp);
+  const long grid = (long)((T + bm - 1) / bm) * B * (n_head / hp);
   if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
                               softmax_scale);
@@ -247,6 +248,7 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
   a.T = T;
   a.total_tokens = B * T;
   a.window = window;
+  a.hp = hp;
   a.seqlens = seqlens;
   a.krot = use_ws ? workspace : nullptr;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
@@ -380,8 +382,9 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
 
   hipStream_t s = (hipStream_t)stream;
   int32_t* sched = (int32_t*)workspace;
+  const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
   hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
-                                             cgr::fwd_block_rows(head_dim), cgr::fwd_tile_keys(head_dim),
+                                             cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
                                              mask == CGR_MASK_CAUSAL, sched,
                                              (int)max_items, s);
   if (e != hipSuccess) return hip_fail("schedule launch", e);
@@ -393,9 +396,10 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   a.T = max_seqlen;
   a.total_tokens = total_tokens;
   a.window = window;
+  a.hp = hp;
   // Persistent grid: two workgroups per compute unit, never more than the units.
   long grid = 2L * cus;
-  if (grid > max_items * n_head) grid = max_items * n_head;
+  if (grid > max_items * (n_head / hp)) grid = max_items * (n_head / hp);
   if (grid < 1) grid = 1;
   e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
   if (e != hipSuccess) return hip_fail("attention launch", e);
