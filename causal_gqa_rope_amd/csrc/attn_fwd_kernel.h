@@ -996,10 +996,82 @@ struct UnitFast {
       return m_run;
     };
     float m_fin;
-    if (W > 0) {
+    if (W > 0 && bm > BN) {
       // Q fragments straight from global memory, each lane its own row.
       load_q_direct();
       m_fin = rescale_pass(std::true_type{});
+    } else if (W > 0) {
+      // ---- Windowed fast path (units of at most one tile of rows, so every
+      // row's own key lies in the unit's last tile jl). That tile goes first
+      // and gives each row its reference m, the row's max over it; then the
+      // window's tiles jb .. jl-1 in order, with S starting from -m. Tiles
+      // below jl hold no key past any row (no causal mask); those starting
+      // before the last row's window need the window's left edge.
+      // Processing order i = 0, 1, ..: tile tl(i), LDS stages by i's parity.
+      const int jl = n_tiles - 1, n_it = jl - j0 + 1;
+      auto tl = [&](int i) { return i == 0 ? jl : j0 + i - 1; };
+      auto wactive = [&](int tile) {
+        return wave_has_rows && tile * BN <= wave_last && tile * BN + BN - 1 >= qw0 - W + 1;
+      };
+      const int lo_all = q_hi - 1 - W + 1;  // tiles starting at or after this need no edge mask
+      float m_ref = 0.f;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+      l_run = 0.f;
+      u32x4 kw1[KI][2];
+      f32x4 kc1[KI][2], ksn1[KI][2];
+      if constexpr (!C::KPRE) {
+        load_k(jl * BN, ks0, kw, kc, ksn);
+        if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
+      }
+      __syncthreads();  // earlier users of this workgroup's LDS are done
+      if constexpr (C::KPRE) {
+        load_k(jl * BN, ks0, kw, kc, ksn);
+        if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
+      }
+      load_v(jl * BN, vs0, vw);
+      stage_q();
+      store_k(jl * BN, ks0, kw, kc, ksn, vw);
+      wait_vmem();
+      __syncthreads();
+      f32x16 s_cur[C::NKB];
+      if (wave_has_rows) {
+        scores(ks0, s_cur, (f32x16){});
+        mask_window(jl, s_cur);
+        m_ref = rowmax(s_cur);
+        // Only lanes past the sequence end can see no key here; 0 keeps their
+        // arithmetic finite (their rows are never stored).
+        if (m_ref == -INFINITY) m_ref = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] -= m_ref;
+      }
+      if (n_it > 1) store_k(tl(1) * BN, ks1, kw1, kc1, ksn1, vw);
+      wait_vmem();
+      __syncthreads();
+      const f32x16 negm = (f32x16){} - m_ref;
+      for (int i = 0; i < n_it; ++i) {
+        char* ki = stage_of(i, ks0, ks1);
+        char* ki1 = stage_of(i + 1, ks0, ks1);
+        char* vi = stage_of(i, vs0, vs1);
+        char* vi1 = stage_of(i + 1, vs0, vs1);
+        const int tc = tl(i);
+        if (i + 1 < n_it) load_v(tl(i + 1) * BN, vi1, vw);
+        if (i + 2 < n_it) load_k(tl(i + 2) * BN, ki, kw, kc, ksn);
+        f32x16 s_next[C::NKB];
+        if (i + 1 < n_it && wactive(tl(i + 1))) scores(ki1, s_next, negm);
+        if (wactive(tc)) {
+          if (i > 0 && tc * BN < lo_all) mask_window(tc, s_cur);
+          softmax_pv(vi, s_cur, std::false_type{}, 0.f, std::false_type{}, 1.f);
+        }
+        if (i + 2 < n_it) store_k(tl(i + 2) * BN, ki, kw, kc, ksn, vw);
+        wait_vmem();
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
+      }
+      m_fin = m_ref;
+      const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
+      if (__syncthreads_or(overflow)) m_fin = rescale_pass(std::true_type{});
     } else {
       float m_ref = 0.f;
       {

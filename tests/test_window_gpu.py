@@ -116,3 +116,29 @@ def test_window_decode(gpu, win, Tq, lens):
     o, lse = cgr.gqa_rope_attn_decode(q.to(gpu), kr, v.to(gpu), lens_t.to(gpu), S, cos, sin, window=win)
     ro, rl = oracle.attention_decode(q, k, v, lens, base=1e4, window=win)
     assert_close(f"decode W{win}", f64(o), ro, f64(lse), rl, "bf16")
+
+
+@pytest.mark.parametrize("magnitude", [40.0, 140.0])
+def test_window_scores_far_above_the_diagonal_tile(gpu, magnitude):
+    """Windowed units whose rows fit one key tile take their reference from the
+    tile holding each row's own key and then walk the window's earlier tiles;
+    here keys early in every window score far above the diagonal tile's (by
+    ~76 log2 units at magnitude 140), so the row sums pass their bound and the
+    unit must fall back to the rescaling loop and still match the oracle."""
+    T, H, KV, win = 300, 8, 2, 200
+    w = W.custom("win_growth", B=1, T=T, n_head=H, n_kv_head=KV, head_dim=128, base=1e4, seed=23)
+    announce(f"window {win}: scores far above the diagonal tile, magnitude {magnitude}")
+    x = W.make_inputs(w)
+    q = x["q"].float()
+    k = x["k"].float().clone()
+    for kvh in range(KV):
+        dirn = q[0, :, 4 * kvh:4 * kvh + 4].mean(dim=(0, 1))
+        k[0, 100:200, kvh] = k[0, 100:200, kvh] + magnitude * dirn / dirn.norm()
+    x["k"] = k.to(torch.bfloat16)
+    d_ = to_dev(x, gpu)
+    cos, sin = cgr.rope_tables(T, 128, w.base, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd(d_["q"], d_["k"], d_["v"], cos, sin, window=win)
+    ro, rl = oracle.attention_dense(x["q"], x["k"], x["v"], causal=True, base=w.base, window=win)
+    o, lse = f64(o), f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), "overflow must route to the rescaling loop"
+    assert_close(f"window growth {magnitude}", o, ro, lse, rl, "bf16")
