@@ -107,6 +107,8 @@ def dense(**kw):
     (dict(window=8, mask=0), 1, "CGR_MASK_CAUSAL"),
     (dict(ws=P, wsb=100), 4, "needs"),
     (dict(seqlens=PMIS), 3, "seqlens"),
+    # 32-bit byte offsets inside one sequence: (T + 256) * H * d * 4 must fit in int32
+    (dict(T=130816, H=32, KV=8, D=128, P=130816), 2, "exceeds 2 GiB"),
     (dict(ws=PMIS, wsb=1 << 20), 3, "aligned"),
 ])
 def test_dense_rejects_bad_arguments(kw, status, needle):

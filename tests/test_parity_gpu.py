@@ -349,3 +349,23 @@ def test_pre_rotated_keys_give_the_same_bits(gpu, T, H, KV, d, causal, style):
     o2, l2 = cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, causal=causal, rope_style=style)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_longest_sequence_the_offsets_allow(gpu):
+    """T = 120000 with 32 query heads of 128 (one sequence of 0.98 GB of q, byte
+    offsets up to 2^31 within a sequence): sampled rows, the last rows of every
+    K/V group among them, against the oracle. The host check rejects T past
+    130815 for this width (tests/test_abi.py)."""
+    w = W.custom("longest", B=1, T=120000, n_head=32, n_kv_head=8, head_dim=128, base=500000.0, seed=29)
+    announce(f"{w.name}: T={w.T}, sampled rows")
+    x = W.make_inputs(w)
+    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    o, lse = f64(o), f64(lse)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(29)
+    ts = [0, 63, 64, 65535, 65536, 119935, 119936, 119999] + [int(t) for t in rng.integers(0, w.T, 12)]
+    rows = [(0, t, int(rng.integers(0, 32))) for t in ts] + [(0, 119999, h) for h in range(0, 32, 4)]
+    ro, rl = oracle.attention_rows(x["q"], x["k"], x["v"], rows, causal=True, base=w.base)
+    go = np.stack([o[b, t, h] for (b, t, h) in rows])
+    gl = np.array([lse[b, h, t] for (b, t, h) in rows])
+    assert_close(w.name + " (sampled)", go, ro, gl, rl, "bf16")
