@@ -1049,7 +1049,7 @@ struct UnitFast {
       wait_vmem();
       __syncthreads();
       const f32x16 negm = (f32x16){} - m_ref;
-      for (int i = 0; i < n_it; ++i) {
+      auto witer = [&](int i) {
         char* ki = stage_of(i, ks0, ks1);
         char* ki1 = stage_of(i + 1, ks0, ks1);
         char* vi = stage_of(i, vs0, vs1);
@@ -1068,7 +1068,35 @@ struct UnitFast {
         __syncthreads();
 #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) s_cur[kb] = s_next[kb];
+      };
+      // Steady run: iterations whose tile needs no mask for any row and whose
+      // two successors are window tiles too (consecutive keys), unrolled by
+      // two with the stages fixed at compile time as in the causal path.
+      f32x16 s_alt[C::NKB];
+      auto wsteady = [&](int i, f32x16 (&s_in)[C::NKB], f32x16 (&s_out)[C::NKB], char* ki, char* ki1, char* vi,
+                         char* vi1) {
+        const int tc = tl(i);
+        load_v((tc + 1) * BN, vi1, vw);
+        load_k((tc + 2) * BN, ki, kw, kc, ksn);
+        __builtin_amdgcn_sched_barrier(0);
+        scores(ki1, s_out, negm);
+        softmax_pv(vi, s_in, std::false_type{}, 0.f, std::false_type{}, 1.f);
+        store_k((tc + 2) * BN, ki, kw, kc, ksn, vw);
+        wait_vmem();
+        __syncthreads();
+      };
+      // First steady iteration: tile tl(i) >= lo_all (i >= 1), rounded up to
+      // an odd i so that the stage of iteration i is stage 1 (i odd).
+      int i = 0;
+      const int i_first = max(1, (max(lo_all, 0) + BN - 1) / BN - j0 + 1);
+      for (; i < n_it && (i < i_first || (i & 1) == 0); ++i) witer(i);
+      if (wave_has_rows) {
+        for (; i + 3 < n_it; i += 2) {
+          wsteady(i, s_cur, s_alt, ks1, ks0, vs1, vs0);
+          wsteady(i + 1, s_alt, s_cur, ks0, ks1, vs0, vs1);
+        }
       }
+      for (; i < n_it; ++i) witer(i);
       m_fin = m_ref;
       const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
       if (__syncthreads_or(overflow)) m_fin = rescale_pass(std::true_type{});
