@@ -1251,16 +1251,20 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(Attn
   const int G = a.H / a.KV, GH = G / a.hp, groups = a.B * a.KV;
   const int u = blockIdx.x;
   int rank, g, hq;
+  // The items of a rank are rotated by the rank: an XCD deals its workgroups
+  // out over its shader engines in turn, and a fixed order would hand one
+  // engine the same (entry, heads) item rank after rank (all the long entry's
+  // work, in a batch of mixed lengths).
   if ((groups & 7) == 0) {
     const int x = u & 7, i = u >> 3, per = (groups >> 3) * GH;
     rank = i / per;
-    const int rem = i - rank * per;
+    const int rem = (i - rank * per + rank) % per;
     g = (rem / GH) * 8 + x;
     hq = rem % GH;
   } else {
     const int per = groups * GH;
     rank = u / per;
-    const int rem = u - rank * per;
+    const int rem = (u - rank * per + rank) % per;
     g = rem / GH;
     hq = rem % GH;
   }
