@@ -144,8 +144,12 @@ def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
             cu = inputs["cu_seqlens"].to(dev)
             lengths = (inputs["cu_seqlens"][1:] - inputs["cu_seqlens"][:-1]).tolist()
             lse = torch.empty((w.n_head, q.shape[0]), dtype=torch.float32, device=dev)
-            ws = torch.empty(max(16, cgr.cgr_attn_fwd_varlen_workspace_size(len(lengths), q.shape[0])),
-                             dtype=torch.uint8, device=dev)
+            # bf16: room for the once-rotated keys as well as the schedule.
+            need = cgr.cgr_attn_fwd_varlen_workspace_size(len(lengths), q.shape[0])
+            if w.dtype == "bf16":
+                need = max(need, cgr.cgr_attn_fwd_varlen_rotated_workspace_size(len(lengths), q.shape[0],
+                                                                                w.n_kv_head, w.head_dim))
+            ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
 
             def call():
                 cgr.gqa_rope_attn_fwd_varlen(q, k, v, cu, int(inputs["max_seqlen"]), cos, sin,

@@ -33,6 +33,7 @@ __all__ = [
     "cgr_attn_fwd_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_attn_fwd_varlen_workspace_size",
+    "cgr_attn_fwd_varlen_rotated_workspace_size",
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
@@ -68,6 +69,7 @@ EXPORTED_SYMBOLS = (
     "cgr_gqa_rope_attn_fwd",
     "cgr_attn_fwd_workspace_size",
     "cgr_attn_fwd_varlen_workspace_size",
+    "cgr_attn_fwd_varlen_rotated_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
@@ -129,6 +131,8 @@ def library() -> ctypes.CDLL:
     lib.cgr_gqa_rope_attn_fwd_fp8.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_attn_fwd_varlen_rotated_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.cgr_attn_fwd_varlen_rotated_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                                  i32, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp,
                                                  ctypes.c_size_t, vp]
@@ -325,6 +329,12 @@ def cgr_attn_fwd_varlen_workspace_size(num_seqs: int, total_tokens: int) -> int:
     return int(library().cgr_attn_fwd_varlen_workspace_size(int(num_seqs), int(total_tokens)))
 
 
+def cgr_attn_fwd_varlen_rotated_workspace_size(num_seqs: int, total_tokens: int, n_kv_head: int,
+                                               head_dim: int) -> int:
+    return int(library().cgr_attn_fwd_varlen_rotated_workspace_size(int(num_seqs), int(total_tokens),
+                                                                     int(n_kv_head), int(head_dim)))
+
+
 def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                  cu_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
                                  rope_sin: torch.Tensor, *, causal: bool = True,
@@ -332,9 +342,11 @@ def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
                                  softmax_scale: Optional[float] = None,
                                  qk_operand: str = "f16", out: Optional[torch.Tensor] = None,
                                  lse: Optional[torch.Tensor] = None, return_lse: bool = True,
-                                 workspace: Optional[torch.Tensor] = None):
+                                 workspace: Optional[torch.Tensor] = None, rotate_keys_once: bool = True):
     """Packed forward: q [total,H,d], k/v [total,KV,d], cu_seqlens int32 [n+1] (device).
 
+    Without a workspace one is allocated: for bf16 with room for the once-rotated
+    keys unless rotate_keys_once is False (then K is rotated per tile).
     Returns (o [total,H,d], lse [H,total] float32 or None).
     """
     lib = library()
@@ -361,6 +373,8 @@ def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     if lse is not None:
         _dev_tensor("lse", lse, torch.float32)
     need = lib.cgr_attn_fwd_varlen_workspace_size(max(nseq, 1), total)
+    if rotate_keys_once and q.dtype == torch.bfloat16:
+        need = max(need, lib.cgr_attn_fwd_varlen_rotated_workspace_size(max(nseq, 1), total, k.shape[1], D))
     if workspace is None:
         workspace = torch.empty(max(int(need), 16), dtype=torch.uint8, device=q.device)
     _dev_tensor("workspace", workspace)

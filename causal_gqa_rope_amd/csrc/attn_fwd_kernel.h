@@ -59,7 +59,11 @@ struct AttnArgs {
   const int32_t* cu_seqlens;  // packed batches
   const int32_t* seqlens;     // dense batches: valid tokens per entry (right padding), or null
   int32_t* sched;             // packed batches: [0] items, [1] queue counter, [2] error, then items
-  void* krot;                 // dense batches with a workspace: k rotated, in the Q.K^T operand type
+  void* krot;                 // with a workspace (16-bit I/O): k rotated once, in the Q.K^T operand type,
+                              // as tile images
+  const int32_t* kimg_base;   // packed batches with k images: first image slot of each sequence
+                              // ([num_seqs + 1], prefix sums of the sequences' tile counts)
+  int kimg_slots;             // packed batches with k images: image slots per K/V head
   int B, T, H, KV;
   int total_tokens;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
@@ -569,7 +573,8 @@ struct UnitFast {
   }
 
   static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head0,
-                                             long lse_b, long lse_h, CGR_LDS_PARAMS) {
+                                             long lse_b, long lse_h, long img0, long img_kvs,
+                                             CGR_LDS_PARAMS) {
     // `wave` is the same in every lane: keeping it scalar makes every wave-level
     // decision below (active tiles, masking, V blocks) a scalar branch.
     const int tid = threadIdx.x, lane = tid & 63;
@@ -586,12 +591,12 @@ struct UnitFast {
     const uint16_t* kbase = (const uint16_t*)a.k + (long)tok0 * ks + (long)kvh * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (long)tok0 * ks + (long)kvh * D;
     const rsrc_t rq = make_rsrc(qbase, (uint32_t)(((L - 1) * qs + D) * 2));
-    // Once-rotated keys (dense batches): tile images of K_IMG bytes per
-    // (entry, K/V head); one unit's images are one range.
-    const int n_img = (a.T + BN - 1) / BN;
+    // Once-rotated keys: the sequence's tile images of K_IMG bytes for this
+    // K/V head are consecutive, from image img0 + kvh * img_kvs on; one
+    // unit's images are one range.
     const rsrc_t rk = C::KPRE
-        ? make_rsrc((const char*)a.krot + ((long)(tok0 / a.T) * a.KV + kvh) * n_img * C::K_IMG,
-                    (uint32_t)(n_img * C::K_IMG))
+        ? make_rsrc((const char*)a.krot + (img0 + kvh * img_kvs) * C::K_IMG,
+                    (uint32_t)(((L + BN - 1) / BN) * C::K_IMG))
         : make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
     const rsrc_t rv = make_rsrc(vbase, (uint32_t)(((L - 1) * ks + D) * 2));
     const rsrc_t rc = make_rsrc(a.rope_cos, (uint32_t)(L * (D / 2) * 4));
@@ -1227,13 +1232,15 @@ struct UnitFast {
   }
 };
 
+// img0, img_kvs: the first K tile image of the unit's sequence (K/V head 0)
+// and the images between consecutive K/V heads (used with once-rotated keys).
 template <class C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head0, long lse_b,
-                                         long lse_h, CGR_LDS_PARAMS) {
+                                         long lse_h, long img0, long img_kvs, CGR_LDS_PARAMS) {
   if constexpr (C::F32)
     Unit<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, ks0, ks1, vs0, vs1, qst);
   else
-    UnitFast<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, ks0, ks1, vs0, vs1, qst);
+    UnitFast<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, img0, img_kvs, ks0, ks1, vs0, vs1, qst);
 }
 
 // Dense batch: one workgroup per unit (entry, K/V group, hp heads of the
@@ -1275,7 +1282,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(Attn
   // writes only those rows; units past them have nothing to do.
   const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
   if (qb * bm >= L) return;
-  run_unit<C>(a, b * a.T, L, qb, head0, (long)b * a.H * a.T, a.T, k0, k1, v0, v1, qst);
+  // Images of a dense batch: per (entry, K/V head), ceil(T / BN) tiles.
+  const long n_img = (a.T + C::BN - 1) / C::BN;
+  run_unit<C>(a, b * a.T, L, qb, head0, (long)b * a.H * a.T, a.T, (long)b * a.KV * n_img, n_img, k0, k1, v0, v1,
+              qst);
 }
 
 // Packed batch: a persistent grid pulls (sequence, query block) items from the
@@ -1300,7 +1310,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
     const int2 sq = items[it];
     const int tok0 = a.cu_seqlens[sq.x];
     const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    run_unit<C>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, k0, k1, v0, v1, qst);
+    // Images of a packed batch: per K/V head, kimg_slots slots; sequence s
+    // owns slots kimg_base[s] .. kimg_base[s + 1] - 1.
+    const long img0 = C::KPRE ? (long)a.kimg_base[sq.x] : 0;
+    run_unit<C>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, img0, a.kimg_slots, k0, k1, v0, v1, qst);
   }
 }
 
@@ -1343,6 +1356,52 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
   *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
 }
 
+// The same images for a packed batch: per K/V head, kimg_slots slots of one
+// tile each; sequence s owns slots kimg_base[s] .. kimg_base[s + 1] - 1 (its
+// tiles in order, token t of the sequence at position t), written by the
+// schedule prepass. Slots past the last sequence's are left alone. The owner
+// of a slot is the last sequence whose first slot is at or before it (empty
+// sequences own none). A malformed cu_seqlens (the prepass's error word set)
+// leaves the images unwritten; every read stays inside q/k and the tables
+// whatever the arrays hold.
+template <class C>
+__global__ __launch_bounds__(256) void krot_varlen_kernel(AttnArgs a) {
+  constexpr int D = C::D, BN = C::BN, IPR = D / 16;
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long item = tid / IPR;
+  if (item >= (long)a.KV * a.kimg_slots * BN) return;
+  if (a.sched[2] != 0) return;
+  const int g = (int)(tid % IPR), r = (int)(item % BN);
+  const long img = item / BN;  // kv * kimg_slots + slot
+  const int slot = (int)(img % a.kimg_slots), kv = (int)(img / a.kimg_slots);
+  const int nseq = a.B;
+  if (slot >= a.kimg_base[nseq]) return;
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.kimg_base[mid] <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  const int t = (slot - a.kimg_base[lo]) * BN + r;
+  const int c0 = a.cu_seqlens[lo], L = a.cu_seqlens[lo + 1] - c0;
+  u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+  if (t < L && t < a.T && c0 >= 0 && c0 + t < a.total_tokens) {
+    const uint16_t* kp = (const uint16_t*)a.k + ((long)(c0 + t) * a.KV + kv) * D;
+    u32x4 i0[1] = {*(const u32x4*)(kp + 8 * g)}, i1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
+    float x0[8], x1[8];
+    raw_to_f32<uint16_t>(i0, x0);
+    raw_to_f32<uint16_t>(i1, x1);
+    f32x4 c[2], s[2];
+    load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
+    rope_pair<C::STYLE>(x0, x1, c, s);
+    w0 = to_frag<typename C::QK>(x0).v;
+    w1 = to_frag<typename C::QK>(x1).v;
+  }
+  char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
+  *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
+  *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
+}
+
 // Launch one instance. Host-side, after the arguments are validated.
 template <class C>
 hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t stream) {
@@ -1363,6 +1422,18 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+  return hipGetLastError();
+}
+
+// Packed batch with the K rotation done once up front (a.krot, a.kimg_base
+// set; the schedule prepass has run on the stream).
+template <class C>
+hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stream) {
+  const long items = (long)a.KV * a.kimg_slots * C::BN * (C::D / 16);
+  hipLaunchKernelGGL((krot_varlen_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
   return hipGetLastError();
 }
 
@@ -1389,8 +1460,9 @@ hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, 
                          bool varlen, int grid, hipStream_t stream) {
 #define CGR_LAUNCH(IO, QK, CAU, STY, WIN)                                                       \
   if constexpr (!std::is_same<IO, float>::value) {                                               \
-    if (!varlen && a.krot != nullptr)                                                             \
-      return launch_attn_kpre<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream);             \
+    if (a.krot != nullptr)                                                                        \
+      return varlen ? launch_attn_kpre_varlen<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream) \
+                    : launch_attn_kpre<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream);    \
   }                                                                                               \
   return launch_attn<Cfg<D, IO, QK, CAU, STY, WIN>>(a, varlen, grid, stream)
 #define CGR_BY_STYLE(IO, QK, CAU, WIN) \

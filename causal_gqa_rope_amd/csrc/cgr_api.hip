@@ -347,6 +347,32 @@ size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens) {
   return (size_t)cgr::kSchedHeaderInts * 4 + (size_t)varlen_max_items(num_seqs, total_tokens) * 8;
 }
 
+// Workspace of a packed call that rotates the keys once: the schedule, then
+// the first image slot of every sequence, then the K tile images ([K/V head]
+// [slot], slots = ceil(total / BN) + num_seqs, which bounds the sum of the
+// sequences' tile counts); each part starts on a 256-byte boundary.
+struct VarlenLayout {
+  size_t kimg_base, images, total;
+  long slots;
+};
+VarlenLayout varlen_layout(int num_seqs, int total_tokens, int n_kv_head, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  VarlenLayout l{};
+  const int bn = cgr::fwd_tile_keys(head_dim);
+  l.slots = ((long)total_tokens + bn - 1) / bn + num_seqs;
+  l.kimg_base = up(cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens));
+  l.images = up(l.kimg_base + ((size_t)num_seqs + 1) * 4);
+  l.total = l.images + (size_t)n_kv_head * l.slots * cgr::fwd_kimg_bytes(head_dim);
+  return l;
+}
+
+size_t cgr_attn_fwd_varlen_rotated_workspace_size(int num_seqs, int total_tokens, int n_kv_head,
+                                                  int head_dim) {
+  if (num_seqs < 1 || total_tokens < 0 || n_kv_head < 1) return 0;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return 0;
+  return varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim).total;
+}
+
 cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                                         float* lse, const int32_t* cu_seqlens, int num_seqs,
                                         int total_tokens, int max_seqlen, int n_head,
@@ -380,13 +406,20 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   const int ce = cu_count(&cus);
   if (ce != 0) return hip_fail("device query", (hipError_t)ce);
 
+  // Keys rotated once (16-bit I/O) when the workspace also holds their images.
+  const VarlenLayout lay = varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim);
+  const bool use_kimg = dtype == CGR_BF16 && workspace_bytes >= lay.total;
+  if (use_kimg && (long)n_kv_head * lay.slots > INT_MAX)
+    return fail(CGR_ERR_INVALID_ARG, "too many key tiles");
+
   hipStream_t s = (hipStream_t)stream;
   int32_t* sched = (int32_t*)workspace;
+  int32_t* kimg_base = use_kimg ? (int32_t*)((char*)workspace + lay.kimg_base) : nullptr;
   const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
   hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
                                              cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
                                              mask == CGR_MASK_CAUSAL, sched,
-                                             (int)max_items, s);
+                                             (int)max_items, kimg_base, s);
   if (e != hipSuccess) return hip_fail("schedule launch", e);
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
                               softmax_scale);
@@ -397,6 +430,11 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
   a.total_tokens = total_tokens;
   a.window = window;
   a.hp = hp;
+  if (use_kimg) {
+    a.krot = (char*)workspace + lay.images;
+    a.kimg_base = kimg_base;
+    a.kimg_slots = (int)lay.slots;
+  }
   // Persistent grid: two workgroups per compute unit, never more than the units.
   long grid = 2L * cus;
   if (grid > max_items * (n_head / hp)) grid = max_items * (n_head / hp);

@@ -46,9 +46,10 @@ hipError_t launch_qkv_d128(const QkvArgs& a, int style, hipStream_t stream);
 hipError_t launch_rope_tables(int max_pos, int head_dim, double base, float* cos_out,
                               float* sin_out, hipStream_t stream);
 
-// Builds the work list of a packed batch into `sched` (see varlen_sched.hip).
+// Builds the work list of a packed batch into `sched` and, if kimg_base is
+// non-null, the first K image slot of every sequence (see varlen_sched.hip).
 hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                   int max_seqlen, int bm, int bn, int causal, int32_t* sched,
-                                  int max_items, hipStream_t stream);
+                                  int max_items, int32_t* kimg_base, hipStream_t stream);
 
 }  // namespace cgr

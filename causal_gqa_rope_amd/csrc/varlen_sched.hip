@@ -13,6 +13,10 @@
 // Layout of `sched` (int32): [0] number of items, [1] queue counter (reset to
 // 0 here), [2] error word (0 = well formed), [3] unused, then items as
 // (sequence, query block) int pairs.
+//
+// When the call rotates the keys once (kimg_base non-null), the prepass also
+// writes kimg_base[s] = sum over s' < s of ceil(L_s' / bn), s = 0 .. num_seqs:
+// the first K tile image slot of every sequence.
 #include <hip/hip_runtime.h>
 
 #include "attn_fwd_kernel.h"
@@ -30,7 +34,7 @@ __device__ __forceinline__ int cost_bin(int qb, int L, int bm, int bn, int causa
 
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     const int32_t* cu, int nseq, int total, int max_seqlen, int bm, int bn, int causal,
-    int32_t* sched, int max_items) {
+    int32_t* sched, int max_items, int32_t* kimg_base) {
   __shared__ int hist[kBins];
   __shared__ int part[kSchedThreads];
   __shared__ int err;
@@ -101,6 +105,30 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
       if (pos < max_items) items[pos] = make_int2(s, qb);
     }
   }
+  // 4. First image slot of every sequence: each thread sums the tiles of a
+  //    run of consecutive sequences, a scan over the threads gives the runs'
+  //    starts.
+  if (kimg_base != nullptr) {
+    const int chunk = (nseq + kSchedThreads - 1) / kSchedThreads;
+    const int s0 = min(tid * chunk, nseq), s1 = min(s0 + chunk, nseq);
+    int own = 0;
+    for (int s = s0; s < s1; ++s) own += (cu[s + 1] - cu[s] + bn - 1) / bn;
+    __syncthreads();  // every thread is done with part[] above
+    part[tid] = own;
+    __syncthreads();
+    for (int off = 1; off < kSchedThreads; off <<= 1) {
+      const int add = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += add;
+      __syncthreads();
+    }
+    int at = part[tid] - own;
+    for (int s = s0; s < s1; ++s) {
+      kimg_base[s] = at;
+      at += (cu[s + 1] - cu[s] + bn - 1) / bn;
+    }
+    if (tid == kSchedThreads - 1) kimg_base[nseq] = part[tid];
+  }
   if (tid == 0) {
     sched[0] = min(n_items, max_items);
     sched[1] = 0;
@@ -110,9 +138,9 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
 
 hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                   int max_seqlen, int bm, int bn, int causal, int32_t* sched,
-                                  int max_items, hipStream_t stream) {
+                                  int max_items, int32_t* kimg_base, hipStream_t stream) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, max_seqlen, bm, bn, causal, sched, max_items);
+                     num_seqs, total_tokens, max_seqlen, bm, bn, causal, sched, max_items, kimg_base);
   return hipGetLastError();
 }
 

@@ -193,6 +193,20 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const
 CGR_API size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens);
 
 /*
+ * Bytes of device workspace with which cgr_gqa_rope_attn_fwd_varlen (bf16
+ * I/O) also rotates every key once up front: the schedule above, then the
+ * first tile slot of every sequence, then the rotated keys as tile images
+ * (per K/V head, ceil(total_tokens / BN) + num_seqs tiles of BN keys x
+ * head_dim, BN = 64, or 32 at head_dim 256, in the Q.K^T operand type), each
+ * part on a 256-byte boundary. The rotation is the same arithmetic as the
+ * per-tile one, so the results are bit-identical. Returns 0 for invalid
+ * sizes (num_seqs < 1, total_tokens < 0, n_kv_head < 1, or a head_dim other
+ * than 32, 64, 128, 256).
+ */
+CGR_API size_t cgr_attn_fwd_varlen_rotated_workspace_size(int num_seqs, int total_tokens, int n_kv_head,
+                                                          int head_dim);
+
+/*
  * Packed variable-length batch forward. Sequence s holds tokens
  * cu_seqlens[s] .. cu_seqlens[s+1]-1; RoPE positions restart at 0 in every
  * sequence and the mask never crosses a sequence boundary.
@@ -207,6 +221,9 @@ CGR_API size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens
  *     cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens) bytes,
  *     16-byte aligned, used as scratch by this call only (it holds the
  *     work schedule); calls that overlap in time need separate workspaces.
+ *     With bf16 I/O and at least cgr_attn_fwd_varlen_rotated_workspace_size(
+ *     num_seqs, total_tokens, n_kv_head, head_dim) bytes, the keys are
+ *     rotated once into it before the attention kernel (same results).
  * cu_seqlens lives on the device, so its contents are checked there: a
  * malformed array schedules no work (o and lse are left unwritten) and sets
  * an error word that cgr_varlen_device_status() reports.

@@ -62,6 +62,16 @@ def test_version_and_workspace_size():
     assert 16 < small < big
     # one 8-byte item per (sequence, query block of >= 64 rows), plus a header
     assert big >= 16 + 8 * (32226 // 64 + 32)
+    # with the once-rotated keys: the schedule, the per-sequence first slots,
+    # then per K/V head ceil(total / BN) + num_seqs tile images, each part on a
+    # 256-byte boundary
+    up = lambda x: (x + 255) // 256 * 256
+    rot = lib.cgr_attn_fwd_varlen_rotated_workspace_size
+    assert rot(32, 32226, 1, 128) == up(up(big) + 33 * 4) + 1 * ((32226 + 63) // 64 + 32) * 64 * 128 * 2
+    assert rot(3, 100, 2, 256) == (up(up(lib.cgr_attn_fwd_varlen_workspace_size(3, 100)) + 4 * 4)
+                                   + 2 * ((100 + 31) // 32 + 3) * 32 * 256 * 2)
+    assert rot(0, 10, 1, 64) == 0 and rot(1, -1, 1, 64) == 0 and rot(1, 10, 0, 64) == 0
+    assert rot(1, 10, 1, 96) == 0
 
 
 no_gpu = pytest.mark.skipif(

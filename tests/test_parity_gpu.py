@@ -235,17 +235,19 @@ def test_qk_bf16_operand_option(gpu):
     assert_close("qk-bf16", f64(o), ro, f64(lse), rl, "bf16")
 
 
+@pytest.mark.parametrize("rotated", [False, True], ids=["schedule_ws", "rotated_ws"])
 @pytest.mark.parametrize("cu,code", [([1, 5, 9], 1), ([0, 6, 4, 9], 2), ([0, 2, 9], 3),
                                      ([0, 4, 8], 4)])
-def test_malformed_cu_seqlens_schedules_nothing(gpu, cu, code):
-    announce(f"malformed cu_seqlens {cu}")
+def test_malformed_cu_seqlens_schedules_nothing(gpu, cu, code, rotated):
+    announce(f"malformed cu_seqlens {cu} rotated-keys workspace={rotated}")
     total = 9
     q = torch.randn(total, 2, 64, device=gpu).to(torch.bfloat16)
     kv = torch.randn(total, 1, 64, device=gpu).to(torch.bfloat16)
     cos, sin = cgr.rope_tables(8, 64, 1e4, device=gpu)
     o = torch.full_like(q, float("nan"))
-    ws = torch.zeros(cgr.cgr_attn_fwd_varlen_workspace_size(len(cu) - 1, total), dtype=torch.uint8,
-                     device=gpu)
+    n = (cgr.cgr_attn_fwd_varlen_rotated_workspace_size(len(cu) - 1, total, 1, 64) if rotated
+         else cgr.cgr_attn_fwd_varlen_workspace_size(len(cu) - 1, total))
+    ws = torch.zeros(n, dtype=torch.uint8, device=gpu)
     cgr.gqa_rope_attn_fwd_varlen(q, kv, kv, torch.tensor(cu, dtype=torch.int32, device=gpu), 6,
                                  cos, sin, out=o, workspace=ws)
     assert cgr.cgr_varlen_device_status(ws) == code
@@ -349,6 +351,39 @@ def test_pre_rotated_keys_give_the_same_bits(gpu, T, H, KV, d, causal, style):
     o2, l2 = cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, causal=causal, rope_style=style)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+PACKED_PREROT = [
+    # lengths, H, KV, d, causal, style, window
+    ([5, 1, 0, 130, 64, 257, 1], 4, 1, 128, True, "interleaved", 0),
+    ([0, 300, 17], 6, 2, 64, False, "half", 0),
+    ([129, 128, 127, 2], 4, 4, 32, True, "interleaved", 0),
+    ([700, 0, 0, 33, 1000], 8, 2, 128, True, "half", 100),
+    ([300, 65, 64, 63], 4, 2, 256, True, "interleaved", 0),
+]
+
+
+@pytest.mark.parametrize("lengths,H,KV,d,causal,style,win", PACKED_PREROT,
+                         ids=[f"p{i}" for i in range(len(PACKED_PREROT))])
+def test_packed_pre_rotated_keys_give_the_same_bits(gpu, lengths, H, KV, d, causal, style, win):
+    """A packed batch with the keys rotated once into the workspace (tile
+    images per sequence, empty sequences owning none) gives the bits of the
+    per-tile rotation, and both match the oracle."""
+    announce(f"packed pre-rotated keys lengths={lengths} H={H} KV={KV} d={d} causal={causal} {style} W={win}")
+    x = packed_inputs(lengths, H, KV, d, "bf16", seed=sum(lengths) + d)
+    xd = to_dev(x, gpu)
+    ms = max(max(lengths), 1)
+    cos, sin = cgr.rope_tables(ms, d, 5e5, device=gpu)
+    args = (xd["q"], xd["k"], xd["v"], xd["cu_seqlens"], ms, cos, sin)
+    kw = dict(causal=causal, rope_style=style, window=win)
+    o1, l1 = cgr.gqa_rope_attn_fwd_varlen(*args, rotate_keys_once=False, **kw)
+    o2, l2 = cgr.gqa_rope_attn_fwd_varlen(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if sum(lengths):
+        ro, rl = oracle.attention_varlen(x["q"], x["k"], x["v"], x["cu_seqlens"].numpy(), causal=causal,
+                                         base=5e5, style=style, window=win)
+        assert_close("packed pre-rotated", f64(o2), ro, f64(l2), rl, "bf16")
 
 
 def test_longest_sequence_the_offsets_allow(gpu):
