@@ -116,22 +116,26 @@ __device__ __forceinline__ void rope_head(f32x16* const (&blk)[D / 32], const fl
   }
 }
 
-// Workgroup tile: 128 output features (whole heads) x 256 tokens, 4 waves of
-// 64 tokens; K steps of 32 features of x through LDS (direct loads, double
-// buffered, rows of 64 bytes with the swizzle of tile_common.h).
-template <int D, int STYLE>
-__global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
-  constexpr int BO = 128, BT = 256, KB = 32;
+// Workgroup tile: 256 output features (whole heads) x 256 tokens, 8 waves of
+// 128 features x 64 tokens (one workgroup per CU); K steps of KB features of x
+// through LDS (direct loads, rows of 2 * KB bytes with the swizzle of
+// tile_common.h): KB = 64 with two stages when the width allows (half the
+// barriers of KB = 32: +6 %), else KB = 32 with three.
+template <int D, int STYLE, int KB>
+__global__ __launch_bounds__(512, 1) void qkv_gemm_kernel(QkvArgs a) {
+  constexpr int BO = 256, BT = 256, NWV = 8;
+  constexpr int NS = KB == 64 ? 2 : 3;  // LDS stages
   constexpr int AT = BO * KB * 2, BTB = BT * KB * 2;
-  static_assert(BO % D == 0, "whole heads per tile");
-  // Three stages (separate arrays, named at compile time in the unrolled
-  // loop): tile j + 2 loads while tile j is multiplied, so each load has two
-  // steps of matrix work to arrive in.
-  __shared__ __attribute__((aligned(16))) char a0[AT], a1[AT], a2[AT];
-  __shared__ __attribute__((aligned(16))) char b0[BTB], b1[BTB], b2[BTB];
+  static_assert(128 % D == 0, "whole heads per wave");
+  static_assert(KB == 32 || KB == 64, "K step");
+  // Stages as separate arrays, named at compile time in the unrolled loop:
+  // tile j + NS - 1 loads while tile j is multiplied.
+  __shared__ __attribute__((aligned(16))) char a0[AT], a1[AT], a2[NS == 3 ? AT : 16];
+  __shared__ __attribute__((aligned(16))) char b0[BTB], b1[BTB], b2[NS == 3 ? BTB : 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
+  const int fh = wave >> 2, tw = wave & 3;  // this wave: features 128 fh .., tokens 64 tw ..
   // Tile order: consecutive workgroups go to the 8 XCDs in turn. When the
   // token tiles split evenly over the XCDs, XCD x takes token tiles
   // [x n_tt/8, (x+1) n_tt/8), walked token-fastest, so the workgroups it runs
@@ -153,8 +157,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
   const rsrc_t rx = make_rsrc(a.x, (uint32_t)((long)a.N * a.C * 2));
   const int nk = a.C / KB;
   auto issue = [&](int j, char* at, char* bt) {
-    tile_to_lds<KB, BO>(rw, at, a.C * 2, (o0 * a.C + j * KB) * 2, wave, 4, lane);
-    tile_to_lds<KB, BT>(rx, bt, a.C * 2, (t0 * a.C + j * KB) * 2, wave, 4, lane);
+    tile_to_lds<KB, BO>(rw, at, a.C * 2, (o0 * a.C + j * KB) * 2, wave, NWV, lane);
+    tile_to_lds<KB, BT>(rx, bt, a.C * 2, (t0 * a.C + j * KB) * 2, wave, NWV, lane);
   };
   f32x16 acc[4][2];
 #pragma unroll
@@ -164,40 +168,47 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
     for (int s = 0; s < KB / 16; ++s) {
       Frag<OpBF16> af[4], bf[2];
 #pragma unroll
-      for (int ob = 0; ob < 4; ++ob) af[ob] = frag<OpBF16>(row_frag<KB>(at, 32 * ob + l32, s, hh));
+      for (int ob = 0; ob < 4; ++ob) af[ob] = frag<OpBF16>(row_frag<KB>(at, 128 * fh + 32 * ob + l32, s, hh));
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) bf[tb] = frag<OpBF16>(row_frag<KB>(bt, 64 * wave + 32 * tb + l32, s, hh));
+      for (int tb = 0; tb < 2; ++tb) bf[tb] = frag<OpBF16>(row_frag<KB>(bt, 64 * tw + 32 * tb + l32, s, hh));
 #pragma unroll
       for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) acc[ob][tb] = mma32(af[ob], bf[tb], acc[ob][tb]);
     }
   };
-  // Step j: wait for this wave's loads of tile j (tile j + 1's may still be in
+  // Step j: wait for this wave's loads of tile j (later tiles' may still be in
   // flight), barrier (tile j complete in LDS, and every wave done with tile
-  // j - 1, whose stage tile j + 2 then takes), issue tile j + 2, multiply j.
-  constexpr int LOADS = (AT / 1024 + BTB / 1024) / 4;  // this wave's loads per tile
+  // j - 1, whose stage tile j + NS - 1 then takes), issue that tile, multiply j.
+  constexpr int LOADS = (AT / 1024 + BTB / 1024) / NWV;  // this wave's loads per tile
   auto step = [&](int j, const char* at, const char* bt, char* an, char* bn) {
-    if (j + 1 < nk)
+    if (NS == 3 && j + 1 < nk)
       wait_vmem_le<LOADS>();
     else
       wait_vmem_le<0>();
     __syncthreads();
-    if (j + 2 < nk) issue(j + 2, an, bn);
+    if (j + NS - 1 < nk) issue(j + NS - 1, an, bn);
     compute(at, bt);
   };
   issue(0, a0, b0);
-  if (1 < nk) issue(1, a1, b1);
-  for (int j = 0; j < nk; j += 3) {
-    step(j, a0, b0, a2, b2);
-    if (j + 1 < nk) step(j + 1, a1, b1, a0, b0);
-    if (j + 2 < nk) step(j + 2, a2, b2, a1, b1);
+  if constexpr (NS == 3) {
+    if (1 < nk) issue(1, a1, b1);
+    for (int j = 0; j < nk; j += 3) {
+      step(j, a0, b0, a2, b2);
+      if (j + 1 < nk) step(j + 1, a1, b1, a0, b0);
+      if (j + 2 < nk) step(j + 2, a2, b2, a1, b1);
+    }
+  } else {
+    for (int j = 0; j < nk; j += 2) {
+      step(j, a0, b0, a1, b1);
+      if (j + 1 < nk) step(j + 1, a1, b1, a0, b0);
+    }
   }
 
   // Epilogue: lane column = token; block ob = features o0 + 32 ob ...
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int t = t0 + 64 * wave + 32 * tb + l32;
+    const int t = t0 + 64 * tw + 32 * tb + l32;
     if (t >= a.N) continue;
     const int p = a.positions[t];
     if (p < 0 || p >= a.P) {
@@ -210,8 +221,8 @@ __global__ __launch_bounds__(256, 2) void qkv_gemm_kernel(QkvArgs a) {
     const float* cs = a.rope_cos + (long)p * (D / 2);
     const float* sn = a.rope_sin + (long)p * (D / 2);
 #pragma unroll
-    for (int hb = 0; hb < BO / D; ++hb) {  // heads in the tile
-      const int head = (o0 + hb * D) / D;
+    for (int hb = 0; hb < 128 / D; ++hb) {  // heads in this wave's 128 features
+      const int head = (o0 + 128 * fh + hb * D) / D;
       if (head >= a.H + 2 * a.KV) break;
       const bool is_q = head < a.H, is_k = !is_q && head < a.H + a.KV;
       if ((is_q && a.rot_q) || (is_k && a.rot_k)) {
@@ -245,11 +256,19 @@ hipError_t launch_qkv_d(const QkvArgs& a, int style, hipStream_t stream) {
   hipLaunchKernelGGL(qkv_prep_kernel<D>, dim3((unsigned)(nrb + nwb)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)(((a.O + 127) / 128) * (long)((a.N + 255) / 256));
-  if (style == STYLE_HALF)
-    hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_HALF>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_INTERLEAVED>), dim3(grid), dim3(256), 0, stream, a);
+  const unsigned grid = (unsigned)(((a.O + 255) / 256) * (long)((a.N + 255) / 256));
+  const bool k64 = a.C % 64 == 0;
+  if (style == STYLE_HALF) {
+    if (k64)
+      hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_HALF, 64>), dim3(grid), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_HALF, 32>), dim3(grid), dim3(512), 0, stream, a);
+  } else {
+    if (k64)
+      hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_INTERLEAVED, 64>), dim3(grid), dim3(512), 0, stream, a);
+    else
+      hipLaunchKernelGGL((qkv_gemm_kernel<D, STYLE_INTERLEAVED, 32>), dim3(grid), dim3(512), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -58,11 +58,13 @@ def test_qkv_workload_full(gpu, name):
 
 
 # (B, T, C, H, KV, d, style, rotate q, rotate k): ragged token counts (not a
-# multiple of the 256-token tile), n_embd down to one 32-wide step, heads that
-# split a 128-feature tile across q/k/v, every head_dim, both pairings, each
-# rotation choice.
+# multiple of the 256-token tile), n_embd down to one 32-wide step and widths
+# that are not a multiple of 64 (the 32-wide K-step instance), output features
+# that end inside a 256-feature tile, heads that split a tile across q/k/v,
+# every head_dim, both pairings, each rotation choice.
 EDGE = [
     (1, 300, 256, 4, 2, 64, "interleaved", True, True),
+    (2, 260, 160, 6, 2, 64, "interleaved", True, True),
     (3, 77, 32, 2, 1, 32, "half", True, False),
     (1, 513, 384, 6, 3, 64, "half", False, True),
     (2, 129, 512, 4, 4, 128, "interleaved", False, False),
