@@ -693,9 +693,11 @@ struct UnitFast {
         } else {
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
+            // Explicit FMAs (as for K): the bits must not depend on how the
+            // compiler contracts the products in a given instance.
             const float x = x0[2 * m], y = x0[2 * m + 1];
-            x0[2 * m] = x * q_cos[i][0][m] - y * q_sin[i][0][m];
-            x0[2 * m + 1] = x * q_sin[i][0][m] + y * q_cos[i][0][m];
+            x0[2 * m] = rot_a(x, y, q_cos[i][0][m], q_sin[i][0][m]);
+            x0[2 * m + 1] = rot_b(x, y, q_cos[i][0][m], q_sin[i][0][m]);
           }
         }
 #pragma unroll
