@@ -1324,38 +1324,42 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
 // per (entry, K/V head, tile of BN keys), the tile exactly as the unit's LDS
 // stage will hold it (rows of 2*D bytes, 16-byte chunks swizzled by tswz), so
 // the unit copies each tile into LDS with 1-KiB direct loads. Keys past the
-// entry's length are zeros. Item = (image row, group g < D/16) carrying the
-// chunk pair (g, g + D/16), as in the K loader.
+// entry's length are zeros. Item = (entry, image row, group g < D/16) carrying
+// the chunk pair (g, g + D/16), as in the K loader, for every K/V head: the
+// cos/sin values of the position are loaded once for all heads.
 template <class C>
 __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
   constexpr int D = C::D, BN = C::BN, IPR = D / 16;
   const int n_img = (a.T + BN - 1) / BN;
   const long tid = (long)blockIdx.x * 256 + threadIdx.x;
   const long item = tid / IPR;
-  if (item >= (long)a.B * a.KV * n_img * BN) return;
+  if (item >= (long)a.B * n_img * BN) return;
   const int g = (int)(tid % IPR), r = (int)(item % BN);
-  const long img = item / BN;  // (b * KV + kv) * n_img + tile
-  const int tile = (int)(img % n_img);
-  const long bk = img / n_img;
-  const int kv = (int)(bk % a.KV), b = (int)(bk / a.KV);
+  const long bt = item / BN;  // b * n_img + tile
+  const int tile = (int)(bt % n_img), b = (int)(bt / n_img);
   const int t = tile * BN + r;
   const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
-  u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-  if (t < L) {
-    const uint16_t* kp = (const uint16_t*)a.k + (((long)b * a.T + t) * a.KV + kv) * D;
-    u32x4 i0[1] = {*(const u32x4*)(kp + 8 * g)}, i1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
-    float x0[8], x1[8];
-    raw_to_f32<uint16_t>(i0, x0);
-    raw_to_f32<uint16_t>(i1, x1);
-    f32x4 c[2], s[2];
-    load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
-    rope_pair<C::STYLE>(x0, x1, c, s);
-    w0 = to_frag<typename C::QK>(x0).v;
-    w1 = to_frag<typename C::QK>(x1).v;
+  const bool ok = t < L;
+  f32x4 c[2], s[2];
+  load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, ok, c, s);
+  const uint16_t* kp = (const uint16_t*)a.k + ((long)b * a.T + t) * a.KV * D;
+  for (int kv = 0; kv < a.KV; ++kv) {
+    u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
+    if (ok) {
+      const uint16_t* kh = kp + (long)kv * D;
+      u32x4 i0[1] = {*(const u32x4*)(kh + 8 * g)}, i1[1] = {*(const u32x4*)(kh + 8 * g + D / 2)};
+      float x0[8], x1[8];
+      raw_to_f32<uint16_t>(i0, x0);
+      raw_to_f32<uint16_t>(i1, x1);
+      rope_pair<C::STYLE>(x0, x1, c, s);
+      w0 = to_frag<typename C::QK>(x0).v;
+      w1 = to_frag<typename C::QK>(x1).v;
+    }
+    const long img = ((long)b * a.KV + kv) * n_img + tile;
+    char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
+    *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
+    *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
   }
-  char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
-  *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
-  *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
 }
 
 // The same images for a packed batch: per K/V head, kimg_slots slots of one
@@ -1419,7 +1423,7 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
 // Dense batch with the K rotation done once up front (a.krot set).
 template <class C>
 hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
-  const long items = (long)a.B * a.KV * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
+  const long items = (long)a.B * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
   hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
