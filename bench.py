@@ -126,9 +126,11 @@ def copy_calibration(torch, dev) -> None:
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
-def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
+def all_configs(torch, cgr, W, dev, steps: int, warmup: int, graph: bool = False) -> None:
     """Time the attention call alone on every workload configuration (HIP events on
-    the launch stream, mean over `steps` launches after `warmup`)."""
+    the launch stream, mean over `steps` launches after `warmup`). With `graph`,
+    also the same `steps` calls captured once in a HIP graph and replayed (no
+    per-call host work: the device time of launch-bound configurations)."""
     stream = torch.cuda.current_stream(dev)
     for w in W.WORKLOADS.values():
         inputs = W.make_inputs(w)
@@ -172,9 +174,22 @@ def all_configs(torch, cgr, W, dev, steps: int, warmup: int) -> None:
         us = e0.elapsed_time(e1) * 1e3 / steps
         flops = W.algorithmic_flops(w.n_head, w.head_dim, lengths, w.causal)
         tf = flops / (us * 1e-6) / 1e12
-        print(json.dumps({"workload": w.name, "io": "f32" if w.dtype == "f32" else "bf16",
-                          "us_per_call": round(us, 2), "flops": flops, "tflops": round(tf, 3),
-                          "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2)}), flush=True)
+        line = {"workload": w.name, "io": "f32" if w.dtype == "f32" else "bf16", "us_per_call": round(us, 2),
+                "flops": flops, "tflops": round(tf, 3), "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2)}
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(steps):
+                    call()
+            g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gus = e0.elapsed_time(e1) * 1e3 / steps
+            line.update(graph_us_per_call=round(gus, 2), graph_tflops=round(flops / (gus * 1e-6) / 1e12, 3))
+        print(json.dumps(line), flush=True)
 
 
 BWD_METRIC = "causal GQA+RoPE attention bwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
@@ -564,6 +579,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--all-configs", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --all-configs: also time the calls captured in a HIP graph and replayed")
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
@@ -592,7 +609,7 @@ def main() -> int:
         copy_calibration(torch, dev)
         return 0
     if args.all_configs:
-        all_configs(torch, cgr, W, dev, args.steps, args.warmup)
+        all_configs(torch, cgr, W, dev, args.steps, args.warmup, graph=args.graph)
         return 0
     if args.backward:
         backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline, args.window)
