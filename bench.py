@@ -9,10 +9,14 @@ Inputs are already resident in HBM when the timed region starts.
 Prints one JSON line. `value` is algorithmic TFLOP/s of the step (causal
 FLOPs counted exactly: 4*d per visible (query, key) pair per query head).
 The forward is given a workspace, so the keys are rotated once by a small
-kernel before the attention kernel; both run inside the timed step.
-`roofline` reports the attention kernel itself: its average launch duration
-measured with HIP events on the stream it is launched on, against the MI355X
-dense f16/bf16 MFMA peak; `traffic` is HBM bytes per launch from rocprofv3
+kernel before the attention kernel; both run inside the timed step, enqueued
+through the forward's two halves (cgr_attn_fwd_rotate_keys, then
+cgr_gqa_rope_attn_fwd_rotated: the kernels and bits of one
+cgr_gqa_rope_attn_fwd call) so that the attention kernel has HIP events of
+its own. `roofline` reports that kernel alone: its mean launch duration (and
+median) from those events on the launch stream, against the MI355X dense
+f16/bf16 MFMA peak, with the whole call beside it and the graphics clock
+sampled from amd-smi meanwhile; `traffic` is HBM bytes per launch from rocprofv3
 counters (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
 read from profiles/ and reported only while the kernel sources still hash to
 the value recorded with them. `cpu_baseline` times the float64 oracle on a
@@ -21,7 +25,9 @@ bounded sample of the same workload on this host's cores.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --copy-calibration   (plain copies, for counter scaling)
   python bench.py --all-configs        (one JSON line per workload configuration,
-                                        attention call only; not the headline line)
+                                        attention call only; not the headline line;
+                                        --only NAME: that workload alone; --graph: also
+                                        replayed from a HIP graph)
   python bench.py --backward           (one JSON line for the backward on the same
                                         workload; not the headline line)
   python bench.py --decode             (one JSON line for decode against a KV cache,
@@ -45,7 +51,9 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -87,6 +95,56 @@ def read_traffic():
         return None
 
 
+class ClockSampler:
+    """The GPU's graphics clock (MHz), sampled from amd-smi every 2 ms on a
+    thread while started; summary() gives the samples' median, min, max and
+    count, or None where amd-smi is unavailable."""
+
+    def __init__(self):
+        self.samples = []
+        self._run = False
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) == 1:
+                self._handle = handles[0]
+                self._amdsmi = amdsmi
+        except Exception:
+            self._handle = None
+
+    def _loop(self):
+        while self._run:
+            try:
+                c = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)["clk"]
+                if isinstance(c, (int, float)) and c > 0:
+                    self.samples.append(float(c))
+            except Exception:
+                pass
+            time.sleep(0.002)
+
+    def start(self):
+        if self._handle is None:
+            return
+        self._run = True
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._run = False
+        if self._thread is not None:
+            self._thread.join()
+            self._thread = None
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median": statistics.median(self.samples), "min": min(self.samples), "max": max(self.samples),
+                "samples": len(self.samples), "source": "amd-smi GFX clock during the timed steps and 0.3 s more"}
+
+
 def cpu_baseline(inputs, w) -> dict:
     """The float64 oracle, as it stands, on the whole workload (every query
     head at the full T = 8192), about 10 s on 16 host cores."""
@@ -126,13 +184,15 @@ def copy_calibration(torch, dev) -> None:
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "copies": 3}), flush=True)
 
 
-def all_configs(torch, cgr, W, dev, steps: int, warmup: int, graph: bool = False) -> None:
+def all_configs(torch, cgr, W, dev, steps: int, warmup: int, graph: bool = False, only=None) -> None:
     """Time the attention call alone on every workload configuration (HIP events on
     the launch stream, mean over `steps` launches after `warmup`). With `graph`,
     also the same `steps` calls captured once in a HIP graph and replayed (no
     per-call host work: the device time of launch-bound configurations)."""
     stream = torch.cuda.current_stream(dev)
     for w in W.WORKLOADS.values():
+        if only and w.name != only:
+            continue
         inputs = W.make_inputs(w)
         q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
         max_pos = inputs["max_seqlen"] if w.varlen else w.T
@@ -581,6 +641,7 @@ def main() -> int:
     ap.add_argument("--all-configs", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="with --all-configs: also time the calls captured in a HIP graph and replayed")
+    ap.add_argument("--only", default=None, help="with --all-configs: this workload only")
     ap.add_argument("--backward", action="store_true")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
@@ -609,7 +670,7 @@ def main() -> int:
         copy_calibration(torch, dev)
         return 0
     if args.all_configs:
-        all_configs(torch, cgr, W, dev, args.steps, args.warmup, graph=args.graph)
+        all_configs(torch, cgr, W, dev, args.steps, args.warmup, graph=args.graph, only=args.only)
         return 0
     if args.backward:
         backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline, args.window)
@@ -648,31 +709,59 @@ def main() -> int:
 
     ws = torch.empty(cgr.cgr_attn_fwd_workspace_size(w.B, w.T, w.n_kv_head, w.head_dim), dtype=torch.uint8,
                      device=dev)
+    kw = dict(rope_style=w.rope_style, seqlens=seqlens)
+
+    # The forward with a workspace, in its two halves (the same kernels and bits
+    # as one cgr_gqa_rope_attn_fwd call): the key rotation, then the attention
+    # kernel alone between its own pair of HIP events.
+    def rotate():
+        cgr.attn_fwd_rotate_keys(k, cos, sin, ws, **kw)
 
     def attention():
-        cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=args.window,
-                              out=o, lse=lse, workspace=ws, seqlens=seqlens)
+        cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws, causal=True, window=args.window, out=o, lse=lse, **kw)
+
+    def step():
+        tables()
+        rotate()
+        attention()
 
     for _ in range(args.warmup):
-        tables()
-        attention()
+        step()
     torch.cuda.synchronize()
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    clock = ClockSampler()
     torch.cuda.synchronize()
+    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         tables()
         ev[i][0].record(stream)
-        attention()
+        rotate()
         ev[i][1].record(stream)
+        attention()
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.stop()
+    # The clock under this load, sampled again over a longer stretch of the same
+    # steps after the timed region (the timed region itself may be too short
+    # for more than a few samples).
+    clock.start()
+    t1 = time.perf_counter()
+    while time.perf_counter() - t1 < 0.3:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    clock.stop()
 
     flops = W.algorithmic_flops(w.n_head, w.head_dim, lens, True, args.window)
     ms_step = wall * 1e3 / args.steps
-    kernel_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    kern = [b.elapsed_time(c) for _, b, c in ev]
+    call = [a.elapsed_time(c) for a, _, c in ev]
+    rot = [a.elapsed_time(b) for a, b, _ in ev]
+    kernel_ms, kernel_med = sum(kern) / len(kern), statistics.median(kern)
+    call_ms, call_med = sum(call) / len(call), statistics.median(call)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     headline = args.window == 0 and not args.padded and not args.wide
     traffic = read_traffic() if headline else None
@@ -695,7 +784,8 @@ def main() -> int:
             "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
             "io": "bf16", "qk_operand": "f16", "pv_operand": "bf16", "accumulate": "f32",
             **({"valid_lengths": lens} if args.padded else {}),
-            "step": "rope_tables + gqa_rope_attn_fwd", "window": args.window, "flops_per_step": flops,
+            "step": "rope_tables + attn_fwd_rotate_keys + gqa_rope_attn_fwd_rotated (= gqa_rope_attn_fwd)",
+            "window": args.window, "flops_per_step": flops,
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
         "roofline": {
@@ -705,9 +795,16 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "the attention call: krot_kernel (keys rotated once) + attn_fwd_dense_kernel "
-                      f"(head_dim {w.head_dim}, bf16 I/O, f16 QK, causal, interleaved); HIP events around the call",
+            "kernel": f"attn_fwd_dense_kernel (head_dim {w.head_dim}, bf16 I/O, f16 QK, causal, {w.rope_style}); "
+                      "HIP events around its launch alone, on the launch stream",
             "kernel_ms": round(kernel_ms, 5),
+            "kernel_ms_median": round(kernel_med, 5),
+            "achieved_at_median": round(flops / (kernel_med * 1e-3) / 1e12, 3),
+            "call_ms": round(call_ms, 5),
+            "call_ms_median": round(call_med, 5),
+            "call_tflops": round(flops / (call_ms * 1e-3) / 1e12, 3),
+            "rotate_keys_ms": round(sum(rot) / len(rot), 5),
+            "clock_mhz": clock.summary(),
         },
         "cpu_baseline": None if args.no_cpu_baseline or not headline else cpu_baseline(inputs, w),
     }

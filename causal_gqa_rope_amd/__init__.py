@@ -31,6 +31,8 @@ __all__ = [
     "cgr_rope_tables",
     "cgr_gqa_rope_attn_fwd",
     "cgr_attn_fwd_workspace_size",
+    "cgr_attn_fwd_rotate_keys",
+    "cgr_gqa_rope_attn_fwd_rotated",
     "cgr_gqa_rope_attn_fwd_varlen",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_attn_fwd_varlen_rotated_workspace_size",
@@ -68,6 +70,8 @@ EXPORTED_SYMBOLS = (
     "cgr_rope_tables",
     "cgr_gqa_rope_attn_fwd",
     "cgr_attn_fwd_workspace_size",
+    "cgr_attn_fwd_rotate_keys",
+    "cgr_gqa_rope_attn_fwd_rotated",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_attn_fwd_varlen_rotated_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
@@ -124,6 +128,11 @@ def library() -> ctypes.CDLL:
     lib.cgr_gqa_rope_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp,
                                           i32, i32, i32, i32, f32, i32, vp, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd.restype = i32
+    lib.cgr_attn_fwd_rotate_keys.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, i32, i32, i32, vp, vp,
+                                             ctypes.c_size_t, vp]
+    lib.cgr_attn_fwd_rotate_keys.restype = i32
+    lib.cgr_gqa_rope_attn_fwd_rotated.argtypes = lib.cgr_gqa_rope_attn_fwd.argtypes
+    lib.cgr_gqa_rope_attn_fwd_rotated.restype = i32
     lib.cgr_attn_fwd_fp8_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.cgr_attn_fwd_fp8_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, vp, vp,
@@ -213,20 +222,9 @@ def cgr_rope_tables(max_pos: int, head_dim: int, base: float,
     return cos, sin
 
 
-def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope_cos: torch.Tensor,
-                          rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
-                          window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
-                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                          return_lse: bool = True, workspace=None, seqlens: Optional[torch.Tensor] = None):
-    """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None).
-
-    workspace: None allocates one (bf16 I/O: the keys are then rotated once up
-    front), a uint8 device tensor of cgr_attn_fwd_workspace_size bytes is used
-    as given, and False passes none (the keys are rotated on every tile).
-    seqlens: optional int32 device tensor [B] of valid tokens per entry (right
-    padding): keys past them are hidden, rows past them are left unwritten.
-    """
-    lib = library()
+def _dense_fwd_args(q, k, v, rope_cos, rope_sin, causal, rope_style, window, softmax_scale, qk_operand, out, lse,
+                    return_lse, seqlens):
+    """Checks and the C argument list (without workspace and stream) of a dense forward call."""
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(n, t)
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -255,6 +253,30 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
         _dev_tensor("seqlens", seqlens, torch.int32)
         if tuple(seqlens.shape) != (B,):
             raise CgrError(CGR_ERR_INVALID_ARG, "seqlens must be [B]")
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
+            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
+            CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _ptr(seqlens)]
+    return args, out, lse
+
+
+def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope_cos: torch.Tensor,
+                          rope_sin: torch.Tensor, *, causal: bool = True, rope_style: str = "interleaved",
+                          window: int = 0, softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                          out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                          return_lse: bool = True, workspace=None, seqlens: Optional[torch.Tensor] = None):
+    """Dense forward: q [B,T,H,d], k/v [B,T,KV,d] -> (o [B,T,H,d], lse [B,H,T] float32 or None).
+
+    workspace: None allocates one (bf16 I/O: the keys are then rotated once up
+    front), a uint8 device tensor of cgr_attn_fwd_workspace_size bytes is used
+    as given, and False passes none (the keys are rotated on every tile).
+    seqlens: optional int32 device tensor [B] of valid tokens per entry (right
+    padding): keys past them are hidden, rows past them are left unwritten.
+    """
+    lib = library()
+    args, out, lse = _dense_fwd_args(q, k, v, rope_cos, rope_sin, causal, rope_style, window, softmax_scale,
+                                     qk_operand, out, lse, return_lse, seqlens)
+    B, T, _, D = q.shape
     if workspace is None and q.dtype == torch.bfloat16:
         workspace = torch.empty(int(lib.cgr_attn_fwd_workspace_size(B, T, k.shape[2], D)), dtype=torch.uint8,
                                 device=q.device)
@@ -264,12 +286,48 @@ def cgr_gqa_rope_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rop
         _dev_tensor("workspace", workspace)
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
-        _check(lib.cgr_gqa_rope_attn_fwd(
-            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, _DTYPES[q.dtype],
-            _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
-            CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
-            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _ptr(seqlens), ws_ptr,
-            ws_bytes, _stream(q.device)))
+        _check(lib.cgr_gqa_rope_attn_fwd(*args, ws_ptr, ws_bytes, _stream(q.device)))
+    return out, lse
+
+
+def cgr_attn_fwd_rotate_keys(k: torch.Tensor, rope_cos: torch.Tensor, rope_sin: torch.Tensor,
+                             workspace: torch.Tensor, *, rope_style: str = "interleaved", qk_operand: str = "f16",
+                             seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The first half of a dense bf16 forward: k [B,T,KV,d] rotated once into `workspace`
+    (uint8, cgr_attn_fwd_workspace_size bytes). Returns the workspace."""
+    lib = library()
+    _dev_tensor("k", k, torch.bfloat16)
+    _dev_tensor("workspace", workspace)
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if k.dim() != 4:
+        raise CgrError(CGR_ERR_INVALID_ARG, "k must be 4-D [B, T, n_kv_head, head_dim]")
+    B, T, KV, D = k.shape
+    if seqlens is not None:
+        _dev_tensor("seqlens", seqlens, torch.int32)
+    with torch.cuda.device(k.device):
+        _check(lib.cgr_attn_fwd_rotate_keys(
+            _ptr(k), B, T, KV, D, CGR_BF16, _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style],
+            _QK[qk_operand], _ptr(seqlens), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(k.device)))
+    return workspace
+
+
+def cgr_gqa_rope_attn_fwd_rotated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rope_cos: torch.Tensor,
+                                  rope_sin: torch.Tensor, workspace: torch.Tensor, *, causal: bool = True,
+                                  rope_style: str = "interleaved", window: int = 0,
+                                  softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                  return_lse: bool = True, seqlens: Optional[torch.Tensor] = None):
+    """The second half of a dense bf16 forward: attention over the keys that
+    cgr_attn_fwd_rotate_keys left in `workspace` (same k, tables, style, operand, seqlens)."""
+    lib = library()
+    args, out, lse = _dense_fwd_args(q, k, v, rope_cos, rope_sin, causal, rope_style, window, softmax_scale,
+                                     qk_operand, out, lse, return_lse, seqlens)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_fwd_rotated(*args, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                 _stream(q.device)))
     return out, lse
 
 
@@ -594,6 +652,8 @@ def cgr_rmsnorm_qkv_rope(x: torch.Tensor, norm_weight: torch.Tensor, eps: float,
 
 rope_tables = cgr_rope_tables
 gqa_rope_attn_fwd = cgr_gqa_rope_attn_fwd
+attn_fwd_rotate_keys = cgr_attn_fwd_rotate_keys
+gqa_rope_attn_fwd_rotated = cgr_gqa_rope_attn_fwd_rotated
 gqa_rope_attn_fwd_fp8 = cgr_gqa_rope_attn_fwd_fp8
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd

@@ -1420,14 +1420,21 @@ hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t str
   return hipGetLastError();
 }
 
+// What a dense-batch launch with once-rotated keys (a.krot set) enqueues:
+// the key rotation into the workspace, the attention kernel over it, or both.
+enum { PHASE_ROTATE = 1, PHASE_ATTEND = 2, PHASE_ALL = 3 };
+
 // Dense batch with the K rotation done once up front (a.krot set).
 template <class C>
-hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream) {
-  const long items = (long)a.B * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
-  hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int phases) {
+  if (phases & PHASE_ROTATE) {
+    const long items = (long)a.B * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
+    hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & PHASE_ATTEND)
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
   return hipGetLastError();
 }
 
@@ -1461,14 +1468,15 @@ constexpr int kMinBM = 32;  // smallest query block of any unit
 // Bytes of one K tile image of the once-rotated keys (16-bit operands).
 constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_dim) * 2 * head_dim; }
 
+// phases (dense batches with a.krot set): PHASE_ROTATE, PHASE_ATTEND or both.
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                         bool varlen, int grid, hipStream_t stream) {
+                         bool varlen, int grid, hipStream_t stream, int phases) {
 #define CGR_LAUNCH(IO, QK, CAU, STY, WIN)                                                       \
   if constexpr (!std::is_same<IO, float>::value) {                                               \
     if (a.krot != nullptr)                                                                        \
       return varlen ? launch_attn_kpre_varlen<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream) \
-                    : launch_attn_kpre<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream);    \
+                    : launch_attn_kpre<Cfg<D, IO, QK, CAU, STY, WIN, true>>(a, grid, stream, phases); \
   }                                                                                               \
   return launch_attn<Cfg<D, IO, QK, CAU, STY, WIN>>(a, varlen, grid, stream)
 #define CGR_BY_STYLE(IO, QK, CAU, WIN) \

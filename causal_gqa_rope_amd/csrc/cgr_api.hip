@@ -131,14 +131,14 @@ cgr::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, fl
 
 hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, cgr_qk_operand qk,
                          cgr_rope_style style, cgr_mask mask, bool varlen, int grid,
-                         hipStream_t s) {
+                         hipStream_t s, int phases = cgr::PHASE_ALL) {
   const int f32 = dtype == CGR_F32, qkb = qk == CGR_QK_BF16, sty = (int)style,
             cau = mask == CGR_MASK_CAUSAL;
   switch (head_dim) {
-    case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s);
-    case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s);
-    case 128: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s);
-    default: return cgr::launch_attn_d256(a, f32, qkb, sty, cau, varlen, grid, s);
+    case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s, phases);
+    case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s, phases);
+    case 128: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s, phases);
+    default: return cgr::launch_attn_d256(a, f32, qkb, sty, cau, varlen, grid, s, phases);
   }
 }
 
@@ -194,35 +194,14 @@ DecodePlan decode_plan(int B, int Tq, int max_seqlen, int n_head, int n_kv_head,
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float* cos_out, float* sin_out,
-                           void* stream) {
-  if (!cos_out || !sin_out) return fail(CGR_ERR_INVALID_ARG, "cos_out and sin_out must be non-null");
-  if (max_pos < 1) return fail(CGR_ERR_INVALID_ARG, "max_pos (%d) must be >= 1", max_pos);
-  if (head_dim < 2 || head_dim % 2 != 0)
-    return fail(CGR_ERR_INVALID_ARG, "head_dim (%d) must be even and >= 2", head_dim);
-  if (!(base > 0.0) || !std::isfinite(base))
-    return fail(CGR_ERR_INVALID_ARG, "base must be positive and finite");
-  if (!aligned(cos_out, 4) || !aligned(sin_out, 4))
-    return fail(CGR_ERR_ALIGNMENT, "tables must be 4-byte aligned");
-  if ((long)max_pos * (head_dim / 2) > (long)INT_MAX * 256)
-    return fail(CGR_ERR_INVALID_ARG, "table too large");
-  const hipError_t e = cgr::launch_rope_tables(max_pos, head_dim, base, cos_out, sin_out,
-                                               (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail("rope_tables launch", e);
-  return CGR_OK;
-}
-
-cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                                 int B, int T, int n_head, int n_kv_head, int head_dim,
-                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
-                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
-                                 float softmax_scale, cgr_qk_operand qk_operand,
-                                 const int32_t* seqlens, void* workspace, size_t workspace_bytes,
-                                 void* stream) {
+// The dense-batch forward behind cgr_gqa_rope_attn_fwd and its two halves
+// (cgr_attn_fwd_rotate_keys, cgr_gqa_rope_attn_fwd_rotated): checks, launch
+// configuration, then the phases asked for.
+cgr_status dense_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int T,
+                     int n_head, int n_kv_head, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                     const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                     int window, float softmax_scale, cgr_qk_operand qk_operand, const int32_t* seqlens,
+                     void* workspace, size_t workspace_bytes, void* stream, int phases) {
   if (seqlens != nullptr && !aligned(seqlens, 4))
     return fail(CGR_ERR_ALIGNMENT, "seqlens must be 4-byte aligned");
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
@@ -252,9 +231,70 @@ cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, vo
   a.seqlens = seqlens;
   a.krot = use_ws ? workspace : nullptr;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
-                                     (hipStream_t)stream);
+                                     (hipStream_t)stream, phases);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   return CGR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float* cos_out, float* sin_out,
+                           void* stream) {
+  if (!cos_out || !sin_out) return fail(CGR_ERR_INVALID_ARG, "cos_out and sin_out must be non-null");
+  if (max_pos < 1) return fail(CGR_ERR_INVALID_ARG, "max_pos (%d) must be >= 1", max_pos);
+  if (head_dim < 2 || head_dim % 2 != 0)
+    return fail(CGR_ERR_INVALID_ARG, "head_dim (%d) must be even and >= 2", head_dim);
+  if (!(base > 0.0) || !std::isfinite(base))
+    return fail(CGR_ERR_INVALID_ARG, "base must be positive and finite");
+  if (!aligned(cos_out, 4) || !aligned(sin_out, 4))
+    return fail(CGR_ERR_ALIGNMENT, "tables must be 4-byte aligned");
+  if ((long)max_pos * (head_dim / 2) > (long)INT_MAX * 256)
+    return fail(CGR_ERR_INVALID_ARG, "table too large");
+  const hipError_t e = cgr::launch_rope_tables(max_pos, head_dim, base, cos_out, sin_out,
+                                               (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail("rope_tables launch", e);
+  return CGR_OK;
+}
+
+cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int T, int n_head, int n_kv_head, int head_dim,
+                                 cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                 int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                                 float softmax_scale, cgr_qk_operand qk_operand,
+                                 const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  return dense_fwd(q, k, v, o, lse, B, T, n_head, n_kv_head, head_dim, dtype, rope_cos, rope_sin, rope_max_pos,
+                   style, mask, window, softmax_scale, qk_operand, seqlens, workspace, workspace_bytes, stream,
+                   cgr::PHASE_ALL);
+}
+
+cgr_status cgr_attn_fwd_rotate_keys(const void* k, int B, int T, int n_kv_head, int head_dim, cgr_dtype dtype,
+                                    const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                                    cgr_rope_style style, cgr_qk_operand qk_operand, const int32_t* seqlens,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != CGR_BF16) return fail(CGR_ERR_UNSUPPORTED, "keys are rotated once for CGR_BF16 I/O only");
+  if (workspace == nullptr) return fail(CGR_ERR_WORKSPACE, "the rotated keys need a workspace");
+  // Only k, the tables and the workspace are read or written; the query-side
+  // checks see k in place of q, v and o, and one query head per K/V head.
+  return dense_fwd(k, k, k, const_cast<void*>(k), nullptr, B, T, n_kv_head, n_kv_head, head_dim, dtype, rope_cos,
+                   rope_sin, rope_max_pos, style, CGR_MASK_CAUSAL, 0, 0.f, qk_operand, seqlens, workspace,
+                   workspace_bytes, stream, cgr::PHASE_ROTATE);
+}
+
+cgr_status cgr_gqa_rope_attn_fwd_rotated(const void* q, const void* k, const void* v, void* o, float* lse,
+                                         int B, int T, int n_head, int n_kv_head, int head_dim,
+                                         cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                         int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                                         float softmax_scale, cgr_qk_operand qk_operand,
+                                         const int32_t* seqlens, const void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (dtype != CGR_BF16) return fail(CGR_ERR_UNSUPPORTED, "keys are rotated once for CGR_BF16 I/O only");
+  if (workspace == nullptr) return fail(CGR_ERR_WORKSPACE, "the rotated keys need a workspace");
+  return dense_fwd(q, k, v, o, lse, B, T, n_head, n_kv_head, head_dim, dtype, rope_cos, rope_sin, rope_max_pos,
+                   style, mask, window, softmax_scale, qk_operand, seqlens, const_cast<void*>(workspace),
+                   workspace_bytes, stream, cgr::PHASE_ATTEND);
 }
 
 size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim) {

@@ -149,6 +149,42 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const voi
                                  void* stream);
 
 /*
+ * The two halves of cgr_gqa_rope_attn_fwd with a workspace (bf16 I/O), for a
+ * caller that attends several times to the same keys, or that times the
+ * attention kernel on its own. Enqueued back to back with the same
+ * arguments they give the bits of the one call.
+ *
+ * cgr_attn_fwd_rotate_keys: rotates every key of k (device [B, T, n_kv_head,
+ *   head_dim], bf16) at its position ("Embeddings & the Residual Stream",
+ *   "Positional information: RoPE") and writes it, rounded once to the
+ *   qk_operand type, into `workspace` (cgr_attn_fwd_workspace_size(B, T,
+ *   n_kv_head, head_dim) bytes, 16-byte aligned). seqlens as for the forward
+ *   (keys past an entry's length become zeros). Reads nothing else.
+ *   dtype must be CGR_BF16 and workspace non-NULL (else CGR_ERR_UNSUPPORTED /
+ *   CGR_ERR_WORKSPACE); the other checks are those of the forward.
+ *
+ * cgr_gqa_rope_attn_fwd_rotated: the attention of cgr_gqa_rope_attn_fwd over
+ *   the keys cgr_attn_fwd_rotate_keys left in `workspace` (which this call
+ *   only reads). Every argument means what it means for the forward; k,
+ *   rope_cos/rope_sin, rope_style, qk_operand and seqlens must be those the
+ *   keys were rotated with (the kernel cannot tell, and other values give a
+ *   wrong result, not an error). k is still read where a unit recomputes its
+ *   scores from the raw keys.
+ */
+CGR_API cgr_status cgr_attn_fwd_rotate_keys(const void* k, int B, int T, int n_kv_head, int head_dim,
+                                    cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                    int rope_max_pos, cgr_rope_style style, cgr_qk_operand qk_operand,
+                                    const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+CGR_API cgr_status cgr_gqa_rope_attn_fwd_rotated(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int B, int T, int n_head, int n_kv_head,
+                                         int head_dim, cgr_dtype dtype, const float* rope_cos,
+                                         const float* rope_sin, int rope_max_pos, cgr_rope_style style,
+                                         cgr_mask mask, int window, float softmax_scale,
+                                         cgr_qk_operand qk_operand, const int32_t* seqlens,
+                                         const void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of the workspace of cgr_gqa_rope_attn_fwd_fp8: the rotated keys and
  * the transposed values as 64-key tile images, 2 * B * n_kv_head *
  * ceil(T / 64) * 64 * head_dim. Returns 0 for invalid sizes (head_dim must be

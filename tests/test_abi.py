@@ -127,6 +127,49 @@ def test_dense_rejects_bad_arguments(kw, status, needle):
     assert needle in msg
 
 
+def rotate_keys(**kw):
+    a = dict(k=P, B=1, T=16, KV=2, D=64, dtype=1, cos=P, sin=P, P=16, style=0, qk=0, seqlens=None, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_attn_fwd_rotate_keys(a["k"], a["B"], a["T"], a["KV"], a["D"], a["dtype"], a["cos"], a["sin"],
+                                      a["P"], a["style"], a["qk"], a["seqlens"], a["ws"], a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+def rotated(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
+             P=16, style=0, mask=1, window=0, scale=0.0, qk=0, seqlens=None, ws=P, wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_fwd_rotated(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"],
+                                           a["KV"], a["D"], a["dtype"], a["cos"], a["sin"], a["P"], a["style"],
+                                           a["mask"], a["window"], a["scale"], a["qk"], a["seqlens"], a["ws"],
+                                           a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("fn,kw,status,needle", [
+    (rotate_keys, dict(ws=None), 4, "workspace"),
+    (rotate_keys, dict(wsb=100), 4, "needs"),
+    (rotate_keys, dict(dtype=0), 2, "CGR_BF16"),
+    (rotate_keys, dict(k=None), 1, "non-null"),
+    (rotate_keys, dict(P=15), 1, "positions"),
+    (rotate_keys, dict(D=96), 2, "not one of"),
+    (rotate_keys, dict(ws=PMIS), 3, "aligned"),
+    (rotated, dict(ws=None), 4, "workspace"),
+    (rotated, dict(wsb=100), 4, "needs"),
+    (rotated, dict(dtype=0), 2, "CGR_BF16"),
+    (rotated, dict(H=6, KV=4), 1, "divisible"),
+    (rotated, dict(window=4, mask=0), 1, "CGR_MASK_CAUSAL"),
+])
+def test_rotate_keys_and_rotated_reject_bad_arguments(fn, kw, status, needle):
+    st, msg = fn(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def fp8(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=128, qd=0.01, kd=0.01, vd=0.01, cos=P, sin=P,
              P=16, style=0, mask=1, scale=0.0, ws=P, wsb=1 << 20)
