@@ -651,6 +651,11 @@ struct UnitFast {
       }
     }
     Frag<QK> qf[C::KSTEPS];
+    // f16 operands: a rotated query (times scale*log2(e)) or key outside the
+    // f16 range enters the product as NaN (to_frag_or_nan, here and in the key
+    // rotation), so every row that meets it ends with a NaN row sum and the
+    // unit is redone by wide_pass.
+    constexpr bool F16OP = std::is_same<QK, OpF16>::value;
     // Q fragments straight from global memory (the windowed path): each lane
     // loads its own row's groups, k-step s2 holding group g = 2 s2 + hh and
     // k-step s2 + D/32 group g + D/16.
@@ -674,8 +679,8 @@ struct UnitFast {
           x0[j] *= a.qscale;
           x1[j] *= a.qscale;
         }
-        qf[s2] = to_frag<QK>(x0);
-        qf[s2 + D / 32] = to_frag<QK>(x1);
+        qf[s2] = to_frag_or_nan<QK>(x0);
+        qf[s2 + D / 32] = to_frag_or_nan<QK>(x1);
       }
     };
     auto stage_q = [&]() {
@@ -702,11 +707,11 @@ struct UnitFast {
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) x0[j] *= a.qscale;
-        *(u32x4*)dst = to_frag<QK>(x0).v;
+        *(u32x4*)dst = to_frag_or_nan<QK>(x0).v;
         if constexpr (Q_HALF) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) x1[j] *= a.qscale;
-          *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+          *(u32x4*)(dst + D) = to_frag_or_nan<QK>(x1).v;
         }
       }
       // Operand fragments: k-step s of lane (l32, hh) holds elements 16s+8hh..+7
@@ -801,8 +806,8 @@ struct UnitFast {
             raw_to_f32<uint16_t>(w0, x0);
             raw_to_f32<uint16_t>(w1, x1);
             rope_pair<C::STYLE>(x0, x1, kc[u], ksn[u]);
-            *(u32x4*)dst = to_frag<QK>(x0).v;
-            *(u32x4*)(dst + D) = to_frag<QK>(x1).v;
+            *(u32x4*)dst = to_frag_or_nan<QK>(x0).v;
+            *(u32x4*)(dst + D) = to_frag_or_nan<QK>(x1).v;
           }
         }
       }
@@ -1002,11 +1007,124 @@ struct UnitFast {
       }
       return m_run;
     };
+    // ---- Wide-range pass: units whose rotated queries or keys leave the range
+    // of the f16 operand (a NaN row sum: see to_frag_or_nan). The classic online softmax over the unit's
+    // tiles, one LDS stage, with every operand carried as a bf16 hi + lo pair:
+    // S = K_hi Q_hi + K_hi Q_lo + K_lo Q_hi (16 significant bits, f32's range;
+    // K_lo Q_lo is below the f32 accumulation's rounding). Queries and keys are
+    // rotated again from the raw inputs, so nothing out of range is reused.
+    auto wide_pass = [&](auto win_tag) -> float {
+      constexpr bool WIN = decltype(win_tag)::value;
+      const int jb = WIN ? j0 : 0;
+      Frag<OpBF16> qh[C::KSTEPS], ql[C::KSTEPS];
+      {
+        const bool ok = my_q < L;
+        const long tq = (long)(ok ? my_q : 0);
+#pragma unroll
+        for (int s2 = 0; s2 < D / 32; ++s2) {
+          const int g = 2 * s2 + hh;
+          u32x4 w0[1], w1[1];
+          load8_raw<uint16_t>(qbase + tq * qs + 8 * g, ok, w0);
+          load8_raw<uint16_t>(qbase + tq * qs + 8 * g + D / 2, ok, w1);
+          f32x4 c[2], s[2];
+          load_tab<D, C::STYLE>(a.rope_cos + tq * (D / 2), a.rope_sin + tq * (D / 2), g, ok, c, s);
+          float x0[8], x1[8];
+          raw_to_f32<uint16_t>(w0, x0);
+          raw_to_f32<uint16_t>(w1, x1);
+          rope_pair<C::STYLE>(x0, x1, c, s);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            x0[j] *= a.qscale;
+            x1[j] *= a.qscale;
+          }
+          split_bf16(x0, qh[s2], ql[s2]);
+          split_bf16(x1, qh[s2 + D / 32], ql[s2 + D / 32]);
+        }
+      }
+      const rsrc_t rkr = make_rsrc(kbase, (uint32_t)(((L - 1) * ks + D) * 2));
+      float m_run = -INFINITY;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) oacc[db] = (f32x16){};
+      l_run = 0.f;
+      for (int j = jb; j < n_tiles; ++j) {
+        __syncthreads();  // the stages' earlier readers are done
+        load_v(j * BN, vs0, vw);
+        // Raw K of tile j at its positions, split into hi (stage ks0) and lo
+        // (stage ks1), padded rows as in the per-tile rotation.
+#pragma unroll
+        for (int u = 0; u < KI; ++u) {
+          if (has_k(u)) {
+            const int so = (j * BN + u * RPU) * ks * 2, st = (j * BN + u * RPU) * (D / 2) * 4;
+            const u32x4 w0[1] = {buf_load16(rkr, k_vo, so)}, w1[1] = {buf_load16(rkr, k_vo + D, so)};
+            const f32x4 c[2] = {buf_load16f(rc, t_vo, st), buf_load16f(rc, t_vo + TAB_O1, st)};
+            const f32x4 sn[2] = {buf_load16f(rs, t_vo, st), buf_load16f(rs, t_vo + TAB_O1, st)};
+            float x0[8], x1[8];
+            raw_to_f32<uint16_t>(w0, x0);
+            raw_to_f32<uint16_t>(w1, x1);
+            rope_pair<C::STYLE>(x0, x1, c, sn);
+            Frag<OpBF16> h0, l0, h1, l1;
+            split_bf16(x0, h0, l0);
+            split_bf16(x1, h1, l1);
+            const int o = k_lds + u * RPU * C::K_STRIDE;
+            *(u32x4*)(ks0 + o) = h0.v;
+            *(u32x4*)(ks0 + o + D) = h1.v;
+            *(u32x4*)(ks1 + o) = l0.v;
+            *(u32x4*)(ks1 + o + D) = l1.v;
+          }
+        }
+        wait_vmem();
+        __syncthreads();
+        if (wave_has_rows && (!C::CAUSAL || j * BN <= wave_last) &&
+            (!WIN || j * BN + BN - 1 >= qw0 - W + 1)) {
+          f32x16 sacc[C::NKB];
+#pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) sacc[kb] = (f32x16){};
+#pragma unroll
+          for (int s = 0; s < C::KSTEPS; ++s)
+#pragma unroll
+            for (int kb = 0; kb < C::NKB; ++kb) {
+              Frag<OpBF16> kh, kl;
+              kh.v = *(const u32x4*)(ks0 + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
+              kl.v = *(const u32x4*)(ks1 + k_rd + kb * 32 * C::K_STRIDE + 32 * s);
+              sacc[kb] = mma32(kh, qh[s], sacc[kb]);
+              sacc[kb] = mma32(kh, ql[s], sacc[kb]);
+              sacc[kb] = mma32(kl, qh[s], sacc[kb]);
+            }
+          if constexpr (WIN)
+            mask_window(j, sacc);
+          else
+            mask(j, sacc);
+          const float m_new = fmaxf(m_run, rowmax(sacc));
+          const float m_use = m_new == -INFINITY ? 0.f : m_new;
+          const float alpha = fast_exp2(m_run - m_use);
+          m_run = m_new;
+          l_run *= alpha;
+          softmax_pv(vs0, sacc, std::true_type{}, m_use, std::true_type{}, alpha);
+        }
+      }
+      return m_run;
+    };
+    // After a fast pass: a unit out of the f16 range goes to wide_pass, one
+    // whose row sums outgrew the fixed reference to rescale_pass (one barrier
+    // when neither happened).
+    auto finish_unit = [&](float m_ref, auto win_tag) -> float {
+      const float l_chk = pair_sum(l_run);
+      const bool overflow = !(l_chk <= 1.099511627776e12f);  // 2^40; NaN-safe
+      if (!__syncthreads_or(overflow)) return m_ref;
+      if constexpr (F16OP) {
+        if (__syncthreads_or(l_chk != l_chk)) return wide_pass(win_tag);
+      }
+      return rescale_pass(win_tag);
+    };
     float m_fin;
     if (W > 0 && bm > BN) {
       // Q fragments straight from global memory, each lane its own row.
       load_q_direct();
       m_fin = rescale_pass(std::true_type{});
+      if constexpr (F16OP) {
+        const float l_chk = pair_sum(l_run);
+        if (__syncthreads_or(l_chk != l_chk)) m_fin = wide_pass(std::true_type{});
+      }
     } else if (W > 0) {
       // ---- Windowed fast path (units of at most one tile of rows, so every
       // row's own key lies in the unit's last tile jl). That tile goes first
@@ -1104,9 +1222,7 @@ struct UnitFast {
         }
       }
       for (; i < n_it; ++i) witer(i);
-      m_fin = m_ref;
-      const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
-      if (__syncthreads_or(overflow)) m_fin = rescale_pass(std::true_type{});
+      m_fin = finish_unit(m_ref, std::true_type{});
     } else {
       float m_ref = 0.f;
       {
@@ -1199,9 +1315,7 @@ struct UnitFast {
           iter(j, std::true_type{}, stage_of(j, ks0, ks1), stage_of(j + 1, ks0, ks1),
                stage_of(j, vs0, vs1), stage_of(j + 1, vs0, vs1));
       }
-      m_fin = m_ref;
-      const bool overflow = !(pair_sum(l_run) <= 1.099511627776e12f);  // 2^40; NaN-safe
-      if (__syncthreads_or(overflow)) m_fin = rescale_pass(std::false_type{});
+      m_fin = finish_unit(m_ref, std::false_type{});
     }
 
     // ---- Epilogue: O = O^T / l, rounded to bf16, goes through the wave's
@@ -1352,8 +1466,8 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
       raw_to_f32<uint16_t>(i0, x0);
       raw_to_f32<uint16_t>(i1, x1);
       rope_pair<C::STYLE>(x0, x1, c, s);
-      w0 = to_frag<typename C::QK>(x0).v;
-      w1 = to_frag<typename C::QK>(x1).v;
+      w0 = to_frag_or_nan<typename C::QK>(x0).v;
+      w1 = to_frag_or_nan<typename C::QK>(x1).v;
     }
     const long img = ((long)b * a.KV + kv) * n_img + tile;
     char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
@@ -1400,8 +1514,8 @@ __global__ __launch_bounds__(256) void krot_varlen_kernel(AttnArgs a) {
     f32x4 c[2], s[2];
     load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
     rope_pair<C::STYLE>(x0, x1, c, s);
-    w0 = to_frag<typename C::QK>(x0).v;
-    w1 = to_frag<typename C::QK>(x1).v;
+    w0 = to_frag_or_nan<typename C::QK>(x0).v;
+    w1 = to_frag_or_nan<typename C::QK>(x1).v;
   }
   char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
   *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;

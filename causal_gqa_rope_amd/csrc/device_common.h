@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace cgr {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -63,6 +65,48 @@ __device__ __forceinline__ Frag<OpF32> to_frag<OpF32>(const float (&x)[8]) {
   Frag<OpF32> f;
   f.v = (f32x8){x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
   return f;
+}
+
+// Range of the f16 operand: the largest finite f16 is 65504, and values of
+// magnitude 65520 or more round to infinity.
+constexpr float kF16Limit = 65520.f;
+
+// max |x_i| over eight values.
+__device__ __forceinline__ float absmax8(const float (&x)[8]) {
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  return m;
+}
+
+// Eight floats -> one fragment; for f16, a value outside its range becomes NaN
+// (not infinity), so that every score it enters is NaN whatever it is
+// multiplied by, and a row that sees it ends with a NaN row sum.
+template <typename Op>
+__device__ __forceinline__ Frag<Op> to_frag_or_nan(const float (&x)[8]) {
+  if constexpr (std::is_same<Op, OpF16>::value) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = fabsf(x[i]) < kF16Limit ? x[i] : __builtin_nanf("");
+    return to_frag<Op>(y);
+  } else {
+    return to_frag<Op>(x);
+  }
+}
+
+// bf16 hi + lo parts of eight floats: hi = x rounded to bf16, lo = (x - hi)
+// rounded to bf16, so hi + lo carries 16 significant bits and f32's range.
+__device__ __forceinline__ void split_bf16(const float (&x)[8], Frag<OpBF16>& hi, Frag<OpBF16>& lo) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h = pack2(OpBF16{}, x[2 * i], x[2 * i + 1]);
+    hi.v[i] = h;
+    r[2 * i] = x[2 * i] - bf16_lo(h);
+    r[2 * i + 1] = x[2 * i + 1] - bf16_hi(h);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo.v[i] = pack2(OpBF16{}, r[2 * i], r[2 * i + 1]);
 }
 
 // D = A(32x16) * B(16x32) + C on the matrix cores. Lane l supplies row/column

@@ -82,9 +82,14 @@ typedef enum { CGR_MASK_NONE = 0, CGR_MASK_CAUSAL = 1 } cgr_mask;
 
 /* Operand type of the Q.K^T matrix product (bf16 I/O only; f32 I/O always
  * multiplies in f32). RoPE is applied in f32 and rounded once to this type.
- *   CGR_QK_F16 (default): 3 more mantissa bits than bf16. Every |rotated q *
- *     softmax_scale * log2(e)| and |rotated k| must stay below 65504, or the
- *     output holds inf/NaN: inputs with |x| < 46000 always qualify.
+ *   CGR_QK_F16 (default): 3 more mantissa bits than bf16, range +-65504. A
+ *     work unit (the rows of one query block) in which a rotated query times
+ *     softmax_scale * log2(e), or a rotated key it can see, reaches 65520 or
+ *     more (which f16 cannot hold) is found by the forward and recomputed with
+ *     the scores taken from bf16 hi + lo parts of the rotated operands (16
+ *     significant bits, f32's range): the result is never NaN or infinite
+ *     from that cause, at the cost of a slower unit. The backward has no such
+ *     path: there the rotated values must stay below 65504.
  *   CGR_QK_BF16: bf16's full range, coarser rounding.
  * The P.V product always multiplies bf16 P by bf16 V, accumulating in f32. */
 typedef enum { CGR_QK_F16 = 0, CGR_QK_BF16 = 1 } cgr_qk_operand;
