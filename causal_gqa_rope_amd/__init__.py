@@ -34,6 +34,7 @@ __all__ = [
     "cgr_attn_fwd_rotate_keys",
     "cgr_gqa_rope_attn_fwd_rotated",
     "cgr_gqa_rope_attn_fwd_varlen",
+    "cgr_gqa_rope_attn_fwd_varlen_noalloc",
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_attn_fwd_varlen_rotated_workspace_size",
     "cgr_varlen_device_status",
@@ -75,6 +76,7 @@ EXPORTED_SYMBOLS = (
     "cgr_attn_fwd_varlen_workspace_size",
     "cgr_attn_fwd_varlen_rotated_workspace_size",
     "cgr_gqa_rope_attn_fwd_varlen",
+    "cgr_gqa_rope_attn_fwd_varlen_noalloc",
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
@@ -146,6 +148,9 @@ def library() -> ctypes.CDLL:
                                                  i32, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp,
                                                  ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd_varlen.restype = i32
+    lib.cgr_gqa_rope_attn_fwd_varlen_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                                         vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.cgr_gqa_rope_attn_fwd_varlen_noalloc.restype = i32
     lib.cgr_attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     lib.cgr_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
@@ -446,6 +451,43 @@ def cgr_gqa_rope_attn_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tens
     return out, lse
 
 
+def cgr_gqa_rope_attn_fwd_varlen_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                         cu_seqlens: torch.Tensor, max_seqlen: int, rope_cos: torch.Tensor,
+                                         rope_sin: torch.Tensor, *, out: torch.Tensor, lse: Optional[torch.Tensor],
+                                         causal: bool = True, rope_style: str = "interleaved", window: int = 0,
+                                         softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                                         device_status: Optional[torch.Tensor] = None):
+    """The packed forward that allocates nothing (its schedule lives in the
+    library's own device array): the caller passes out [total,H,d], lse [H,total]
+    float32 (or None) and optionally device_status (int32 device tensor [1])."""
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _dev_tensor(n, t)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 3-D [total, heads, head_dim]")
+    total, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != total or k.shape[2] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DTYPES or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise CgrError(CGR_ERR_UNSUPPORTED, "q, k, v must all be float32 or all bfloat16")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    _dev_tensor("out", out, q.dtype)
+    if lse is not None:
+        _dev_tensor("lse", lse, torch.float32)
+    if device_status is not None:
+        _dev_tensor("device_status", device_status, torch.int32)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_fwd_varlen_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens), cu_seqlens.numel() - 1, total,
+            int(max_seqlen), H, k.shape[1], D, _DTYPES[q.dtype], _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
+            _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE, int(window),
+            0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand], _ptr(device_status),
+            _stream(q.device)))
+    return out, lse
+
+
 def cgr_varlen_device_status(workspace: torch.Tensor) -> int:
     """Device error word of the last varlen call on `workspace` (0 = well formed). Synchronises."""
     lib = library()
@@ -656,6 +698,7 @@ attn_fwd_rotate_keys = cgr_attn_fwd_rotate_keys
 gqa_rope_attn_fwd_rotated = cgr_gqa_rope_attn_fwd_rotated
 gqa_rope_attn_fwd_fp8 = cgr_gqa_rope_attn_fwd_fp8
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
+gqa_rope_attn_fwd_varlen_noalloc = cgr_gqa_rope_attn_fwd_varlen_noalloc
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd
 rope_rotate = cgr_rope_rotate
 gqa_rope_attn_decode = cgr_gqa_rope_attn_decode

@@ -28,6 +28,7 @@ SOURCES = [
     "cgr_api.hip",
     "rope_tables.hip",
     "varlen_sched.hip",
+    "noalloc.hip",
     "attn_fwd_d32.hip",
     "attn_fwd_d64.hip",
     "attn_fwd_d128.hip",

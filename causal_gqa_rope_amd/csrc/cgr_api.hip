@@ -236,7 +236,114 @@ cgr_status dense_fwd(const void* q, const void* k, const void* v, void* o, float
   return CGR_OK;
 }
 
+// Workspace of a packed call that rotates the keys once: the schedule, then
+// the first image slot of every sequence, then the K tile images ([K/V head]
+// [slot], slots = ceil(total / BN) + num_seqs, which bounds the sum of the
+// sequences' tile counts); each part starts on a 256-byte boundary.
+struct VarlenLayout {
+  size_t kimg_base, images, total;
+  long slots;
+};
+VarlenLayout varlen_layout(int num_seqs, int total_tokens, int n_kv_head, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  VarlenLayout l{};
+  const int bn = cgr::fwd_tile_keys(head_dim);
+  l.slots = ((long)total_tokens + bn - 1) / bn + num_seqs;
+  l.kimg_base = up(cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens));
+  l.images = up(l.kimg_base + ((size_t)num_seqs + 1) * 4);
+  l.total = l.images + (size_t)n_kv_head * l.slots * cgr::fwd_kimg_bytes(head_dim);
+  return l;
+}
+
 }  // namespace
+
+namespace cgr {
+cgr_status report_error(cgr_status st, const char* msg) { return fail(st, "%s", msg); }
+
+// Every host check of a packed-batch forward call except those of the workspace.
+cgr_status varlen_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen, int n_head,
+                        int n_kv_head, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                        const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                        int window, float softmax_scale, cgr_qk_operand qk_operand) {
+  if (!cu_seqlens) return fail(CGR_ERR_INVALID_ARG, "cu_seqlens must be non-null");
+  if (!aligned(cu_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cu_seqlens must be 4-byte aligned");
+  if (num_seqs < 1) return fail(CGR_ERR_INVALID_ARG, "num_seqs (%d) must be >= 1", num_seqs);
+  if (total_tokens < 0 || max_seqlen < 0)
+    return fail(CGR_ERR_INVALID_ARG, "total_tokens and max_seqlen must be >= 0");
+  if (max_seqlen > total_tokens)
+    return fail(CGR_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen,
+                total_tokens);
+  cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
+                               rope_sin, rope_max_pos, max_seqlen, style, mask, softmax_scale,
+                               qk_operand);
+  if (st != CGR_OK) return st;
+  return check_window(window, mask);
+}
+
+// The packed-batch forward behind cgr_gqa_rope_attn_fwd_varlen and
+// cgr_gqa_rope_attn_fwd_varlen_noalloc: checks, the schedule prepass, the
+// attention kernel. status_out (optional) receives the prepass's error word.
+cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen, int n_head,
+                      int n_kv_head, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                      const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                      float softmax_scale, cgr_qk_operand qk_operand, void* workspace, size_t workspace_bytes,
+                      int32_t* status_out, void* stream) {
+  cgr_status st = varlen_check(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, max_seqlen, n_head,
+                               n_kv_head, head_dim, dtype, rope_cos, rope_sin, rope_max_pos, style, mask, window,
+                               softmax_scale, qk_operand);
+  if (st != CGR_OK) return st;
+  const size_t need = cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
+                need);
+  const long max_items = varlen_max_items(num_seqs, total_tokens);
+  if (max_items * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  int cus = 0;
+  const int ce = cu_count(&cus);
+  if (ce != 0) return hip_fail("device query", (hipError_t)ce);
+
+  // Keys rotated once (16-bit I/O) when the workspace also holds their images.
+  const VarlenLayout lay = varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim);
+  const bool use_kimg = dtype == CGR_BF16 && workspace_bytes >= lay.total;
+  if (use_kimg && (long)n_kv_head * lay.slots > INT_MAX)
+    return fail(CGR_ERR_INVALID_ARG, "too many key tiles");
+
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* sched = (int32_t*)workspace;
+  int32_t* kimg_base = use_kimg ? (int32_t*)((char*)workspace + lay.kimg_base) : nullptr;
+  const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
+  hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                             cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
+                                             mask == CGR_MASK_CAUSAL, sched,
+                                             (int)max_items, kimg_base, status_out, s);
+  if (e != hipSuccess) return hip_fail("schedule launch", e);
+  cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
+                              softmax_scale);
+  a.cu_seqlens = cu_seqlens;
+  a.sched = sched;
+  a.B = num_seqs;
+  a.T = max_seqlen;
+  a.total_tokens = total_tokens;
+  a.window = window;
+  a.hp = hp;
+  if (use_kimg) {
+    a.krot = (char*)workspace + lay.images;
+    a.kimg_base = kimg_base;
+    a.kimg_slots = (int)lay.slots;
+  }
+  // Persistent grid: two workgroups per compute unit, never more than the units.
+  long grid = 2L * cus;
+  if (grid > max_items * (n_head / hp)) grid = max_items * (n_head / hp);
+  if (grid < 1) grid = 1;
+  e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
+  if (e != hipSuccess) return hip_fail("attention launch", e);
+  return CGR_OK;
+}
+}  // namespace cgr
 
 extern "C" {
 
@@ -387,25 +494,6 @@ size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens) {
   return (size_t)cgr::kSchedHeaderInts * 4 + (size_t)varlen_max_items(num_seqs, total_tokens) * 8;
 }
 
-// Workspace of a packed call that rotates the keys once: the schedule, then
-// the first image slot of every sequence, then the K tile images ([K/V head]
-// [slot], slots = ceil(total / BN) + num_seqs, which bounds the sum of the
-// sequences' tile counts); each part starts on a 256-byte boundary.
-struct VarlenLayout {
-  size_t kimg_base, images, total;
-  long slots;
-};
-VarlenLayout varlen_layout(int num_seqs, int total_tokens, int n_kv_head, int head_dim) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  VarlenLayout l{};
-  const int bn = cgr::fwd_tile_keys(head_dim);
-  l.slots = ((long)total_tokens + bn - 1) / bn + num_seqs;
-  l.kimg_base = up(cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens));
-  l.images = up(l.kimg_base + ((size_t)num_seqs + 1) * 4);
-  l.total = l.images + (size_t)n_kv_head * l.slots * cgr::fwd_kimg_bytes(head_dim);
-  return l;
-}
-
 size_t cgr_attn_fwd_varlen_rotated_workspace_size(int num_seqs, int total_tokens, int n_kv_head,
                                                   int head_dim) {
   if (num_seqs < 1 || total_tokens < 0 || n_kv_head < 1) return 0;
@@ -421,67 +509,9 @@ cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, const void
                                         int rope_max_pos, cgr_rope_style style, cgr_mask mask,
                                         int window, float softmax_scale, cgr_qk_operand qk_operand,
                                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (!cu_seqlens) return fail(CGR_ERR_INVALID_ARG, "cu_seqlens must be non-null");
-  if (!aligned(cu_seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "cu_seqlens must be 4-byte aligned");
-  if (num_seqs < 1) return fail(CGR_ERR_INVALID_ARG, "num_seqs (%d) must be >= 1", num_seqs);
-  if (total_tokens < 0 || max_seqlen < 0)
-    return fail(CGR_ERR_INVALID_ARG, "total_tokens and max_seqlen must be >= 0");
-  if (max_seqlen > total_tokens)
-    return fail(CGR_ERR_INVALID_ARG, "max_seqlen (%d) exceeds total_tokens (%d)", max_seqlen,
-                total_tokens);
-  cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
-                               rope_sin, rope_max_pos, max_seqlen, style, mask, softmax_scale,
-                               qk_operand);
-  if (st != CGR_OK) return st;
-  if ((st = check_window(window, mask)) != CGR_OK) return st;
-  const size_t need = cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens);
-  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
-  if (!aligned(workspace, 16)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 16-byte aligned");
-  if (workspace_bytes < need)
-    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
-                need);
-  const long max_items = varlen_max_items(num_seqs, total_tokens);
-  if (max_items * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
-  int cus = 0;
-  const int ce = cu_count(&cus);
-  if (ce != 0) return hip_fail("device query", (hipError_t)ce);
-
-  // Keys rotated once (16-bit I/O) when the workspace also holds their images.
-  const VarlenLayout lay = varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim);
-  const bool use_kimg = dtype == CGR_BF16 && workspace_bytes >= lay.total;
-  if (use_kimg && (long)n_kv_head * lay.slots > INT_MAX)
-    return fail(CGR_ERR_INVALID_ARG, "too many key tiles");
-
-  hipStream_t s = (hipStream_t)stream;
-  int32_t* sched = (int32_t*)workspace;
-  int32_t* kimg_base = use_kimg ? (int32_t*)((char*)workspace + lay.kimg_base) : nullptr;
-  const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
-  hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
-                                             cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
-                                             mask == CGR_MASK_CAUSAL, sched,
-                                             (int)max_items, kimg_base, s);
-  if (e != hipSuccess) return hip_fail("schedule launch", e);
-  cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
-                              softmax_scale);
-  a.cu_seqlens = cu_seqlens;
-  a.sched = sched;
-  a.B = num_seqs;
-  a.T = max_seqlen;
-  a.total_tokens = total_tokens;
-  a.window = window;
-  a.hp = hp;
-  if (use_kimg) {
-    a.krot = (char*)workspace + lay.images;
-    a.kimg_base = kimg_base;
-    a.kimg_slots = (int)lay.slots;
-  }
-  // Persistent grid: two workgroups per compute unit, never more than the units.
-  long grid = 2L * cus;
-  if (grid > max_items * (n_head / hp)) grid = max_items * (n_head / hp);
-  if (grid < 1) grid = 1;
-  e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
-  if (e != hipSuccess) return hip_fail("attention launch", e);
-  return CGR_OK;
+  return cgr::varlen_fwd(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, max_seqlen, n_head, n_kv_head,
+                         head_dim, dtype, rope_cos, rope_sin, rope_max_pos, style, mask, window, softmax_scale,
+                         qk_operand, workspace, workspace_bytes, nullptr, stream);
 }
 
 size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_head, int head_dim) {

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cgr.h"
+
 namespace cgr {
 
 struct AttnArgs;
@@ -50,6 +52,27 @@ hipError_t launch_rope_tables(int max_pos, int head_dim, double base, float* cos
 // non-null, the first K image slot of every sequence (see varlen_sched.hip).
 hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                   int max_seqlen, int bm, int bn, int causal, int32_t* sched,
-                                  int max_items, int32_t* kimg_base, hipStream_t stream);
+                                  int max_items, int32_t* kimg_base, int32_t* status_out,
+                                  hipStream_t stream);
+
+// Records `msg` as cgr_last_error() and returns st.
+cgr_status report_error(cgr_status st, const char* msg);
+
+// Every host check of a packed-batch forward call except the workspace's (cgr_api.hip).
+cgr_status varlen_check(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                        const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen, int n_head,
+                        int n_kv_head, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                        const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+                        int window, float softmax_scale, cgr_qk_operand qk_operand);
+
+// The packed-batch forward of cgr_gqa_rope_attn_fwd_varlen on a given
+// workspace (cgr_api.hip); status_out, if non-null, receives the schedule's
+// error word as well.
+cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens, int num_seqs, int total_tokens, int max_seqlen, int n_head,
+                      int n_kv_head, int head_dim, cgr_dtype dtype, const float* rope_cos,
+                      const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                      float softmax_scale, cgr_qk_operand qk_operand, void* workspace, size_t workspace_bytes,
+                      int32_t* status_out, void* stream);
 
 }  // namespace cgr

@@ -14,6 +14,9 @@
 // 0 here), [2] error word (0 = well formed), [3] unused, then items as
 // (sequence, query block) int pairs.
 //
+// status_out (optional): a second copy of the error word, for callers that
+// pass no workspace of their own.
+//
 // When the call rotates the keys once (kimg_base non-null), the prepass also
 // writes kimg_base[s] = sum over s' < s of ceil(L_s' / bn), s = 0 .. num_seqs:
 // the first K tile image slot of every sequence.
@@ -34,7 +37,7 @@ __device__ __forceinline__ int cost_bin(int qb, int L, int bm, int bn, int causa
 
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     const int32_t* cu, int nseq, int total, int max_seqlen, int bm, int bn, int causal,
-    int32_t* sched, int max_items, int32_t* kimg_base) {
+    int32_t* sched, int max_items, int32_t* kimg_base, int32_t* status_out) {
   __shared__ int hist[kBins];
   __shared__ int part[kSchedThreads];
   __shared__ int err;
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
       sched[0] = 0;
       sched[1] = 0;
       sched[2] = err;
+      if (status_out != nullptr) *status_out = err;
     }
     return;
   }
@@ -133,14 +137,16 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     sched[0] = min(n_items, max_items);
     sched[1] = 0;
     sched[2] = 0;
+    if (status_out != nullptr) *status_out = 0;
   }
 }
 
 hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                   int max_seqlen, int bm, int bn, int causal, int32_t* sched,
-                                  int max_items, int32_t* kimg_base, hipStream_t stream) {
+                                  int max_items, int32_t* kimg_base, int32_t* status_out, hipStream_t stream) {
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, max_seqlen, bm, bn, causal, sched, max_items, kimg_base);
+                     num_seqs, total_tokens, max_seqlen, bm, bn, causal, sched, max_items, kimg_base,
+                     status_out);
   return hipGetLastError();
 }
 

@@ -431,6 +431,31 @@ CGR_API cgr_status cgr_rmsnorm_qkv_rope(const void* x, const void* norm_weight, 
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * cgr_gqa_rope_attn_fwd_varlen with no workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. The call allocates nothing. The
+ * batch's work schedule lives in a 1 MiB device array inside the library,
+ * one per GPU, held until the process ends; the caller passes only inputs
+ * and outputs. Arguments as for cgr_gqa_rope_attn_fwd_varlen, except:
+ *   device_status: NULL, or device int32, 4-byte aligned, that receives the
+ *     schedule's error word (0, or the codes cgr_varlen_device_status
+ *     reports for a malformed cu_seqlens).
+ * Limit: cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens) must not
+ * exceed 1 MiB (about 4 million tokens), else CGR_ERR_WORKSPACE and nothing
+ * is enqueued. The keys are rotated once when the batch's tile images fit in
+ * the array as well (small batches), else per tile; the results are the same
+ * bits either way, and those of cgr_gqa_rope_attn_fwd_varlen.
+ * Every call on a GPU uses that GPU's one array: calls that overlap on one GPU
+ * (other streams, or other threads without ordering) race and give undefined
+ * results.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen_noalloc(
+    const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens, int num_seqs,
+    int total_tokens, int max_seqlen, int n_head, int n_kv_head, int head_dim, cgr_dtype dtype,
+    const float* rope_cos, const float* rope_sin, int rope_max_pos, cgr_rope_style style, cgr_mask mask,
+    int window, float softmax_scale, cgr_qk_operand qk_operand, int32_t* device_status, void* stream);
+
+/*
  * Reads the device error word the last varlen, decode or rmsnorm_qkv_rope call on `workspace` left:
  * waits for `stream`, then stores 0 (the device-side sizes were well formed)
  * or a positive code in *host_status. Varlen: 1: cu_seqlens[0] != 0,

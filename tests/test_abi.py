@@ -170,6 +170,36 @@ def test_rotate_keys_and_rotated_reject_bad_arguments(fn, kw, status, needle):
     assert needle in msg
 
 
+def varlen_noalloc(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, cu=P, n=2, total=100, maxs=60, H=4, KV=2, D=64, dtype=1, cos=P, sin=P,
+             P=64, style=0, mask=1, window=0, scale=0.0, qk=0, status=None)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_fwd_varlen_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu"], a["n"],
+                                                  a["total"], a["maxs"], a["H"], a["KV"], a["D"], a["dtype"],
+                                                  a["cos"], a["sin"], a["P"], a["style"], a["mask"], a["window"],
+                                                  a["scale"], a["qk"], a["status"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    # 16 bytes + 8 per (sequence, 32-row block): past 1 MiB from ~4.19 M tokens
+    (dict(total=4_200_000, maxs=4_200_000, P=4_200_000, H=1, KV=1, D=32), 4, "no-alloc scratch holds"),
+    (dict(status=PMIS), 3, "device_status"),
+    (dict(q=None), 1, "non-null"),
+    (dict(cu=None), 1, "cu_seqlens"),
+    (dict(n=0), 1, "num_seqs"),
+    (dict(maxs=200), 1, "exceeds total_tokens"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(window=3, mask=0), 1, "CGR_MASK_CAUSAL"),
+])
+def test_varlen_noalloc_rejects_bad_arguments(kw, status, needle):
+    st, msg = varlen_noalloc(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def fp8(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=128, qd=0.01, kd=0.01, vd=0.01, cos=P, sin=P,
              P=16, style=0, mask=1, scale=0.0, ws=P, wsb=1 << 20)
