@@ -94,7 +94,7 @@ def rope_inv_freq(head_dim: int, base: float) -> np.ndarray:
     base (theta).
     """
     if head_dim % 2:
-        raise ValueError("RoPE needs an even head_dim")
+        raise ValueError("head_dim must be even: RoPE rotates feature pairs")
     i = np.arange(head_dim // 2, dtype=np.float64)
     return np.power(np.float64(base), -2.0 * i / head_dim)
 
