@@ -1419,7 +1419,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
   for (;;) {
     if (threadIdx.x == 0) s_unit = atomicAdd(counter, 1);
     __syncthreads();
-    const int u = s_unit;
+    // The same in every lane; readfirstlane tells the compiler so, which keeps
+    // the loop's exit a scalar branch: a loop whose exit it thought divergent
+    // would let waves leave it under partial exec masks and miss barriers.
+    const int u = __builtin_amdgcn_readfirstlane(s_unit);
     __syncthreads();
     if (u >= n_units) break;
     const int it = u / HG, hg = u - it * HG;
