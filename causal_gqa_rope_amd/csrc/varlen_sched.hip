@@ -5,7 +5,8 @@
 // the list of (sequence, query block) items sorted by cost, most expensive
 // first, where cost = number of key tiles the item visits (under the causal
 // mask, query block qb of a sequence of length L sees ceil(min((qb+1)*BM, L)
-// / BN) tiles). A counting sort over cost bins keeps this one pass. The
+// / BN) tiles). A counting sort over cost bins keeps this to two passes over
+// the items, each spread evenly over the workgroup's threads. The
 // attention kernel's persistent workgroups then pull items in that order
 // (longest-processing-time-first), which balances the causal triangle of
 // every sequence over the compute units.
@@ -27,42 +28,98 @@
 
 namespace cgr {
 
-constexpr int kSchedThreads = 1024;
+constexpr int kSchedThreads = 512;
+constexpr int kSchedWaves = kSchedThreads / 64;
 constexpr int kBins = 2048;  // costs >= kBins - 1 share the last bin
 
-__device__ __forceinline__ int cost_bin(int qb, int L, int bm, int bn, int causal) {
-  const int keys = causal ? min((qb + 1) * bm, L) : L;
-  return min((keys + bn - 1) / bn, kBins - 1);
+// Key tiles (of 1 << lbn keys) that query block qb (rows qb << lbm ..) of a
+// sequence of L tokens visits.
+__device__ __forceinline__ int cost_bin(int qb, int L, int lbm, int lbn, int causal) {
+  const int keys = causal ? min((qb + 1) << lbm, L) : L;
+  return min((keys + (1 << lbn) - 1) >> lbn, kBins - 1);
+}
+
+// Inclusive sum of v over the workgroup (wave shuffles, then the wave totals
+// through LDS); *total receives the sum over all threads. Every thread calls it.
+__device__ __forceinline__ int block_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int t = __shfl_up(v, off, 64);
+    if (lane >= off) v += t;
+  }
+  if (lane == 63) wsum[w] = v;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSchedWaves; ++i) {
+    const int x = wsum[i];
+    before += i < w ? x : 0;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return v + before;
 }
 
 __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
-    const int32_t* cu, int nseq, int total, int max_seqlen, int bm, int bn, int causal,
+    const int32_t* cu, int nseq, int total, int max_seqlen, int lbm, int lbn, int causal,
     int32_t* sched, int max_items, int32_t* kimg_base, int32_t* status_out) {
   __shared__ int hist[kBins];
-  __shared__ int part[kSchedThreads];
+  __shared__ int incl[kSchedThreads];  // a round's items per sequence, inclusive sums
+  __shared__ int lens[kSchedThreads];
+  __shared__ int wsum[kSchedWaves];
   __shared__ int err;
   const int tid = threadIdx.x;
   for (int b = tid; b < kBins; b += kSchedThreads) hist[b] = 0;
   if (tid == 0) err = 0;
   __syncthreads();
 
-  // 1. Check every sequence boundary and count items per cost bin.
-  for (int s = tid; s < nseq; s += kSchedThreads) {
-    const int c0 = cu[s], c1 = cu[s + 1];
-    int e = 0;
-    if (s == 0 && c0 != 0) e = 1;
-    else if (c1 < c0) e = 2;
-    else if (c1 - c0 > max_seqlen) e = 3;
-    else if (s == nseq - 1 && c1 != total) e = 4;
-    if (e) {
-      atomicCAS(&err, 0, e);
-      continue;
+  // The items of kSchedThreads sequences at a time, spread evenly over the
+  // threads whatever the lengths: one thread per sequence counts its query
+  // blocks, a scan numbers the round's items, and thread tid takes items tid,
+  // tid + kSchedThreads, ..., finding each one's sequence by a binary search
+  // over the inclusive counts. With check set, the round also checks every
+  // sequence boundary (a bad sequence contributes no items). act(s, qb, L)
+  // runs once per item.
+  auto for_items = [&](bool check, auto&& act) {
+    for (int s0 = 0; s0 < nseq; s0 += kSchedThreads) {
+      const int s = s0 + tid;
+      int L = 0;
+      if (s < nseq) {
+        const int c0 = cu[s], c1 = cu[s + 1];
+        int e = 0;
+        if (check) {
+          if (s == 0 && c0 != 0) e = 1;
+          else if (c1 < c0) e = 2;
+          else if (c1 - c0 > max_seqlen) e = 3;
+          else if (s == nseq - 1 && c1 != total) e = 4;
+          if (e) atomicCAS(&err, 0, e);
+        }
+        L = e ? 0 : c1 - c0;
+      }
+      const int nq = (L + (1 << lbm) - 1) >> lbm;
+      int n_round;
+      const int inc = block_scan(nq, wsum, &n_round);
+      incl[tid] = inc;
+      lens[tid] = L;
+      __syncthreads();
+      for (int g = tid; g < n_round; g += kSchedThreads) {
+        // i = the first entry with incl[i] > g (the number of entries <= g).
+        int i = 0;
+#pragma unroll
+        for (int step = kSchedThreads / 2; step > 0; step >>= 1)
+          if (incl[i + step - 1] <= g) i += step;
+        const int Li = lens[i];
+        const int qb = g - (incl[i] - ((Li + (1 << lbm) - 1) >> lbm));
+        act(s0 + i, qb, Li);
+      }
+      __syncthreads();  // incl and lens are rewritten by the next round
     }
-    const int L = c1 - c0;
-    const int nq = (L + bm - 1) / bm;
-    for (int qb = 0; qb < nq; ++qb) atomicAdd(&hist[cost_bin(qb, L, bm, bn, causal)], 1);
-  }
-  __syncthreads();
+  };
+
+  // 1. Check the boundaries and count items per cost bin.
+  for_items(true, [&](int, int qb, int L) { atomicAdd(&hist[cost_bin(qb, L, lbm, lbn, causal)], 1); });
   if (err != 0) {
     if (tid == 0) {
       sched[0] = 0;
@@ -79,15 +136,8 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
   int local = 0;
 #pragma unroll
   for (int k = 0; k < per; ++k) local += hist[kBins - 1 - (tid * per + k)];
-  part[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  int run = part[tid] - local;
+  int n_items;
+  int run = block_scan(local, wsum, &n_items) - local;
 #pragma unroll
   for (int k = 0; k < per; ++k) {
     const int b = kBins - 1 - (tid * per + k);
@@ -95,43 +145,28 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
     hist[b] = run;
     run += c;
   }
-  const int n_items = part[kSchedThreads - 1];
   __syncthreads();
 
   // 3. Scatter the items to their slots (order inside a bin is arbitrary).
   int2* items = (int2*)(sched + kSchedHeaderInts);
-  for (int s = tid; s < nseq; s += kSchedThreads) {
-    const int c0 = cu[s];
-    const int L = cu[s + 1] - c0;
-    const int nq = (L + bm - 1) / bm;
-    for (int qb = 0; qb < nq; ++qb) {
-      const int pos = atomicAdd(&hist[cost_bin(qb, L, bm, bn, causal)], 1);
-      if (pos < max_items) items[pos] = make_int2(s, qb);
-    }
-  }
-  // 4. First image slot of every sequence: each thread sums the tiles of a
-  //    run of consecutive sequences, a scan over the threads gives the runs'
-  //    starts.
+  for_items(false, [&](int s, int qb, int L) {
+    const int pos = atomicAdd(&hist[cost_bin(qb, L, lbm, lbn, causal)], 1);
+    if (pos < max_items) items[pos] = make_int2(s, qb);
+  });
+
+  // 4. First image slot of every sequence: a running scan of the sequences'
+  //    tile counts.
   if (kimg_base != nullptr) {
-    const int chunk = (nseq + kSchedThreads - 1) / kSchedThreads;
-    const int s0 = min(tid * chunk, nseq), s1 = min(s0 + chunk, nseq);
-    int own = 0;
-    for (int s = s0; s < s1; ++s) own += (cu[s + 1] - cu[s] + bn - 1) / bn;
-    __syncthreads();  // every thread is done with part[] above
-    part[tid] = own;
-    __syncthreads();
-    for (int off = 1; off < kSchedThreads; off <<= 1) {
-      const int add = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += add;
-      __syncthreads();
+    int base = 0;
+    for (int s0 = 0; s0 < nseq; s0 += kSchedThreads) {
+      const int s = s0 + tid;
+      const int tiles = s < nseq ? (cu[s + 1] - cu[s] + (1 << lbn) - 1) >> lbn : 0;
+      int round_tiles;
+      const int inc = block_scan(tiles, wsum, &round_tiles);
+      if (s < nseq) kimg_base[s] = base + inc - tiles;
+      base += round_tiles;
     }
-    int at = part[tid] - own;
-    for (int s = s0; s < s1; ++s) {
-      kimg_base[s] = at;
-      at += (cu[s + 1] - cu[s] + bn - 1) / bn;
-    }
-    if (tid == kSchedThreads - 1) kimg_base[nseq] = part[tid];
+    if (tid == 0) kimg_base[nseq] = base;
   }
   if (tid == 0) {
     sched[0] = min(n_items, max_items);
@@ -144,8 +179,11 @@ __global__ __launch_bounds__(kSchedThreads) void varlen_schedule_kernel(
 hipError_t launch_varlen_schedule(const int32_t* cu_seqlens, int num_seqs, int total_tokens,
                                   int max_seqlen, int bm, int bn, int causal, int32_t* sched,
                                   int max_items, int32_t* kimg_base, int32_t* status_out, hipStream_t stream) {
+  // Query blocks and key tiles are powers of two: the kernel shifts.
+  if (bm <= 0 || bn <= 0 || (bm & (bm - 1)) != 0 || (bn & (bn - 1)) != 0) return hipErrorInvalidValue;
+  const int lbm = __builtin_ctz(bm), lbn = __builtin_ctz(bn);
   hipLaunchKernelGGL(varlen_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, cu_seqlens,
-                     num_seqs, total_tokens, max_seqlen, bm, bn, causal, sched, max_items, kimg_base,
+                     num_seqs, total_tokens, max_seqlen, lbm, lbn, causal, sched, max_items, kimg_base,
                      status_out);
   return hipGetLastError();
 }
