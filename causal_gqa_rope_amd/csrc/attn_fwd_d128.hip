@@ -4,7 +4,7 @@
 
 namespace cgr {
 hipError_t launch_attn_d128(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                           bool varlen, int grid, hipStream_t stream, int phases) {
-  return launch_attn_d<128>(a, f32_io, qk_bf16, style, causal, varlen, grid, stream, phases);
+                           bool varlen, int grid, hipStream_t stream, int phases, bool small) {
+  return launch_attn_d<128>(a, f32_io, qk_bf16, style, causal, varlen, grid, stream, phases, small);
 }
 }  // namespace cgr

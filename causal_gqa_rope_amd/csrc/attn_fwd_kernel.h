@@ -93,8 +93,9 @@ constexpr int v_stride_dwords(int row_dwords) {
   return s;
 }
 
+// NW_: waves per workgroup (0: the default for the head_dim).
 template <int D_, typename IO_, typename QK_, bool CAUSAL_, int STYLE_, bool WIN_ = false,
-          bool KPRE_ = false>
+          bool KPRE_ = false, int NW_ = 0>
 struct Cfg {
   static constexpr int D = D_;
   using IO = IO_;  // float, or uint16_t holding bf16 bits
@@ -120,7 +121,7 @@ struct Cfg {
   // file (its O accumulator alone is 128 registers per lane), four waves per
   // workgroup and 32-key tiles, so K, V and the Q staging fit in LDS.
   static constexpr bool WIDE = D_ == 256;
-  static constexpr int NW = WIDE ? 4 : CGR_NW;
+  static constexpr int NW = WIDE ? 4 : NW_ > 0 ? NW_ : CGR_NW;
   static constexpr int WPS = WIDE ? 1 : CGR_WAVES_PER_SIMD;  // waves per SIMD
   static constexpr int THREADS = 64 * NW;
   static constexpr int BM = 32 * NW;  // query rows per unit
@@ -1473,7 +1474,7 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
       w1 = to_frag_or_nan<typename C::QK>(x1).v;
     }
     const long img = ((long)b * a.KV + kv) * n_img + tile;
-    char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
+    char* row = (char*)a.krot + (long)img * C::K_IMG + r * 2 * D;
     *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
     *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
   }
@@ -1487,16 +1488,20 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
 // sequences own none). A malformed cu_seqlens (the prepass's error word set)
 // leaves the images unwritten; every read stays inside q/k and the tables
 // whatever the arrays hold.
+constexpr int kKrotVarlenThreads = 128;
 template <class C>
-__global__ __launch_bounds__(256) void krot_varlen_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kKrotVarlenThreads) void krot_varlen_kernel(AttnArgs a) {
   constexpr int D = C::D, BN = C::BN, IPR = D / 16;
-  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
-  const long item = tid / IPR;
-  if (item >= (long)a.KV * a.kimg_slots * BN) return;
+  static_assert(IPR * BN % kKrotVarlenThreads == 0, "a workgroup's items lie in one image");
+  // The workgroup's image (kv * kimg_slots + slot) is the same in every lane:
+  // the search for its sequence below is uniform.
+  const long first = (long)blockIdx.x * kKrotVarlenThreads;
+  const int img = __builtin_amdgcn_readfirstlane((int)(first / (IPR * BN)));
+  if (img >= a.KV * a.kimg_slots) return;
   if (a.sched[2] != 0) return;
-  const int g = (int)(tid % IPR), r = (int)(item % BN);
-  const long img = item / BN;  // kv * kimg_slots + slot
-  const int slot = (int)(img % a.kimg_slots), kv = (int)(img / a.kimg_slots);
+  const int within = (int)(first % (IPR * BN)) + (int)threadIdx.x;
+  const int g = within % IPR, r = within / IPR;
+  const int slot = img % a.kimg_slots, kv = img / a.kimg_slots;
   const int nseq = a.B;
   if (slot >= a.kimg_base[nseq]) return;
   int lo = 0, hi = nseq - 1;
@@ -1520,7 +1525,7 @@ __global__ __launch_bounds__(256) void krot_varlen_kernel(AttnArgs a) {
     w0 = to_frag_or_nan<typename C::QK>(x0).v;
     w1 = to_frag_or_nan<typename C::QK>(x1).v;
   }
-  char* row = (char*)a.krot + img * C::K_IMG + r * 2 * D;
+  char* row = (char*)a.krot + (long)img * C::K_IMG + r * 2 * D;
   *(u32x4*)(row + 16 * (g ^ tswz<D>(r))) = w0;
   *(u32x4*)(row + 16 * ((g + D / 16) ^ tswz<D>(r))) = w1;
 }
@@ -1560,7 +1565,8 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int
 template <class C>
 hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stream) {
   const long items = (long)a.KV * a.kimg_slots * C::BN * (C::D / 16);
-  hipLaunchKernelGGL((krot_varlen_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((krot_varlen_kernel<C>), dim3((unsigned)(items / kKrotVarlenThreads)), dim3(kKrotVarlenThreads),
+                     0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
@@ -1573,22 +1579,51 @@ hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stre
 // Waves per workgroup, query heads per unit (the largest power of two that
 // divides both the waves and the group size G), query rows per unit and keys
 // per tile of the forward instances of a head_dim.
-constexpr int fwd_waves(int head_dim) { return head_dim == 256 ? 4 : CGR_NW; }
-constexpr int fwd_heads_per_unit(int head_dim, int G) {
+// nw: the waves of an instance built with a count of its own (0: the default).
+constexpr int fwd_waves(int head_dim, int nw = 0) { return head_dim == 256 ? 4 : nw > 0 ? nw : CGR_NW; }
+constexpr int fwd_heads_per_unit(int head_dim, int G, int nw = 0) {
   int hp = 1;
-  while (2 * hp <= fwd_waves(head_dim) && 2 * hp <= CGR_MAX_HP && G % (2 * hp) == 0) hp *= 2;
+  while (2 * hp <= fwd_waves(head_dim, nw) && 2 * hp <= CGR_MAX_HP && G % (2 * hp) == 0) hp *= 2;
   return hp;
 }
-constexpr int fwd_block_rows(int head_dim, int hp) { return 32 * fwd_waves(head_dim) / hp; }
+constexpr int fwd_block_rows(int head_dim, int hp, int nw = 0) { return 32 * fwd_waves(head_dim, nw) / hp; }
+// Waves of the dense instances for grids that would leave compute units idle
+// (bf16 I/O, keys rotated on every tile, no window): twice the units of the
+// default, each half as long.
+constexpr int kSmallNW = 4;
 constexpr int fwd_tile_keys(int head_dim) { return head_dim == 256 ? 32 : CGR_BN; }
 constexpr int kMinBM = 32;  // smallest query block of any unit
 // Bytes of one K tile image of the once-rotated keys (16-bit operands).
 constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_dim) * 2 * head_dim; }
 
+template <class C>
+hipError_t launch_attn_dense(const AttnArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+  return hipGetLastError();
+}
+
 // phases (dense batches with a.krot set): PHASE_ROTATE, PHASE_ATTEND or both.
+// small: a dense bf16 call without window or once-rotated keys, on the
+// kSmallNW-wave instances.
 template <int D>
 hipError_t launch_attn_d(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                         bool varlen, int grid, hipStream_t stream, int phases) {
+                         bool varlen, int grid, hipStream_t stream, int phases, bool small) {
+  if (small) {
+    if (f32_io || varlen || a.window > 0 || a.krot != nullptr || D == 256) return hipErrorInvalidValue;
+    if constexpr (D != 256) {
+#define CGR_SMALL(QK, CAU)                                                                                  \
+  return style == STYLE_HALF                                                                                \
+      ? launch_attn_dense<Cfg<D, uint16_t, QK, CAU, STYLE_HALF, false, false, kSmallNW>>(a, grid, stream) \
+      : launch_attn_dense<Cfg<D, uint16_t, QK, CAU, STYLE_INTERLEAVED, false, false, kSmallNW>>(a, grid, stream)
+      if (qk_bf16) {
+        if (causal) CGR_SMALL(OpBF16, true);
+        CGR_SMALL(OpBF16, false);
+      }
+      if (causal) CGR_SMALL(OpF16, true);
+      CGR_SMALL(OpF16, false);
+#undef CGR_SMALL
+    }
+  }
 #define CGR_LAUNCH(IO, QK, CAU, STY, WIN)                                                       \
   if constexpr (!std::is_same<IO, float>::value) {                                               \
     if (a.krot != nullptr)                                                                        \

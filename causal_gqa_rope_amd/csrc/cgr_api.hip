@@ -131,14 +131,14 @@ cgr::AttnArgs make_args(const void* q, const void* k, const void* v, void* o, fl
 
 hipError_t launch_by_dim(const cgr::AttnArgs& a, int head_dim, cgr_dtype dtype, cgr_qk_operand qk,
                          cgr_rope_style style, cgr_mask mask, bool varlen, int grid,
-                         hipStream_t s, int phases = cgr::PHASE_ALL) {
+                         hipStream_t s, int phases = cgr::PHASE_ALL, bool small = false) {
   const int f32 = dtype == CGR_F32, qkb = qk == CGR_QK_BF16, sty = (int)style,
             cau = mask == CGR_MASK_CAUSAL;
   switch (head_dim) {
-    case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s, phases);
-    case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s, phases);
-    case 128: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s, phases);
-    default: return cgr::launch_attn_d256(a, f32, qkb, sty, cau, varlen, grid, s, phases);
+    case 32: return cgr::launch_attn_d32(a, f32, qkb, sty, cau, varlen, grid, s, phases, small);
+    case 64: return cgr::launch_attn_d64(a, f32, qkb, sty, cau, varlen, grid, s, phases, small);
+    case 128: return cgr::launch_attn_d128(a, f32, qkb, sty, cau, varlen, grid, s, phases, small);
+    default: return cgr::launch_attn_d256(a, f32, qkb, sty, cau, varlen, grid, s, phases, small);
   }
 }
 
@@ -217,9 +217,27 @@ cgr_status dense_fwd(const void* q, const void* k, const void* v, void* o, float
       return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, need);
   }
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
-  const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
-  const int bm = cgr::fwd_block_rows(head_dim, hp);
-  const long grid = (long)((T + bm - 1) / bm) * B * (n_head / hp);
+  const int G = n_head / n_kv_head;
+  int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, G);
+  long grid = (long)((T + cgr::fwd_block_rows(head_dim, hp) - 1) / cgr::fwd_block_rows(head_dim, hp)) * B *
+              (n_head / hp);
+  // A whole (not split) bf16 call whose grid would leave compute units idle
+  // runs on the small-unit instances (twice the units, each half as long) and
+  // rotates its keys on every tile: at that size a separate rotation pass
+  // costs more than it saves. Any workspace given is then left untouched. The
+  // results are the same bits either way (every row's arithmetic is the same).
+  bool small = false;
+  if (dtype == CGR_BF16 && window == 0 && phases == cgr::PHASE_ALL && head_dim != 256) {
+    int cus = 0;
+    const int ce = cu_count(&cus);
+    if (ce != 0) return hip_fail("device query", (hipError_t)ce);
+    if (grid < cus) {
+      small = true;
+      hp = cgr::fwd_heads_per_unit(head_dim, G, cgr::kSmallNW);
+      const int bm = cgr::fwd_block_rows(head_dim, hp, cgr::kSmallNW);
+      grid = (long)((T + bm - 1) / bm) * B * (n_head / hp);
+    }
+  }
   if (grid > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
                               softmax_scale);
@@ -229,9 +247,9 @@ cgr_status dense_fwd(const void* q, const void* k, const void* v, void* o, float
   a.window = window;
   a.hp = hp;
   a.seqlens = seqlens;
-  a.krot = use_ws ? workspace : nullptr;
+  a.krot = use_ws && !small ? workspace : nullptr;
   const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, false, (int)grid,
-                                     (hipStream_t)stream, phases);
+                                     (hipStream_t)stream, phases, small);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   return CGR_OK;
 }

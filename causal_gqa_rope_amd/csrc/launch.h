@@ -15,13 +15,13 @@ struct QkvArgs;
 struct Fp8Args;
 
 hipError_t launch_attn_d32(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                           bool varlen, int grid, hipStream_t stream, int phases);
+                           bool varlen, int grid, hipStream_t stream, int phases, bool small);
 hipError_t launch_attn_d64(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                           bool varlen, int grid, hipStream_t stream, int phases);
+                           bool varlen, int grid, hipStream_t stream, int phases, bool small);
 hipError_t launch_attn_d128(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                            bool varlen, int grid, hipStream_t stream, int phases);
+                            bool varlen, int grid, hipStream_t stream, int phases, bool small);
 hipError_t launch_attn_d256(const AttnArgs& a, int f32_io, int qk_bf16, int style, int causal,
-                            bool varlen, int grid, hipStream_t stream, int phases);
+                            bool varlen, int grid, hipStream_t stream, int phases, bool small);
 hipError_t launch_attn_fp8(const Fp8Args& a, int style, int causal, hipStream_t stream);
 
 hipError_t launch_attn_bwd_d32(const BwdArgs& a, int qk_bf16, int style, int causal, hipStream_t stream);

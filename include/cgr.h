@@ -142,7 +142,11 @@ CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head
  *     cgr_attn_fwd_workspace_size(B, T, n_kv_head, head_dim) bytes, 16-byte
  *     aligned, scratch for this call only. With it the keys are rotated
  *     once, before the attention kernel, instead of on every tile that reads
- *     them (the results are the same bits either way). Ignored for CGR_F32.
+ *     them (the results are the same bits either way). Ignored for CGR_F32,
+ *     and left untouched by a call without window whose default grid of
+ *     work units would leave compute units idle: such a call runs units half
+ *     as tall (twice as many) and rotates the keys per tile, since at that
+ *     size a separate rotation pass costs more than it saves (same bits).
  * o and lse must not overlap the inputs.
  */
 CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -79,3 +79,20 @@ def run_oracle(w: W.Workload, inputs: dict, scale=None):
                                        style=w.rope_style, scale=scale)
     return oracle.attention_dense(inputs["q"], inputs["k"], inputs["v"], causal=w.causal,
                                   base=w.base, style=w.rope_style, scale=scale)
+
+
+def default_grid(B: int, T: int, H: int, KV: int, d: int) -> int:
+    """Workgroups of a dense bf16 call on the default (8-wave) instances: units
+    of hp heads x 256/hp query rows, hp the largest power of two <= 8 dividing
+    the group size. The library runs calls whose count is below the device's
+    compute units on its 4-wave instances (without window or split entries)."""
+    nw = 4 if d == 256 else 8
+    G, hp = H // KV, 1
+    while 2 * hp <= nw and G % (2 * hp) == 0:
+        hp *= 2
+    bm = 32 * nw // hp
+    return -(-T // bm) * B * (H // hp)
+
+
+def compute_units(dev) -> int:
+    return torch.cuda.get_device_properties(dev).multi_processor_count

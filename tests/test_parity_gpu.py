@@ -9,7 +9,8 @@ import torch
 import causal_gqa_rope_amd as cgr
 import oracle
 import workloads as W
-from tests.gpu_cases import TOL, announce, assert_close, f64, run_gpu, run_oracle, to_dev
+from tests.gpu_cases import (TOL, announce, assert_close, compute_units, default_grid, f64, run_gpu,
+                             run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -326,13 +327,15 @@ def test_first_tile_dominates(gpu):
     assert_close("sink", f64(o), ro, f64(lse), rl, "bf16")
 
 
-@pytest.mark.parametrize("T,H,KV,d,causal,style", [(300, 8, 2, 128, True, "interleaved"),
-                                                   (129, 4, 1, 64, False, "half"),
-                                                   (1000, 6, 3, 32, True, "half")])
-def test_pre_rotated_keys_give_the_same_bits(gpu, T, H, KV, d, causal, style):
+@pytest.mark.parametrize("B,T,H,KV,d,causal,style", [(4, 2100, 8, 2, 128, True, "interleaved"),
+                                                     (4, 2100, 8, 2, 64, False, "half"),
+                                                     (4, 4100, 6, 3, 32, True, "half")])
+def test_pre_rotated_keys_give_the_same_bits(gpu, B, T, H, KV, d, causal, style):
     """With a workspace the keys are rotated once up front; without, on every
-    tile: the same arithmetic in the same order, so the same bits."""
-    w = W.custom("prerot", B=2, T=T, n_head=H, n_kv_head=KV, head_dim=d, causal=causal, rope_style=style,
+    tile: the same arithmetic in the same order, so the same bits. (Grids that
+    fill the device, so both calls run the default instances.)"""
+    assert default_grid(B, T, H, KV, d) >= compute_units(gpu)
+    w = W.custom("prerot", B=B, T=T, n_head=H, n_kv_head=KV, head_dim=d, causal=causal, rope_style=style,
                  seed=T + d)
     x = to_dev(W.make_inputs(w), gpu)
     cos, sin = cgr.rope_tables(T, d, w.base, device=gpu)
@@ -351,7 +354,8 @@ def test_pre_rotated_keys_give_the_same_bits(gpu, T, H, KV, d, causal, style):
 ])
 def test_rotate_keys_then_rotated_gives_the_same_bits(gpu, T, H, KV, d, causal, style, win, padded):
     """cgr_attn_fwd_rotate_keys followed by cgr_gqa_rope_attn_fwd_rotated is the
-    forward with a workspace, split in two: the same bits."""
+    forward with a workspace, split in two: the same bits (the one call runs
+    the small-unit instances here when no window is set)."""
     w = W.custom("split", B=2, T=T, n_head=H, n_kv_head=KV, head_dim=d, causal=causal, rope_style=style,
                  seed=T + 7 * d)
     announce(f"rotate_keys + rotated vs one call: T={T} H={H} KV={KV} d={d} causal={causal} {style} W={win} "
@@ -370,6 +374,38 @@ def test_rotate_keys_then_rotated_gives_the_same_bits(gpu, T, H, KV, d, causal, 
     cgr.gqa_rope_attn_fwd_rotated(x["q"], x["k"], x["v"], cos, sin, ws, out=o2, lse=l2, **kw)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("qk", ["f16", "bf16"])
+@pytest.mark.parametrize("causal,style", [(True, "interleaved"), (False, "half"), (True, "half")])
+def test_small_grid_units_give_the_same_bits(gpu, d, qk, causal, style):
+    """A call whose default grid leaves compute units idle runs 4-wave units
+    with keys rotated per tile; the split entries always run the default
+    8-wave units on once-rotated keys. Every row's arithmetic is the same, so
+    the bits are too (ragged T, a padded entry)."""
+    B, T, H, KV = 2, 203, 6, 2
+    assert default_grid(B, T, H, KV, d) < compute_units(gpu)
+    w = W.custom("smallgrid", B=B, T=T, n_head=H, n_kv_head=KV, head_dim=d, causal=causal, rope_style=style,
+                 seed=d + (qk == "bf16"))
+    announce(f"small-grid units vs split entries: d={d} qk={qk} causal={causal} {style}")
+    x = to_dev(W.make_inputs(w), gpu)
+    cos, sin = cgr.rope_tables(T, d, w.base, device=gpu)
+    sl = torch.tensor([T, 150], dtype=torch.int32, device=gpu)
+    kw = dict(causal=causal, rope_style=style, qk_operand=qk, seqlens=sl)
+    o1 = torch.full_like(x["q"], 7.0)
+    l1 = torch.full((B, H, T), 7.0, device=gpu)
+    ws1 = torch.full((cgr.cgr_attn_fwd_workspace_size(B, T, KV, d),), 5, dtype=torch.uint8, device=gpu)
+    cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, out=o1, lse=l1, workspace=ws1, **kw)
+    ws2 = torch.empty_like(ws1)
+    cgr.attn_fwd_rotate_keys(x["k"], cos, sin, ws2, rope_style=style, qk_operand=qk, seqlens=sl)
+    o2 = torch.full_like(x["q"], 7.0)
+    l2 = torch.full((B, H, T), 7.0, device=gpu)
+    cgr.gqa_rope_attn_fwd_rotated(x["q"], x["k"], x["v"], cos, sin, ws2, out=o2, lse=l2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # The small-grid call leaves the workspace it was given untouched.
+    assert bool((ws1 == 5).all())
 
 
 PACKED_PREROT = [
