@@ -1014,9 +1014,12 @@ struct UnitFast {
     // ---- Fast path. Each row's reference m is its exact max over tile 0;
     // the S^T accumulator of later tiles starts from -m, so the matrix cores
     // return s - m and p = 2^(s - m) needs no further arithmetic. p may exceed
-    // 1 when later keys score higher; that is exact as long as no p
-    // overflows, which the row sum checks below (any row sum above 2^40, or
-    // not finite, sends the unit to the rescaling path).
+    // 1 when later keys score higher; the result is as exact as with the
+    // running max as long as nothing overflows: bf16 p has f32's exponent
+    // range, and p is only ever larger than with the running max (no extra
+    // underflow). The checks after the pass (a row sum not below 2^126, which
+    // bounds every p, or an O accumulator that is not finite) send the unit to
+    // the rescaling path.
     //
     // Software-pipelined by one tile: iteration j computes S of tile j+1 on
     // the matrix cores while the vector units turn S of tile j into P, then
@@ -1160,7 +1163,12 @@ struct UnitFast {
     // when neither happened).
     auto finish_unit = [&](float m_ref, auto win_tag) -> float {
       const float l_chk = pair_sum(l_run);
-      const bool overflow = !(l_chk <= 1.099511627776e12f);  // 2^40; NaN-safe
+      float o_chk = 0.f;  // inf or NaN if any accumulator is (or the sum overflows)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o_chk += oacc[db][e];
+      const bool overflow = !(l_chk < 0x1p126f) || !(fabsf(o_chk) <= 3.4028234663852886e38f);  // NaN-safe
       if (!__syncthreads_or(overflow)) return m_ref;
       if constexpr (F16OP) {
         if (__syncthreads_or(l_chk != l_chk)) return wide_pass(win_tag);

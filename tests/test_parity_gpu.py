@@ -262,12 +262,13 @@ def test_runs_on_the_callers_stream(gpu):
     assert_close("stream", f64(o), ro, f64(lse), rl, "bf16")
 
 
-@pytest.mark.parametrize("magnitude", [140.0, 600.0])
+@pytest.mark.parametrize("magnitude", [140.0, 250.0, 600.0])
 def test_scores_growing_far_beyond_the_first_tile(gpu, magnitude):
-    """Keys in later tiles score far above every key of the first tile (by up
-    to ~76 log2 units at magnitude 140; past the float range of 2^(s - m) at
-    600), so the fast path's row sums exceed their bound: the unit must take
-    the rescaling path and still match the oracle."""
+    """Keys in later tiles score far above every key of the first tile: by up
+    to ~76 log2 units at magnitude 140, where 2^(s - m) against the first
+    tile's reference stays inside the float range (the fast path holds), and
+    by ~135 and ~300 at 250 and 600, past that range: there the unit must take
+    the rescaling path. Either way it matches the oracle."""
     w = W.custom("growth", B=1, T=300, n_head=4, n_kv_head=2, head_dim=128, base=1e4, seed=21)
     announce(f"scores growing beyond the first tile's reference, magnitude {magnitude}")
     x = W.make_inputs(w)
