@@ -96,15 +96,20 @@ def read_traffic():
 
 
 class ClockSampler:
-    """The GPU's graphics clock (MHz), sampled from amd-smi every 2 ms on a
-    thread while started; summary() gives the samples' median, min, max and
-    count, or None where amd-smi is unavailable."""
+    """The graphics clock (MHz) under the step's load, from amd-smi.
+
+    amd-smi's clock readings trail the load by the better part of a second
+    (the first readings of a burst still show the idle clock), so measure()
+    runs the step back to back for `seconds`, samples every 5 ms on a thread,
+    and keeps only the samples of the last `tail` seconds. Per sample it takes
+    the per-XCD clocks (gpu metrics ``current_gfxclks``) where the driver
+    gives them, else the single GFX clock. summary() is None where amd-smi is
+    unavailable."""
 
     def __init__(self):
-        self.samples = []
-        self._run = False
-        self._thread = None
         self._handle = None
+        self._kept = []
+        self._source = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -115,34 +120,57 @@ class ClockSampler:
         except Exception:
             self._handle = None
 
-    def _loop(self):
-        while self._run:
-            try:
-                c = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)["clk"]
-                if isinstance(c, (int, float)) and c > 0:
-                    self.samples.append(float(c))
-            except Exception:
-                pass
-            time.sleep(0.002)
+    def _read(self):
+        try:
+            m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+            per = [float(c) for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+            if per:
+                return per, "amd-smi gpu metrics current_gfxclks (per XCD)"
+        except Exception:
+            pass
+        try:
+            c = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)["clk"]
+            if isinstance(c, (int, float)) and c > 0:
+                return [float(c)], "amd-smi GFX clock"
+        except Exception:
+            pass
+        return None, None
 
-    def start(self):
+    def measure(self, step, seconds: float = 2.0, tail: float = 0.8):
         if self._handle is None:
             return
-        self._run = True
-        self._thread = threading.Thread(target=self._loop, daemon=True)
-        self._thread.start()
+        import torch
+        samples, run = [], [True]
 
-    def stop(self):
-        self._run = False
-        if self._thread is not None:
-            self._thread.join()
-            self._thread = None
+        def loop():
+            while run[0]:
+                v, src = self._read()
+                if v is not None:
+                    samples.append((time.perf_counter(), v, src))
+                time.sleep(0.005)
+
+        th = threading.Thread(target=loop, daemon=True)
+        t0 = time.perf_counter()
+        th.start()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
+        run[0] = False
+        th.join()
+        t_end = time.perf_counter()
+        self._kept = [(v, src) for t, v, src in samples if t >= t_end - tail]
+        self._source = self._kept[-1][1] if self._kept else None
 
     def summary(self):
-        if not self.samples:
+        if not self._kept:
             return None
-        return {"median": statistics.median(self.samples), "min": min(self.samples), "max": max(self.samples),
-                "samples": len(self.samples), "source": "amd-smi GFX clock during the timed steps and 0.3 s more"}
+        means = [sum(v) / len(v) for v, _ in self._kept]
+        n_x = len(self._kept[-1][0])
+        per_x = [statistics.median(v[i] for v, _ in self._kept if len(v) == n_x) for i in range(n_x)]
+        return {"median": round(statistics.median(means), 1), "xcd_min": min(per_x), "xcd_max": max(per_x),
+                "samples": len(self._kept),
+                "source": f"{self._source}, the last 0.8 s of 2 s of back-to-back steps after the timed region"}
 
 
 def cpu_baseline(inputs, w) -> dict:
@@ -732,7 +760,6 @@ def main() -> int:
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     clock = ClockSampler()
     torch.cuda.synchronize()
-    clock.start()
     t0 = time.perf_counter()
     for i in range(args.steps):
         tables()
@@ -743,17 +770,8 @@ def main() -> int:
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    clock.stop()
-    # The clock under this load, sampled again over a longer stretch of the same
-    # steps after the timed region (the timed region itself may be too short
-    # for more than a few samples).
-    clock.start()
-    t1 = time.perf_counter()
-    while time.perf_counter() - t1 < 0.3:
-        for _ in range(8):
-            step()
-        torch.cuda.synchronize()
-    clock.stop()
+    # The clock under this load, after the timed region.
+    clock.measure(step)
 
     flops = W.algorithmic_flops(w.n_head, w.head_dim, lens, True, args.window)
     ms_step = wall * 1e3 / args.steps
