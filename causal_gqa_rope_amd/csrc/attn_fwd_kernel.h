@@ -573,16 +573,12 @@ struct UnitFast {
     else return 0;
   }
 
-  // tid_in: threadIdx.x (the persistent kernel passes it through an opaque
-  // copy, see attn_fwd_varlen_kernel). SHARED_Q: the Q prologue's mapping
-  // (see below).
-  template <bool SHARED_Q>
   static __device__ __forceinline__ void run(const AttnArgs& a, int tok0, int L, int qb, int head0,
-                                             long lse_b, long lse_h, long img0, long img_kvs, int tid_in,
+                                             long lse_b, long lse_h, long img0, long img_kvs,
                                              CGR_LDS_PARAMS) {
     // `wave` is the same in every lane: keeping it scalar makes every wave-level
     // decision below (active tiles, masking, V blocks) a scalar branch.
-    const int tid = tid_in, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     // The unit's waves split over hp query heads of one K/V group x 32-row
     // blocks: each K/V tile in LDS serves all of them.
@@ -595,6 +591,7 @@ struct UnitFast {
     const uint16_t* qbase = (const uint16_t*)a.q + (long)tok0 * qs + (long)head * D;
     const uint16_t* kbase = (const uint16_t*)a.k + (long)tok0 * ks + (long)kvh * D;
     const uint16_t* vbase = (const uint16_t*)a.v + (long)tok0 * ks + (long)kvh * D;
+    const rsrc_t rq = make_rsrc(qbase, (uint32_t)(((L - 1) * qs + D) * 2));
     // Once-rotated keys: the sequence's tile images of K_IMG bytes for this
     // K/V head are consecutive, from image img0 + kvh * img_kvs on; one
     // unit's images are one range.
@@ -621,79 +618,37 @@ struct UnitFast {
 
     // ---- Q. A lane of the matrix-core operand holds one query row, so loading
     // Q (and its cos/sin rows) straight into that layout would touch 32 rows
-    // per wave instruction. Instead the rows are loaded with whole rows per
-    // instruction, rotated at their positions in that layout (scale*log2(e)
-    // folded in, one rounding to the operand type), written to the LDS
-    // staging area of the wave that owns them, and every wave reads its rows
-    // back as operand fragments. The loads are issued here; the rest
-    // (stage_q) runs once the first K tiles' loads are in flight too.
+    // per wave instruction. Instead each wave loads its 32 rows with whole
+    // rows per instruction, rotates them at their positions in that layout
+    // (scale*log2(e) folded in, one rounding to the operand type), writes them
+    // to its own LDS staging area and reads them back as operand fragments.
+    // The loads are issued here; the rest (stage_q) runs once the first K
+    // tiles' loads are in flight too.
     constexpr int QCH = D / 8;  // 16-byte chunks (8 elements) per row
     constexpr bool Q_HALF = C::STYLE == STYLE_HALF;
     // An item is one chunk (interleaved pairs sit inside it) or, for the half
-    // pairing, a chunk and its partner chunk D/2 further on. A slot is an
-    // item position (row of the unit, item of the row); the unit has hp items
-    // per slot, one per head, all rotated by the slot's cos/sin.
+    // pairing, a chunk and its partner chunk D/2 further on.
     constexpr int QI_PER_ROW = Q_HALF ? QCH / 2 : QCH;
     constexpr int QI = 32 * QI_PER_ROW / 64;  // items per lane
     static_assert(32 * QI_PER_ROW % 64 == 0, "whole items per lane");
     char* const q_stage = qst + wave * 32 * C::Q_STRIDE;
-    // SHARED_Q (the persistent kernel): lane t's item i is
-    // e = (i / hp) * THREADS * hp + t * min(QI, hp) + i % hp of the unit's
-    // slot-major list (slot e / hp, head e % hp): runs of hp items share a
-    // slot, so the tables are read once per run rather than once per head
-    // (when QI < hp, hp / QI lanes share a slot); for a given i the lanes of a
-    // wave cover whole rows of one or two heads, and the fragments are read
-    // after the next barrier. Otherwise each wave stages its own 32 rows (item
-    // i of lane l: row (i * 64 + l) / QI_PER_ROW of the wave's block) with a
-    // table read per item, and reads its fragments straight back: no barrier
-    // between, which is the faster choice where the prologue is not repeated
-    // back to back.
-    const int lhp = __builtin_ctz(hp), run_hp = min(QI, hp);
-    const rsrc_t rqg = make_rsrc((const uint16_t*)a.q + (long)tok0 * qs + (long)head0 * D,
-                                 (uint32_t)(((L - 1) * qs + hp * D) * 2));
-    // Item i of this lane: its slot's row R within the unit, item c of the row
-    // and head hq within the unit's heads.
-    auto q_item = [&](int i, int& R, int& c, int& hq) {
-      if constexpr (SHARED_Q) {
-        const int e = ((i >> lhp) * THREADS << lhp) + tid * run_hp + (i & (hp - 1));
-        const int slot = e >> lhp;
-        hq = e & (hp - 1);
-        R = slot / QI_PER_ROW;
-        c = slot % QI_PER_ROW;
-      } else {
-        const int flat = i * 64 + lane;
-        hq = wave & (hp - 1);
-        R = (wave >> lhp) * 32 + flat / QI_PER_ROW;
-        c = flat % QI_PER_ROW;
-      }
-    };
     u32x4 q_raw[QI][Q_HALF ? 2 : 1];
     f32x4 q_cos[QI][Q_HALF ? 2 : 1], q_sin[QI][Q_HALF ? 2 : 1];
 #pragma unroll
     for (int i = 0; i < QI; ++i) {
-      int R, c, hq;
-      q_item(i, R, c, hq);
-      const int row = q0 + R;  // rows past the sequence read as zeros (buffer range)
-      const int qo = row * qs * 2 + hq * D * 2 + c * 16, to = row * (D / 2) * 4;
-      q_raw[i][0] = buf_load16(rqg, qo, 0);
-      if constexpr (Q_HALF) q_raw[i][1] = buf_load16(rqg, qo + D, 0);
-      // A new slot at i == 0 and at every run start; otherwise the run's tables.
-      if (!SHARED_Q || i == 0 || (i & (hp - 1)) == 0) {
-        if constexpr (Q_HALF) {
-          q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
-          q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
-          q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
-          q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
-        } else {
-          q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
-          q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
-        }
+      const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+      const int row = qw0 + r;  // rows past the sequence read as zeros (buffer range)
+      const int qo = row * qs * 2 + c * 16, to = row * (D / 2) * 4;
+      q_raw[i][0] = buf_load16(rq, qo, 0);
+      if constexpr (Q_HALF) {
+        q_raw[i][1] = buf_load16(rq, qo + D, 0);
+        q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
+        q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
+        q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
+        q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
       } else {
-#pragma unroll
-        for (int h = 0; h < (Q_HALF ? 2 : 1); ++h) {
-          q_cos[i][h] = q_cos[i - 1][h];
-          q_sin[i][h] = q_sin[i - 1][h];
-        }
+        q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
+        q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
       }
     }
     Frag<QK> qf[C::KSTEPS];
@@ -732,10 +687,8 @@ struct UnitFast {
     auto stage_q = [&]() {
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
-        // The owner of row R of head hq is wave (R / 32) * hp + hq.
-        int R, c, hq;
-        q_item(i, R, c, hq);
-        char* dst = qst + (((R >> 5) << lhp) + hq) * 32 * C::Q_STRIDE + (R & 31) * C::Q_STRIDE + c * 16;
+        const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+        char* dst = q_stage + r * C::Q_STRIDE + c * 16;
         float x0[8], x1[8];
         const u32x4 w0[1] = {q_raw[i][0]};
         raw_to_f32<uint16_t>(w0, x0);
@@ -762,11 +715,8 @@ struct UnitFast {
           *(u32x4*)(dst + D) = to_frag_or_nan<QK>(x1).v;
         }
       }
-    };
-    // The wave's operand fragments (SHARED_Q: after a barrier that follows
-    // stage_q); k-step s of lane (l32, hh) holds elements 16s+8hh..+7 of row
-    // l32, the same split as the K fragments.
-    auto read_q = [&]() {
+      // Operand fragments: k-step s of lane (l32, hh) holds elements 16s+8hh..+7
+      // of row l32, the same split as the K fragments.
 #pragma unroll
       for (int s2 = 0; s2 < C::KSTEPS; ++s2)
         qf[s2].v = *(const u32x4*)(q_stage + l32 * C::Q_STRIDE + 32 * s2 + 16 * hh);
@@ -1215,11 +1165,9 @@ struct UnitFast {
       }
       load_v(jl * BN, vs0, vw);
       stage_q();
-      if constexpr (!SHARED_Q) read_q();
       store_k(jl * BN, ks0, kw, kc, ksn, vw);
       wait_vmem();
       __syncthreads();
-      if constexpr (SHARED_Q) read_q();
       f32x16 s_cur[C::NKB];
       if (wave_has_rows) {
         scores(ks0, s_cur, (f32x16){});
@@ -1306,11 +1254,9 @@ struct UnitFast {
         }
         load_v(0, vs0, vw);
         stage_q();
-        if constexpr (!SHARED_Q) read_q();
         store_k(0, ks0, kw, kc, ksn, vw);
         wait_vmem();
         __syncthreads();
-        if constexpr (SHARED_Q) read_q();
         // S_0 and the reference; K_1 into LDS.
         f32x16 s_cur[C::NKB];
         if (wave_has_rows) {
@@ -1413,14 +1359,13 @@ struct UnitFast {
 
 // img0, img_kvs: the first K tile image of the unit's sequence (K/V head 0)
 // and the images between consecutive K/V heads (used with once-rotated keys).
-template <class C, bool SHARED_Q>
+template <class C>
 __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int qb, int head0, long lse_b,
-                                         long lse_h, long img0, long img_kvs, int tid, CGR_LDS_PARAMS) {
+                                         long lse_h, long img0, long img_kvs, CGR_LDS_PARAMS) {
   if constexpr (C::F32)
     Unit<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, ks0, ks1, vs0, vs1, qst);
   else
-    UnitFast<C>::template run<SHARED_Q>(a, tok0, L, qb, head0, lse_b, lse_h, img0, img_kvs, tid, ks0, ks1, vs0,
-                                        vs1, qst);
+    UnitFast<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, img0, img_kvs, ks0, ks1, vs0, vs1, qst);
 }
 
 // Dense batch: one workgroup per unit (entry, K/V group, hp heads of the
@@ -1464,53 +1409,33 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(Attn
   if (qb * bm >= L) return;
   // Images of a dense batch: per (entry, K/V head), ceil(T / BN) tiles.
   const long n_img = (a.T + C::BN - 1) / C::BN;
-  run_unit<C, false>(a, b * a.T, L, qb, head0, (long)b * a.H * a.T, a.T, (long)b * a.KV * n_img, n_img, threadIdx.x, k0,
-              k1, v0, v1, qst);
+  run_unit<C>(a, b * a.T, L, qb, head0, (long)b * a.H * a.T, a.T, (long)b * a.KV * n_img, n_img, k0, k1, v0, v1,
+              qst);
 }
 
-// Packed batch: a persistent grid pulls (sequence, query block) items from the
-// schedule in order (most expensive first); each item expands to all heads.
+// Packed batch: one workgroup per unit, unit u = (schedule item u / HG, head
+// group u % HG), each item expanding to all its heads. The grid is the
+// bound on the units the host can compute; workgroups past the schedule's
+// count exit at once. The schedule lists items most expensive first, and the
+// device hands out workgroups in index order as compute units free up, which
+// balances the load (longest-processing-time-first) without a work queue.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
-  __shared__ int s_unit;
   const int HG = a.H / a.hp;  // head groups of hp heads
-  const int n_units = a.sched[0] * HG;
-  int* counter = a.sched + 1;
+  const int u = blockIdx.x;
+  if (u >= a.sched[0] * HG) return;
   const int2* items = (const int2*)(a.sched + kSchedHeaderInts);
-  if (threadIdx.x == 0) s_unit = atomicAdd(counter, 1);
-  __syncthreads();
-  // The unit index is the same in every lane; readfirstlane tells the compiler
-  // so, which keeps the loop's exit a scalar branch: a loop whose exit it
-  // thought divergent would let waves leave it under partial exec masks and
-  // miss barriers.
-  int u = __builtin_amdgcn_readfirstlane(s_unit);
-  while (u < n_units) {
-    // Claim the next unit now: the atomic's round trip passes while this one
-    // runs. Its result is published after the unit (whose barriers separate
-    // the write from every wave's read of the current index).
-    int next = 0;
-    if (threadIdx.x == 0) next = atomicAdd(counter, 1);
-    const int it = u / HG, hg = u - it * HG;
-    const int2 sq = items[it];
-    const int tok0 = a.cu_seqlens[sq.x];
-    const int L = a.cu_seqlens[sq.x + 1] - tok0;
-    // Images of a packed batch: per K/V head, kimg_slots slots; sequence s
-    // owns slots kimg_base[s] .. kimg_base[s + 1] - 1.
-    const long img0 = C::KPRE ? (long)a.kimg_base[sq.x] : 0;
-    // The lane index, opaque to the compiler: it would otherwise hoist every
-    // per-lane address of the unit (most of them used only by the rare
-    // fallback passes) out of this loop and keep them live, and spilled,
-    // across all of it; each unit recomputes them instead.
-    int tid = threadIdx.x;
-    __asm__ volatile("" : "+v"(tid));
-    run_unit<C, true>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, img0, a.kimg_slots, tid, k0, k1, v0, v1, qst);
-    if (threadIdx.x == 0) s_unit = next;
-    __syncthreads();
-    u = __builtin_amdgcn_readfirstlane(s_unit);
-  }
+  const int it = u / HG, hg = u - it * HG;
+  const int2 sq = items[it];
+  const int tok0 = a.cu_seqlens[sq.x];
+  const int L = a.cu_seqlens[sq.x + 1] - tok0;
+  // Images of a packed batch: per K/V head, kimg_slots slots; sequence s
+  // owns slots kimg_base[s] .. kimg_base[s + 1] - 1.
+  const long img0 = C::KPRE ? (long)a.kimg_base[sq.x] : 0;
+  run_unit<C>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, img0, a.kimg_slots, k0, k1, v0, v1, qst);
 }
 
 // K rotated once at its positions (token t of a dense batch entry is at

@@ -320,9 +320,6 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
                 need);
   const long max_items = varlen_max_items(num_seqs, total_tokens);
   if (max_items * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
-  int cus = 0;
-  const int ce = cu_count(&cus);
-  if (ce != 0) return hip_fail("device query", (hipError_t)ce);
 
   // Keys rotated once (16-bit I/O) when the workspace also holds their images.
   const VarlenLayout lay = varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim);
@@ -353,9 +350,9 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
     a.kimg_base = kimg_base;
     a.kimg_slots = (int)lay.slots;
   }
-  // Persistent grid: two workgroups per compute unit, never more than the units.
-  long grid = 2L * cus;
-  if (grid > max_items * (n_head / hp)) grid = max_items * (n_head / hp);
+  // One workgroup per unit of the bound on the units (those past the
+  // schedule's count exit at once).
+  long grid = max_items * (n_head / hp);
   if (grid < 1) grid = 1;
   e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
   if (e != hipSuccess) return hip_fail("attention launch", e);
