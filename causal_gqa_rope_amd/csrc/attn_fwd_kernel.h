@@ -1413,22 +1413,25 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(Attn
               qst);
 }
 
-// Packed batch: one workgroup per unit, unit u = (schedule item u / HG, head
-// group u % HG), each item expanding to all its heads. The grid is the
-// bound on the units the host can compute; workgroups past the schedule's
-// count exit at once. The schedule lists items most expensive first, and the
-// device hands out workgroups in index order as compute units free up, which
-// balances the load (longest-processing-time-first) without a work queue.
+// Packed batch: one workgroup per unit (schedule item, head group of hp
+// heads). The schedule lists items most expensive first, and the device hands
+// out workgroups in index order as compute units free up, which balances the
+// load (longest-processing-time-first) without a work queue. Workgroup u runs
+// on XCD u % 8 and takes item (u / 8 / HG) * 8 + u % 8, head group
+// (u / 8) % HG: the head groups of an item follow one another on one XCD,
+// whose L2 then serves the item's K/V tiles to all of them. The grid covers
+// the host's bound on the items, rounded up to 8, times HG; workgroups past
+// the schedule's count exit at once.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) char k0[C::K_BYTES], k1[C::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v0[C::V_BYTES], v1[C::V_BYTES];
   extern __shared__ __attribute__((aligned(16))) char qst[];
   const int HG = a.H / a.hp;  // head groups of hp heads
-  const int u = blockIdx.x;
-  if (u >= a.sched[0] * HG) return;
+  const int j = blockIdx.x >> 3;
+  const int it = (j / HG) * 8 + (blockIdx.x & 7), hg = j % HG;
+  if (it >= a.sched[0]) return;
   const int2* items = (const int2*)(a.sched + kSchedHeaderInts);
-  const int it = u / HG, hg = u - it * HG;
   const int2 sq = items[it];
   const int tok0 = a.cu_seqlens[sq.x];
   const int L = a.cu_seqlens[sq.x + 1] - tok0;

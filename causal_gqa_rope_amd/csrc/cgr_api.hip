@@ -319,7 +319,7 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
     return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
                 need);
   const long max_items = varlen_max_items(num_seqs, total_tokens);
-  if (max_items * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  if ((max_items + 7) * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
 
   // Keys rotated once (16-bit I/O) when the workspace also holds their images.
   const VarlenLayout lay = varlen_layout(num_seqs, total_tokens, n_kv_head, head_dim);
@@ -350,10 +350,9 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
     a.kimg_base = kimg_base;
     a.kimg_slots = (int)lay.slots;
   }
-  // One workgroup per unit of the bound on the units (those past the
-  // schedule's count exit at once).
-  long grid = max_items * (n_head / hp);
-  if (grid < 1) grid = 1;
+  // One workgroup per unit of the bound on the items (rounded up to 8) times
+  // the head groups; those past the schedule's count exit at once.
+  long grid = (max_items + 7) / 8 * 8 * (n_head / hp);
   e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   return CGR_OK;
