@@ -58,7 +58,7 @@ struct AttnArgs {
   const float* rope_sin;
   const int32_t* cu_seqlens;  // packed batches
   const int32_t* seqlens;     // dense batches: valid tokens per entry (right padding), or null
-  int32_t* sched;             // packed batches: [0] items, [1] queue counter, [2] error, then items
+  int32_t* sched;             // packed batches: [0] items, [1] unused, [2] error, then items
   void* krot;                 // with a workspace (16-bit I/O): k rotated once, in the Q.K^T operand type,
                               // as tile images
   const int32_t* kimg_base;   // packed batches with k images: first image slot of each sequence

@@ -6,14 +6,15 @@
 // first, where cost = number of key tiles the item visits (under the causal
 // mask, query block qb of a sequence of length L sees ceil(min((qb+1)*BM, L)
 // / BN) tiles). A counting sort over cost bins keeps this to two passes over
-// the items, each spread evenly over the workgroup's threads. The
-// attention kernel's persistent workgroups then pull items in that order
-// (longest-processing-time-first), which balances the causal triangle of
-// every sequence over the compute units.
+// the items, each spread evenly over the workgroup's threads. The attention
+// kernel's workgroups take the items in that order (the device hands them
+// out by index as compute units free up: longest-processing-time-first),
+// which balances the causal triangle of every sequence over the compute
+// units.
 //
-// Layout of `sched` (int32): [0] number of items, [1] queue counter (reset to
-// 0 here), [2] error word (0 = well formed), [3] unused, then items as
-// (sequence, query block) int pairs.
+// Layout of `sched` (int32): [0] number of items, [1] set to 0 (unused),
+// [2] error word (0 = well formed), [3] unused, then items as (sequence,
+// query block) int pairs.
 //
 // status_out (optional): a second copy of the error word, for callers that
 // pass no workspace of their own.
