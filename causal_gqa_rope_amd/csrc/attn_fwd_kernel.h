@@ -38,6 +38,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "varlen_schedule.h"
 
 namespace cgr {
 
@@ -61,9 +62,9 @@ struct AttnArgs {
   int32_t* sched;             // packed batches: [0] items, [1] unused, [2] error, then items
   void* krot;                 // with a workspace (16-bit I/O): k rotated once, in the Q.K^T operand type,
                               // as tile images
-  const int32_t* kimg_base;   // packed batches with k images: first image slot of each sequence
-                              // ([num_seqs + 1], prefix sums of the sequences' tile counts)
   int kimg_slots;             // packed batches with k images: image slots per K/V head
+  int max_items;              // packed batches: room for work items in `sched`
+  int32_t* status_out;        // packed batches: optional second copy of the schedule's error word
   int B, T, H, KV;
   int total_tokens;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
@@ -72,7 +73,6 @@ struct AttnArgs {
   float qscale;  // softmax_scale * log2(e), folded into Q
 };
 
-constexpr int kSchedHeaderInts = 4;
 
 // The workgroup's LDS: two stages of K and two of V, each its own array, so
 // the compiler can tell a direct-to-LDS load into one of them from reads of
@@ -1435,9 +1435,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_varlen_kernel(Att
   const int2 sq = items[it];
   const int tok0 = a.cu_seqlens[sq.x];
   const int L = a.cu_seqlens[sq.x + 1] - tok0;
-  // Images of a packed batch: per K/V head, kimg_slots slots; sequence s
-  // owns slots kimg_base[s] .. kimg_base[s + 1] - 1.
-  const long img0 = C::KPRE ? (long)a.kimg_base[sq.x] : 0;
+  // Images of a packed batch: per K/V head, kimg_slots slots; sequence s's
+  // tiles start at slot tok0 / BN + s (see varlen_prep_kernel).
+  const long img0 = C::KPRE ? (long)(tok0 / C::BN + sq.x) : 0;
   run_unit<C>(a, tok0, L, sq.y, hg * a.hp, tok0, a.total_tokens, img0, a.kimg_slots, k0, k1, v0, v1, qst);
 }
 
@@ -1484,48 +1484,56 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
   }
 }
 
-// The same images for a packed batch: per K/V head, kimg_slots slots of one
-// tile each; sequence s owns slots kimg_base[s] .. kimg_base[s + 1] - 1 (its
-// tiles in order, token t of the sequence at position t), written by the
-// schedule prepass. Slots past the last sequence's are left alone. The owner
-// of a slot is the last sequence whose first slot is at or before it (empty
-// sequences own none). A malformed cu_seqlens (the prepass's error word set)
-// leaves the images unwritten; every read stays inside q/k and the tables
-// whatever the arrays hold.
-constexpr int kKrotVarlenThreads = 128;
+// Packed batch with the keys rotated once: workgroup 0 builds the work
+// schedule (schedule_body) while the others write the K tile images, as for
+// a dense batch, per K/V head in kimg_slots slots of one tile. Sequence s's
+// tiles take the slots from floor(c_s / BN) + s on (c_s = cu_seqlens[s]): the
+// next sequence starts past s's last tile (floor(c_s / BN) + ceil(L_s / BN)
+// <= floor(c_{s+1} / BN) + 1), every slot stays below ceil(total / BN) +
+// num_seqs, and the attention kernel finds a sequence's first slot from its
+// first token, so the rotation needs nothing from the schedule and both run
+// in one launch. A slot belongs to the last sequence whose first slot is at
+// or before it; rows past that sequence's end, and slots between sequences,
+// are zeros. With a malformed cu_seqlens the schedule sets the error word and
+// schedules nothing, and the images (which then no unit reads) hold whatever
+// the search finds; every read stays inside k and the tables regardless.
+constexpr int kPrepThreads = kSchedThreads;
 template <class C>
-__global__ __launch_bounds__(kKrotVarlenThreads) void krot_varlen_kernel(AttnArgs a) {
-  constexpr int D = C::D, BN = C::BN, IPR = D / 16;
-  static_assert(IPR * BN % kKrotVarlenThreads == 0, "a workgroup's items lie in one image");
-  // The workgroup's image (kv * kimg_slots + slot) is the same in every lane:
-  // the search for its sequence below is uniform.
-  const long first = (long)blockIdx.x * kKrotVarlenThreads;
-  const int img = __builtin_amdgcn_readfirstlane((int)(first / (IPR * BN)));
+__global__ __launch_bounds__(kPrepThreads) void varlen_prep_kernel(AttnArgs a) {
+  constexpr int D = C::D, BN = C::BN, IPR = D / 16, IPI = IPR * BN;  // items per image
+  if (blockIdx.x == 0) {
+    const int bm = 32 * C::NW / a.hp;
+    schedule_body(a.cu_seqlens, a.B, a.total_tokens, a.T, __builtin_ctz(bm), __builtin_ctz(BN), C::CAUSAL,
+                  a.sched, a.max_items, a.status_out);
+    return;
+  }
+  const long tid = (long)(blockIdx.x - 1) * kPrepThreads + threadIdx.x;
+  int img = (int)(tid / IPI);  // kv * kimg_slots + slot
+  // A workgroup's items lie in one image when images are at least a
+  // workgroup long: the search below is then uniform (scalar loads).
+  if constexpr (IPI % kPrepThreads == 0) img = __builtin_amdgcn_readfirstlane(img);
   if (img >= a.KV * a.kimg_slots) return;
-  if (a.sched[2] != 0) return;
-  const int within = (int)(first % (IPR * BN)) + (int)threadIdx.x;
+  const int within = (int)(tid % IPI);
   const int g = within % IPR, r = within / IPR;
   const int slot = img % a.kimg_slots, kv = img / a.kimg_slots;
-  const int nseq = a.B;
-  if (slot >= a.kimg_base[nseq]) return;
-  int lo = 0, hi = nseq - 1;
+  int lo = 0, hi = a.B - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (a.kimg_base[mid] <= slot) lo = mid;
+    if (a.cu_seqlens[mid] / BN + mid <= slot) lo = mid;
     else hi = mid - 1;
   }
-  const int t = (slot - a.kimg_base[lo]) * BN + r;
   const int c0 = a.cu_seqlens[lo], L = a.cu_seqlens[lo + 1] - c0;
+  const int t = (slot - (c0 / BN + lo)) * BN + r;
   u32x4 w0 = {0u, 0u, 0u, 0u}, w1 = {0u, 0u, 0u, 0u};
-  if (t < L && t < a.T && c0 >= 0 && c0 + t < a.total_tokens) {
+  if (t >= 0 && t < L && t < a.T && c0 >= 0 && c0 + t < a.total_tokens) {
     const uint16_t* kp = (const uint16_t*)a.k + ((long)(c0 + t) * a.KV + kv) * D;
     u32x4 i0[1] = {*(const u32x4*)(kp + 8 * g)}, i1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
     float x0[8], x1[8];
     raw_to_f32<uint16_t>(i0, x0);
     raw_to_f32<uint16_t>(i1, x1);
-    f32x4 c[2], s[2];
-    load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, s);
-    rope_pair<C::STYLE>(x0, x1, c, s);
+    f32x4 c[2], sn[2];
+    load_tab<D, C::STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, sn);
+    rope_pair<C::STYLE>(x0, x1, c, sn);
     w0 = to_frag_or_nan<typename C::QK>(x0).v;
     w1 = to_frag_or_nan<typename C::QK>(x1).v;
   }
@@ -1564,13 +1572,13 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int
   return hipGetLastError();
 }
 
-// Packed batch with the K rotation done once up front (a.krot, a.kimg_base
-// set; the schedule prepass has run on the stream).
+// Packed batch with the K rotation done once up front (a.krot set): the
+// schedule and the rotation in one launch, then the attention kernel.
 template <class C>
 hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stream) {
   const long items = (long)a.KV * a.kimg_slots * C::BN * (C::D / 16);
-  hipLaunchKernelGGL((krot_varlen_kernel<C>), dim3((unsigned)(items / kKrotVarlenThreads)), dim3(kKrotVarlenThreads),
-                     0, stream, a);
+  hipLaunchKernelGGL((varlen_prep_kernel<C>), dim3((unsigned)(1 + (items + kPrepThreads - 1) / kPrepThreads)),
+                     dim3(kPrepThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);

@@ -255,11 +255,11 @@ cgr_status dense_fwd(const void* q, const void* k, const void* v, void* o, float
 }
 
 // Workspace of a packed call that rotates the keys once: the schedule, then
-// the first image slot of every sequence, then the K tile images ([K/V head]
-// [slot], slots = ceil(total / BN) + num_seqs, which bounds the sum of the
-// sequences' tile counts); each part starts on a 256-byte boundary.
+// (on a 256-byte boundary) the K tile images ([K/V head][slot], slots =
+// ceil(total / BN) + num_seqs, which bounds the slots the sequences' tiles
+// take; see varlen_prep_kernel).
 struct VarlenLayout {
-  size_t kimg_base, images, total;
+  size_t images, total;
   long slots;
 };
 VarlenLayout varlen_layout(int num_seqs, int total_tokens, int n_kv_head, int head_dim) {
@@ -267,8 +267,7 @@ VarlenLayout varlen_layout(int num_seqs, int total_tokens, int n_kv_head, int he
   VarlenLayout l{};
   const int bn = cgr::fwd_tile_keys(head_dim);
   l.slots = ((long)total_tokens + bn - 1) / bn + num_seqs;
-  l.kimg_base = up(cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens));
-  l.images = up(l.kimg_base + ((size_t)num_seqs + 1) * 4);
+  l.images = up(cgr_attn_fwd_varlen_workspace_size(num_seqs, total_tokens));
   l.total = l.images + (size_t)n_kv_head * l.slots * cgr::fwd_kimg_bytes(head_dim);
   return l;
 }
@@ -329,13 +328,7 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
 
   hipStream_t s = (hipStream_t)stream;
   int32_t* sched = (int32_t*)workspace;
-  int32_t* kimg_base = use_kimg ? (int32_t*)((char*)workspace + lay.kimg_base) : nullptr;
   const int hp = dtype == CGR_F32 ? 1 : cgr::fwd_heads_per_unit(head_dim, n_head / n_kv_head);
-  hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
-                                             cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
-                                             mask == CGR_MASK_CAUSAL, sched,
-                                             (int)max_items, kimg_base, status_out, s);
-  if (e != hipSuccess) return hip_fail("schedule launch", e);
   cgr::AttnArgs a = make_args(q, k, v, o, lse, rope_cos, rope_sin, n_head, n_kv_head, head_dim,
                               softmax_scale);
   a.cu_seqlens = cu_seqlens;
@@ -345,15 +338,22 @@ cgr_status varlen_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.total_tokens = total_tokens;
   a.window = window;
   a.hp = hp;
+  a.max_items = (int)max_items;
+  a.status_out = status_out;
   if (use_kimg) {
+    // The schedule runs inside the key rotation's launch.
     a.krot = (char*)workspace + lay.images;
-    a.kimg_base = kimg_base;
     a.kimg_slots = (int)lay.slots;
+  } else {
+    hipError_t e = cgr::launch_varlen_schedule(cu_seqlens, num_seqs, total_tokens, max_seqlen,
+                                               cgr::fwd_block_rows(head_dim, hp), cgr::fwd_tile_keys(head_dim),
+                                               mask == CGR_MASK_CAUSAL, sched, (int)max_items, status_out, s);
+    if (e != hipSuccess) return hip_fail("schedule launch", e);
   }
   // One workgroup per unit of the bound on the items (rounded up to 8) times
   // the head groups; those past the schedule's count exit at once.
   long grid = (max_items + 7) / 8 * 8 * (n_head / hp);
-  e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
+  const hipError_t e = launch_by_dim(a, head_dim, dtype, qk_operand, style, mask, true, (int)grid, s);
   if (e != hipSuccess) return hip_fail("attention launch", e);
   return CGR_OK;
 }

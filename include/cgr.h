@@ -239,12 +239,11 @@ CGR_API size_t cgr_attn_fwd_varlen_workspace_size(int num_seqs, int total_tokens
 
 /*
  * Bytes of device workspace with which cgr_gqa_rope_attn_fwd_varlen (bf16
- * I/O) also rotates every key once up front: the schedule above, then the
- * first tile slot of every sequence, then the rotated keys as tile images
- * (per K/V head, ceil(total_tokens / BN) + num_seqs tiles of BN keys x
- * head_dim, BN = 64, or 32 at head_dim 256, in the Q.K^T operand type), each
- * part on a 256-byte boundary. The rotation is the same arithmetic as the
- * per-tile one, so the results are bit-identical. Returns 0 for invalid
+ * I/O) also rotates every key once up front: the schedule above, then, on a
+ * 256-byte boundary, the rotated keys as tile images (per K/V head,
+ * ceil(total_tokens / BN) + num_seqs tiles of BN keys x head_dim, BN = 64, or
+ * 32 at head_dim 256, in the Q.K^T operand type). The rotation is the same
+ * arithmetic as the per-tile one, so the results are bit-identical. Returns 0 for invalid
  * sizes (num_seqs < 1, total_tokens < 0, n_kv_head < 1, or a head_dim other
  * than 32, 64, 128, 256).
  */
