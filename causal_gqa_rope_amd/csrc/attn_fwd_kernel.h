@@ -1154,15 +1154,9 @@ struct UnitFast {
       l_run = 0.f;
       u32x4 kw1[KI][2];
       f32x4 kc1[KI][2], ksn1[KI][2];
-      if constexpr (!C::KPRE) {
-        load_k(jl * BN, ks0, kw, kc, ksn);
-        if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
-      }
-      __syncthreads();  // earlier users of this workgroup's LDS are done
-      if constexpr (C::KPRE) {
-        load_k(jl * BN, ks0, kw, kc, ksn);
-        if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
-      }
+      // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
+      load_k(jl * BN, ks0, kw, kc, ksn);
+      if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
       load_v(jl * BN, vs0, vw);
       stage_q();
       store_k(jl * BN, ks0, kw, kc, ksn, vw);
@@ -1243,15 +1237,9 @@ struct UnitFast {
         l_run = 0.f;
         u32x4 kw1[KI][2];
         f32x4 kc1[KI][2], ksn1[KI][2];
-        if constexpr (!C::KPRE) {
-          load_k(0, ks0, kw, kc, ksn);
-          if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
-        }
-        __syncthreads();  // earlier users of this workgroup's LDS are done
-        if constexpr (C::KPRE) {
-          load_k(0, ks0, kw, kc, ksn);
-          if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
-        }
+        // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
+        load_k(0, ks0, kw, kc, ksn);
+        if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
         load_v(0, vs0, vw);
         stage_q();
         store_k(0, ks0, kw, kc, ksn, vw);
