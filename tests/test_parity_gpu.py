@@ -442,6 +442,30 @@ def test_packed_pre_rotated_keys_give_the_same_bits(gpu, lengths, H, KV, d, caus
         assert_close("packed pre-rotated", f64(o2), ro, f64(l2), rl, "bf16")
 
 
+@pytest.mark.parametrize("rotate_keys_once", [True, False], ids=["rotated_once", "per_tile"])
+def test_packed_batch_of_many_short_sequences(gpu, rotate_keys_once):
+    """1300 sequences of 0 to 70 tokens (the schedule handles 512 sequences per
+    round; empty sequences leave unowned image slots between their
+    neighbours'): against the oracle, and the two key paths bit for bit."""
+    rng = np.random.default_rng(77)
+    lengths = [int(x) for x in rng.integers(0, 71, 1300)]
+    lengths[100:110] = [0] * 10
+    lengths[-1] = 0
+    announce(f"packed batch of {len(lengths)} short sequences, {sum(lengths)} tokens, "
+             f"rotate_keys_once={rotate_keys_once}")
+    x = packed_inputs(lengths, 4, 1, 64, "bf16", seed=78)
+    xd = to_dev(x, gpu)
+    ms = max(lengths)
+    cos, sin = cgr.rope_tables(ms, 64, 1e4, device=gpu)
+    args = (xd["q"], xd["k"], xd["v"], xd["cu_seqlens"], ms, cos, sin)
+    o, lse = cgr.gqa_rope_attn_fwd_varlen(*args, rotate_keys_once=rotate_keys_once)
+    o2, l2 = cgr.gqa_rope_attn_fwd_varlen(*args, rotate_keys_once=not rotate_keys_once)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    ro, rl = oracle.attention_varlen(x["q"], x["k"], x["v"], x["cu_seqlens"].numpy(), causal=True, base=1e4)
+    assert_close("many short sequences", f64(o), ro, f64(lse), rl, "bf16")
+
+
 def test_longest_sequence_the_offsets_allow(gpu):
     """T = 120000 with 32 query heads of 128 (one sequence of 0.98 GB of q, byte
     offsets up to 2^31 within a sequence): sampled rows, the last rows of every
