@@ -29,7 +29,8 @@ bounded sample of the same workload on this host's cores.
                                         --only NAME: that workload alone; --graph: also
                                         replayed from a HIP graph)
   python bench.py --backward           (one JSON line for the backward on the same
-                                        workload; not the headline line)
+                                        workload; not the headline line; --varlen: on the
+                                        packed MQA batch of 32 sequences instead)
   python bench.py --decode             (one JSON line for decode against a KV cache,
                                         16 sequences x 1 new token; not the headline line)
   python bench.py --window W           (the forward or --backward line with a causal
@@ -62,6 +63,7 @@ if ROOT not in sys.path:
 
 METRIC = "causal GQA+RoPE attention fwd TFLOP/s on 1 MI355X; % of bf16 MFMA peak"
 WORKLOAD = "long_context_T8192_H32_KV8_d128"
+VARLEN_WORKLOAD = "varlen_mqa_32seqs_16to2048_H16_KV1_d128"
 PADDED_WORKLOAD = "padded_B4_T8192_len2048to8192_H32_KV8_d128"
 WIDE_WORKLOAD = "long_context_T8192_H16_KV8_d256"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
@@ -318,24 +320,38 @@ def cpu_baseline_bwd(inputs, dout, w) -> dict:
     }
 
 
-def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window: int = 0) -> None:
+def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window: int = 0,
+             varlen: bool = False) -> None:
     """One step = one backward call (prepass, dk/dv kernel, dq kernel) on the
-    long-context workload; o and lse come from one forward before timing."""
-    w = W.get(WORKLOAD)
+    long-context workload (varlen: the packed MQA batch); o and lse come from
+    one forward before timing."""
+    w = W.get(VARLEN_WORKLOAD if varlen else WORKLOAD)
     inputs = W.make_inputs(w)
     q, k, v = (inputs[n].to(dev) for n in ("q", "k", "v"))
     dout_cpu = W.make_dout(w, inputs["q"])
     dout = dout_cpu.to(dev)
-    cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
-    o, lse = cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=True, rope_style=w.rope_style, window=window)
+    kw = dict(causal=True, rope_style=w.rope_style, window=window)
+    if varlen:
+        cu, ms = inputs["cu_seqlens"].to(dev), inputs["max_seqlen"]
+        lens = [int(n) for n in inputs["lengths"]]
+        cos, sin = cgr.rope_tables(ms, w.head_dim, w.base, device=dev)
+        o, lse = cgr.gqa_rope_attn_fwd_varlen(q, k, v, cu, ms, cos, sin, **kw)
+        nbytes = cgr.cgr_attn_bwd_varlen_workspace_size(len(lens), sum(lens), w.n_head, w.n_kv_head, w.head_dim)
+    else:
+        lens = [w.T] * w.B
+        cos, sin = cgr.rope_tables(w.T, w.head_dim, w.base, device=dev)
+        o, lse = cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, **kw)
+        nbytes = cgr.cgr_attn_bwd_workspace_size(w.B, w.T, w.n_head, w.n_kv_head, w.head_dim)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(cgr.cgr_attn_bwd_workspace_size(w.B, w.T, w.n_head, w.n_kv_head, w.head_dim),
-                     dtype=torch.uint8, device=dev)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def call():
-        cgr.gqa_rope_attn_bwd(q, k, v, o, lse, dout, cos, sin, causal=True, rope_style=w.rope_style,
-                              window=window, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if varlen:
+            cgr.gqa_rope_attn_bwd_varlen(q, k, v, o, lse, dout, cu, ms, cos, sin, **kw, dq=dq, dk=dk, dv=dv,
+                                         workspace=ws)
+        else:
+            cgr.gqa_rope_attn_bwd(q, k, v, o, lse, dout, cos, sin, **kw, dq=dq, dk=dk, dv=dv, workspace=ws)
 
     for _ in range(warmup):
         call()
@@ -348,7 +364,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, [w.T] * w.B, True, window)
+    flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, lens, True, window)
     ms_step = wall * 1e3 / steps
     call_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     achieved = flops / (call_ms * 1e-3) / 1e12
@@ -366,9 +382,10 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window
         "dtype": "f16/bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
-            "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
-            "io": "bf16", "qk_operand": "f16", "accumulate": "f32", "step": "gqa_rope_attn_bwd",
+            "workload": w.name, "B": len(lens), "T": max(lens), "total_tokens": sum(lens), "n_head": w.n_head,
+            "n_kv_head": w.n_kv_head, "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style,
+            "mask": "causal", "io": "bf16", "qk_operand": "f16", "accumulate": "f32",
+            "step": "gqa_rope_attn_bwd_varlen" if varlen else "gqa_rope_attn_bwd",
             "window": window, "flops_per_step": flops,
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
@@ -383,7 +400,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window
                       "(head_dim 128, f16 QK, causal, interleaved)",
             "kernel_ms": round(call_ms, 5),
         },
-        "cpu_baseline": cpu_baseline_bwd(inputs, dout_cpu, w) if with_cpu and window == 0 else None,
+        "cpu_baseline": cpu_baseline_bwd(inputs, dout_cpu, w) if with_cpu and window == 0 and not varlen else None,
     }
     print(json.dumps(result), flush=True)
 
@@ -678,6 +695,7 @@ def main() -> int:
                     help="with --all-configs: also time the calls captured in a HIP graph and replayed")
     ap.add_argument("--only", default=None, help="with --all-configs: this workload only")
     ap.add_argument("--backward", action="store_true")
+    ap.add_argument("--varlen", action="store_true", help="with --backward: the packed MQA batch")
     ap.add_argument("--decode", action="store_true")
     ap.add_argument("--window", type=int, default=0)
     ap.add_argument("--qkv", action="store_true")
@@ -708,7 +726,8 @@ def main() -> int:
         all_configs(torch, cgr, W, dev, args.steps, args.warmup, graph=args.graph, only=args.only)
         return 0
     if args.backward:
-        backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline, args.window)
+        backward(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline, args.window,
+                 varlen=args.varlen)
         return 0
     if args.decode:
         decode(torch, cgr, W, dev, args.steps, args.warmup, not args.no_cpu_baseline)

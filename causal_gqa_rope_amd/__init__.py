@@ -5,10 +5,11 @@ kernels of ``libcgr.so``; torch supplies device memory and the current
 stream. The functions carry the names of the C entry points declared in
 ``include/cgr.h`` (``cgr_rope_tables``, ``cgr_gqa_rope_attn_fwd``,
 ``cgr_gqa_rope_attn_fwd_varlen``, ``cgr_gqa_rope_attn_bwd``,
-``cgr_rope_rotate``, ``cgr_gqa_rope_attn_decode``, ...); the short names
-(``rope_tables``, ``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``,
-``gqa_rope_attn_bwd``, ``rope_rotate``, ``gqa_rope_attn_decode``) are the same
-functions.
+``cgr_gqa_rope_attn_bwd_varlen``, ``cgr_rope_rotate``,
+``cgr_gqa_rope_attn_decode``, ...); the short names (``rope_tables``,
+``gqa_rope_attn_fwd``, ``gqa_rope_attn_fwd_varlen``, ``gqa_rope_attn_bwd``,
+``gqa_rope_attn_bwd_varlen``, ``rope_rotate``, ``gqa_rope_attn_decode``) are
+the same functions.
 
 The library leaves the HIP runtime's symbols unresolved; before loading it,
 the binding makes the runtime torch already loaded globally visible, so the
@@ -40,6 +41,8 @@ __all__ = [
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
+    "cgr_attn_bwd_varlen_workspace_size",
+    "cgr_gqa_rope_attn_bwd_varlen",
     "cgr_rope_rotate",
     "cgr_attn_decode_workspace_size",
     "cgr_gqa_rope_attn_decode",
@@ -50,6 +53,7 @@ __all__ = [
     "gqa_rope_attn_fwd",
     "gqa_rope_attn_fwd_varlen",
     "gqa_rope_attn_bwd",
+    "gqa_rope_attn_bwd_varlen",
     "rope_rotate",
     "gqa_rope_attn_decode",
     "rmsnorm_qkv_rope",
@@ -80,6 +84,8 @@ EXPORTED_SYMBOLS = (
     "cgr_varlen_device_status",
     "cgr_attn_bwd_workspace_size",
     "cgr_gqa_rope_attn_bwd",
+    "cgr_attn_bwd_varlen_workspace_size",
+    "cgr_gqa_rope_attn_bwd_varlen",
     "cgr_rope_rotate",
     "cgr_attn_decode_workspace_size",
     "cgr_gqa_rope_attn_decode",
@@ -157,6 +163,12 @@ def library() -> ctypes.CDLL:
                                           i32, vp, vp, i32, i32, i32, i32, f32, i32, vp, ctypes.c_size_t,
                                           vp]
     lib.cgr_gqa_rope_attn_bwd.restype = i32
+    lib.cgr_attn_bwd_varlen_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    lib.cgr_attn_bwd_varlen_workspace_size.restype = ctypes.c_size_t
+    lib.cgr_gqa_rope_attn_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                 i32, i32, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp,
+                                                 ctypes.c_size_t, vp]
+    lib.cgr_gqa_rope_attn_bwd_varlen.restype = i32
     lib.cgr_rope_rotate.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, i32, i32, vp, vp]
     lib.cgr_rope_rotate.restype = i32
     lib.cgr_attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
@@ -551,6 +563,65 @@ def cgr_gqa_rope_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: 
     return dq, dk, dv
 
 
+def cgr_attn_bwd_varlen_workspace_size(num_seqs: int, total_tokens: int, n_head: int, n_kv_head: int,
+                                       head_dim: int) -> int:
+    return int(library().cgr_attn_bwd_varlen_workspace_size(int(num_seqs), int(total_tokens), int(n_head),
+                                                             int(n_kv_head), int(head_dim)))
+
+
+def cgr_gqa_rope_attn_bwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                                 lse: torch.Tensor, dout: torch.Tensor, cu_seqlens: torch.Tensor, max_seqlen: int,
+                                 rope_cos: torch.Tensor, rope_sin: torch.Tensor, *, causal: bool = True,
+                                 rope_style: str = "interleaved", window: int = 0,
+                                 softmax_scale: Optional[float] = None, qk_operand: str = "f16",
+                                 dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                                 dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Packed backward: the packed forward's q, k, v, o [total,.,d], lse [H,total],
+    cu_seqlens and dL/dO -> (dq, dk, dv).
+
+    Every argument that the forward also takes must be the same as in that
+    forward call (bf16 tensors only).
+    """
+    lib = library()
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _dev_tensor(n, t, torch.bfloat16)
+    _dev_tensor("cu_seqlens", cu_seqlens, torch.int32)
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise CgrError(CGR_ERR_INVALID_ARG, "q, k, v must be 3-D [total, heads, head_dim]")
+    total, H, D = q.shape
+    if k.shape != v.shape or k.shape[0] != total or k.shape[2] != D:
+        raise CgrError(CGR_ERR_INVALID_ARG, f"k/v shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise CgrError(CGR_ERR_INVALID_ARG, "o and dout must have q's shape")
+    _dev_tensor("lse", lse, torch.float32)
+    if tuple(lse.shape) != (H, total):
+        raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [H, total]")
+    _dev_tensor("rope_cos", rope_cos, torch.float32)
+    _dev_tensor("rope_sin", rope_sin, torch.float32)
+    if rope_cos.shape != rope_sin.shape or rope_cos.dim() != 2 or rope_cos.shape[1] != D // 2:
+        raise CgrError(CGR_ERR_INVALID_ARG, "rope tables must be [max_pos, head_dim/2]")
+    nseq = cu_seqlens.numel() - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for n, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _dev_tensor(n, t, torch.bfloat16)
+        if t.shape != ref.shape:
+            raise CgrError(CGR_ERR_INVALID_ARG, f"{n} must have shape {tuple(ref.shape)}")
+    need = lib.cgr_attn_bwd_varlen_workspace_size(max(nseq, 1), total, H, k.shape[1], D)
+    if workspace is None:
+        workspace = torch.empty(max(int(need), 256), dtype=torch.uint8, device=q.device)
+    _dev_tensor("workspace", workspace)
+    with torch.cuda.device(q.device):
+        _check(lib.cgr_gqa_rope_attn_bwd_varlen(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(cu_seqlens), nseq, total, int(max_seqlen), H, k.shape[1], D, CGR_BF16, _ptr(rope_cos),
+            _ptr(rope_sin), rope_cos.shape[0], _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
+            int(window), 0.0 if softmax_scale is None else float(softmax_scale), _QK[qk_operand],
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)))
+    return dq, dk, dv
+
+
 def cgr_rope_rotate(x: torch.Tensor, positions: torch.Tensor, rope_cos: torch.Tensor,
                     rope_sin: torch.Tensor, *, rope_style: str = "interleaved",
                     out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None):
@@ -700,6 +771,7 @@ gqa_rope_attn_fwd_fp8 = cgr_gqa_rope_attn_fwd_fp8
 gqa_rope_attn_fwd_varlen = cgr_gqa_rope_attn_fwd_varlen
 gqa_rope_attn_fwd_varlen_noalloc = cgr_gqa_rope_attn_fwd_varlen_noalloc
 gqa_rope_attn_bwd = cgr_gqa_rope_attn_bwd
+gqa_rope_attn_bwd_varlen = cgr_gqa_rope_attn_bwd_varlen
 rope_rotate = cgr_rope_rotate
 gqa_rope_attn_decode = cgr_gqa_rope_attn_decode
 rmsnorm_qkv_rope = cgr_rmsnorm_qkv_rope

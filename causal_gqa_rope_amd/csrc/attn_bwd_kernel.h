@@ -52,14 +52,45 @@ struct BwdArgs {
   // Workspace (written by bwd_prep_kernel).
   void* qr;   // [B, T, H, D] operand type: R q * scale * log2(e)
   void* kr;   // [B, T, KV, D] operand type: R k
-  float* ld;  // [B, H, NT][64]: per 32-row tile, -lse*log2(e) (rows 0..31) then -D
+  float* ld;  // [B, H, NT][64] (dense) or [H, NSL][64] (packed): per 32-row tile,
+              // -lse*log2(e) (rows 0..31) then -D
   int B, T, H, KV, NT;
+  // Packed batches (cu_seqlens non-null): nseq sequences, total tokens, T =
+  // max_seqlen; tensors [total, heads, D], lse [H, total]. Sequence s's blocks
+  // of 2^k rows take slots (c_s >> k) + s on (slot_owner); NSL is the number
+  // of 32-row slots per head in ld.
+  const int32_t* cu_seqlens;
+  int nseq, total, NSL;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
   float qscale;  // scale * log2(e)
   float scale;
 };
 
 constexpr int kBwdTileRows = 32;  // rows per ld tile
+
+// Packed batches: sequence s's blocks of 2^lb tokens take slots (c_s >> lb) + s
+// on (c_s = cu_seqlens[s]). The next sequence's first slot lies past s's last
+// ((c_s >> lb) + ceil(L_s / 2^lb) <= (c_{s+1} >> lb) + 1), so no slot has two
+// sequences, and all stay below ceil(total / 2^lb) + nseq. The owner of a
+// slot is the last sequence whose first slot is at or before it; callers
+// check that the block lies inside it (slots between sequences belong to
+// none). The search's reads stay inside cu_seqlens whatever it holds.
+__device__ __forceinline__ int slot_owner(const int32_t* cu, int nseq, int lb, int slot) {
+  int lo = 0, hi = nseq - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((cu[mid] >> lb) + mid <= slot) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Packed batches: whether sequence s (tokens c0 .. c0 + L - 1) lies inside the
+// batch as the forward validated it; a unit of a sequence that does not
+// touches no memory.
+__device__ __forceinline__ bool seq_ok(const BwdArgs& a, int c0, int L) {
+  return c0 >= 0 && L >= 0 && L <= a.T && c0 <= a.total - L;
+}
 
 // ---------------------------------------------------------------------------
 // Prepass. Item = (row, group g < D/16), covering the chunk pair (g, g + D/16)
@@ -139,6 +170,97 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
+// The prepass of a packed batch. Query items (32-row slot, head, row of the
+// slot, group) write the rotated q of their token and the slot's starting
+// values (rows past their sequence, and slots between sequences, get -inf and
+// 0); key items (token, K/V head, group) find their token's sequence by
+// binary search over cu_seqlens (positions restart at 0 in every sequence).
+template <int D, typename QK, int STYLE>
+__global__ __launch_bounds__(256) void bwd_prep_varlen_kernel(BwdArgs a) {
+  constexpr int IPR = D / 16;
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  const long nq = (long)a.NSL * a.H * kBwdTileRows * IPR;
+  const long nk = (long)a.total * a.KV * IPR;
+  const int g = (int)(tid % IPR);
+  if (tid < nq) {
+    const long row = tid / IPR;  // (slot * H + h) * 32 + r
+    const int r = (int)(row % kBwdTileRows);
+    const long sh = row / kBwdTileRows;
+    const int h = (int)(sh % a.H), slot = (int)(sh / a.H);
+    const int s = slot_owner(a.cu_seqlens, a.nseq, 5, slot);
+    const int c0 = a.cu_seqlens[s], L = a.cu_seqlens[s + 1] - c0;
+    const int t = (slot - ((c0 >> 5) + s)) * kBwdTileRows + r;
+    const bool ok = seq_ok(a, c0, L) && t >= 0 && t < L;
+    float dot = 0.f;
+    if (ok) {
+      const long e0 = ((long)(c0 + t) * a.H + h) * D;
+      const uint16_t* qp = (const uint16_t*)a.q + e0;
+      u32x4 w0[1] = {*(const u32x4*)(qp + 8 * g)}, w1[1] = {*(const u32x4*)(qp + 8 * g + D / 2)};
+      float x0[8], x1[8];
+      raw_to_f32<uint16_t>(w0, x0);
+      raw_to_f32<uint16_t>(w1, x1);
+      f32x4 c[2], sn[2];
+      load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, sn);
+      rope_pair<STYLE>(x0, x1, c, sn);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        x0[j] *= a.qscale;
+        x1[j] *= a.qscale;
+      }
+      uint16_t* qo = (uint16_t*)a.qr + e0;
+      *(u32x4*)(qo + 8 * g) = to_frag<QK>(x0).v;
+      *(u32x4*)(qo + 8 * g + D / 2) = to_frag<QK>(x1).v;
+      const uint16_t* op = (const uint16_t*)a.o + e0;
+      const uint16_t* dp = (const uint16_t*)a.dout + e0;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int off = 8 * g + half * (D / 2);
+        u32x4 wo[1] = {*(const u32x4*)(op + off)}, wd[1] = {*(const u32x4*)(dp + off)};
+        float xo[8], xd[8];
+        raw_to_f32<uint16_t>(wo, xo);
+        raw_to_f32<uint16_t>(wd, xd);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot += xo[j] * xd[j];
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < IPR; m <<= 1) dot += __shfl_xor(dot, m, 64);
+    if (g == 0) {
+      float* l = a.ld + ((long)h * a.NSL + slot) * 64 + r;
+      l[0] = ok ? -a.lse[(long)h * a.total + c0 + t] * 1.4426950408889634f : -INFINITY;
+      l[32] = ok ? -dot : 0.f;
+    }
+  } else if (tid < nq + nk) {
+    const long row = (tid - nq) / IPR;  // p * KV + kv
+    const int p = (int)(row / a.KV);
+    // The sequence holding token p: the last s with cu_seqlens[s] <= p.
+    int lo = 0, hi = a.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_seqlens[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const int t = p - a.cu_seqlens[lo];
+    const long e0 = row * D;
+    u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
+    if (t >= 0 && t < a.T) {
+      const uint16_t* kp = (const uint16_t*)a.k + e0;
+      u32x4 w0[1] = {*(const u32x4*)(kp + 8 * g)}, w1[1] = {*(const u32x4*)(kp + 8 * g + D / 2)};
+      float x0[8], x1[8];
+      raw_to_f32<uint16_t>(w0, x0);
+      raw_to_f32<uint16_t>(w1, x1);
+      f32x4 c[2], sn[2];
+      load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, sn);
+      rope_pair<STYLE>(x0, x1, c, sn);
+      o0 = to_frag<QK>(x0).v;
+      o1 = to_frag<QK>(x1).v;
+    }
+    uint16_t* ko = (uint16_t*)a.kr + e0;
+    *(u32x4*)(ko + 8 * g) = o0;
+    *(u32x4*)(ko + 8 * g + D / 2) = o1;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // dk, dv. Workgroup = 8 waves = two groups of 4; wave w holds keys
 // k0 + 32(w%4) .. +31 of the workgroup's 128. The work items are (32-row
@@ -180,23 +302,45 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int grp = wave >> 2, wig = wave & 3;
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.H / a.KV;
-  const int nK = (a.T + C::BK - 1) / C::BK;
-  // Heavy blocks first (causal: the first keys see the most queries); when
-  // the (batch, K/V head) groups divide evenly over the 8 XCDs, each XCD keeps
-  // whole groups, whose queries it then streams through one L2.
-  const int u = blockIdx.x, groups = a.B * a.KV;
-  int rank, gsel;
-  if ((groups & 7) == 0) {
-    const int x = u & 7, i = u >> 3, per = groups >> 3;
-    rank = i / per;
-    gsel = (i - rank * per) * 8 + x;
+  const int u = blockIdx.x;
+  int kb, kvh, L, tok0;
+  long ldt0, ldh;  // ld tile of the sequence's row 0 at head 0; tiles per head
+  if (a.cu_seqlens) {
+    // Packed: unit = (128-key slot, K/V head), the heads innermost (with 8 or
+    // more K/V heads each XCD keeps the same heads). Each sequence's first
+    // (heaviest, causal) block comes before its later ones.
+    static_assert(C::BK == 1 << 7, "slots of 128 keys");
+    const int slot = u / a.KV;
+    kvh = u - slot * a.KV;
+    const int s = slot_owner(a.cu_seqlens, a.nseq, 7, slot);
+    tok0 = a.cu_seqlens[s];
+    L = a.cu_seqlens[s + 1] - tok0;
+    kb = slot - ((tok0 >> 7) + s);
+    if (!seq_ok(a, tok0, L) || kb < 0 || kb * C::BK >= L) return;
+    ldt0 = (tok0 >> 5) + s;
+    ldh = a.NSL;
   } else {
-    rank = u / groups;
-    gsel = u - rank * groups;
+    // Heavy blocks first (causal: the first keys see the most queries); when
+    // the (batch, K/V head) groups divide evenly over the 8 XCDs, each XCD
+    // keeps whole groups, whose queries it then streams through one L2.
+    const int groups = a.B * a.KV;
+    int rank, gsel;
+    if ((groups & 7) == 0) {
+      const int x = u & 7, i = u >> 3, per = groups >> 3;
+      rank = i / per;
+      gsel = (i - rank * per) * 8 + x;
+    } else {
+      rank = u / groups;
+      gsel = u - rank * groups;
+    }
+    kb = rank;
+    const int b = gsel / a.KV;
+    kvh = gsel - b * a.KV;
+    L = a.T;
+    tok0 = b * a.T;
+    ldt0 = (long)b * a.H * a.NT;
+    ldh = a.NT;
   }
-  const int kb = rank;
-  const int b = gsel / a.KV, kvh = gsel - b * a.KV;
-  const int L = a.T, tok0 = b * a.T;
   const int k0 = kb * C::BK, kw0 = k0 + 32 * wig;
   const int qs = a.H * D, ks = a.KV * D;  // token strides (elements)
 
@@ -222,7 +366,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int n_steps = (q_end - q_first + 31) / 32;
   const int n_items = G * n_steps;
   const int n_iter = (n_items + 1) / 2;
-  const rsrc_t rld = make_rsrc(a.ld, (uint32_t)((long)a.B * a.H * a.NT * 256));
+  const long ld_tiles = a.cu_seqlens ? (long)a.H * a.NSL : (long)a.B * a.H * a.NT;
+  const rsrc_t rld = make_rsrc(a.ld, (uint32_t)(ld_tiles * 256));
 
   // Item n = (query step, head g) with the heads innermost and the steps from
   // the last rows back: the workgroups of one K/V head (which share an XCD)
@@ -247,7 +392,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
     tile_to_lds<D, 32>(rq, gs, qs * 2, qrow0 * qs * 2, wig, 4, lane);
     tile_to_lds<D, 32>(rd, gs + C::TILE, qs * 2, qrow0 * qs * 2, wig, 4, lane);
     if (wig == 0) {
-      const long t = ((long)b * a.H + h) * a.NT + qrow0 / 32;
+      const long t = ldt0 + (long)h * ldh + qrow0 / 32;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_void*)(gs + 2 * C::TILE), 4, lane * 4,
                                                (int)(t * 256), 0, 0);
     }
@@ -394,25 +539,58 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.H / a.KV;
-  const int nQ = (a.T + C::BQ - 1) / C::BQ;
-  const int u = blockIdx.x, groups = a.B * a.KV;
-  int rank, gsel, hq;
-  if ((groups & 7) == 0) {
-    const int x = u & 7, i = u >> 3, per = (groups >> 3) * G;
-    rank = i / per;
-    const int rem = i - rank * per;
-    gsel = (rem / G) * 8 + x;
-    hq = rem % G;
+  const int u = blockIdx.x;
+  int qb, kvh, hq, L, tok0;
+  long ldt0, ldh;  // ld tile of the sequence's row 0 at head 0; tiles per head
+  if (a.cu_seqlens) {
+    // Packed: unit = (256-row slot, query head), the heads innermost and the
+    // slots from the last back (causal: each sequence's last, heaviest block
+    // first). With a multiple of 8 K/V heads, head i of a slot takes K/V head
+    // ((i / 8) / G) * 8 + i % 8, so each XCD keeps the same K/V heads.
+    static_assert(C::BQ == 1 << 8, "slots of 256 rows");
+    const int per = a.H;
+    const int slot = (int)gridDim.x / per - 1 - u / per;  // the grid has every slot
+    const int i = u - (u / per) * per;
+    if ((a.KV & 7) == 0) {
+      kvh = ((i >> 3) / G) * 8 + (i & 7);
+      hq = (i >> 3) % G;
+    } else {
+      kvh = i / G;
+      hq = i % G;
+    }
+    const int s = slot_owner(a.cu_seqlens, a.nseq, 8, slot);
+    tok0 = a.cu_seqlens[s];
+    L = a.cu_seqlens[s + 1] - tok0;
+    qb = slot - ((tok0 >> 8) + s);
+    if (!seq_ok(a, tok0, L) || qb < 0 || qb * C::BQ >= L) return;
+    ldt0 = (tok0 >> 5) + s;
+    ldh = a.NSL;
   } else {
-    const int per = groups * G;
-    rank = u / per;
-    const int rem = u - rank * per;
-    gsel = rem / G;
-    hq = rem % G;
+    const int nQ = (a.T + C::BQ - 1) / C::BQ;
+    const int groups = a.B * a.KV;
+    int rank, gsel;
+    if ((groups & 7) == 0) {
+      const int x = u & 7, i = u >> 3, per = (groups >> 3) * G;
+      rank = i / per;
+      const int rem = i - rank * per;
+      gsel = (rem / G) * 8 + x;
+      hq = rem % G;
+    } else {
+      const int per = groups * G;
+      rank = u / per;
+      const int rem = u - rank * per;
+      gsel = rem / G;
+      hq = rem % G;
+    }
+    qb = C::CAUSAL ? nQ - 1 - rank : rank;
+    const int b = gsel / a.KV;
+    kvh = gsel - b * a.KV;
+    L = a.T;
+    tok0 = b * a.T;
+    ldt0 = (long)b * a.H * a.NT;
+    ldh = a.NT;
   }
-  const int qb = C::CAUSAL ? nQ - 1 - rank : rank;
-  const int b = gsel / a.KV, kvh = gsel - b * a.KV, head = kvh * G + hq;
-  const int L = a.T, tok0 = b * a.T;
+  const int head = kvh * G + hq;
   const int qs = a.H * D, ks = a.KV * D;
   const int q0 = qb * C::BQ, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
   const bool wave_has_rows = qw0 < L;
@@ -436,7 +614,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   }
   float neg_lse = -INFINITY, neg_d = 0.f;
   if (my_q < L) {
-    const float* l = a.ld + (((long)b * a.H + head) * a.NT + my_q / 32) * 64 + my_q % 32;
+    const float* l = a.ld + (ldt0 + (long)head * ldh + my_q / 32) * 64 + my_q % 32;
     neg_lse = l[0];
     neg_d = l[32];
   }
@@ -521,19 +699,33 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // Launch the three kernels of one instance (arguments validated by the caller).
+// Packed batches: a grid of every 128-key slot (dk, dv) and every 256-row
+// slot (dq) of the batch; units of slots that hold no block exit at once.
 template <class C>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   constexpr int D = C::D;
-  const long items = ((long)a.B * a.NT * kBwdTileRows * a.H + (long)a.B * a.T * a.KV) * (D / 16);
-  hipLaunchKernelGGL((bwd_prep_kernel<D, typename C::QK, C::STYLE>), dim3((unsigned)((items + 255) / 256)),
-                     dim3(256), 0, stream, a);
+  long items, k_units, q_units;
+  if (a.cu_seqlens) {
+    items = ((long)a.NSL * kBwdTileRows * a.H + (long)a.total * a.KV) * (D / 16);
+    k_units = ((long)a.total + C::BK - 1) / C::BK + a.nseq;
+    q_units = ((long)a.total + C::BQ - 1) / C::BQ + a.nseq;
+  } else {
+    items = ((long)a.B * a.NT * kBwdTileRows * a.H + (long)a.B * a.T * a.KV) * (D / 16);
+    k_units = (long)(a.T + C::BK - 1) / C::BK * a.B;
+    q_units = (long)(a.T + C::BQ - 1) / C::BQ * a.B;
+  }
+  if (a.cu_seqlens)
+    hipLaunchKernelGGL((bwd_prep_varlen_kernel<D, typename C::QK, C::STYLE>),
+                       dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<D, typename C::QK, C::STYLE>), dim3((unsigned)((items + 255) / 256)),
+                       dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int nK = (a.T + C::BK - 1) / C::BK, nQ = (a.T + C::BQ - 1) / C::BQ;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3(nK * a.B * a.KV), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)(k_units * a.KV)), dim3(512), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3(nQ * a.B * a.H), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3((unsigned)(q_units * a.H)), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

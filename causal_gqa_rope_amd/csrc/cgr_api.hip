@@ -166,6 +166,83 @@ BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
   return l;
 }
 
+// Packed batches: the same parts over total_tokens rows, the per-tile values
+// in 32-row slots (ceil(total / 32) + num_seqs per head: each sequence starts
+// a slot of its own).
+long bwd_varlen_slots(int num_seqs, int total_tokens) {
+  return ((long)total_tokens + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows + num_seqs;
+}
+BwdLayout bwd_varlen_layout(int num_seqs, int total_tokens, int n_head, int n_kv_head, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  BwdLayout l;
+  l.qr = 0;
+  l.kr = up((size_t)total_tokens * n_head * head_dim * 2);
+  l.ld = l.kr + up((size_t)total_tokens * n_kv_head * head_dim * 2);
+  l.total = l.ld + (size_t)n_head * bwd_varlen_slots(num_seqs, total_tokens) * 64 * 4;
+  return l;
+}
+
+// The checks that the dense and the packed backward share beyond the
+// forward's own.
+cgr_status bwd_check(const float* lse, const void* dout, void* dq, void* dk, void* dv, int head_dim,
+                     cgr_dtype dtype, int window, cgr_mask mask, const void* workspace, size_t workspace_bytes,
+                     const BwdLayout& lay) {
+  if (head_dim == 256) return fail(CGR_ERR_UNSUPPORTED, "the backward is built for head_dim 32, 64, 128");
+  cgr_status st = check_window(window, mask);
+  if (st != CGR_OK) return st;
+  if (!lse || !dout || !dq || !dk || !dv)
+    return fail(CGR_ERR_INVALID_ARG, "lse, dout, dq, dk and dv must be non-null");
+  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
+    return fail(CGR_ERR_ALIGNMENT, "dout, dq, dk and dv must be 16-byte aligned");
+  if (dtype != CGR_BF16)
+    return fail(CGR_ERR_UNSUPPORTED, "the backward takes bf16 tensors only (dtype %d)", (int)dtype);
+  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
+  if (!aligned(workspace, 256)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < lay.total)
+    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, lay.total);
+  // The kernels address the per-tile values with one 32-bit buffer range.
+  if (lay.total - lay.ld > (size_t)UINT32_MAX)
+    return fail(CGR_ERR_UNSUPPORTED, "n_head x the query rows is too large for one call");
+  return CGR_OK;
+}
+
+// Fill in the tensors, workspace parts and scales, then launch the three
+// kernels of the instance (sizes and the packed fields set by the caller).
+cgr_status bwd_launch(cgr::BwdArgs& a, const void* q, const void* k, const void* v, const void* o,
+                      const float* lse, const void* dout, void* dq, void* dk, void* dv, int head_dim,
+                      const float* rope_cos, const float* rope_sin, cgr_rope_style style, cgr_mask mask,
+                      int window, float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                      const BwdLayout& lay, void* stream) {
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.qr = (char*)workspace + lay.qr;
+  a.kr = (char*)workspace + lay.kr;
+  a.ld = (float*)((char*)workspace + lay.ld);
+  a.window = window;
+  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
+  a.scale = (float)scale;
+  a.qscale = (float)(scale * 1.4426950408889634074);
+  const int qkb = qk_operand == CGR_QK_BF16, sty = (int)style, cau = mask == CGR_MASK_CAUSAL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (head_dim) {
+    case 32: e = cgr::launch_attn_bwd_d32(a, qkb, sty, cau, s); break;
+    case 64: e = cgr::launch_attn_bwd_d64(a, qkb, sty, cau, s); break;
+    default: e = cgr::launch_attn_bwd_d128(a, qkb, sty, cau, s); break;
+  }
+  if (e != hipSuccess) return hip_fail("backward launch", e);
+  return CGR_OK;
+}
+
 // Decode split policy, a function of the sizes alone (so the workspace size
 // needs no device): about 2048 single-wave workgroups (eight per CU are
 // resident at once, so every chunk starts in the first wave of them), chunks
@@ -544,61 +621,60 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
   cgr_status st = check_common(q, k, v, o, lse, n_head, n_kv_head, head_dim, dtype, rope_cos,
                                rope_sin, rope_max_pos, T, style, mask, softmax_scale, qk_operand);
   if (st != CGR_OK) return st;
-  if (head_dim == 256) return fail(CGR_ERR_UNSUPPORTED, "the backward is built for head_dim 32, 64, 128");
-  if ((st = check_window(window, mask)) != CGR_OK) return st;
-  if (!lse || !dout || !dq || !dk || !dv)
-    return fail(CGR_ERR_INVALID_ARG, "lse, dout, dq, dk and dv must be non-null");
-  if (!aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16))
-    return fail(CGR_ERR_ALIGNMENT, "dout, dq, dk and dv must be 16-byte aligned");
-  if (dtype != CGR_BF16)
-    return fail(CGR_ERR_UNSUPPORTED, "the backward takes bf16 tensors only (dtype %d)", (int)dtype);
   if ((long)B * T > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "B*T must fit in int32");
   const BwdLayout lay = bwd_layout(B, T, n_head, n_kv_head, head_dim);
-  if (!workspace) return fail(CGR_ERR_WORKSPACE, "workspace must be non-null");
-  if (!aligned(workspace, 256)) return fail(CGR_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
-  if (workspace_bytes < lay.total)
-    return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes,
-                lay.total);
-  const int nt = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
-  // The kernels address the per-tile values with one 32-bit buffer range.
-  if (lay.total - lay.ld > (size_t)UINT32_MAX)
-    return fail(CGR_ERR_UNSUPPORTED, "B * n_head * T is too large for one call");
+  if ((st = bwd_check(lse, dout, dq, dk, dv, head_dim, dtype, window, mask, workspace, workspace_bytes, lay)) !=
+      CGR_OK)
+    return st;
   const long grid_q = (long)((T + 255) / 256) * B * n_head;
   if (grid_q > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
   cgr::BwdArgs a{};
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.rope_cos = rope_cos;
-  a.rope_sin = rope_sin;
-  a.qr = (char*)workspace + lay.qr;
-  a.kr = (char*)workspace + lay.kr;
-  a.ld = (float*)((char*)workspace + lay.ld);
   a.B = B;
   a.T = T;
   a.H = n_head;
   a.KV = n_kv_head;
-  a.NT = nt;
-  a.window = window;
-  const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
-  a.scale = (float)scale;
-  a.qscale = (float)(scale * 1.4426950408889634074);
-  const int qkb = qk_operand == CGR_QK_BF16, sty = (int)style, cau = mask == CGR_MASK_CAUSAL;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  switch (head_dim) {
-    case 32: e = cgr::launch_attn_bwd_d32(a, qkb, sty, cau, s); break;
-    case 64: e = cgr::launch_attn_bwd_d64(a, qkb, sty, cau, s); break;
-    default: e = cgr::launch_attn_bwd_d128(a, qkb, sty, cau, s); break;
-  }
-  if (e != hipSuccess) return hip_fail("backward launch", e);
-  return CGR_OK;
+  a.NT = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
+  return bwd_launch(a, q, k, v, o, lse, dout, dq, dk, dv, head_dim, rope_cos, rope_sin, style, mask, window,
+                    softmax_scale, qk_operand, workspace, lay, stream);
+}
+
+size_t cgr_attn_bwd_varlen_workspace_size(int num_seqs, int total_tokens, int n_head, int n_kv_head,
+                                          int head_dim) {
+  if (num_seqs < 1 || total_tokens < 0 || n_head < 1 || n_kv_head < 1 || head_dim < 2) return 0;
+  return bwd_varlen_layout(num_seqs, total_tokens, n_head, n_kv_head, head_dim).total;
+}
+
+cgr_status cgr_gqa_rope_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                        const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                                        int max_seqlen, int n_head, int n_kv_head, int head_dim,
+                                        cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                        int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                                        float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+  cgr_status st = cgr::varlen_check(q, k, v, o, lse, cu_seqlens, num_seqs, total_tokens, max_seqlen, n_head,
+                               n_kv_head, head_dim, dtype, rope_cos, rope_sin, rope_max_pos, style, mask, window,
+                               softmax_scale, qk_operand);
+  if (st != CGR_OK) return st;
+  const BwdLayout lay = bwd_varlen_layout(num_seqs, total_tokens, n_head, n_kv_head, head_dim);
+  if ((st = bwd_check(lse, dout, dq, dk, dv, head_dim, dtype, window, mask, workspace, workspace_bytes, lay)) !=
+      CGR_OK)
+    return st;
+  const long slots = bwd_varlen_slots(num_seqs, total_tokens);
+  if (slots * n_head > INT_MAX) return fail(CGR_ERR_INVALID_ARG, "too many work units");
+  if (total_tokens == 0) return CGR_OK;  // nothing to write
+  cgr::BwdArgs a{};
+  a.B = 1;
+  a.T = max_seqlen;
+  a.H = n_head;
+  a.KV = n_kv_head;
+  a.NT = 0;
+  a.cu_seqlens = cu_seqlens;
+  a.nseq = num_seqs;
+  a.total = total_tokens;
+  a.NSL = (int)slots;
+  return bwd_launch(a, q, k, v, o, lse, dout, dq, dk, dv, head_dim, rope_cos, rope_sin, style, mask, window,
+                    softmax_scale, qk_operand, workspace, lay, stream);
 }
 
 size_t cgr_attn_decode_workspace_size(int B, int Tq, int max_seqlen, int n_head, int n_kv_head,

@@ -324,6 +324,48 @@ CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const voi
                                  size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace cgr_gqa_rope_attn_bwd_varlen needs (0 for invalid
+ * sizes): the rotated q and k of the total_tokens rows in the Q.K^T operand
+ * type plus two floats per head for every row of ceil(total_tokens / 32) +
+ * num_seqs slots of 32 rows (each sequence starts a slot of its own).
+ */
+CGR_API size_t cgr_attn_bwd_varlen_workspace_size(int num_seqs, int total_tokens, int n_head, int n_kv_head,
+                                                  int head_dim);
+
+/*
+ * Packed variable-length batch backward: for every sequence of the batch,
+ * the gradients that cgr_gqa_rope_attn_bwd gives for it alone (same chain
+ * rule through RoPE and attention, "Train It & Run for Real", section
+ * "Coming from CUDA: where's .backward()?"; positions restart at 0 in every
+ * sequence and no row sees another sequence's keys).
+ *   q, k, v, cu_seqlens, num_seqs, total_tokens, max_seqlen, rope tables,
+ *     sizes, style, mask, window, softmax_scale, qk_operand: as given to
+ *     cgr_gqa_rope_attn_fwd_varlen.
+ *   o: device [total_tokens, n_head, head_dim], lse: device float32 [n_head,
+ *     total_tokens] -- that forward's outputs.
+ *   dout: device [total_tokens, n_head, head_dim], dL/dO.
+ *   dq: device [total_tokens, n_head, head_dim]; dk, dv: device
+ *     [total_tokens, n_kv_head, head_dim]; every row is written once, none
+ *     may overlap an input.
+ *   dtype: CGR_BF16 only; the arithmetic is that of cgr_gqa_rope_attn_bwd
+ *     (the same bits as that call on each sequence alone).
+ *   workspace: device memory of at least cgr_attn_bwd_varlen_workspace_size(
+ *     ...) bytes, 256-byte aligned, scratch for this call only.
+ * cu_seqlens must be an array that the forward accepted (its checks run on the
+ * device there); the kernels read it but do not check it again. With any
+ * contents no access leaves the tensors, but rows outside every well-formed
+ * sequence are then left unwritten.
+ */
+CGR_API cgr_status cgr_gqa_rope_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                                const int32_t* cu_seqlens, int num_seqs, int total_tokens,
+                                                int max_seqlen, int n_head, int n_kv_head, int head_dim,
+                                                cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
+                                                int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
+                                                float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+
+/*
  * RoPE on rows at given positions ("Embeddings & the Residual Stream",
  * "Positional information: RoPE"): out[t, h, :] = R(positions[t]) x[t, h, :]
  * for x, out device [n_tokens, n_heads, head_dim] (dtype; out may equal x).

@@ -341,6 +341,57 @@ def test_backward_rejects_bad_arguments(kw, status, needle):
     assert needle in msg
 
 
+def test_backward_varlen_workspace_size():
+    lib = cgr.library()
+    assert lib.cgr_attn_bwd_varlen_workspace_size(0, 16, 4, 2, 64) == 0
+    assert lib.cgr_attn_bwd_varlen_workspace_size(1, -1, 4, 2, 64) == 0
+    assert lib.cgr_attn_bwd_varlen_workspace_size(1, 16, 4, 0, 64) == 0
+    # rotated q and k over the packed rows on 256-byte boundaries, then 2
+    # floats per (head, row) over ceil(total / 32) + num_seqs slots of 32 rows
+    up = lambda x: (x + 255) // 256 * 256
+    n = lib.cgr_attn_bwd_varlen_workspace_size(3, 100, 8, 2, 128)
+    assert n == up(100 * 8 * 128 * 2) + up(100 * 2 * 128 * 2) + 8 * (4 + 3) * 64 * 4
+    n = lib.cgr_attn_bwd_varlen_workspace_size(2, 33, 4, 1, 64)
+    assert n == up(33 * 4 * 64 * 2) + up(33 * 1 * 64 * 2) + 4 * (2 + 2) * 64 * 4
+
+
+def backward_varlen(**kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, dout=P, dq=P, dk=P, dv=P, cu=P, nseq=2, total=100, maxlen=60, H=4, KV=2,
+             D=64, dtype=1, cos=P, sin=P, P=60, style=0, mask=1, window=0, scale=0.0, qk=0,
+             ws=ctypes.c_void_p(0x10000), wsb=1 << 20)
+    a.update(kw)
+    lib = cgr.library()
+    st = lib.cgr_gqa_rope_attn_bwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dout"], a["dq"], a["dk"],
+                                          a["dv"], a["cu"], a["nseq"], a["total"], a["maxlen"], a["H"], a["KV"],
+                                          a["D"], a["dtype"], a["cos"], a["sin"], a["P"], a["style"], a["mask"],
+                                          a["window"], a["scale"], a["qk"], a["ws"], a["wsb"], None)
+    return st, lib.cgr_last_error().decode()
+
+
+@no_gpu
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(cu=None), 1, "cu_seqlens"),
+    (dict(nseq=0), 1, "num_seqs"),
+    (dict(total=-1), 1, ">= 0"),
+    (dict(maxlen=101), 1, "exceeds"),
+    (dict(P=59), 1, "positions"),
+    (dict(lse=None), 1, "non-null"),
+    (dict(dv=None), 1, "non-null"),
+    (dict(dtype=0), 2, "bf16"),
+    (dict(dk=PMIS), 3, "aligned"),
+    (dict(ws=None), 4, "workspace"),
+    (dict(wsb=100), 4, "needs"),
+    (dict(ws=ctypes.c_void_p(0x10010)), 3, "256-byte"),
+    (dict(H=6, KV=4), 1, "divisible"),
+    (dict(D=256), 2, "backward is built for"),
+    (dict(window=4, mask=0), 1, "CGR_MASK_CAUSAL"),
+])
+def test_backward_varlen_rejects_bad_arguments(kw, status, needle):
+    st, msg = backward_varlen(**kw)
+    assert st == status, msg
+    assert needle in msg
+
+
 def test_decode_workspace_size():
     lib = cgr.library()
     assert lib.cgr_attn_decode_workspace_size(0, 1, 10, 4, 2, 64) == 0

@@ -158,3 +158,105 @@ def test_backward_binding_checks(gpu):
     with pytest.raises(cgr.CgrError):  # workspace too small
         cgr.gqa_rope_attn_bwd(x["q"], x["k"], x["v"], o, lse, o, cos, sin,
                               workspace=torch.empty(256, dtype=torch.uint8, device=gpu))
+
+
+# Packed batches: (lengths, H, KV, d, causal, style, window). Empty and
+# one-token sequences, sequences that end on and just past the 32-row,
+# 128-key and 256-row block edges, MHA/GQA/MQA, every head_dim, both masks and
+# pairings, a sliding window.
+VARLEN_BWD = [
+    ([5, 1, 0, 130, 64, 257, 1], 4, 1, 128, True, "interleaved", 0),
+    ([0, 300, 17], 6, 2, 64, False, "half", 0),
+    ([129, 128, 127, 2], 4, 4, 32, True, "interleaved", 0),
+    ([1], 2, 1, 64, True, "half", 0),
+    ([700, 0, 0, 33], 8, 2, 128, True, "interleaved", 0),
+    ([256, 255, 512, 31, 32, 33], 8, 8, 64, True, "half", 0),
+    ([400, 90, 3], 4, 2, 128, True, "interleaved", 100),
+]
+
+
+def packed_bwd_inputs(lengths, H, KV, d, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    total = sum(lengths)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(lengths), 0).to(torch.int32)
+    q = torch.randn((total, H, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((total, KV, d), generator=g).to(torch.bfloat16)
+    v = torch.randn((total, KV, d), generator=g).to(torch.bfloat16)
+    dout = torch.randn((total, H, d), generator=g).to(torch.bfloat16)
+    return dict(q=q, k=k, v=v, dout=dout, cu_seqlens=cu, max_seqlen=max(lengths))
+
+
+def packed_fwd_bwd(x, dev, causal, style, window, base, poison=False):
+    """HIP packed forward then HIP packed backward; returns the device (dq, dk, dv)
+    (poison: the outputs start as NaN, so rows left unwritten show)."""
+    d = to_dev(x, dev)
+    dout = x["dout"].to(dev)
+    cos, sin = cgr.rope_tables(max(x["max_seqlen"], 1), x["q"].shape[2], base, device=dev)
+    kw = dict(causal=causal, rope_style=style, window=window)
+    o, lse = cgr.gqa_rope_attn_fwd_varlen(d["q"], d["k"], d["v"], d["cu_seqlens"], x["max_seqlen"], cos, sin, **kw)
+    outs = {}
+    if poison:
+        outs = dict(dq=torch.full_like(d["q"], float("nan")), dk=torch.full_like(d["k"], float("nan")),
+                    dv=torch.full_like(d["v"], float("nan")))
+    grads = cgr.gqa_rope_attn_bwd_varlen(d["q"], d["k"], d["v"], o, lse, dout, d["cu_seqlens"], x["max_seqlen"],
+                                         cos, sin, **kw, **outs)
+    return grads, (o, lse, cos, sin)
+
+
+@pytest.mark.parametrize("lengths,H,KV,d,causal,style,window", VARLEN_BWD,
+                         ids=[f"vb{i}" for i in range(len(VARLEN_BWD))])
+def test_backward_varlen_small_full(gpu, lengths, H, KV, d, causal, style, window):
+    announce(f"packed backward lengths={lengths} H={H} KV={KV} d={d} causal={causal} {style} window={window}")
+    x = packed_bwd_inputs(lengths, H, KV, d, seed=len(lengths) * 11 + d + window)
+    grads, _ = packed_fwd_bwd(x, gpu, causal, style, window, 1e4, poison=True)
+    ref = oracle.attention_varlen_bwd(x["q"], x["k"], x["v"], x["dout"], x["cu_seqlens"].numpy(), causal=causal,
+                                      base=1e4, style=style, window=window)
+    assert_grads_close(f"packed {lengths}", [f64(g) for g in grads], ref)
+
+
+def test_backward_varlen_equals_dense_per_sequence(gpu):
+    """A packed backward is, bit for bit, the dense backward of each of its
+    sequences (same forward outputs, same tables)."""
+    lengths = [200, 77, 1, 0, 129, 300]
+    announce(f"packed backward vs dense, lengths {lengths}")
+    x = packed_bwd_inputs(lengths, 8, 2, 128, seed=9)
+    (dq, dk, dv), (o, lse, cos, sin) = packed_fwd_bwd(x, gpu, True, "interleaved", 0, 1e4)
+    d = to_dev(x, gpu)
+    dout = x["dout"].to(gpu)
+    cu = x["cu_seqlens"].tolist()
+    for s, L in enumerate(lengths):
+        if L == 0:
+            continue
+        a = cu[s]
+        sl = lambda t: t[None, a:a + L].contiguous()
+        gq, gk, gv = cgr.gqa_rope_attn_bwd(sl(d["q"]), sl(d["k"]), sl(d["v"]), sl(o),
+                                           lse[None, :, a:a + L].contiguous(), sl(dout), cos, sin)
+        assert torch.equal(dq[a:a + L], gq[0]) and torch.equal(dk[a:a + L], gk[0]) and torch.equal(dv[a:a + L], gv[0])
+
+
+def test_backward_varlen_workload_full_size(gpu):
+    """The packed MQA workload at full size (32 sequences, 32,226 tokens, 16
+    query heads, one K/V head, head_dim 128): every gradient of every sequence
+    against the oracle."""
+    w = W.get("varlen_mqa_32seqs_16to2048_H16_KV1_d128")
+    announce(f"packed backward {w.name}: full size, every element")
+    x = W.make_inputs(w)
+    x["dout"] = W.make_dout(w, x["q"])
+    grads, _ = packed_fwd_bwd(x, gpu, w.causal, w.rope_style, 0, w.base, poison=True)
+    ref = oracle.attention_varlen_bwd(x["q"], x["k"], x["v"], x["dout"], x["cu_seqlens"].numpy(), causal=w.causal,
+                                      base=w.base, style=w.rope_style)
+    assert_grads_close(w.name, [f64(g) for g in grads], ref)
+
+
+def test_backward_varlen_binding_checks(gpu):
+    x = to_dev(packed_bwd_inputs([3, 5], 4, 2, 64, seed=1), gpu)
+    cos, sin = cgr.rope_tables(8, 64, 1e4, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd_varlen(x["q"], x["k"], x["v"], x["cu_seqlens"], 5, cos, sin)
+    args = (x["q"], x["k"], x["v"], o, lse, x["dout"].to(gpu), x["cu_seqlens"], 5, cos, sin)
+    with pytest.raises(cgr.CgrError):  # lse of the dense layout
+        cgr.gqa_rope_attn_bwd_varlen(*args[:4], lse[None], *args[5:])
+    with pytest.raises(cgr.CgrError):  # max_seqlen past the tables
+        cgr.gqa_rope_attn_bwd_varlen(*args[:7], 9, cos, sin)
+    with pytest.raises(cgr.CgrError):  # workspace too small
+        cgr.gqa_rope_attn_bwd_varlen(*args, workspace=torch.empty(256, dtype=torch.uint8, device=gpu))
