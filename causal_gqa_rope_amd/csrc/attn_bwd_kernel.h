@@ -14,19 +14,22 @@
 //   dq = R^T dq~,  dk = R^T dk~   (the transposed rotation, at the row's position)
 // dk and dv sum over the G query heads that share the K/V head.
 //
-// Three kernels:
+// Three kernels (and a fourth with many query heads per K/V head):
 //   * bwd_prep_kernel: q~ * scale*log2(e) and k~ in the Q.K^T operand type (so
 //     the rotation is done once, not once per tile that reads them), and per
 //     32-row tile of every (sequence, head) the two accumulator starting
 //     values -lse*log2(e) and -D.
-//   * attn_bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128 keys).
-//     Each wave keeps 32 keys' k~ and v in registers as matrix-core operands
-//     and accumulates dk~^T and dv^T for them over every query row and every
-//     query head of the group; S = q~ k~^T puts one key per lane column, so P
-//     and dS feed dv^T += dO^T P and dk~^T += q~^T dS straight from registers.
-//   * attn_bwd_dq_kernel: one workgroup per (sequence, query head, 256 rows),
-//     the forward's layout: S^T = k~ q~^T puts one query per lane column and
-//     dq~^T += k~^T dS^T takes dS^T from registers.
+//   * attn_bwd_dkdv_kernel: one workgroup per (sequence, K/V head, 128 keys,
+//     group of up to 4 query heads). Each wave keeps 32 keys' k~ in registers
+//     as a matrix-core operand and accumulates dk~^T and dv^T for them over
+//     every query row of its query heads; S = q~ k~^T puts one key per lane
+//     column, so P and dS feed dv^T += dO^T P and dk~^T += q~^T dS straight
+//     from registers. With more than 4 query heads per K/V head the head
+//     groups write f32 partial sums and bwd_dkv_reduce_kernel adds them.
+//   * attn_bwd_dq_kernel: one workgroup per (sequence, 2^lhp query heads of
+//     one K/V head, 256 / 2^lhp rows), the forward's layout: S^T = k~ q~^T
+//     puts one query per lane column and dq~^T += k~^T dS^T takes dS^T from
+//     registers.
 // Recomputing S and dP in both kernels costs two extra matrix products per
 // tile against sharing dS through memory, and buys a backward without atomics
 // or a dS round trip: every output element is written once, by one lane, in a
@@ -61,12 +64,28 @@ struct BwdArgs {
   // of 32-row slots per head in ld.
   const int32_t* cu_seqlens;
   int nseq, total, NSL;
+  // dk/dv units take at most kBwdHeadsPerUnit query heads of their K/V head;
+  // with more (hsplit > 1) each writes f32 partial sums, dv then dk~ (before
+  // the transposed rotation), to part[split][row][K/V head][D], rows = B*T or
+  // total, dv's splits first, and bwd_dkv_reduce_kernel adds them in split
+  // order.
+  int hsplit;
+  long part_rows;
+  float* part;
+  // dq units: 2^lhp query heads of one K/V head (lhp <= 3, 2^lhp divides G)
+  // x 256 / 2^lhp rows; wave w takes head w >> (3 - lhp) of the unit's heads
+  // and rows 32 (w mod 2^(3 - lhp)) on.
+  int lhp;
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
   float qscale;  // scale * log2(e)
   float scale;
 };
 
 constexpr int kBwdTileRows = 32;  // rows per ld tile
+// Query heads per dk/dv unit: with G > 4 (MQA, few K/V heads) a K/V head's
+// keys are split over ceil(G / 4) units so that the grid fills the chip and
+// no single unit carries all G heads' rows.
+constexpr int kBwdHeadsPerUnit = 4;
 
 // Packed batches: sequence s's blocks of 2^lb tokens take slots (c_s >> lb) + s
 // on (c_s = cu_seqlens[s]). The next sequence's first slot lies past s's last
@@ -286,7 +305,7 @@ struct BwdCfg {
   static constexpr int GSTAGE = 2 * TILE + 256;          // q~, dO, ld of one group
   static constexpr int KV_STAGE = 2 * GSTAGE;            // both groups
   static constexpr int BK = 128;                         // keys per dk/dv workgroup
-  static constexpr int BQ = 256;                         // rows per dq workgroup
+  static constexpr int BQ = 256;                         // rows x heads per dq workgroup
   static constexpr int BN = 64;                          // keys per dq tile
   static constexpr int KT = BN * 2 * D;                  // one dq key tile
 };
@@ -302,7 +321,9 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int grp = wave >> 2, wig = wave & 3;
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.H / a.KV;
-  const int u = blockIdx.x;
+  // Split sp of a unit takes query heads g0 .. g0 + nh - 1 of the K/V head.
+  const int sp = (int)(blockIdx.x % (unsigned)a.hsplit), u = (int)(blockIdx.x / (unsigned)a.hsplit);
+  const int g0 = sp * kBwdHeadsPerUnit, nh = min(kBwdHeadsPerUnit, G - g0);
   int kb, kvh, L, tok0;
   long ldt0, ldh;  // ld tile of the sequence's row 0 at head 0; tiles per head
   if (a.cu_seqlens) {
@@ -364,7 +385,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   const int q_first = C::CAUSAL ? k0 : 0;
   const int q_end = W > 0 ? min(L, k0 + C::BK - 1 + W) : L;
   const int n_steps = (q_end - q_first + 31) / 32;
-  const int n_items = G * n_steps;
+  const int n_items = nh * n_steps;
   const int n_iter = (n_items + 1) / 2;
   const long ld_tiles = a.cu_seqlens ? (long)a.H * a.NSL : (long)a.B * a.H * a.NT;
   const rsrc_t rld = make_rsrc(a.ld, (uint32_t)(ld_tiles * 256));
@@ -374,8 +395,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   // then stream the same query rows at about the same time, and both groups
   // of a workgroup work on the same rows, so most reloads hit L2.
   auto item = [&](int n, int& g, int& qrow0) {
-    const int sidx = n / G;
-    g = n - sidx * G;
+    const int sidx = n / nh;
+    g = g0 + n - sidx * nh;
     qrow0 = q_first + 32 * (n_steps - 1 - sidx);
   };
   // Loads of iteration i (this group's item 2i + grp) into a stage.
@@ -513,6 +534,15 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   if (grp != 0) return;
 
   const int key = kw0 + l32;
+  if (a.hsplit > 1) {
+    // This split's f32 partial sums; the reduction pass finishes them.
+    const long split_elems = a.part_rows * ks;
+    const uint32_t range = (uint32_t)(((L - 1) * ks + D) * 4);
+    const long off = (long)tok0 * ks + kvh * D;
+    store_acc_f32<D>(dv, make_rsrc(a.part + sp * split_elems + off, range), key * ks * 4, hh);
+    store_acc_f32<D>(dk, make_rsrc(a.part + (a.hsplit + sp) * split_elems + off, range), key * ks * 4, hh);
+    return;
+  }
   const rsrc_t rdv = make_rsrc((uint16_t*)a.dv + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
   const rsrc_t rdk = make_rsrc((uint16_t*)a.dk + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
   store_acc_bf16<D>(dv, 1.f, rdv, key * ks * 2, hh);
@@ -521,10 +551,80 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
   store_acc_bf16<D>(dk, 0.69314718055994531f, rdk, key * ks * 2, hh);
 }
 
+// The end of a split dk/dv (hsplit > 1): per (row, K/V head) the splits'
+// partial sums of dv and dk~ added in split order, dk = R^T dk~ * ln 2 at the
+// row's position (the q~ operand carried scale*log2(e)), both rounded to
+// bf16. Thread = (row, K/V head, group g): elements 8g..8g+7 and the same
+// eight D/2 further on, which hold whole rotation pairs in both pairings.
+template <int D, int STYLE>
+__global__ __launch_bounds__(256) void bwd_dkv_reduce_kernel(BwdArgs a) {
+  constexpr int IPR = D / 16;
+  const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+  if (tid >= a.part_rows * a.KV * IPR) return;
+  const int g = (int)(tid % IPR);
+  const long row = tid / IPR;  // token * KV + kvh
+  const int p = (int)(row / a.KV);
+  int t;
+  if (a.cu_seqlens) {
+    // Rows of a sequence whose units exited (not inside the batch) stay unwritten.
+    int lo = 0, hi = a.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (a.cu_seqlens[mid] <= p) lo = mid;
+      else hi = mid - 1;
+    }
+    const int c0 = a.cu_seqlens[lo], L = a.cu_seqlens[lo + 1] - c0;
+    t = p - c0;
+    if (!seq_ok(a, c0, L) || t < 0 || t >= L) return;
+  } else {
+    t = p % a.T;
+  }
+  const long split_elems = a.part_rows * a.KV * D;
+  const float* pv = a.part + row * D + 8 * g;
+  const float* pk = pv + a.hsplit * split_elems;
+  float v0[8], v1[8], k0[8], k1[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v0[j] = v1[j] = k0[j] = k1[j] = 0.f;
+  for (int sp = 0; sp < a.hsplit; ++sp) {
+    const long o = sp * split_elems;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a0 = *(const f32x4*)(pv + o + 4 * h), a1 = *(const f32x4*)(pv + o + D / 2 + 4 * h);
+      const f32x4 b0 = *(const f32x4*)(pk + o + 4 * h), b1 = *(const f32x4*)(pk + o + D / 2 + 4 * h);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        v0[4 * h + m] += a0[m];
+        v1[4 * h + m] += a1[m];
+        k0[4 * h + m] += b0[m];
+        k1[4 * h + m] += b1[m];
+      }
+    }
+  }
+  // R^T is the rotation by the negated angle.
+  f32x4 c[2], sn[2];
+  load_tab<D, STYLE>(a.rope_cos + (long)t * (D / 2), a.rope_sin + (long)t * (D / 2), g, true, c, sn);
+  sn[0] = -sn[0];
+  sn[1] = -sn[1];
+  rope_pair<STYLE>(k0, k1, c, sn);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    k0[j] *= 0.69314718055994531f;
+    k1[j] *= 0.69314718055994531f;
+  }
+  uint16_t* dvo = (uint16_t*)a.dv + row * D + 8 * g;
+  uint16_t* dko = (uint16_t*)a.dk + row * D + 8 * g;
+  *(u32x4*)dvo = to_frag<OpBF16>(v0).v;
+  *(u32x4*)(dvo + D / 2) = to_frag<OpBF16>(v1).v;
+  *(u32x4*)dko = to_frag<OpBF16>(k0).v;
+  *(u32x4*)(dko + D / 2) = to_frag<OpBF16>(k1).v;
+}
+
 // ---------------------------------------------------------------------------
-// dq. Workgroup = 8 waves x 32 query rows of one query head; key tiles of 64
-// stream through LDS (k~ and v, double-buffered, direct loads). Per tile and
-// wave:
+// dq. Workgroup = 8 waves x 32 query rows: 2^lhp query heads of one K/V head
+// (the largest power of two up to 8 that divides G) x 256 / 2^lhp rows, so
+// that with several heads the waves' rows end close together at the causal
+// diagonal; key tiles of 64 stream through LDS (k~ and v, double-buffered,
+// direct loads) for all of them. Per tile and wave:
 //   S^T  = k~ q~^T - lse      (rows = keys, lane column = query)
 //   dP^T = v dO^T - D
 //   P^T = 2^S^T;  dS^T = P^T dP^T
@@ -539,48 +639,51 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
   const int G = a.H / a.KV;
+  // A unit: 2^lhp heads (head group hg of the K/V head) x BQ = 256 / 2^lhp rows.
+  const int lhp = a.lhp, NHG = G >> lhp;
+  const int lbq = 8 - lhp, BQ = 1 << lbq;
   const int u = blockIdx.x;
-  int qb, kvh, hq, L, tok0;
+  int qb, kvh, hg, L, tok0;
   long ldt0, ldh;  // ld tile of the sequence's row 0 at head 0; tiles per head
   if (a.cu_seqlens) {
-    // Packed: unit = (256-row slot, query head), the heads innermost and the
-    // slots from the last back (causal: each sequence's last, heaviest block
-    // first). With a multiple of 8 K/V heads, head i of a slot takes K/V head
-    // ((i / 8) / G) * 8 + i % 8, so each XCD keeps the same K/V heads.
-    static_assert(C::BQ == 1 << 8, "slots of 256 rows");
-    const int per = a.H;
+    // Packed: unit = (BQ-row slot, head group), the head groups innermost and
+    // the slots from the last back (causal: each sequence's last, heaviest
+    // block first). With a multiple of 8 K/V heads, group i of a slot takes
+    // K/V head ((i / 8) / NHG) * 8 + i % 8, so each XCD keeps the same K/V
+    // heads.
+    const int per = a.H >> lhp;
     const int slot = (int)gridDim.x / per - 1 - u / per;  // the grid has every slot
     const int i = u - (u / per) * per;
     if ((a.KV & 7) == 0) {
-      kvh = ((i >> 3) / G) * 8 + (i & 7);
-      hq = (i >> 3) % G;
+      kvh = ((i >> 3) / NHG) * 8 + (i & 7);
+      hg = (i >> 3) % NHG;
     } else {
-      kvh = i / G;
-      hq = i % G;
+      kvh = i / NHG;
+      hg = i % NHG;
     }
-    const int s = slot_owner(a.cu_seqlens, a.nseq, 8, slot);
+    const int s = slot_owner(a.cu_seqlens, a.nseq, lbq, slot);
     tok0 = a.cu_seqlens[s];
     L = a.cu_seqlens[s + 1] - tok0;
-    qb = slot - ((tok0 >> 8) + s);
-    if (!seq_ok(a, tok0, L) || qb < 0 || qb * C::BQ >= L) return;
+    qb = slot - ((tok0 >> lbq) + s);
+    if (!seq_ok(a, tok0, L) || qb < 0 || qb * BQ >= L) return;
     ldt0 = (tok0 >> 5) + s;
     ldh = a.NSL;
   } else {
-    const int nQ = (a.T + C::BQ - 1) / C::BQ;
+    const int nQ = (a.T + BQ - 1) >> lbq;
     const int groups = a.B * a.KV;
     int rank, gsel;
     if ((groups & 7) == 0) {
-      const int x = u & 7, i = u >> 3, per = (groups >> 3) * G;
+      const int x = u & 7, i = u >> 3, per = (groups >> 3) * NHG;
       rank = i / per;
       const int rem = i - rank * per;
-      gsel = (rem / G) * 8 + x;
-      hq = rem % G;
+      gsel = (rem / NHG) * 8 + x;
+      hg = rem % NHG;
     } else {
-      const int per = groups * G;
+      const int per = groups * NHG;
       rank = u / per;
       const int rem = u - rank * per;
-      gsel = rem / G;
-      hq = rem % G;
+      gsel = rem / NHG;
+      hg = rem % NHG;
     }
     qb = C::CAUSAL ? nQ - 1 - rank : rank;
     const int b = gsel / a.KV;
@@ -590,12 +693,12 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     ldt0 = (long)b * a.H * a.NT;
     ldh = a.NT;
   }
-  const int head = kvh * G + hq;
+  const int head = kvh * G + (hg << lhp) + (wave >> (3 - lhp));
   const int qs = a.H * D, ks = a.KV * D;
-  const int q0 = qb * C::BQ, qw0 = q0 + 32 * wave, my_q = qw0 + l32;
+  const int q0 = qb * BQ, qw0 = q0 + 32 * (wave & ((8 >> lhp) - 1)), my_q = qw0 + l32;
   const bool wave_has_rows = qw0 < L;
   const int wave_last = min(qw0 + 31, L - 1);
-  const int q_hi = min(q0 + C::BQ, L);
+  const int q_hi = min(q0 + BQ, L);
   const int n_tiles = C::CAUSAL ? (q_hi + BN - 1) / BN : (L + BN - 1) / BN;
   // Sliding window: from the tile holding the first row's earliest visible key.
   const int W = C::WIN ? a.window : 0;
@@ -708,11 +811,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (a.cu_seqlens) {
     items = ((long)a.NSL * kBwdTileRows * a.H + (long)a.total * a.KV) * (D / 16);
     k_units = ((long)a.total + C::BK - 1) / C::BK + a.nseq;
-    q_units = ((long)a.total + C::BQ - 1) / C::BQ + a.nseq;
+    q_units = ((long)a.total + (C::BQ >> a.lhp) - 1) / (C::BQ >> a.lhp) + a.nseq;
   } else {
     items = ((long)a.B * a.NT * kBwdTileRows * a.H + (long)a.B * a.T * a.KV) * (D / 16);
     k_units = (long)(a.T + C::BK - 1) / C::BK * a.B;
-    q_units = (long)(a.T + C::BQ - 1) / C::BQ * a.B;
+    q_units = (long)(a.T + (C::BQ >> a.lhp) - 1) / (C::BQ >> a.lhp) * a.B;
   }
   if (a.cu_seqlens)
     hipLaunchKernelGGL((bwd_prep_varlen_kernel<D, typename C::QK, C::STYLE>),
@@ -722,10 +825,18 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
                        dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)(k_units * a.KV)), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)(k_units * a.KV * a.hsplit)), dim3(512), 0, stream,
+                     a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3((unsigned)(q_units * a.H)), dim3(512), 0, stream, a);
+  if (a.hsplit > 1) {
+    const long threads = a.part_rows * a.KV * (D / 16);
+    hipLaunchKernelGGL((bwd_dkv_reduce_kernel<D, C::STYLE>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3((unsigned)(q_units * (a.H >> a.lhp))), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -151,19 +151,32 @@ long varlen_max_items(int num_seqs, int total_tokens) {
 }
 
 // Backward workspace: the rotated q (operand type) and k, then the per-tile
-// accumulator starting values; each part starts on a 256-byte boundary.
+// accumulator starting values, then (more than kBwdHeadsPerUnit query heads
+// per K/V head) the dk/dv units' f32 partial sums; each part starts on a
+// 256-byte boundary.
 struct BwdLayout {
-  size_t qr, kr, ld, total;
+  size_t qr, kr, ld, part, total;
+  int hsplit;
 };
-BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
+int bwd_hsplit(int n_head, int n_kv_head) {
+  const int G = n_head / n_kv_head;
+  return (G + cgr::kBwdHeadsPerUnit - 1) / cgr::kBwdHeadsPerUnit;
+}
+BwdLayout bwd_layout_rows(size_t rows, size_t ld_tiles, int n_head, int n_kv_head, int head_dim) {
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const int nt = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
   BwdLayout l;
   l.qr = 0;
-  l.kr = up((size_t)B * T * n_head * head_dim * 2);
-  l.ld = l.kr + up((size_t)B * T * n_kv_head * head_dim * 2);
-  l.total = l.ld + (size_t)B * n_head * nt * 64 * 4;
+  l.kr = up(rows * n_head * head_dim * 2);
+  l.ld = l.kr + up(rows * n_kv_head * head_dim * 2);
+  l.part = l.ld + up(ld_tiles * 64 * 4);
+  l.hsplit = bwd_hsplit(n_head, n_kv_head);
+  l.total = l.hsplit > 1 ? l.part + 2 * (size_t)l.hsplit * rows * n_kv_head * head_dim * 4
+                         : l.ld + ld_tiles * 64 * 4;
   return l;
+}
+BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
+  const size_t nt = ((size_t)T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
+  return bwd_layout_rows((size_t)B * T, (size_t)B * n_head * nt, n_head, n_kv_head, head_dim);
 }
 
 // Packed batches: the same parts over total_tokens rows, the per-tile values
@@ -173,13 +186,8 @@ long bwd_varlen_slots(int num_seqs, int total_tokens) {
   return ((long)total_tokens + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows + num_seqs;
 }
 BwdLayout bwd_varlen_layout(int num_seqs, int total_tokens, int n_head, int n_kv_head, int head_dim) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  BwdLayout l;
-  l.qr = 0;
-  l.kr = up((size_t)total_tokens * n_head * head_dim * 2);
-  l.ld = l.kr + up((size_t)total_tokens * n_kv_head * head_dim * 2);
-  l.total = l.ld + (size_t)n_head * bwd_varlen_slots(num_seqs, total_tokens) * 64 * 4;
-  return l;
+  return bwd_layout_rows((size_t)total_tokens, (size_t)n_head * bwd_varlen_slots(num_seqs, total_tokens), n_head,
+                         n_kv_head, head_dim);
 }
 
 // The checks that the dense and the packed backward share beyond the
@@ -201,7 +209,7 @@ cgr_status bwd_check(const float* lse, const void* dout, void* dq, void* dk, voi
   if (workspace_bytes < lay.total)
     return fail(CGR_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", workspace_bytes, lay.total);
   // The kernels address the per-tile values with one 32-bit buffer range.
-  if (lay.total - lay.ld > (size_t)UINT32_MAX)
+  if (lay.part - lay.ld > (size_t)UINT32_MAX)
     return fail(CGR_ERR_UNSUPPORTED, "n_head x the query rows is too large for one call");
   return CGR_OK;
 }
@@ -212,7 +220,7 @@ cgr_status bwd_launch(cgr::BwdArgs& a, const void* q, const void* k, const void*
                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int head_dim,
                       const float* rope_cos, const float* rope_sin, cgr_rope_style style, cgr_mask mask,
                       int window, float softmax_scale, cgr_qk_operand qk_operand, void* workspace,
-                      const BwdLayout& lay, void* stream) {
+                      const BwdLayout& lay, long rows, void* stream) {
   a.q = q;
   a.k = k;
   a.v = v;
@@ -227,6 +235,15 @@ cgr_status bwd_launch(cgr::BwdArgs& a, const void* q, const void* k, const void*
   a.qr = (char*)workspace + lay.qr;
   a.kr = (char*)workspace + lay.kr;
   a.ld = (float*)((char*)workspace + lay.ld);
+  a.hsplit = lay.hsplit;
+  {
+    // dq units of 2^lhp heads: the largest power of two <= 8 dividing G.
+    const int G = a.H / a.KV;
+    a.lhp = 0;
+    while (a.lhp < 3 && (G >> a.lhp) % 2 == 0) ++a.lhp;
+  }
+  a.part_rows = rows;
+  a.part = (float*)((char*)workspace + lay.part);
   a.window = window;
   const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
   a.scale = (float)scale;
@@ -635,7 +652,7 @@ cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const void* v, co
   a.KV = n_kv_head;
   a.NT = (T + cgr::kBwdTileRows - 1) / cgr::kBwdTileRows;
   return bwd_launch(a, q, k, v, o, lse, dout, dq, dk, dv, head_dim, rope_cos, rope_sin, style, mask, window,
-                    softmax_scale, qk_operand, workspace, lay, stream);
+                    softmax_scale, qk_operand, workspace, lay, (long)B * T, stream);
 }
 
 size_t cgr_attn_bwd_varlen_workspace_size(int num_seqs, int total_tokens, int n_head, int n_kv_head,
@@ -674,7 +691,7 @@ cgr_status cgr_gqa_rope_attn_bwd_varlen(const void* q, const void* k, const void
   a.total = total_tokens;
   a.NSL = (int)slots;
   return bwd_launch(a, q, k, v, o, lse, dout, dq, dk, dv, head_dim, rope_cos, rope_sin, style, mask, window,
-                    softmax_scale, qk_operand, workspace, lay, stream);
+                    softmax_scale, qk_operand, workspace, lay, total_tokens, stream);
 }
 
 size_t cgr_attn_decode_workspace_size(int B, int Tq, int max_seqlen, int n_head, int n_kv_head,

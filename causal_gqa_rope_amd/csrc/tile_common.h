@@ -135,4 +135,18 @@ __device__ __forceinline__ void store_acc_bf16(const f32x16 (&acc)[D / 32], floa
     }
 }
 
+// Store an accumulator as f32 (lane column = row `pos` of a [.., D] f32
+// tensor): 16 bytes (4 consecutive elements) per (db, row group).
+template <int D>
+__device__ __forceinline__ void store_acc_f32(const f32x16 (&acc)[D / 32], rsrc_t r, int row_off, int hh) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * hh;
+      const f32x4 w = {acc[db][4 * g], acc[db][4 * g + 1], acc[db][4 * g + 2], acc[db][4 * g + 3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, w), r, row_off + d * 4, 0, 0);
+    }
+}
+
 }  // namespace cgr

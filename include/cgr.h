@@ -284,7 +284,9 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, co
 /*
  * Bytes of device workspace cgr_gqa_rope_attn_bwd needs for these sizes
  * (0 for invalid sizes): the rotated q and k in the Q.K^T operand type plus
- * two floats per query row and head.
+ * two floats per query row and head; with more than 4 query heads per K/V
+ * head, also f32 partial sums of dk and dv, 2 * ceil(G / 4) * B * T *
+ * n_kv_head * head_dim floats (G = n_head / n_kv_head).
  */
 CGR_API size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_head, int head_dim);
 
@@ -327,7 +329,9 @@ CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const voi
  * Bytes of device workspace cgr_gqa_rope_attn_bwd_varlen needs (0 for invalid
  * sizes): the rotated q and k of the total_tokens rows in the Q.K^T operand
  * type plus two floats per head for every row of ceil(total_tokens / 32) +
- * num_seqs slots of 32 rows (each sequence starts a slot of its own).
+ * num_seqs slots of 32 rows (each sequence starts a slot of its own); with
+ * more than 4 query heads per K/V head, also 2 * ceil(G / 4) * total_tokens *
+ * n_kv_head * head_dim floats of partial sums, as for the dense call.
  */
 CGR_API size_t cgr_attn_bwd_varlen_workspace_size(int num_seqs, int total_tokens, int n_head, int n_kv_head,
                                                   int head_dim);

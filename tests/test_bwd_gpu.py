@@ -81,7 +81,9 @@ def test_backward_workload_full(gpu, name):
 
 # (T, H, KV, d, causal, style, B): single and two tokens, tile and block
 # boundaries (32-row steps, 64-key tiles, 128-key and 256-row blocks), ragged
-# tails, MHA, GQA, MQA, every head_dim, both masks and pairings, B > 1.
+# tails, MHA, GQA, MQA, every head_dim, both masks and pairings, B > 1, and
+# more than 4 query heads per K/V head (the dk/dv units split the heads into
+# groups of 4 and a last smaller one: G = 6, 7, 8, 16).
 EDGE = [
     (1, 4, 2, 64, True, "interleaved", 1),
     (2, 2, 1, 128, True, "interleaved", 1),
@@ -94,6 +96,9 @@ EDGE = [
     (521, 4, 4, 64, True, "half", 1),
     (1000, 8, 2, 128, True, "interleaved", 1),
     (200, 6, 2, 64, True, "interleaved", 3),
+    (300, 12, 2, 32, True, "half", 1),
+    (129, 7, 1, 64, False, "interleaved", 2),
+    (520, 16, 1, 128, True, "interleaved", 1),
 ]
 
 
@@ -163,7 +168,7 @@ def test_backward_binding_checks(gpu):
 # Packed batches: (lengths, H, KV, d, causal, style, window). Empty and
 # one-token sequences, sequences that end on and just past the 32-row,
 # 128-key and 256-row block edges, MHA/GQA/MQA, every head_dim, both masks and
-# pairings, a sliding window.
+# pairings, sliding windows, split head groups (G = 6, 16).
 VARLEN_BWD = [
     ([5, 1, 0, 130, 64, 257, 1], 4, 1, 128, True, "interleaved", 0),
     ([0, 300, 17], 6, 2, 64, False, "half", 0),
@@ -172,6 +177,8 @@ VARLEN_BWD = [
     ([700, 0, 0, 33], 8, 2, 128, True, "interleaved", 0),
     ([256, 255, 512, 31, 32, 33], 8, 8, 64, True, "half", 0),
     ([400, 90, 3], 4, 2, 128, True, "interleaved", 100),
+    ([33, 260, 0, 129], 16, 1, 64, True, "interleaved", 0),
+    ([200, 70], 12, 2, 128, True, "half", 50),
 ]
 
 
