@@ -144,7 +144,7 @@ def library() -> ctypes.CDLL:
     lib.cgr_attn_fwd_fp8_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.cgr_attn_fwd_fp8_workspace_size.restype = ctypes.c_size_t
     lib.cgr_gqa_rope_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, vp, vp,
-                                              i32, i32, i32, f32, vp, ctypes.c_size_t, vp]
+                                              i32, i32, i32, f32, vp, vp, ctypes.c_size_t, vp]
     lib.cgr_gqa_rope_attn_fwd_fp8.restype = i32
     lib.cgr_attn_fwd_varlen_workspace_size.argtypes = [i32, i32]
     lib.cgr_attn_fwd_varlen_workspace_size.restype = ctypes.c_size_t
@@ -356,9 +356,11 @@ def cgr_gqa_rope_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                               v_descale: float, rope_cos: torch.Tensor, rope_sin: torch.Tensor, *,
                               causal: bool = True, rope_style: str = "interleaved",
                               softmax_scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                              lse: Optional[torch.Tensor] = None, return_lse: bool = True, workspace=None):
+                              lse: Optional[torch.Tensor] = None, return_lse: bool = True, workspace=None,
+                              seqlens: Optional[torch.Tensor] = None):
     """fp8 forward: q [B,T,H,128], k/v [B,T,KV,128] as torch.float8_e4m3fn (the real inputs are the
-    codes times the descales) -> (o [B,T,H,128] bfloat16, lse [B,H,T] float32 or None)."""
+    codes times the descales) -> (o [B,T,H,128] bfloat16, lse [B,H,T] float32 or None).
+    seqlens: optional int32 [B] device tensor of valid tokens per entry (right padding)."""
     lib = library()
     for n, t in (("q", q), ("k", k), ("v", v)):
         _dev_tensor(n, t, torch.float8_e4m3fn)
@@ -382,6 +384,10 @@ def cgr_gqa_rope_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _dev_tensor("lse", lse, torch.float32)
         if tuple(lse.shape) != (B, H, T):
             raise CgrError(CGR_ERR_INVALID_ARG, "lse must be [B, H, T]")
+    if seqlens is not None:
+        _dev_tensor("seqlens", seqlens, torch.int32)
+        if seqlens.numel() != B:
+            raise CgrError(CGR_ERR_INVALID_ARG, "seqlens must hold B entries")
     if workspace is None:
         workspace = torch.empty(max(16, int(lib.cgr_attn_fwd_fp8_workspace_size(B, T, k.shape[2], D))),
                                 dtype=torch.uint8, device=q.device)
@@ -391,7 +397,7 @@ def cgr_gqa_rope_attn_fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
             _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, T, H, k.shape[2], D, float(q_descale),
             float(k_descale), float(v_descale), _ptr(rope_cos), _ptr(rope_sin), rope_cos.shape[0],
             _STYLES[rope_style], CGR_MASK_CAUSAL if causal else CGR_MASK_NONE,
-            0.0 if softmax_scale is None else float(softmax_scale), _ptr(workspace),
+            0.0 if softmax_scale is None else float(softmax_scale), _ptr(seqlens), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream(q.device)))
     return out, lse
 

@@ -50,6 +50,7 @@ struct Fp8Args {
   float* lse;        // [B, H, T] or null
   const float* rope_cos;
   const float* rope_sin;
+  const int32_t* seqlens;  // valid tokens per entry (right padding), or null: T
   int B, T, H, KV, NT;
   float qgamma;      // rotated q (in e4m3 units) times this is the Q operand
   int kscale;        // e8m0 block scale 2^E of the K operand, in every byte
@@ -116,11 +117,12 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Args a) {
   const long ks = (long)a.KV * D;  // token stride
   const uint8_t* kb = a.k + ((long)b * a.T) * ks + (long)kv * D;
   const uint8_t* vb = a.v + ((long)b * a.T) * ks + (long)kv * D;
+  const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
   // K: BN rows x D/16 items, 2 per thread.
   for (int it = tid; it < BN * (D / 16); it += 256) {
     const int r = it / (D / 16), g = it % (D / 16), t = t0 + r;
     u32x2 w0 = {0u, 0u}, w1 = {0u, 0u};
-    if (t < a.T) {
+    if (t < L) {
       const uint8_t* src = kb + (long)t * ks;
       const u32x2 i0 = *(const u32x2*)(src + 8 * g), i1 = *(const u32x2*)(src + 8 * g + D / 2);
       float x0[8], x1[8];
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(256) void fp8_prep_kernel(Fp8Args a) {
   for (int it = tid; it < BN * D / 16; it += 256) {
     const int r = it / (D / 16), c = it % (D / 16), t = t0 + r;
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (t < a.T) w = *(const u32x4*)(vb + (long)t * ks + 16 * c);
+    if (t < L) w = *(const u32x4*)(vb + (long)t * ks + 16 * c);
     *(u32x4*)(vt + r * D + 16 * c) = w;
   }
   __syncthreads();
@@ -186,14 +188,15 @@ struct UnitFp8 {
   static constexpr int D = kFp8D, BN = kFp8BN, NW = kFp8NW, BM = kFp8BM;
   static constexpr int NKB = BN / 32, DB = D / 32;
 
-  static __device__ __forceinline__ void run(const Fp8Args& a, int b, int qb, int head, CGR_FP8_LDS) {
+  // Entry b's first L tokens (L <= T, the entry stride).
+  static __device__ __forceinline__ void run(const Fp8Args& a, int b, int L, int qb, int head, CGR_FP8_LDS) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hh = lane >> 5;
-    const int L = a.T;
+    const int T = a.T;
     const int G = a.H / a.KV, kvh = head / G;
     const int qs = a.H * D;  // token stride of q and o (elements)
-    const uint8_t* qbase = a.q + ((long)b * L) * qs + (long)head * D;
+    const uint8_t* qbase = a.q + ((long)b * T) * qs + (long)head * D;
     const long img0 = ((long)b * a.KV + kvh) * a.NT * kFp8Tile;
     const rsrc_t rk = make_rsrc(a.kimg + img0, (uint32_t)(a.NT * kFp8Tile));
     const rsrc_t rv = make_rsrc(a.vimg + img0, (uint32_t)(a.NT * kFp8Tile));
@@ -433,7 +436,7 @@ struct UnitFp8 {
     // from the accumulators (rows past the sequence fall outside the range).
     const float l_tot = pair_sum(l_run);
     const float inv = a.vdescale / l_tot;
-    uint16_t* obase = (uint16_t*)a.o + ((long)b * L) * qs + (long)head * D;
+    uint16_t* obase = (uint16_t*)a.o + ((long)b * T) * qs + (long)head * D;
     const rsrc_t ro = make_rsrc(obase, (uint32_t)(((L - 1) * qs + D) * 2));
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -445,7 +448,7 @@ struct UnitFp8 {
         __builtin_amdgcn_raw_buffer_store_b64(ov, ro, (my_q * qs + d) * 2, 0, 0);
       }
     if (a.lse != nullptr && hh == 0 && my_q < L)
-      a.lse[((long)b * a.H + head) * L + my_q] = (m_fin + log2f(l_tot)) * 0.69314718055994531f;
+      a.lse[((long)b * a.H + head) * T + my_q] = (m_fin + log2f(l_tot)) * 0.69314718055994531f;
   }
 };
 
@@ -477,7 +480,10 @@ __global__ __launch_bounds__(64 * kFp8NW, 2) void attn_fwd_fp8_kernel(Fp8Args a)
   }
   const int qb = CAUSAL ? nQ - 1 - rank : rank;
   const int b = g / a.KV, kvh = g - b * a.KV;
-  UnitFp8<CAUSAL, STYLE>::run(a, b, qb, kvh * G + hq, k0, k1, v0, v1, qst);
+  // A padded entry is its first L tokens; units past them have nothing to do.
+  const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
+  if (qb * kFp8BM >= L) return;
+  UnitFp8<CAUSAL, STYLE>::run(a, b, L, qb, kvh * G + hq, k0, k1, v0, v1, qst);
 }
 
 template <bool CAUSAL, int STYLE>

@@ -530,7 +530,8 @@ cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const void* v
                                      float q_descale, float k_descale, float v_descale,
                                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
                                      cgr_rope_style style, cgr_mask mask, float softmax_scale,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+                                     const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
   if (!q || !k || !v || !o) return fail(CGR_ERR_INVALID_ARG, "q, k, v and o must be non-null");
   if (!rope_cos || !rope_sin) return fail(CGR_ERR_INVALID_ARG, "rope_cos and rope_sin must be non-null");
   if (B < 1 || T < 1) return fail(CGR_ERR_INVALID_ARG, "B (%d) and T (%d) must be >= 1", B, T);
@@ -551,6 +552,7 @@ cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const void* v
       !aligned(rope_sin, 16))
     return fail(CGR_ERR_ALIGNMENT, "q, k, v, o, rope_cos and rope_sin must be 16-byte aligned");
   if (lse && !aligned(lse, 4)) return fail(CGR_ERR_ALIGNMENT, "lse must be 4-byte aligned");
+  if (seqlens && !aligned(seqlens, 4)) return fail(CGR_ERR_ALIGNMENT, "seqlens must be 4-byte aligned");
   if (rope_max_pos < T)
     return fail(CGR_ERR_INVALID_ARG, "rope tables cover %d positions, the call needs %d", rope_max_pos, T);
   if ((long)(T + 256) * n_head * head_dim * 2 > (long)INT_MAX)
@@ -583,6 +585,7 @@ cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const void* v
   a.lse = lse;
   a.rope_cos = rope_cos;
   a.rope_sin = rope_sin;
+  a.seqlens = seqlens;
   a.B = B;
   a.T = T;
   a.H = n_head;

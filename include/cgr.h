@@ -209,10 +209,14 @@ CGR_API size_t cgr_attn_fwd_fp8_workspace_size(int B, int T, int n_kv_head, int 
  *     OCP fp8 e4m3 (1 sign, 4 exponent bits with bias 7, 3 mantissa bits;
  *     0x7f / 0xff are NaN; largest finite 448). The real inputs are the
  *     codes times q_descale, k_descale, v_descale (finite, > 0).
- *   o: device bf16 [B, T, n_head, 128], written in full.
+ *   o: device bf16 [B, T, n_head, 128], written in full (without seqlens).
  *   lse: device float32 [B, n_head, T], or NULL.
  *   head_dim must be 128; mask CGR_MASK_CAUSAL or CGR_MASK_NONE; RoPE tables
  *     as for cgr_gqa_rope_attn_fwd (rope_max_pos >= T).
+ *   seqlens: NULL, or device int32 [B] valid tokens per entry (right padding),
+ *     exactly as for cgr_gqa_rope_attn_fwd: keys at or past L_b are hidden,
+ *     rows at or past L_b of o and lse are left as they were, each L_b is
+ *     clamped to [0, T].
  *   workspace: device memory of cgr_attn_fwd_fp8_workspace_size(...) bytes,
  *     16-byte aligned, scratch for this call only (required).
  * Arithmetic: q and k are rotated in f32 and rounded back to e4m3 (q scaled
@@ -228,7 +232,8 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_fp8(const void* q, const void* k, const
                                      float q_descale, float k_descale, float v_descale,
                                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
                                      cgr_rope_style style, cgr_mask mask, float softmax_scale,
-                                     void* workspace, size_t workspace_bytes, void* stream);
+                                     const int32_t* seqlens, void* workspace, size_t workspace_bytes,
+                                     void* stream);
 
 /*
  * Bytes of device workspace cgr_gqa_rope_attn_fwd_varlen needs for a packed

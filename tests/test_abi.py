@@ -201,12 +201,12 @@ def test_varlen_noalloc_rejects_bad_arguments(kw, status, needle):
 
 def fp8(**kw):
     a = dict(q=P, k=P, v=P, o=P, lse=None, B=1, T=16, H=4, KV=2, D=128, qd=0.01, kd=0.01, vd=0.01, cos=P, sin=P,
-             P=16, style=0, mask=1, scale=0.0, ws=P, wsb=1 << 20)
+             P=16, style=0, mask=1, scale=0.0, seqlens=None, ws=P, wsb=1 << 20)
     a.update(kw)
     lib = cgr.library()
     st = lib.cgr_gqa_rope_attn_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["T"], a["H"], a["KV"],
                                        a["D"], a["qd"], a["kd"], a["vd"], a["cos"], a["sin"], a["P"], a["style"],
-                                       a["mask"], a["scale"], a["ws"], a["wsb"], None)
+                                       a["mask"], a["scale"], a["seqlens"], a["ws"], a["wsb"], None)
     return st, lib.cgr_last_error().decode()
 
 
@@ -225,6 +225,7 @@ def fp8(**kw):
     (dict(ws=None), 4, "workspace"),
     (dict(wsb=100), 4, "needs"),
     (dict(qd=1e30, kd=1e30), 1, "out of range"),
+    (dict(seqlens=ctypes.c_void_p(0x10002)), 3, "seqlens"),
 ])
 def test_fp8_rejects_bad_arguments(kw, status, needle):
     st, msg = fp8(**kw)

@@ -164,3 +164,58 @@ def test_fp8_long_context_full_size_sampled(gpu):
         big_o[b, t, h] = ro[i]
         big_l[b, h, t] = rl[i]
     check(w.name + " (sampled)", x, w, o, lse, big_o, big_l, True, "interleaved", rows=rows)
+
+
+# Right-padded batches (valid lengths per entry): (B, T, H, KV, causal,
+# style, lengths): an empty entry, one-token and full entries, lengths at and
+# around the 64-key tile and the 128-row unit, both masks and pairings.
+PADDED = [
+    (3, 300, 4, 2, True, "interleaved", [300, 129, 0]),
+    (2, 256, 8, 1, False, "half", [1, 200]),
+    (4, 130, 6, 3, True, "half", [64, 65, 127, 130]),
+]
+
+
+def entry(x, b, L):
+    """Entry b's first L tokens as a batch of one (codes, descales, dequantized values)."""
+    xb = {n: x[n][b:b + 1, :L].contiguous() for n in ("q", "k", "v")}
+    xb.update({n + "64": x[n + "64"][b:b + 1, :L] for n in ("q", "k", "v")})
+    xb.update({n + "_descale": x[n + "_descale"] for n in ("q", "k", "v")})
+    return xb
+
+
+@pytest.mark.parametrize("B,T,H,KV,causal,style,lengths", PADDED,
+                         ids=[f"B{c[0]}_T{c[1]}_H{c[2]}_KV{c[3]}_{'causal' if c[4] else 'nomask'}_{c[5]}"
+                              for c in PADDED])
+def test_fp8_padded(gpu, B, T, H, KV, causal, style, lengths):
+    """Every valid row of every entry against the oracle of that entry's first L
+    tokens (the format-derived bar) and the rounding model; the padding rows of
+    o and lse keep what they held; each entry gives the same bits as the
+    unpadded call on its first L tokens alone."""
+    w = W.custom(f"fp8_pad_T{T}", B=B, T=T, n_head=H, n_kv_head=KV, head_dim=128, base=5e5, dtype="f32",
+                 seed=700 + T + H)
+    announce(f"fp8 padded forward {w.name} B{B} H{H} KV{KV} causal={causal} {style} lengths={lengths}")
+    x = W.make_fp8_inputs(w)
+    cos, sin = cgr.rope_tables(T, 128, w.base, device=gpu)
+    out = torch.full((B, T, H, 128), float("nan"), dtype=torch.bfloat16, device=gpu)
+    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device=gpu)
+    seqlens = torch.tensor(lengths, dtype=torch.int32, device=gpu)
+    cgr.gqa_rope_attn_fwd_fp8(x["q"].to(gpu), x["k"].to(gpu), x["v"].to(gpu), x["q_descale"], x["k_descale"],
+                              x["v_descale"], cos, sin, causal=causal, rope_style=style, out=out, lse=lse,
+                              seqlens=seqlens)
+    torch.cuda.synchronize()
+    for b, L in enumerate(lengths):
+        assert torch.isnan(out[b, L:]).all() and torch.isnan(lse[b, :, L:]).all(), f"entry {b}: padding rows written"
+        if L == 0:
+            continue
+        xb = entry(x, b, L)
+        wb = W.custom(w.name, B=1, T=L, n_head=H, n_kv_head=KV, head_dim=128, base=w.base, dtype="f32")
+        o_b, l_b = f64(out[b:b + 1, :L]), f64(lse[b:b + 1, :, :L])
+        ro, rl = oracle.attention_dense(xb["q64"], xb["k64"], xb["v64"], causal=causal, base=w.base, style=style)
+        mo, ml = model(wb, xb, causal, style)
+        check_model(f"{w.name} entry {b} (L={L})", o_b, mo, l_b, ml, float(np.abs(xb["v64"]).max()))
+        check(f"{w.name} entry {b} (L={L}) vs the oracle", xb, wb, o_b, l_b, ro, rl, causal, style)
+        od, ld = cgr.gqa_rope_attn_fwd_fp8(xb["q"].to(gpu), xb["k"].to(gpu), xb["v"].to(gpu), x["q_descale"],
+                                           x["k_descale"], x["v_descale"], cos, sin, causal=causal,
+                                           rope_style=style)
+        assert torch.equal(out[b:b + 1, :L], od) and torch.equal(lse[b:b + 1, :, :L], ld), f"entry {b}: bits"
