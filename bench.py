@@ -98,7 +98,7 @@ def read_traffic():
 
 
 class ClockSampler:
-    """The graphics clock (MHz) under the step's load, from amd-smi.
+    """The graphics clock (MHz) and the socket power (W) under the step's load, from amd-smi.
 
     amd-smi's clock readings trail the load by the better part of a second
     (the first readings of a burst still show the idle clock), so measure()
@@ -111,6 +111,7 @@ class ClockSampler:
     def __init__(self):
         self._handle = None
         self._kept = []
+        self._watts = []
         self._source = None
         try:
             import amdsmi
@@ -138,6 +139,23 @@ class ClockSampler:
             pass
         return None, None
 
+    def _power(self):
+        try:
+            p = self._amdsmi.amdsmi_get_power_info(self._handle).get("socket_power")
+            return float(p) if isinstance(p, (int, float)) and 0 < p < 10000 else None
+        except Exception:
+            return None
+
+    def _cap(self):
+        # The socket power limit in W (amd-smi reports it in microwatts).
+        try:
+            c = self._amdsmi.amdsmi_get_power_cap_info(self._handle).get("power_cap")
+            if isinstance(c, (int, float)) and c > 0:
+                return round(c / 1e6, 1) if c > 1e5 else float(c)
+        except Exception:
+            pass
+        return None
+
     def measure(self, step, seconds: float = 2.0, tail: float = 0.8):
         import torch
         if self._handle is None:
@@ -155,7 +173,7 @@ class ClockSampler:
             while run[0]:
                 v, src = self._read()
                 if v is not None:
-                    samples.append((time.perf_counter(), v, src))
+                    samples.append((time.perf_counter(), v, src, self._power()))
                 time.sleep(0.005)
 
         th = threading.Thread(target=loop, daemon=True)
@@ -168,7 +186,8 @@ class ClockSampler:
         run[0] = False
         th.join()
         t_end = time.perf_counter()
-        self._kept = [(v, src) for t, v, src in samples if t >= t_end - tail]
+        self._kept = [(v, src) for t, v, src, _ in samples if t >= t_end - tail]
+        self._watts = [w for t, _, _, w in samples if t >= t_end - tail and w is not None]
         self._source = self._kept[-1][1] if self._kept else None
 
     def summary(self):
@@ -179,7 +198,10 @@ class ClockSampler:
         per_x = [statistics.median(v[i] for v, _ in self._kept if len(v) == n_x) for i in range(n_x)]
         return {"median": round(statistics.median(means), 1), "xcd_min": min(per_x), "xcd_max": max(per_x),
                 "samples": len(self._kept),
-                "source": f"{self._source}, the last 0.8 s of 2 s of back-to-back steps before the warmup steps"}
+                "socket_power_w": round(statistics.median(self._watts), 1) if self._watts else None,
+                "power_cap_w": self._cap(),
+                "source": f"{self._source} and power info socket_power, the last 0.8 s of 2 s of back-to-back "
+                          "steps before the warmup steps"}
 
 
 def cpu_baseline(inputs, w) -> dict:
@@ -812,6 +834,44 @@ def main() -> int:
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     headline = args.window == 0 and not args.padded and not args.wide
     traffic = read_traffic() if headline else None
+    clock_f16 = clock.summary()
+
+    # The same step with both products on bf16 operands (the operand type the
+    # method's statement names; the library's default Q.K^T operand is f16, for
+    # precision on inputs with large keys): the attention kernel alone, at its
+    # own sustained clock and power.
+    bf16_ops = None
+    if headline:
+        ws_b = torch.empty_like(ws)
+
+        def step_b():
+            tables()
+            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand="bf16", **kw)
+            attention_b()
+
+        def attention_b():
+            cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws_b, causal=True, out=o, lse=lse, qk_operand="bf16",
+                                          **kw)
+
+        clock.measure(step_b)
+        for _ in range(args.warmup):
+            step_b()
+        torch.cuda.synchronize()
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            tables()
+            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand="bf16", **kw)
+            evb[i][0].record(stream)
+            attention_b()
+            evb[i][1].record(stream)
+        torch.cuda.synchronize()
+        kb = [a.elapsed_time(b) for a, b in evb]
+        kb_ms = sum(kb) / len(kb)
+        bf16_ops = {"qk_operand": "bf16", "pv_operand": "bf16", "kernel_ms": round(kb_ms, 5),
+                    "kernel_ms_median": round(statistics.median(kb), 5),
+                    "achieved": round(flops / (kb_ms * 1e-3) / 1e12, 3),
+                    "frac": round(flops / (kb_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
+                    "clock_mhz": clock.summary()}
 
     result = {
         "metric": METRIC,
@@ -852,7 +912,8 @@ def main() -> int:
             "call_ms_median": round(call_med, 5),
             "call_tflops": round(flops / (call_ms * 1e-3) / 1e12, 3),
             "rotate_keys_ms": round(sum(rot) / len(rot), 5),
-            "clock_mhz": clock.summary(),
+            "clock_mhz": clock_f16,
+            **({"bf16_operands": bf16_ops} if bf16_ops else {}),
         },
         "cpu_baseline": None if args.no_cpu_baseline or not headline else cpu_baseline(inputs, w),
     }

@@ -43,13 +43,17 @@ def test_long_context_full_size(gpu):
     """The full long-context workload (B=1, T=8192, 32 query heads, 8 K/V heads,
     head_dim 128) in the launch configuration the benchmark times, compared with
     the float64 oracle on every element of O (33.5 M) and of the LSE (262,144
-    rows): max abs and median relative error over the whole config."""
+    rows): max abs and median relative error over the whole config. Both Q.K^T
+    operand types: the default f16 and bf16 (the operand type the method's
+    statement names, which the benchmark also times)."""
     w = W.get("long_context_T8192_H32_KV8_d128")
-    announce(f"{w.name}: full-size run, every element against the oracle")
     x = W.make_inputs(w)
-    o, lse = run_gpu(w, to_dev(x, gpu), gpu)
+    xd = to_dev(x, gpu)
     ro, rl = run_oracle(w, x)
-    assert_close(w.name + " (every element)", f64(o), ro, f64(lse), rl, w.dtype)
+    for qk in ("f16", "bf16"):
+        announce(f"{w.name}: full-size run ({qk} Q.K^T operands), every element against the oracle")
+        o, lse = run_gpu(w, xd, gpu, qk_operand=qk)
+        assert_close(f"{w.name} ({qk} operands, every element)", f64(o), ro, f64(lse), rl, w.dtype)
 
 
 def test_varlen_workload_full_size(gpu):
