@@ -400,6 +400,7 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
     qrow0 = q_first + 32 * (n_steps - 1 - sidx);
   };
   // Loads of iteration i (this group's item 2i + grp) into a stage.
+  const TileCopy<D, 32, 4> qcopy(wig, qs * 2, lane);
   auto issue = [&](int i, char* st) {
     const int n = 2 * i + grp;
     if (n >= n_items) return;
@@ -410,8 +411,8 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
     const long hoff = (long)tok0 * qs + (long)h * D;
     const rsrc_t rq = make_rsrc((const uint16_t*)a.qr + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
     const rsrc_t rd = make_rsrc((const uint16_t*)a.dout + hoff, (uint32_t)(((L - 1) * qs + D) * 2));
-    tile_to_lds<D, 32>(rq, gs, qs * 2, qrow0 * qs * 2, wig, 4, lane);
-    tile_to_lds<D, 32>(rd, gs + C::TILE, qs * 2, qrow0 * qs * 2, wig, 4, lane);
+    qcopy(rq, gs, qrow0 * qs * 2);
+    qcopy(rd, gs + C::TILE, qrow0 * qs * 2);
     if (wig == 0) {
       const long t = ldt0 + (long)h * ldh + qrow0 / 32;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_void*)(gs + 2 * C::TILE), 4, lane * 4,
@@ -724,10 +725,11 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 
   const rsrc_t rkr = make_rsrc((const uint16_t*)a.kr + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
   const rsrc_t rv = make_rsrc((const uint16_t*)a.v + ((long)tok0 * ks + kvh * D), (uint32_t)(((L - 1) * ks + D) * 2));
+  const TileCopy<D, BN, 8> kvcopy(wave, ks * 2, lane);
   auto issue = [&](int j, char* kt, char* vt) {
     if (j >= n_tiles) return;
-    tile_to_lds<D, BN>(rkr, kt, ks * 2, j * BN * ks * 2, wave, 8, lane);
-    tile_to_lds<D, BN>(rv, vt, ks * 2, j * BN * ks * 2, wave, 8, lane);
+    kvcopy(rkr, kt, j * BN * ks * 2);
+    kvcopy(rv, vt, j * BN * ks * 2);
   };
 
   const TrOffsets<D> tro(lane);
@@ -735,10 +737,14 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
 
-  auto compute = [&](int j, const char* Kt, const char* Vt) {
+  // MASK: the body with the causal mask (tiles that reach past the unit's
+  // first row); the other body is for tiles every row sees whole, so the
+  // mask's selects are not executed (predicated) on every tile.
+  auto compute = [&](int j, const char* Kt, const char* Vt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     if (!wave_has_rows || (C::CAUSAL && j * BN > wave_last)) return;
     if (W > 0 && j * BN + BN - 1 < qw0 - W + 1) return;  // left of every row's window
-    const bool domask = C::CAUSAL && j * BN + BN - 1 > qw0;
+    const bool domask = MASK && C::CAUSAL && j * BN + BN - 1 > qw0;
     const bool wmask = W > 0 && j * BN < wave_last - W + 1;
     const int lim = my_q - j * BN - 4 * hh;  // key offset in the tile must be <= lim
     const int lo = my_q - W + 1 - j * BN - 4 * hh;  // ... and >= lo under a window
@@ -778,22 +784,35 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  // Tile j0 + 2m uses stage 0, j0 + 2m + 1 stage 1.
+  // Tile j0 + 2m uses stage 0, j0 + 2m + 1 stage 1. Tiles below n_plain end
+  // before the unit's first row (no causal mask for any wave; windowed units
+  // keep the masked body throughout).
+  const int n_plain = C::CAUSAL && !C::WIN ? min(n_tiles, (q0 + 1) / BN) : j0;
   issue(j0, kt0s, vt0s);
   wait_vmem();
   __syncthreads();
   int j = j0;
-  for (; j + 1 < n_tiles; j += 2) {
+  for (; j + 1 < n_plain; j += 2) {
     issue(j + 1, kt1s, vt1s);
-    compute(j, kt0s, vt0s);
+    compute(j, kt0s, vt0s, std::false_type{});
     wait_vmem();
     __syncthreads();
     issue(j + 2, kt0s, vt0s);
-    compute(j + 1, kt1s, vt1s);
+    compute(j + 1, kt1s, vt1s, std::false_type{});
     wait_vmem();
     __syncthreads();
   }
-  if (j < n_tiles) compute(j, kt0s, vt0s);
+  for (; j + 1 < n_tiles; j += 2) {
+    issue(j + 1, kt1s, vt1s);
+    compute(j, kt0s, vt0s, std::true_type{});
+    wait_vmem();
+    __syncthreads();
+    issue(j + 2, kt0s, vt0s);
+    compute(j + 1, kt1s, vt1s, std::true_type{});
+    wait_vmem();
+    __syncthreads();
+  }
+  if (j < n_tiles) compute(j, kt0s, vt0s, std::true_type{});
 
   if (!wave_has_rows) return;
   if (my_q < L) rope_transpose_acc<D, C::STYLE>(dq, a.rope_cos, a.rope_sin, my_q, hh);

@@ -151,6 +151,13 @@ struct Cfg {
   // reach of the 16-bit offsets of the LDS instructions.
   static constexpr int Q_STRIDE = 2 * D + 16;
   static constexpr int Q_STAGE_BYTES = F32 ? 0 : NW * 32 * Q_STRIDE;
+  // Units of at most 64 rows (head_dim <= 128) stage the cos/sin rows of their
+  // query positions once for all their waves (the waves of a row block share
+  // them): cos, then sin, bm rows of 2*D bytes each, in the second V stage
+  // (free until the first tile's products are issued) and, for 64-row units,
+  // sin in this much more dynamic LDS after the Q staging.
+  static constexpr int TAB_EXTRA = (F32 || WIDE) ? 0 : 64 * 2 * D;
+  static constexpr int DYN_LDS = Q_STAGE_BYTES + TAB_EXTRA;
 
   // Loader work items. K: (row, 8-element group g < D/16), which carries the
   // group pair (g, g + D/16) so that both RoPE pairings find their partners.
@@ -559,6 +566,14 @@ __device__ __forceinline__ void buf_load16_lds(rsrc_t r, char* lds_base, int vof
 // Wait until this wave's outstanding global/buffer loads (including those
 // that write LDS directly) have landed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding (N < 64); later code stays below the wait.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 template <class C>
 struct UnitFast {
@@ -634,23 +649,52 @@ struct UnitFast {
     char* const q_stage = qst + wave * 32 * C::Q_STRIDE;
     u32x4 q_raw[QI][Q_HALF ? 2 : 1];
     f32x4 q_cos[QI][Q_HALF ? 2 : 1], q_sin[QI][Q_HALF ? 2 : 1];
-#pragma unroll
-    for (int i = 0; i < QI; ++i) {
-      const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
-      const int row = qw0 + r;  // rows past the sequence read as zeros (buffer range)
-      const int qo = row * qs * 2 + c * 16, to = row * (D / 2) * 4;
-      q_raw[i][0] = buf_load16(rq, qo, 0);
-      if constexpr (Q_HALF) {
-        q_raw[i][1] = buf_load16(rq, qo + D, 0);
-        q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
-        q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
-        q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
-        q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
-      } else {
-        q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
-        q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
+    // Units of at most 64 rows: the cos/sin rows of the unit's positions are
+    // loaded once, straight into LDS (tab_cos, tab_sin: rows of 2*D bytes), and
+    // every wave reads its rows from there; otherwise each wave loads its own.
+    const bool share_tab = !C::WIDE && bm <= 64;
+    char* const tab_cos = vs1;
+    char* const tab_sin = 2 * bm * 2 * D <= C::V_BYTES ? vs1 + bm * 2 * D : qst + C::Q_STAGE_BYTES;
+    auto issue_q = [&]() {
+      if (share_tab) {
+        // 1-KiB direct loads, RPL rows each: load u of bm / RPL per table.
+        constexpr int RPL = 1024 / (2 * D);
+        const int per = bm / RPL;
+        for (int u = wave; u < 2 * per; u += NW) {
+          const int t = u >= per, blk = u - t * per;
+          buf_load16_lds(t ? rs : rc, (t ? tab_sin : tab_cos) + blk * 1024, lane * 16, (q0 + blk * RPL) * 2 * D);
+        }
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < QI; ++i) {
+        const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+        const int row = qw0 + r;  // rows past the sequence read as zeros (buffer range)
+        const int qo = row * qs * 2 + c * 16, to = row * (D / 2) * 4;
+        q_raw[i][0] = buf_load16(rq, qo, 0);
+        if constexpr (Q_HALF) q_raw[i][1] = buf_load16(rq, qo + D, 0);
+        if (!share_tab) {
+          if constexpr (Q_HALF) {
+            q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
+            q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
+            q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
+            q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
+          } else {
+            q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
+            q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (share_tab) {
+        // The table rows have landed once at most the QI * (1 + Q_HALF) Q
+        // loads issued after them are outstanding; then every wave's rows are
+        // in LDS. (No full __syncthreads: it would wait for the Q rows too.)
+        wait_vmem_le<QI * (Q_HALF ? 2 : 1)>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+    };
     Frag<QK> qf[C::KSTEPS];
     // f16 operands: a rotated query (times scale*log2(e)) or key outside the
     // f16 range enters the product as NaN (to_frag_or_nan, here and in the key
@@ -685,6 +729,19 @@ struct UnitFast {
       }
     };
     auto stage_q = [&]() {
+      if (share_tab) {
+#pragma unroll
+        for (int i = 0; i < QI; ++i) {
+          const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
+          const int to = (wrow * 32 + r) * 2 * D + c * (Q_HALF ? 32 : 16);
+          q_cos[i][0] = *(const f32x4*)(tab_cos + to);
+          q_sin[i][0] = *(const f32x4*)(tab_sin + to);
+          if constexpr (Q_HALF) {
+            q_cos[i][1] = *(const f32x4*)(tab_cos + to + 16);
+            q_sin[i][1] = *(const f32x4*)(tab_sin + to + 16);
+          }
+        }
+      }
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
@@ -1155,6 +1212,7 @@ struct UnitFast {
       u32x4 kw1[KI][2];
       f32x4 kc1[KI][2], ksn1[KI][2];
       // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
+      issue_q();
       load_k(jl * BN, ks0, kw, kc, ksn);
       if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
       load_v(jl * BN, vs0, vw);
@@ -1238,6 +1296,7 @@ struct UnitFast {
         u32x4 kw1[KI][2];
         f32x4 kc1[KI][2], ksn1[KI][2];
         // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
+        issue_q();
         load_k(0, ks0, kw, kc, ksn);
         if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
         load_v(0, vs0, vw);
@@ -1534,10 +1593,10 @@ __global__ __launch_bounds__(kPrepThreads) void varlen_prep_kernel(AttnArgs a) {
 template <class C>
 hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t stream) {
   if (varlen)
-    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
+    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS,
                        stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS,
                        stream, a);
   return hipGetLastError();
 }
@@ -1556,7 +1615,7 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int
     if (e != hipSuccess) return e;
   }
   if (phases & PHASE_ATTEND)
-    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
   return hipGetLastError();
 }
 
@@ -1569,7 +1628,7 @@ hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stre
                      dim3(kPrepThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+  hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
   return hipGetLastError();
 }
 
@@ -1598,7 +1657,7 @@ constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_di
 
 template <class C>
 hipError_t launch_attn_dense(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
+  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
   return hipGetLastError();
 }
 

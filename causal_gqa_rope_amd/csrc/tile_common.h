@@ -8,15 +8,6 @@
 
 namespace cgr {
 
-// Waits until at most n of this wave's vector-memory operations are
-// outstanding (n < 64), then keeps later code from moving above the wait.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-  __builtin_amdgcn_sched_barrier(0);
-}
-
 // Load `rows` rows (row r of the tile at global byte offset r * gstride + soff)
 // into an LDS tile, by the `nw` waves of a group; `wig` is this wave's index in
 // the group. Rows past the buffer's range read as zeros.
@@ -31,6 +22,31 @@ __device__ __forceinline__ void tile_to_lds(rsrc_t rs, char* lds, int gstride, i
     buf_load16_lds(rs, lds + u * 1024, r * gstride + 16 * (pc ^ tswz<D>(r)), soff);
   }
 }
+
+// The same copy for a group of NWG waves with its per-lane global offsets
+// worked out once (they depend on the lane, the wave's index in the group and
+// the row stride only): a loop that copies tile after tile then issues just
+// the loads, each with the tile's scalar offset.
+template <int D, int ROWS, int NWG>
+struct TileCopy {
+  static constexpr int NCH = D / 8;
+  static constexpr int NI = ROWS * NCH / 64;  // 1 KiB wave loads
+  static constexpr int PER = NI / NWG;        // loads per wave
+  static_assert(ROWS * NCH % 64 == 0 && NI % NWG == 0, "whole wave loads, evenly per wave");
+  int wig;
+  int voff[PER];
+  __device__ __forceinline__ TileCopy(int wig_, int gstride, int lane) : wig(wig_) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int slot = (wig + k * NWG) * 64 + lane, r = slot / NCH, pc = slot % NCH;
+      voff[k] = r * gstride + 16 * (pc ^ tswz<D>(r));
+    }
+  }
+  __device__ __forceinline__ void operator()(rsrc_t rs, char* lds, int soff) const {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) buf_load16_lds(rs, lds + (wig + k * NWG) * 1024, voff[k], soff);
+  }
+};
 
 // Operand fragment k-step s of row r (lane half hh): elements 16s + 8hh .. +7.
 template <int D>
