@@ -655,7 +655,11 @@ struct UnitFast {
     const bool share_tab = !C::WIDE && bm <= 64;
     char* const tab_cos = vs1;
     char* const tab_sin = 2 * bm * 2 * D <= C::V_BYTES ? vs1 + bm * 2 * D : qst + C::Q_STAGE_BYTES;
-    auto issue_q = [&]() {
+    // The prologue's loads go out in this order: the shared table rows
+    // (issue_tab), the first K and V tiles, the Q rows (issue_q), so that
+    // waiting for the table rows (tab_ready) does not wait for anything
+    // fetched from HBM.
+    auto issue_tab = [&]() {
       if (share_tab) {
         // 1-KiB direct loads, RPL rows each: load u of bm / RPL per table.
         constexpr int RPL = 1024 / (2 * D);
@@ -665,6 +669,9 @@ struct UnitFast {
           buf_load16_lds(t ? rs : rc, (t ? tab_sin : tab_cos) + blk * 1024, lane * 16, (q0 + blk * RPL) * 2 * D);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto issue_q = [&]() {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
@@ -686,11 +693,16 @@ struct UnitFast {
         }
       }
       __builtin_amdgcn_sched_barrier(0);
+    };
+    // The shared table rows have landed once at most as many loads as every
+    // wave issued after them are outstanding (at least K_MIN + V_MIN 1-KiB
+    // loads of the first tiles, then the Q rows); then every wave's rows are
+    // in LDS. (No full __syncthreads: it would wait for the Q rows too.)
+    constexpr int K_MIN = C::KPRE ? (C::K_IMG / 1024) / NW : 0, V_MIN = (C::V_BYTES / 1024) / NW;
+    auto tab_ready = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
       if (share_tab) {
-        // The table rows have landed once at most the QI * (1 + Q_HALF) Q
-        // loads issued after them are outstanding; then every wave's rows are
-        // in LDS. (No full __syncthreads: it would wait for the Q rows too.)
-        wait_vmem_le<QI * (Q_HALF ? 2 : 1)>();
+        wait_vmem_le<QI * (Q_HALF ? 2 : 1) + K_MIN + V_MIN>();
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
@@ -1212,10 +1224,12 @@ struct UnitFast {
       u32x4 kw1[KI][2];
       f32x4 kc1[KI][2], ksn1[KI][2];
       // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
-      issue_q();
+      issue_tab();
       load_k(jl * BN, ks0, kw, kc, ksn);
-      if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
       load_v(jl * BN, vs0, vw);
+      if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
+      issue_q();
+      tab_ready();
       stage_q();
       store_k(jl * BN, ks0, kw, kc, ksn, vw);
       wait_vmem();
@@ -1296,10 +1310,12 @@ struct UnitFast {
         u32x4 kw1[KI][2];
         f32x4 kc1[KI][2], ksn1[KI][2];
         // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
-        issue_q();
+        issue_tab();
         load_k(0, ks0, kw, kc, ksn);
-        if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
         load_v(0, vs0, vw);
+        if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
+        issue_q();
+        tab_ready();
         stage_q();
         store_k(0, ks0, kw, kc, ksn, vw);
         wait_vmem();
