@@ -113,6 +113,7 @@ class ClockSampler:
         self._kept = []
         self._watts = []
         self._source = None
+        self._thread = None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
@@ -157,37 +158,42 @@ class ClockSampler:
         return None
 
     def measure(self, step, seconds: float = 2.0, tail: float = 0.8):
+        """Run `step` back to back for `seconds` while sampling. The sampler
+        thread is left running, so the caller goes straight on to its warmup
+        and timed steps: an idle gap of a few milliseconds here (joining the
+        thread) lets the clock drop, and the next ~10 ms of steps then run
+        up to 20 % slower while it climbs back. finish() stops the sampler and
+        keeps the samples of the last `tail` seconds of this load."""
         import torch
-        if self._handle is None:
-            # No clock readings: still run the load (it brings the GPU to its
-            # sustained clock before the timed steps).
-            t0 = time.perf_counter()
-            while time.perf_counter() - t0 < seconds:
-                for _ in range(8):
-                    step()
-                torch.cuda.synchronize()
-            return
-        samples, run = [], [True]
+        self._samples, self._run = [], [True]
 
         def loop():
-            while run[0]:
+            while self._run[0]:
                 v, src = self._read()
                 if v is not None:
-                    samples.append((time.perf_counter(), v, src, self._power()))
+                    self._samples.append((time.perf_counter(), v, src, self._power()))
                 time.sleep(0.005)
 
-        th = threading.Thread(target=loop, daemon=True)
+        self._thread = None
+        if self._handle is not None:
+            self._thread = threading.Thread(target=loop, daemon=True)
+            self._thread.start()
         t0 = time.perf_counter()
-        th.start()
         while time.perf_counter() - t0 < seconds:
             for _ in range(8):
                 step()
             torch.cuda.synchronize()
-        run[0] = False
-        th.join()
-        t_end = time.perf_counter()
-        self._kept = [(v, src) for t, v, src, _ in samples if t >= t_end - tail]
-        self._watts = [w for t, _, _, w in samples if t >= t_end - tail and w is not None]
+        self._t_end, self._tail = time.perf_counter(), tail
+
+    def finish(self):
+        if self._thread is None:
+            return
+        self._run[0] = False
+        self._thread.join()
+        self._thread = None
+        lo, hi = self._t_end - self._tail, self._t_end
+        self._kept = [(v, src) for t, v, src, _ in self._samples if lo <= t <= hi]
+        self._watts = [w for t, _, _, w in self._samples if lo <= t <= hi and w is not None]
         self._source = self._kept[-1][1] if self._kept else None
 
     def summary(self):
@@ -281,27 +287,36 @@ def all_configs(torch, cgr, W, dev, steps: int, warmup: int, graph: bool = False
             def call():
                 cgr.gqa_rope_attn_fwd(q, k, v, cos, sin, causal=w.causal, rope_style=w.rope_style,
                                       out=o, lse=lse, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        clock = ClockSampler()
+        clock.measure(call)
         for _ in range(warmup):
             call()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(steps):
             call()
         e1.record(stream)
         torch.cuda.synchronize()
+        clock.finish()
         us = e0.elapsed_time(e1) * 1e3 / steps
         flops = W.algorithmic_flops(w.n_head, w.head_dim, lengths, w.causal)
         tf = flops / (us * 1e-6) / 1e12
+        cs = clock.summary() or {}
         line = {"workload": w.name, "io": "f32" if w.dtype == "f32" else "bf16", "us_per_call": round(us, 2),
-                "flops": flops, "tflops": round(tf, 3), "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2)}
+                "flops": flops, "tflops": round(tf, 3), "pct_of_bf16_peak": round(100.0 * tf / PEAK_TFLOPS, 2),
+                "clock_mhz": cs.get("median"), "socket_power_w": cs.get("socket_power_w")}
         if graph:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for _ in range(steps):
                     call()
-            g.replay()
-            torch.cuda.synchronize()
+            # Replays back to back for half a second first: the capture leaves
+            # the GPU idle long enough for its clock to drop.
+            t_w = time.perf_counter()
+            while time.perf_counter() - t_w < 0.5:
+                g.replay()
+                torch.cuda.synchronize()
             e0.record(stream)
             g.replay()
             e1.record(stream)
@@ -375,16 +390,21 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window
         else:
             cgr.gqa_rope_attn_bwd(q, k, v, o, lse, dout, cos, sin, **kw, dq=dq, dk=dk, dv=dv, workspace=ws)
 
+    # As for the forward: 2 s of back-to-back calls (the sustained clock and
+    # power), then the warmup and timed calls with no idle gap.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    clock = ClockSampler()
+    clock.measure(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         call()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    clock.finish()
     wall = time.perf_counter() - t0
     flops = W.algorithmic_flops_bwd(w.n_head, w.head_dim, lens, True, window)
     ms_step = wall * 1e3 / steps
@@ -412,6 +432,7 @@ def backward(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool, window
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
         "roofline": {
+            "clock_mhz": clock.summary(),
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_TFLOPS,
@@ -482,16 +503,21 @@ def decode(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
         cgr.gqa_rope_attn_decode(q, kc, vc, lens, x["max_seqlen"], cos, sin, rope_style=w.rope_style,
                                  out=o, lse=lse, workspace=ws)
 
+    # As for the forward: 2 s of back-to-back calls (the sustained clock and
+    # power), then the warmup and timed calls with no idle gap.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    clock = ClockSampler()
+    clock.measure(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         call()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    clock.finish()
     wall = time.perf_counter() - t0
     nbytes = W.decode_bytes(w, x["cache_seqlens"].tolist())
     ms_step = wall * 1e3 / steps
@@ -520,6 +546,7 @@ def decode(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
             "pct_of_peak": round(100.0 * nbytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
         },
         "roofline": {
+            "clock_mhz": clock.summary(),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
@@ -557,16 +584,21 @@ def fp8(torch, cgr, W, dev, steps: int, warmup: int) -> None:
         cgr.gqa_rope_attn_fwd_fp8(q, k, v, x["q_descale"], x["k_descale"], x["v_descale"], cos, sin, out=o, lse=lse,
                                   workspace=ws)
 
+    # As for the forward: 2 s of back-to-back calls (the sustained clock and
+    # power), then the warmup and timed calls with no idle gap.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    clock = ClockSampler()
+    clock.measure(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         call()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    clock.finish()
     wall = time.perf_counter() - t0
     flops = W.algorithmic_flops(w.n_head, w.head_dim, [w.T] * w.B, True)
     ms_step = wall * 1e3 / steps
@@ -593,6 +625,7 @@ def fp8(torch, cgr, W, dev, steps: int, warmup: int) -> None:
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 2),
         },
         "roofline": {
+            "clock_mhz": clock.summary(),
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": FP8_PEAK_TFLOPS,
@@ -656,16 +689,21 @@ def qkv(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
         cgr.rmsnorm_qkv_rope(xs, g, w.eps, wq, pos, w.n_head, w.n_kv_head, cos, sin, rope_style=w.rope_style,
                              q=q, k=k, v=v, workspace=ws)
 
+    # As for the forward: 2 s of back-to-back calls (the sustained clock and
+    # power), then the warmup and timed calls with no idle gap.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    clock = ClockSampler()
+    clock.measure(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
         ev[i][0].record(stream)
         call()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
+    clock.finish()
     wall = time.perf_counter() - t0
     flops = 2 * N * C * O
     ms_step = wall * 1e3 / steps
@@ -691,6 +729,7 @@ def qkv(torch, cgr, W, dev, steps: int, warmup: int, with_cpu: bool) -> None:
             "pct_of_peak": round(100.0 * flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS, 2),
         },
         "roofline": {
+            "clock_mhz": clock.summary(),
             "bound": "mfma",
             "achieved": round(achieved, 3),
             "peak": PEAK_TFLOPS,
@@ -805,13 +844,14 @@ def main() -> int:
     # steps. From idle the GPU takes a good part of a second to reach the clock
     # it holds under sustained load, so this also keeps the timed steps from
     # measuring that ramp (a few warmup steps alone last only milliseconds).
+    # The warmup and timed steps follow it with no host work in between (the
+    # events exist beforehand, the clock sampler stops afterwards): even a few
+    # idle milliseconds let the clock drop and slow the next ~20 steps.
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     clock = ClockSampler()
     clock.measure(step)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -823,6 +863,7 @@ def main() -> int:
         ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    clock.finish()
 
     flops = W.algorithmic_flops(w.n_head, w.head_dim, lens, True, args.window)
     ms_step = wall * 1e3 / args.steps
@@ -853,11 +894,11 @@ def main() -> int:
             cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws_b, causal=True, out=o, lse=lse, qk_operand="bf16",
                                           **kw)
 
+        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         clock.measure(step_b)
         for _ in range(args.warmup):
             step_b()
         torch.cuda.synchronize()
-        evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         for i in range(args.steps):
             tables()
             cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand="bf16", **kw)
@@ -865,6 +906,7 @@ def main() -> int:
             attention_b()
             evb[i][1].record(stream)
         torch.cuda.synchronize()
+        clock.finish()
         kb = [a.elapsed_time(b) for a, b in evb]
         kb_ms = sum(kb) / len(kb)
         bf16_ops = {"qk_operand": "bf16", "pv_operand": "bf16", "kernel_ms": round(kb_ms, 5),

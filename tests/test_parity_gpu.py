@@ -488,3 +488,48 @@ def test_longest_sequence_the_offsets_allow(gpu):
     go = np.stack([o[b, t, h] for (b, t, h) in rows])
     gl = np.array([lse[b, h, t] for (b, t, h) in rows])
     assert_close(w.name + " (sampled)", go, ro, gl, rl, "bf16")
+
+
+HEAD_PACKED = [
+    # d, H, KV, style, causal, window: units of 32 rows x 8 heads (G = 8) and of
+    # 64 rows x 4 heads (G = 4), whose waves share the cos/sin rows of their
+    # positions through LDS
+    (32, 8, 1, "interleaved", True, 0),
+    (32, 8, 2, "half", True, 0),
+    (64, 8, 1, "half", True, 0),
+    (64, 8, 2, "interleaved", False, 0),
+    (128, 8, 1, "interleaved", True, 0),
+    (128, 8, 2, "half", True, 0),
+    (128, 8, 1, "half", False, 0),
+    (128, 8, 2, "interleaved", True, 50),
+    (64, 8, 1, "interleaved", True, 33),
+]
+
+
+@pytest.mark.parametrize("d,H,KV,style,causal,window", HEAD_PACKED,
+                         ids=[f"d{e[0]}-G{e[1] // e[2]}-{e[3]}-c{int(e[4])}-w{e[5]}" for e in HEAD_PACKED])
+def test_head_packed_units(gpu, d, H, KV, style, causal, window):
+    """Units whose waves cover several heads of one row block (they stage the
+    positions' cos/sin rows once for all of them): a dense batch with a ragged
+    tail and a packed batch with empty and one-token sequences, element by
+    element against the oracle."""
+    announce(f"head-packed units d={d} H={H} KV={KV} {style} causal={causal} window={window}")
+    w = W.custom("head_packed", B=2, T=300, n_head=H, n_kv_head=KV, head_dim=d, dtype="bf16", causal=causal,
+                 rope_style=style, base=1e4, seed=d + H + 7 * KV + window)
+    x = W.make_inputs(w)
+    xd = to_dev(x, gpu)
+    cos, sin = cgr.rope_tables(w.T, d, w.base, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd(xd["q"], xd["k"], xd["v"], cos, sin, causal=causal, rope_style=style,
+                                   window=window)
+    ro, rl = oracle.attention_dense(x["q"], x["k"], x["v"], causal=causal, base=w.base, style=style,
+                                    window=window)
+    assert_close("head-packed dense", f64(o), ro, f64(lse), rl, "bf16")
+    lengths = [5, 0, 130, 64, 1, 97]
+    xp = packed_inputs(lengths, H, KV, d, "bf16", seed=d * 3 + KV)
+    xpd = to_dev(xp, gpu)
+    cosp, sinp = cgr.rope_tables(max(lengths), d, w.base, device=gpu)
+    o, lse = cgr.gqa_rope_attn_fwd_varlen(xpd["q"], xpd["k"], xpd["v"], xpd["cu_seqlens"], max(lengths), cosp,
+                                          sinp, causal=causal, rope_style=style, window=window)
+    ro, rl = oracle.attention_varlen(xp["q"], xp["k"], xp["v"], xp["cu_seqlens"].numpy(), causal=causal,
+                                     base=w.base, style=style, window=window)
+    assert_close("head-packed packed", f64(o), ro, f64(lse), rl, "bf16")
