@@ -158,21 +158,21 @@ class ClockSampler:
         return None
 
     def measure(self, step, seconds: float = 2.0, tail: float = 0.8):
-        """Run `step` back to back for `seconds` while sampling. The sampler
-        thread is left running, so the caller goes straight on to its warmup
-        and timed steps: an idle gap of a few milliseconds here (joining the
-        thread) lets the clock drop, and the next ~10 ms of steps then run
-        up to 20 % slower while it climbs back. finish() stops the sampler and
-        keeps the samples of the last `tail` seconds of this load."""
+        """Run `step` back to back for `seconds` while sampling, and go on
+        running it until the sampler thread has stopped, so that the caller
+        goes straight on to its warmup and timed steps: an idle gap of a few
+        milliseconds here lets the clock drop, and the next ~10 ms of steps
+        then run up to 20 % slower while it climbs back. finish() keeps the
+        samples of the last `tail` seconds of the sampled load."""
         import torch
-        self._samples, self._run = [], [True]
+        self._samples, stop = [], threading.Event()
 
         def loop():
-            while self._run[0]:
+            while not stop.is_set():
                 v, src = self._read()
                 if v is not None:
                     self._samples.append((time.perf_counter(), v, src, self._power()))
-                time.sleep(0.005)
+                stop.wait(0.005)
 
         self._thread = None
         if self._handle is not None:
@@ -184,11 +184,18 @@ class ClockSampler:
                 step()
             torch.cuda.synchronize()
         self._t_end, self._tail = time.perf_counter(), tail
+        # Stop the sampler, keeping the load on until it has exited: its amd-smi
+        # calls would compete with the timed steps' launches, and waiting for
+        # it with the GPU idle would let the clock drop.
+        stop.set()
+        while self._thread is not None and self._thread.is_alive():
+            for _ in range(8):
+                step()
+            torch.cuda.synchronize()
 
     def finish(self):
         if self._thread is None:
             return
-        self._run[0] = False
         self._thread.join()
         self._thread = None
         lo, hi = self._t_end - self._tail, self._t_end
