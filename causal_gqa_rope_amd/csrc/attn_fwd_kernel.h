@@ -1431,6 +1431,17 @@ __device__ __forceinline__ void run_unit(const AttnArgs& a, int tok0, int L, int
     UnitFast<C>::run(a, tok0, L, qb, head0, lse_b, lse_h, img0, img_kvs, ks0, ks1, vs0, vs1, qst);
 }
 
+// Ranks (query blocks, lightest first) of a causal dense call with once-
+// rotated keys that are claimed at run time rather than placed by workgroup
+// index: the lightest quarter.
+__host__ __device__ constexpr int kfwd_dyn_ranks(int nQ) { return nQ / 4 > 1 ? nQ / 4 : 1; }
+// The claim counter: the int after the tile images in the workspace.
+template <class C>
+__device__ __forceinline__ int* fwd_dyn_counter(const AttnArgs& a) {
+  const long n_img = (long)a.B * a.KV * ((a.T + C::BN - 1) / C::BN);
+  return (int*)((char*)a.krot + n_img * C::K_IMG);
+}
+
 // Dense batch: one workgroup per unit (entry, K/V group, hp heads of the
 // group, query block). Heavy units (late query blocks, which see the most
 // keys under the causal mask) are issued first, and when the (batch, kv-head)
@@ -1446,11 +1457,42 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void attn_fwd_dense_kernel(Attn
   const int G = a.H / a.KV, GH = G / a.hp, groups = a.B * a.KV;
   const int u = blockIdx.x;
   int rank, g, hq;
+  bool claimed = false;
+  if constexpr (C::KPRE && C::CAUSAL && !C::WIN) {
+    // The lightest quarter of the ranks goes to whichever XCD gets there
+    // first: the XCDs run at different clocks (5-6 % apart under this load),
+    // and with every unit placed by workgroup index (XCD u % 8) the slowest
+    // one sets the kernel's end. The grid has two workgroups for each such
+    // unit; each claims the next unit from a counter at the end of the
+    // workspace (zeroed by krot_kernel) or exits when none is left, and the
+    // last claimer sets the counter back to zero for the next call.
+    const int per_rank = groups * GH, R0 = nQ - kfwd_dyn_ranks(nQ);
+    const int S = R0 * per_rank, dyn = (nQ - R0) * per_rank;
+    if (u >= S) {
+      __shared__ int claim;
+      if (threadIdx.x == 0) {
+        int* ctr = fwd_dyn_counter<C>(a);
+        const int d = atomicAdd(ctr, 1);
+        if (d == 2 * dyn - 1) atomicExch(ctr, 0);
+        claim = d;
+      }
+      __syncthreads();
+      const int d = claim;
+      if (d >= dyn) return;
+      rank = R0 + d / per_rank;
+      const int rem = d - (rank - R0) * per_rank;
+      g = rem / GH;
+      hq = rem - g * GH;
+      claimed = true;
+    }
+  }
   // The items of a rank are rotated by the rank: an XCD deals its workgroups
   // out over its shader engines in turn, and a fixed order would hand one
   // engine the same (entry, heads) item rank after rank (all the long entry's
   // work, in a batch of mixed lengths).
-  if ((groups & 7) == 0) {
+  if (claimed) {
+    // placed above
+  } else if ((groups & 7) == 0) {
     const int x = u & 7, i = u >> 3, per = (groups >> 3) * GH;
     rank = i / per;
     const int rem = (i - rank * per + rank) % per;
@@ -1523,6 +1565,7 @@ __global__ __launch_bounds__(256) void krot_kernel(AttnArgs a) {
   const long bt = item / BN;  // b * n_img + tile
   const int tile = (int)(bt % n_img), b = (int)(bt / n_img);
   const int t = tile * BN + r;
+  if (tid == 0) *fwd_dyn_counter<C>(a) = 0;  // the attention kernel's claim counter
   const int L = a.seqlens == nullptr ? a.T : min(max(a.seqlens[b], 0), a.T);
   const bool ok = t < L;
   f32x4 c[2], s[2];
@@ -1629,6 +1672,11 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int
     hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (C::CAUSAL && !C::WIN) {
+    // Two workgroups for every claimed unit (see attn_fwd_dense_kernel).
+    const int bm = 32 * C::NW / a.hp, nQ = (a.T + bm - 1) / bm;
+    grid += kfwd_dyn_ranks(nQ) * a.B * (a.H / a.hp);
   }
   if (phases & PHASE_ATTEND)
     hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);

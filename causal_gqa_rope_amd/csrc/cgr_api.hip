@@ -503,12 +503,12 @@ cgr_status cgr_gqa_rope_attn_fwd_rotated(const void* q, const void* k, const voi
                                          cgr_dtype dtype, const float* rope_cos, const float* rope_sin,
                                          int rope_max_pos, cgr_rope_style style, cgr_mask mask, int window,
                                          float softmax_scale, cgr_qk_operand qk_operand,
-                                         const int32_t* seqlens, const void* workspace,
+                                         const int32_t* seqlens, void* workspace,
                                          size_t workspace_bytes, void* stream) {
   if (dtype != CGR_BF16) return fail(CGR_ERR_UNSUPPORTED, "keys are rotated once for CGR_BF16 I/O only");
   if (workspace == nullptr) return fail(CGR_ERR_WORKSPACE, "the rotated keys need a workspace");
   return dense_fwd(q, k, v, o, lse, B, T, n_head, n_kv_head, head_dim, dtype, rope_cos, rope_sin, rope_max_pos,
-                   style, mask, window, softmax_scale, qk_operand, seqlens, const_cast<void*>(workspace),
+                   style, mask, window, softmax_scale, qk_operand, seqlens, workspace,
                    workspace_bytes, stream, cgr::PHASE_ATTEND);
 }
 
@@ -516,7 +516,8 @@ size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim) {
   if (B < 1 || T < 1 || n_kv_head < 1) return 0;
   if (head_dim != 32 && head_dim != 64 && head_dim != 128 && head_dim != 256) return 0;
   const int bn = cgr::fwd_tile_keys(head_dim);
-  return (size_t)B * n_kv_head * ((T + bn - 1) / bn) * cgr::fwd_kimg_bytes(head_dim);
+  // The tile images, then 256 bytes that hold the attention kernel's work counter.
+  return (size_t)B * n_kv_head * ((T + bn - 1) / bn) * cgr::fwd_kimg_bytes(head_dim) + 256;
 }
 
 size_t cgr_attn_fwd_fp8_workspace_size(int B, int T, int n_kv_head, int head_dim) {

@@ -30,11 +30,12 @@ __device__ __forceinline__ void tile_to_lds(rsrc_t rs, char* lds, int gstride, i
 template <int D, int ROWS, int NWG>
 struct TileCopy {
   static constexpr int NCH = D / 8;
-  static constexpr int NI = ROWS * NCH / 64;  // 1 KiB wave loads
-  static constexpr int PER = NI / NWG;        // loads per wave
-  static_assert(ROWS * NCH % 64 == 0 && NI % NWG == 0, "whole wave loads, evenly per wave");
+  static constexpr int NI = ROWS * NCH / 64;         // 1 KiB wave loads
+  static constexpr int PER = (NI + NWG - 1) / NWG;   // loads per wave, at most
+  static_assert(ROWS * NCH % 64 == 0, "whole wave loads");
   int wig;
   int voff[PER];
+  __device__ __forceinline__ bool has(int k) const { return NI % NWG == 0 || wig + k * NWG < NI; }
   __device__ __forceinline__ TileCopy(int wig_, int gstride, int lane) : wig(wig_) {
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -44,7 +45,8 @@ struct TileCopy {
   }
   __device__ __forceinline__ void operator()(rsrc_t rs, char* lds, int soff) const {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) buf_load16_lds(rs, lds + (wig + k * NWG) * 1024, voff[k], soff);
+    for (int k = 0; k < PER; ++k)
+      if (has(k)) buf_load16_lds(rs, lds + (wig + k * NWG) * 1024, voff[k], soff);
   }
 };
 

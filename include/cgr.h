@@ -110,9 +110,10 @@ CGR_API cgr_status cgr_rope_tables(int max_pos, int head_dim, double base, float
 /*
  * Bytes of the optional workspace of cgr_gqa_rope_attn_fwd (bf16 I/O): the
  * rotated keys in the Q.K^T operand type as tiles of BN keys (BN = 64, 32 for
- * head_dim 256) in the layout the kernel's LDS holds them:
- * B * n_kv_head * ceil(T / BN) * BN * head_dim * 2. Returns 0 for invalid
- * sizes.
+ * head_dim 256) in the layout the kernel's LDS holds them, then 256 bytes for
+ * the attention kernel's work counter (zero between calls):
+ * B * n_kv_head * ceil(T / BN) * BN * head_dim * 2 + 256. Returns 0 for
+ * invalid sizes.
  */
 CGR_API size_t cgr_attn_fwd_workspace_size(int B, int T, int n_kv_head, int head_dim);
 
@@ -173,8 +174,11 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd(const void* q, const void* k, const voi
  *   CGR_ERR_WORKSPACE); the other checks are those of the forward.
  *
  * cgr_gqa_rope_attn_fwd_rotated: the attention of cgr_gqa_rope_attn_fwd over
- *   the keys cgr_attn_fwd_rotate_keys left in `workspace` (which this call
- *   only reads). Every argument means what it means for the forward; k,
+ *   the keys cgr_attn_fwd_rotate_keys left in `workspace`. The call reads the
+ *   keys and uses the workspace's last 256 bytes for a work counter, which
+ *   cgr_attn_fwd_rotate_keys zeroes and every call leaves at zero: calls
+ *   that share a workspace may follow one another but must not overlap
+ *   (they would race on the counter). Every argument means what it means for the forward; k,
  *   rope_cos/rope_sin, rope_style, qk_operand and seqlens must be those the
  *   keys were rotated with (the kernel cannot tell, and other values give a
  *   wrong result, not an error). k is still read where a unit recomputes its
@@ -191,7 +195,7 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_rotated(const void* q, const void* k, c
                                          const float* rope_sin, int rope_max_pos, cgr_rope_style style,
                                          cgr_mask mask, int window, float softmax_scale,
                                          cgr_qk_operand qk_operand, const int32_t* seqlens,
-                                         const void* workspace, size_t workspace_bytes, void* stream);
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of the workspace of cgr_gqa_rope_attn_fwd_fp8: the rotated keys and
