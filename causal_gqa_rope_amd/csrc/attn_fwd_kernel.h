@@ -151,13 +151,6 @@ struct Cfg {
   // reach of the 16-bit offsets of the LDS instructions.
   static constexpr int Q_STRIDE = 2 * D + 16;
   static constexpr int Q_STAGE_BYTES = F32 ? 0 : NW * 32 * Q_STRIDE;
-  // Units of at most 64 rows (head_dim <= 128) stage the cos/sin rows of their
-  // query positions once for all their waves (the waves of a row block share
-  // them): cos, then sin, bm rows of 2*D bytes each, in the second V stage
-  // (free until the first tile's products are issued) and, for 64-row units,
-  // sin in this much more dynamic LDS after the Q staging.
-  static constexpr int TAB_EXTRA = (F32 || WIDE) ? 0 : 64 * 2 * D;
-  static constexpr int DYN_LDS = Q_STAGE_BYTES + TAB_EXTRA;
 
   // Loader work items. K: (row, 8-element group g < D/16), which carries the
   // group pair (g, g + D/16) so that both RoPE pairings find their partners.
@@ -649,62 +642,26 @@ struct UnitFast {
     char* const q_stage = qst + wave * 32 * C::Q_STRIDE;
     u32x4 q_raw[QI][Q_HALF ? 2 : 1];
     f32x4 q_cos[QI][Q_HALF ? 2 : 1], q_sin[QI][Q_HALF ? 2 : 1];
-    // Units of at most 64 rows: the cos/sin rows of the unit's positions are
-    // loaded once, straight into LDS (tab_cos, tab_sin: rows of 2*D bytes), and
-    // every wave reads its rows from there; otherwise each wave loads its own.
-    const bool share_tab = !C::WIDE && bm <= 64;
-    char* const tab_cos = vs1;
-    char* const tab_sin = 2 * bm * 2 * D <= C::V_BYTES ? vs1 + bm * 2 * D : qst + C::Q_STAGE_BYTES;
-    // The prologue's loads go out in this order: the shared table rows
-    // (issue_tab), the first K and V tiles, the Q rows (issue_q), so that
-    // waiting for the table rows (tab_ready) does not wait for anything
-    // fetched from HBM.
-    auto issue_tab = [&]() {
-      if (share_tab) {
-        // 1-KiB direct loads, RPL rows each: load u of bm / RPL per table.
-        constexpr int RPL = 1024 / (2 * D);
-        const int per = bm / RPL;
-        for (int u = wave; u < 2 * per; u += NW) {
-          const int t = u >= per, blk = u - t * per;
-          buf_load16_lds(t ? rs : rc, (t ? tab_sin : tab_cos) + blk * 1024, lane * 16, (q0 + blk * RPL) * 2 * D);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
+    // The prologue's loads go out in this order: the first K and V tiles,
+    // then the Q rows and their cos/sin rows (issue_q), so the tiles, read
+    // from L2, are in flight while the Q rows come from HBM.
     auto issue_q = [&]() {
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
         const int row = qw0 + r;  // rows past the sequence read as zeros (buffer range)
         const int qo = row * qs * 2 + c * 16, to = row * (D / 2) * 4;
         q_raw[i][0] = buf_load16(rq, qo, 0);
-        if constexpr (Q_HALF) q_raw[i][1] = buf_load16(rq, qo + D, 0);
-        if (!share_tab) {
-          if constexpr (Q_HALF) {
-            q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
-            q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
-            q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
-            q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
-          } else {
-            q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
-            q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
-          }
+        if constexpr (Q_HALF) {
+          q_raw[i][1] = buf_load16(rq, qo + D, 0);
+          q_cos[i][0] = buf_load16f(rc, to + c * 32, 0);
+          q_cos[i][1] = buf_load16f(rc, to + c * 32 + 16, 0);
+          q_sin[i][0] = buf_load16f(rs, to + c * 32, 0);
+          q_sin[i][1] = buf_load16f(rs, to + c * 32 + 16, 0);
+        } else {
+          q_cos[i][0] = buf_load16f(rc, to + c * 16, 0);
+          q_sin[i][0] = buf_load16f(rs, to + c * 16, 0);
         }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // The shared table rows have landed once at most as many loads as every
-    // wave issued after them are outstanding (at least K_MIN + V_MIN 1-KiB
-    // loads of the first tiles, then the Q rows); then every wave's rows are
-    // in LDS. (No full __syncthreads: it would wait for the Q rows too.)
-    constexpr int K_MIN = C::KPRE ? (C::K_IMG / 1024) / NW : 0, V_MIN = (C::V_BYTES / 1024) / NW;
-    auto tab_ready = [&]() {
-      __builtin_amdgcn_sched_barrier(0);
-      if (share_tab) {
-        wait_vmem_le<QI * (Q_HALF ? 2 : 1) + K_MIN + V_MIN>();
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
       }
     };
     Frag<QK> qf[C::KSTEPS];
@@ -741,19 +698,6 @@ struct UnitFast {
       }
     };
     auto stage_q = [&]() {
-      if (share_tab) {
-#pragma unroll
-        for (int i = 0; i < QI; ++i) {
-          const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
-          const int to = (wrow * 32 + r) * 2 * D + c * (Q_HALF ? 32 : 16);
-          q_cos[i][0] = *(const f32x4*)(tab_cos + to);
-          q_sin[i][0] = *(const f32x4*)(tab_sin + to);
-          if constexpr (Q_HALF) {
-            q_cos[i][1] = *(const f32x4*)(tab_cos + to + 16);
-            q_sin[i][1] = *(const f32x4*)(tab_sin + to + 16);
-          }
-        }
-      }
 #pragma unroll
       for (int i = 0; i < QI; ++i) {
         const int flat = i * 64 + lane, r = flat / QI_PER_ROW, c = flat % QI_PER_ROW;
@@ -1224,12 +1168,10 @@ struct UnitFast {
       u32x4 kw1[KI][2];
       f32x4 kc1[KI][2], ksn1[KI][2];
       // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
-      issue_tab();
       load_k(jl * BN, ks0, kw, kc, ksn);
       load_v(jl * BN, vs0, vw);
       if (n_it > 1) load_k(tl(1) * BN, ks1, kw1, kc1, ksn1);
       issue_q();
-      tab_ready();
       stage_q();
       store_k(jl * BN, ks0, kw, kc, ksn, vw);
       wait_vmem();
@@ -1310,12 +1252,10 @@ struct UnitFast {
         u32x4 kw1[KI][2];
         f32x4 kc1[KI][2], ksn1[KI][2];
         // (Each workgroup runs one unit: its LDS has no earlier users to wait for.)
-        issue_tab();
         load_k(0, ks0, kw, kc, ksn);
         load_v(0, vs0, vw);
         if (n_tiles > 1) load_k(BN, ks1, kw1, kc1, ksn1);
         issue_q();
-        tab_ready();
         stage_q();
         store_k(0, ks0, kw, kc, ksn, vw);
         wait_vmem();
@@ -1652,10 +1592,10 @@ __global__ __launch_bounds__(kPrepThreads) void varlen_prep_kernel(AttnArgs a) {
 template <class C>
 hipError_t launch_attn(const AttnArgs& a, bool varlen, int grid, hipStream_t stream) {
   if (varlen)
-    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS,
+    hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
                        stream, a);
   else
-    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS,
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES,
                        stream, a);
   return hipGetLastError();
 }
@@ -1679,7 +1619,7 @@ hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int
     grid += kfwd_dyn_ranks(nQ) * a.B * (a.H / a.hp);
   }
   if (phases & PHASE_ATTEND)
-    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
+    hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
   return hipGetLastError();
 }
 
@@ -1692,7 +1632,7 @@ hipError_t launch_attn_kpre_varlen(const AttnArgs& a, int grid, hipStream_t stre
                      dim3(kPrepThreads), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
+  hipLaunchKernelGGL(attn_fwd_varlen_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
   return hipGetLastError();
 }
 
@@ -1721,7 +1661,7 @@ constexpr long fwd_kimg_bytes(int head_dim) { return (long)fwd_tile_keys(head_di
 
 template <class C>
 hipError_t launch_attn_dense(const AttnArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::DYN_LDS, stream, a);
+  hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
   return hipGetLastError();
 }
 

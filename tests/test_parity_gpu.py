@@ -492,8 +492,8 @@ def test_longest_sequence_the_offsets_allow(gpu):
 
 HEAD_PACKED = [
     # d, H, KV, style, causal, window: units of 32 rows x 8 heads (G = 8) and of
-    # 64 rows x 4 heads (G = 4), whose waves share the cos/sin rows of their
-    # positions through LDS
+    # 64 rows x 4 heads (G = 4), whose waves rotate the same positions of
+    # several heads
     (32, 8, 1, "interleaved", True, 0),
     (32, 8, 2, "half", True, 0),
     (64, 8, 1, "half", True, 0),
@@ -509,10 +509,9 @@ HEAD_PACKED = [
 @pytest.mark.parametrize("d,H,KV,style,causal,window", HEAD_PACKED,
                          ids=[f"d{e[0]}-G{e[1] // e[2]}-{e[3]}-c{int(e[4])}-w{e[5]}" for e in HEAD_PACKED])
 def test_head_packed_units(gpu, d, H, KV, style, causal, window):
-    """Units whose waves cover several heads of one row block (they stage the
-    positions' cos/sin rows once for all of them): a dense batch with a ragged
-    tail and a packed batch with empty and one-token sequences, element by
-    element against the oracle."""
+    """Units whose waves cover several heads of one row block: a dense batch
+    with a ragged tail (the small-grid units) and a packed batch with empty and
+    one-token sequences, element by element against the oracle."""
     announce(f"head-packed units d={d} H={H} KV={KV} {style} causal={causal} window={window}")
     w = W.custom("head_packed", B=2, T=300, n_head=H, n_kv_head=KV, head_dim=d, dtype="bf16", causal=causal,
                  rope_style=style, base=1e4, seed=d + H + 7 * KV + window)
