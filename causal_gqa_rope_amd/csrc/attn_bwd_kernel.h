@@ -79,7 +79,24 @@ struct BwdArgs {
   int window;    // > 0 (causal only): keys 0 <= i - j < window; 0: none
   float qscale;  // scale * log2(e)
   float scale;
+  // Dense causal calls: claim counters of the dk/dv ([0]) and dq ([1])
+  // kernels' lightest ranks (zeroed by bwd_prep_kernel; see claim_unit).
+  int32_t* ctr;
 };
+
+// The lightest ranks of a dense causal backward kernel (a quarter of them,
+// kfwd_dyn_ranks) are not placed by workgroup index: the workgroups past the
+// statically placed ones (two for each such unit) claim them in order from a
+// counter, so an XCD that runs ahead of the others (their clocks differ by
+// 5-6 % under load) takes more of them. Returns the claim's number: the index
+// of the claimed unit among those units, or a number past them when none is
+// left. Each of those workgroups calls it once, with all its threads.
+__device__ __forceinline__ int claim_unit(int32_t* ctr) {
+  __shared__ int claim;
+  if (threadIdx.x == 0) claim = atomicAdd(ctr, 1);
+  __syncthreads();
+  return claim;
+}
 
 constexpr int kBwdTileRows = 32;  // rows per ld tile
 // Query heads per dk/dv unit: with G > 4 (MQA, few K/V heads) a K/V head's
@@ -124,6 +141,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   const long nq = (long)a.B * Tp * a.H * IPR;
   const long nk = (long)a.B * a.T * a.KV * IPR;
   const int g = (int)(tid % IPR);
+  if (tid == 0) a.ctr[0] = a.ctr[1] = 0;  // the claim counters of the two gradient kernels
   if (tid < nq) {
     const long row = tid / IPR;  // ((b * Tp + t) * H + h)
     const int h = (int)(row % a.H);
@@ -346,7 +364,13 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dkdv_kernel(BwdArgs a) {
     // keeps whole groups, whose queries it then streams through one L2.
     const int groups = a.B * a.KV;
     int rank, gsel;
-    if ((groups & 7) == 0) {
+    const int nK = (a.T + C::BK - 1) / C::BK, R0 = nK - kfwd_dyn_ranks(nK);
+    if (C::CAUSAL && !C::WIN && a.hsplit == 1 && u >= R0 * groups) {
+      const int d = claim_unit(a.ctr);
+      if (d >= (nK - R0) * groups) return;
+      rank = R0 + d / groups;
+      gsel = d - (rank - R0) * groups;
+    } else if ((groups & 7) == 0) {
       const int x = u & 7, i = u >> 3, per = groups >> 3;
       rank = i / per;
       gsel = (i - rank * per) * 8 + x;
@@ -673,7 +697,15 @@ __global__ __launch_bounds__(512, 2) void attn_bwd_dq_kernel(BwdArgs a) {
     const int nQ = (a.T + BQ - 1) >> lbq;
     const int groups = a.B * a.KV;
     int rank, gsel;
-    if ((groups & 7) == 0) {
+    const int R0 = nQ - kfwd_dyn_ranks(nQ);
+    if (C::CAUSAL && !C::WIN && u >= R0 * groups * NHG) {
+      const int d = claim_unit(a.ctr + 1);
+      if (d >= (nQ - R0) * groups * NHG) return;
+      rank = R0 + d / (groups * NHG);
+      const int rem = d - (rank - R0) * groups * NHG;
+      gsel = rem / NHG;
+      hg = rem - gsel * NHG;
+    } else if ((groups & 7) == 0) {
       const int x = u & 7, i = u >> 3, per = (groups >> 3) * NHG;
       rank = i / per;
       const int rem = i - rank * per;
@@ -844,8 +876,14 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
                        dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)(k_units * a.KV * a.hsplit)), dim3(512), 0, stream,
-                     a);
+  long dkdv_grid = k_units * a.KV * a.hsplit, dq_grid = q_units * (a.H >> a.lhp);
+  if (!a.cu_seqlens && C::CAUSAL && !C::WIN) {
+    // Two workgroups for every claimed unit (claim_unit).
+    const int nK = (a.T + C::BK - 1) / C::BK, nQ = (a.T + (C::BQ >> a.lhp) - 1) / (C::BQ >> a.lhp);
+    if (a.hsplit == 1) dkdv_grid += (long)kfwd_dyn_ranks(nK) * a.B * a.KV;
+    dq_grid += (long)kfwd_dyn_ranks(nQ) * a.B * (a.H >> a.lhp);
+  }
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)dkdv_grid), dim3(512), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.hsplit > 1) {
@@ -855,7 +893,7 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3((unsigned)(q_units * (a.H >> a.lhp))), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel<C>, dim3((unsigned)dq_grid), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

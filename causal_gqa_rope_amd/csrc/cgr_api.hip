@@ -155,7 +155,7 @@ long varlen_max_items(int num_seqs, int total_tokens) {
 // per K/V head) the dk/dv units' f32 partial sums; each part starts on a
 // 256-byte boundary.
 struct BwdLayout {
-  size_t qr, kr, ld, part, total;
+  size_t qr, kr, ld, part, ctr, total;
   int hsplit;
 };
 int bwd_hsplit(int n_head, int n_kv_head) {
@@ -170,8 +170,11 @@ BwdLayout bwd_layout_rows(size_t rows, size_t ld_tiles, int n_head, int n_kv_hea
   l.ld = l.kr + up(rows * n_kv_head * head_dim * 2);
   l.part = l.ld + up(ld_tiles * 64 * 4);
   l.hsplit = bwd_hsplit(n_head, n_kv_head);
-  l.total = l.hsplit > 1 ? l.part + 2 * (size_t)l.hsplit * rows * n_kv_head * head_dim * 4
-                         : l.ld + ld_tiles * 64 * 4;
+  const size_t end = l.hsplit > 1 ? l.part + 2 * (size_t)l.hsplit * rows * n_kv_head * head_dim * 4
+                                  : l.ld + ld_tiles * 64 * 4;
+  // Then 256 bytes for the gradient kernels' claim counters.
+  l.ctr = up(end);
+  l.total = l.ctr + 256;
   return l;
 }
 BwdLayout bwd_layout(int B, int T, int n_head, int n_kv_head, int head_dim) {
@@ -244,6 +247,7 @@ cgr_status bwd_launch(cgr::BwdArgs& a, const void* q, const void* k, const void*
   }
   a.part_rows = rows;
   a.part = (float*)((char*)workspace + lay.part);
+  a.ctr = (int32_t*)((char*)workspace + lay.ctr);
   a.window = window;
   const double scale = softmax_scale > 0.f ? (double)softmax_scale : 1.0 / std::sqrt((double)head_dim);
   a.scale = (float)scale;

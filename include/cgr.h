@@ -295,7 +295,8 @@ CGR_API cgr_status cgr_gqa_rope_attn_fwd_varlen(const void* q, const void* k, co
  * (0 for invalid sizes): the rotated q and k in the Q.K^T operand type plus
  * two floats per query row and head; with more than 4 query heads per K/V
  * head, also f32 partial sums of dk and dv, 2 * ceil(G / 4) * B * T *
- * n_kv_head * head_dim floats (G = n_head / n_kv_head).
+ * n_kv_head * head_dim floats (G = n_head / n_kv_head); then 256 bytes for
+ * the gradient kernels' work counters.
  */
 CGR_API size_t cgr_attn_bwd_workspace_size(int B, int T, int n_head, int n_kv_head, int head_dim);
 
@@ -340,7 +341,8 @@ CGR_API cgr_status cgr_gqa_rope_attn_bwd(const void* q, const void* k, const voi
  * type plus two floats per head for every row of ceil(total_tokens / 32) +
  * num_seqs slots of 32 rows (each sequence starts a slot of its own); with
  * more than 4 query heads per K/V head, also 2 * ceil(G / 4) * total_tokens *
- * n_kv_head * head_dim floats of partial sums, as for the dense call.
+ * n_kv_head * head_dim floats of partial sums, and 256 bytes of counters,
+ * as for the dense call.
  */
 CGR_API size_t cgr_attn_bwd_varlen_workspace_size(int num_seqs, int total_tokens, int n_head, int n_kv_head,
                                                   int head_dim);

@@ -302,13 +302,13 @@ def test_backward_workspace_size():
     assert lib.cgr_attn_bwd_workspace_size(0, 16, 4, 2, 64) == 0
     assert lib.cgr_attn_bwd_workspace_size(1, 16, 4, 0, 64) == 0
     # rotated q and k (2 bytes each) on 256-byte boundaries, then 2 floats per
-    # (head, row) over rows padded to 32
+    # (head, row) over rows padded to 32, then 256 bytes of claim counters
     n = lib.cgr_attn_bwd_workspace_size(2, 100, 8, 2, 128)
-    assert n == 2 * 100 * 8 * 128 * 2 + 2 * 100 * 2 * 128 * 2 + 2 * 8 * 4 * 64 * 4
+    assert n == 2 * 100 * 8 * 128 * 2 + 2 * 100 * 2 * 128 * 2 + 2 * 8 * 4 * 64 * 4 + 256
     # more than 4 query heads per K/V head (G = 16): f32 partial sums of dk
     # and dv for ceil(16 / 4) = 4 head groups follow the per-tile values
     n = lib.cgr_attn_bwd_workspace_size(1, 100, 16, 1, 64)
-    assert n == 100 * 16 * 64 * 2 + (100 * 64 * 2 + 255) // 256 * 256 + 16 * 4 * 64 * 4 + 2 * 4 * 100 * 64 * 4
+    assert n == 100 * 16 * 64 * 2 + (100 * 64 * 2 + 255) // 256 * 256 + 16 * 4 * 64 * 4 + 2 * 4 * 100 * 64 * 4 + 256
 
 
 def backward(**kw):
@@ -353,14 +353,15 @@ def test_backward_varlen_workspace_size():
     assert lib.cgr_attn_bwd_varlen_workspace_size(1, -1, 4, 2, 64) == 0
     assert lib.cgr_attn_bwd_varlen_workspace_size(1, 16, 4, 0, 64) == 0
     # rotated q and k over the packed rows on 256-byte boundaries, then 2
-    # floats per (head, row) over ceil(total / 32) + num_seqs slots of 32 rows
+    # floats per (head, row) over ceil(total / 32) + num_seqs slots of 32 rows,
+    # then 256 bytes of claim counters
     up = lambda x: (x + 255) // 256 * 256
     n = lib.cgr_attn_bwd_varlen_workspace_size(3, 100, 8, 2, 128)
-    assert n == up(100 * 8 * 128 * 2) + up(100 * 2 * 128 * 2) + 8 * (4 + 3) * 64 * 4
+    assert n == up(100 * 8 * 128 * 2) + up(100 * 2 * 128 * 2) + 8 * (4 + 3) * 64 * 4 + 256
     n = lib.cgr_attn_bwd_varlen_workspace_size(2, 33, 4, 1, 64)
-    assert n == up(33 * 4 * 64 * 2) + up(33 * 1 * 64 * 2) + 4 * (2 + 2) * 64 * 4
+    assert n == up(33 * 4 * 64 * 2) + up(33 * 1 * 64 * 2) + 4 * (2 + 2) * 64 * 4 + 256
     n = lib.cgr_attn_bwd_varlen_workspace_size(2, 33, 6, 1, 64)  # G = 6: two head groups
-    assert n == up(33 * 6 * 64 * 2) + up(33 * 1 * 64 * 2) + up(6 * (2 + 2) * 64 * 4) + 2 * 2 * 33 * 64 * 4
+    assert n == up(33 * 6 * 64 * 2) + up(33 * 1 * 64 * 2) + up(6 * (2 + 2) * 64 * 4) + 2 * 2 * 33 * 64 * 4 + 256
 
 
 def backward_varlen(**kw):
