@@ -3,8 +3,9 @@
 One step = one pass of the whole hot path over one batch of synthetic input:
 build the RoPE cos/sin tables, then run the fused forward (RoPE on Q/K tiles,
 online softmax, O and LSE) on the long-context workload B=1, T=8192,
-n_head=32, n_kv_head=8, head_dim=128, bf16 I/O, RoPE base 500000, causal.
-Inputs are already resident in HBM when the timed region starts.
+n_head=32, n_kv_head=8, head_dim=128, bf16 I/O, RoPE base 500000, causal,
+with both products (Q.K^T and P.V) on bf16 matrix-core operands. Inputs are
+already resident in HBM when the timed region starts.
 
 Prints one JSON line. `value` is algorithmic TFLOP/s of the step (causal
 FLOPs counted exactly: 4*d per visible (query, key) pair per query head).
@@ -15,14 +16,15 @@ cgr_gqa_rope_attn_fwd_rotated: the kernels and bits of one
 cgr_gqa_rope_attn_fwd call) so that the attention kernel has HIP events of
 its own. `roofline` reports that kernel alone: its mean launch duration (and
 median) from those events on the launch stream, against the MI355X dense
-f16/bf16 MFMA peak, with the whole call beside it and the graphics clock
-sampled from amd-smi meanwhile; `traffic` is HBM bytes per launch from rocprofv3
+bf16 MFMA peak, with the whole call beside it and the graphics clock
+sampled from amd-smi meanwhile, and the same kernel with the library's
+default f16 Q.K^T operand (`roofline.f16_operands`); `traffic` is HBM bytes per launch from rocprofv3
 counters (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size),
 read from profiles/ and reported only while the kernel sources still hash to
 the value recorded with them. `cpu_baseline` times the float64 oracle on a
 bounded sample of the same workload on this host's cores.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--qk bf16|f16]
   python bench.py --copy-calibration   (plain copies, for counter scaling)
   python bench.py --all-configs        (one JSON line per workload configuration,
                                         attention call only; not the headline line;
@@ -44,6 +46,9 @@ bounded sample of the same workload on this host's cores.
   python bench.py --padded             (the forward line on a right-padded batch of 4 x 8192
                                         tokens, valid lengths U[2048, 8192]; FLOPs over the
                                         valid tokens; not the headline line)
+--qk sets the forward line's Q.K^T operand type: bf16 by default for the
+headline line, the library's default f16 for the --window, --wide and --padded
+lines.
 """
 
 from __future__ import annotations
@@ -80,8 +85,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, if still current."""
+def read_traffic(qk: str = "bf16"):
+    """HBM bytes per launch from the committed counter summary, if still current
+    and taken on the attention kernel with this Q.K^T operand type."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     kv = {}
@@ -89,7 +95,7 @@ def read_traffic():
         if ":" in ln and not ln.startswith("#"):
             key, val = ln.split(":", 1)
             kv[key.strip()] = val.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_hash():
+    if kv.get("kernel_source_sha256") != kernel_source_hash() or kv.get("qk_operand", "f16") != qk:
         return None
     try:
         return int(float(kv["hbm_bytes_per_launch"]))
@@ -773,6 +779,8 @@ def main() -> int:
                     help="head_dim 256: B=1 T=8192 H=16 KV=8 (the long-context width in wider heads)")
     ap.add_argument("--padded", action="store_true",
                     help="right-padded dense batch: B=4 entries of T=8192, valid lengths U[2048, 8192]")
+    ap.add_argument("--qk", choices=("bf16", "f16"), default=None,
+                    help="the forward's Q.K^T operand type (default: bf16 for the headline line, else f16)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -836,11 +844,18 @@ def main() -> int:
     # The forward with a workspace, in its two halves (the same kernels and bits
     # as one cgr_gqa_rope_attn_fwd call): the key rotation, then the attention
     # kernel alone between its own pair of HIP events.
+    headline = args.window == 0 and not args.padded and not args.wide
+    # The headline line computes both products on bf16 operands, the type the
+    # method's statement names; the library's default Q.K^T operand is f16 (three
+    # more mantissa bits, for inputs with large keys), measured beside it.
+    qk = args.qk or ("bf16" if headline else "f16")
+
     def rotate():
-        cgr.attn_fwd_rotate_keys(k, cos, sin, ws, **kw)
+        cgr.attn_fwd_rotate_keys(k, cos, sin, ws, qk_operand=qk, **kw)
 
     def attention():
-        cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws, causal=True, window=args.window, out=o, lse=lse, **kw)
+        cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws, causal=True, window=args.window, out=o, lse=lse,
+                                      qk_operand=qk, **kw)
 
     def step():
         tables()
@@ -880,25 +895,22 @@ def main() -> int:
     kernel_ms, kernel_med = sum(kern) / len(kern), statistics.median(kern)
     call_ms, call_med = sum(call) / len(call), statistics.median(call)
     achieved = flops / (kernel_ms * 1e-3) / 1e12
-    headline = args.window == 0 and not args.padded and not args.wide
-    traffic = read_traffic() if headline else None
-    clock_f16 = clock.summary()
+    traffic = read_traffic(qk) if headline else None
+    clock_main = clock.summary()
 
-    # The same step with both products on bf16 operands (the operand type the
-    # method's statement names; the library's default Q.K^T operand is f16, for
-    # precision on inputs with large keys): the attention kernel alone, at its
-    # own sustained clock and power.
-    bf16_ops = None
+    # The same step with the other Q.K^T operand type: the attention kernel
+    # alone, at its own sustained clock and power.
+    other_ops, other = None, "f16" if qk == "bf16" else "bf16"
     if headline:
         ws_b = torch.empty_like(ws)
 
         def step_b():
             tables()
-            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand="bf16", **kw)
+            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand=other, **kw)
             attention_b()
 
         def attention_b():
-            cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws_b, causal=True, out=o, lse=lse, qk_operand="bf16",
+            cgr.gqa_rope_attn_fwd_rotated(q, k, v, cos, sin, ws_b, causal=True, out=o, lse=lse, qk_operand=other,
                                           **kw)
 
         evb = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
@@ -908,7 +920,7 @@ def main() -> int:
         torch.cuda.synchronize()
         for i in range(args.steps):
             tables()
-            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand="bf16", **kw)
+            cgr.attn_fwd_rotate_keys(k, cos, sin, ws_b, qk_operand=other, **kw)
             evb[i][0].record(stream)
             attention_b()
             evb[i][1].record(stream)
@@ -916,7 +928,7 @@ def main() -> int:
         clock.finish()
         kb = [a.elapsed_time(b) for a, b in evb]
         kb_ms = sum(kb) / len(kb)
-        bf16_ops = {"qk_operand": "bf16", "pv_operand": "bf16", "kernel_ms": round(kb_ms, 5),
+        other_ops = {"qk_operand": other, "pv_operand": "bf16", "kernel_ms": round(kb_ms, 5),
                     "kernel_ms_median": round(statistics.median(kb), 5),
                     "achieved": round(flops / (kb_ms * 1e-3) / 1e12, 3),
                     "frac": round(flops / (kb_ms * 1e-3) / 1e12 / PEAK_TFLOPS, 4),
@@ -933,12 +945,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16/bf16",
+        "dtype": "bf16" if qk == "bf16" else "f16/bf16",
         "data": "synthetic",
         "config": {
             "workload": w.name, "B": w.B, "T": w.T, "n_head": w.n_head, "n_kv_head": w.n_kv_head,
             "head_dim": w.head_dim, "rope_base": w.base, "rope_pairs": w.rope_style, "mask": "causal",
-            "io": "bf16", "qk_operand": "f16", "pv_operand": "bf16", "accumulate": "f32",
+            "io": "bf16", "qk_operand": qk, "pv_operand": "bf16", "accumulate": "f32",
             **({"valid_lengths": lens} if args.padded else {}),
             "step": "rope_tables + attn_fwd_rotate_keys + gqa_rope_attn_fwd_rotated (= gqa_rope_attn_fwd)",
             "before_warmup": "2 s of untimed steps (the clock_mhz sample), so the timed steps run at the sustained clock",
@@ -952,7 +964,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": f"attn_fwd_dense_kernel (head_dim {w.head_dim}, bf16 I/O, f16 QK, causal, {w.rope_style}); "
+            "kernel": f"attn_fwd_dense_kernel (head_dim {w.head_dim}, bf16 I/O, {qk} QK, causal, {w.rope_style}); "
                       "HIP events around its launch alone, on the launch stream",
             "kernel_ms": round(kernel_ms, 5),
             "kernel_ms_median": round(kernel_med, 5),
@@ -961,8 +973,8 @@ def main() -> int:
             "call_ms_median": round(call_med, 5),
             "call_tflops": round(flops / (call_ms * 1e-3) / 1e12, 3),
             "rotate_keys_ms": round(sum(rot) / len(rot), 5),
-            "clock_mhz": clock_f16,
-            **({"bf16_operands": bf16_ops} if bf16_ops else {}),
+            "clock_mhz": clock_main,
+            **({f"{other}_operands": other_ops} if other_ops else {}),
         },
         "cpu_baseline": None if args.no_cpu_baseline or not headline else cpu_baseline(inputs, w),
     }
