@@ -132,6 +132,30 @@ def test_backward_is_deterministic(gpu):
     assert torch.equal(dq1, dq2) and torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
 
 
+def test_backward_calls_share_one_workspace(gpu):
+    """The gradient kernels of a dense causal call hand their lightest blocks
+    out from counters at the workspace's end, which the prepass zeroes: a
+    workspace of 0xFF bytes used for two calls in a row (the second one
+    smaller) gives the bits of calls with a workspace of their own."""
+    KV, d = 2, 128
+    shapes = [(1000, 8), (300, 4)]
+    n = max(cgr.cgr_attn_bwd_workspace_size(1, T, H, KV, d) for T, H in shapes)
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=gpu)
+    for T, H in shapes:
+        w = W.custom("bwd_shared_ws", T=T, n_head=H, n_kv_head=KV, head_dim=d, seed=T)
+        announce(f"backward calls on one workspace: T={T} H={H} KV={KV} d={d}")
+        x = W.make_inputs(w)
+        ref, dout = fwd_bwd(w, x, gpu)
+        dv_ = to_dev(x, gpu)
+        cos, sin = cgr.rope_tables(T, d, w.base, device=gpu)
+        kw = dict(causal=True, rope_style=w.rope_style)
+        o, lse = cgr.gqa_rope_attn_fwd(dv_["q"], dv_["k"], dv_["v"], cos, sin, **kw)
+        got = cgr.gqa_rope_attn_bwd(dv_["q"], dv_["k"], dv_["v"], o, lse, dout.to(gpu), cos, sin, workspace=ws,
+                                    **kw)
+        torch.cuda.synchronize()
+        assert all(torch.equal(a, b) for a, b in zip(got, ref))
+
+
 def test_backward_long_context_full_size(gpu):
     """The long-context workload at full size, in the launch configuration the
     benchmark times: every gradient of two whole K/V groups (the group's 4 query

@@ -381,6 +381,33 @@ def test_rotate_keys_then_rotated_gives_the_same_bits(gpu, T, H, KV, d, causal, 
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("qk", ["f16", "bf16"])
+def test_rotated_calls_share_one_workspace(gpu, qk):
+    """The causal attention over once-rotated keys hands its lightest query
+    blocks out from a counter at the workspace's end: the key rotation zeroes
+    it and each call leaves it at zero. Starting from a workspace of 0xFF
+    bytes, one rotation then three attention calls in a row give the one
+    call's bits every time; then a smaller batch in the same workspace."""
+    H, KV, d = 8, 2, 128
+    big, small = (2, 1000), (1, 333)
+    n = max(cgr.cgr_attn_fwd_workspace_size(B, T, KV, d) for B, T in (big, small))
+    ws = torch.full((n,), 255, dtype=torch.uint8, device=gpu)
+    for B, T in (big, small):
+        w = W.custom("shared_ws", B=B, T=T, n_head=H, n_kv_head=KV, head_dim=d, seed=T)
+        announce(f"rotated calls on one workspace: B={B} T={T} qk={qk}")
+        x = to_dev(W.make_inputs(w), gpu)
+        cos, sin = cgr.rope_tables(T, d, w.base, device=gpu)
+        kw = dict(causal=True, rope_style=w.rope_style, qk_operand=qk)
+        ref_o, ref_l = cgr.gqa_rope_attn_fwd(x["q"], x["k"], x["v"], cos, sin, **kw)
+        cgr.attn_fwd_rotate_keys(x["k"], cos, sin, ws, rope_style=w.rope_style, qk_operand=qk)
+        for _ in range(3):
+            o = torch.full_like(x["q"], 7.0)
+            l = torch.full((B, H, T), 7.0, device=gpu)
+            cgr.gqa_rope_attn_fwd_rotated(x["q"], x["k"], x["v"], cos, sin, ws, out=o, lse=l, **kw)
+            torch.cuda.synchronize()
+            assert torch.equal(o, ref_o) and torch.equal(l, ref_l)
+
+
 @pytest.mark.parametrize("d", [32, 64, 128])
 @pytest.mark.parametrize("qk", ["f16", "bf16"])
 @pytest.mark.parametrize("causal,style", [(True, "interleaved"), (False, "half"), (True, "half")])
