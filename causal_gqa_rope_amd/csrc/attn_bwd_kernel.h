@@ -878,10 +878,12 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   long dkdv_grid = k_units * a.KV * a.hsplit, dq_grid = q_units * (a.H >> a.lhp);
   if (!a.cu_seqlens && C::CAUSAL && !C::WIN) {
-    // Two workgroups for every claimed unit (claim_unit).
+    // Two workgroups for every claimed unit (claim_unit; the placed grid's
+    // own workgroups of those ranks already cover each once).
     const int nK = (a.T + C::BK - 1) / C::BK, nQ = (a.T + (C::BQ >> a.lhp) - 1) / (C::BQ >> a.lhp);
-    if (a.hsplit == 1) dkdv_grid += (long)kfwd_dyn_ranks(nK) * a.B * a.KV;
-    dq_grid += (long)kfwd_dyn_ranks(nQ) * a.B * (a.H >> a.lhp);
+    const long more_k = (long)kfwd_dyn_ranks(nK) * a.B * a.KV, more_q = (long)kfwd_dyn_ranks(nQ) * a.B * (a.H >> a.lhp);
+    if (a.hsplit == 1 && dkdv_grid + more_k <= 0x7fffffffL) dkdv_grid += more_k;
+    if (dq_grid + more_q <= 0x7fffffffL) dq_grid += more_q;
   }
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel<C>, dim3((unsigned)dkdv_grid), dim3(512), 0, stream, a);
   e = hipGetLastError();

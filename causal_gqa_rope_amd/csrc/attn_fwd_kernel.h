@@ -1607,16 +1607,19 @@ enum { PHASE_ROTATE = 1, PHASE_ATTEND = 2, PHASE_ALL = 3 };
 // Dense batch with the K rotation done once up front (a.krot set).
 template <class C>
 hipError_t launch_attn_kpre(const AttnArgs& a, int grid, hipStream_t stream, int phases) {
+  if (C::CAUSAL && !C::WIN) {
+    // Two workgroups for every claimed unit (see attn_fwd_dense_kernel: the
+    // last of the 2 x dyn claims resets the counter, so the count is exact).
+    const int bm = 32 * C::NW / a.hp, nQ = (a.T + bm - 1) / bm;
+    const long more = (long)kfwd_dyn_ranks(nQ) * a.B * (a.H / a.hp);
+    if (grid + more > 0x7fffffffL) return hipErrorInvalidValue;
+    grid += (int)more;
+  }
   if (phases & PHASE_ROTATE) {
     const long items = (long)a.B * ((a.T + C::BN - 1) / C::BN) * C::BN * (C::D / 16);
     hipLaunchKernelGGL((krot_kernel<C>), dim3((unsigned)((items + 255) / 256)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-  }
-  if (C::CAUSAL && !C::WIN) {
-    // Two workgroups for every claimed unit (see attn_fwd_dense_kernel).
-    const int bm = 32 * C::NW / a.hp, nQ = (a.T + bm - 1) / bm;
-    grid += kfwd_dyn_ranks(nQ) * a.B * (a.H / a.hp);
   }
   if (phases & PHASE_ATTEND)
     hipLaunchKernelGGL(attn_fwd_dense_kernel<C>, dim3(grid), dim3(C::THREADS), C::Q_STAGE_BYTES, stream, a);
